@@ -1,0 +1,308 @@
+"""ctypes binding of libcskv.so: argument marshalling only.
+
+Every step of the decode path runs in the library's HIP kernels; this module
+checks tensor devices, dtypes and layouts, passes raw device pointers and the
+current HIP stream, and turns non-zero statuses into exceptions. There is no
+fallback: if the library is missing or fails to load, importing raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcskv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "or `python compressed_sparse_kv_compress_amd/build.py`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
+BF16, F32, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
+C4A, C128A = 0, 1
+KINDS = {"c4a": C4A, "c128a": C128A, C4A: C4A, C128A: C128A}
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+def _sig(name, restype, *argtypes):
+    f = getattr(_lib, name)
+    f.restype = restype
+    f.argtypes = list(argtypes)
+    return f
+
+
+_lib_status_string = _sig("cskv_status_string", ctypes.c_char_p, _i32)
+_lib_last_error = _sig("cskv_last_error", ctypes.c_char_p)
+_lib_version = _sig("cskv_version", _i32)
+_lib_compress = _sig("cskv_compress", _i32, _i32, _p, _p, _i64, _i64, _i32, _i64, _i32, _p, _p, _i64, _p)
+_lib_topk_ws = _sig("cskv_index_topk_workspace", _sz, _i64, _i64, _i32, _i32, _i32, _i32)
+_lib_topk = _sig("cskv_index_topk", _i32, _p, _i32, _p, _p, _p, _i64, _i64, _i32, _i32, _p, _i32, _p, _sz, _p)
+_lib_attend_ws = _sig("cskv_attend_workspace", _sz, _i64, _i32, _i32, _i64, _i32)
+_lib_attend = _sig("cskv_attend", _i32, _p, _i64, _i32, _i32, _i32, _p, _p, _i64, _p, _i32, _p,
+                   _i32, _p, _p, _i32, _i64, _i32, _f32, _p, _f32, _p, _i32, _p, _sz, _p)
+_lib_enc8 = _sig("cskv_encode_fp8_rows", _i32, _i32, _p, _i64, _i32, _p, _p, _p)
+_lib_dec8 = _sig("cskv_decode_fp8_rows", _i32, _p, _p, _i64, _i32, _p, _p)
+_lib_enc4 = _sig("cskv_encode_fp4_g16", _i32, _i32, _p, _i64, _i32, _p, _p, _p)
+_lib_dec4 = _sig("cskv_decode_fp4_g16", _i32, _p, _p, _i64, _i32, _p, _p)
+
+EXPORTS = ["cskv_status_string", "cskv_last_error", "cskv_version", "cskv_compress",
+           "cskv_index_topk_workspace", "cskv_index_topk", "cskv_attend_workspace", "cskv_attend",
+           "cskv_encode_fp8_rows", "cskv_decode_fp8_rows", "cskv_encode_fp4_g16", "cskv_decode_fp4_g16"]
+
+
+class CskvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_lib_status_string(status).decode()}: {message}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != OK:
+        raise CskvError(status, _lib_last_error().decode())
+
+
+def version() -> int:
+    return int(_lib_version())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def _bf16_like(t, name):
+    if t.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise TypeError(f"{name} must hold bf16 bits (bfloat16/uint16/int16), got {t.dtype}")
+
+
+def _dense(t, name):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_workspaces: dict = {}
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    """A zero-initialised scratch buffer per device, grown on demand. Calls on
+    one device are ordered on its current stream, so they can share it."""
+    if nbytes == 0:
+        return None
+    key = torch.device(device).index
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
+    return buf
+
+
+# ------------------------------------------------------------------ compress
+
+def compress(kind, S: torch.Tensor, gate: torch.Tensor, cache: torch.Tensor,
+             cache_scale: torch.Tensor | None = None, first_entry: int = 0) -> int:
+    """Writes the complete entries of the span S [B, T, D] (gate [B, T] fp32)
+    into rows first_entry.. of cache [B, rows, D] (bf16, or uint8 fp8 codes
+    with cache_scale [B, rows] fp32). Returns the number of entries written."""
+    kind = KINDS[kind]
+    _need_cuda(S, gate, cache, cache_scale)
+    _bf16_like(S, "S")
+    _dense(S, "S"); _dense(gate, "gate"); _dense(cache, "cache")
+    B, T, D = S.shape
+    if gate.dtype != torch.float32 or tuple(gate.shape) != (B, T):
+        raise ValueError("gate must be fp32 [B, T]")
+    if cache.dim() != 3 or cache.shape[0] != B or cache.shape[2] != D:
+        raise ValueError("cache must be [B, rows, D]")
+    if cache.dtype == torch.uint8 or cache.dtype == torch.float8_e4m3fn:
+        dt = FP8_E4M3
+        if cache_scale is None or cache_scale.dtype != torch.float32 or tuple(cache_scale.shape) != tuple(cache.shape[:2]):
+            raise ValueError("an fp8 cache needs cache_scale fp32 [B, rows]")
+        _dense(cache_scale, "cache_scale")
+    else:
+        _bf16_like(cache, "cache")
+        dt = BF16
+    _check(_lib_compress(kind, _ptr(S), _ptr(gate), B, T, D, first_entry, dt, _ptr(cache),
+                         _ptr(cache_scale), cache.shape[1], _stream(S.device)))
+    w, s = (8, 4) if kind == C4A else (128, 128)
+    return 0 if T < w else (T - w) // s + 1
+
+
+# ------------------------------------------------------------------ index / top-k
+
+def index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, k: int, k_scale: torch.Tensor | None = None,
+               n_entries: torch.Tensor | None = None, ids: torch.Tensor | None = None,
+               chunk: int = 0) -> torch.Tensor:
+    """ids [B, k] int32 of the best k entries per sequence (ascending, -1 padded).
+    Keys are bf16 [B, N, Di], or fp4 packed uint8 [B, N, Di/2] with k_scale
+    uint8 [B, N, Di/16]."""
+    _need_cuda(q_idx, k_idx, k_scale, n_entries, ids)
+    _bf16_like(q_idx, "q_idx")
+    _dense(q_idx, "q_idx"); _dense(k_idx, "k_idx")
+    B, Di = q_idx.shape
+    if k_scale is None:
+        _bf16_like(k_idx, "k_idx")
+        key_dtype = BF16
+        if k_idx.shape[0] != B or k_idx.shape[2] != Di:
+            raise ValueError("k_idx must be [B, N, Di]")
+    else:
+        key_dtype = FP4_E2M1
+        _dense(k_scale, "k_scale")
+        if k_idx.dtype != torch.uint8 or tuple(k_idx.shape) != (B, k_idx.shape[1], Di // 2):
+            raise ValueError("fp4 k_idx must be uint8 [B, N, Di/2]")
+        if k_scale.dtype != torch.uint8 or tuple(k_scale.shape) != (B, k_idx.shape[1], Di // 16):
+            raise ValueError("k_scale must be uint8 [B, N, Di/16]")
+    N = k_idx.shape[1]
+    if n_entries is not None:
+        _dense(n_entries, "n_entries")
+        if n_entries.dtype != torch.int32 or n_entries.numel() != B:
+            raise ValueError("n_entries must be int32 [B]")
+    if ids is None:
+        ids = torch.empty((B, k), dtype=torch.int32, device=q_idx.device)
+    elif ids.dtype != torch.int32 or tuple(ids.shape) != (B, k) or not ids.is_contiguous():
+        raise ValueError("ids must be contiguous int32 [B, k]")
+    nbytes = _lib_topk_ws(B, N, Di, k, key_dtype, chunk)   # 0 also when the call will reject
+    ws = _workspace(nbytes, q_idx.device)
+    _check(_lib_topk(_ptr(q_idx), key_dtype, _ptr(k_idx), _ptr(k_scale), _ptr(n_entries), B, N, Di, k,
+                     _ptr(ids), chunk, _ptr(ws), 0 if ws is None else ws.numel(), _stream(q_idx.device)))
+    return ids
+
+
+# ------------------------------------------------------------------ attend
+
+def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, window: torch.Tensor | None, *,
+           softmax_scale: float, rope_dims: int = 0, rope_base: float = 10000.0,
+           q_pos: torch.Tensor | None = None, cache_scale: torch.Tensor | None = None,
+           window_scale: torch.Tensor | None = None, n_entries: torch.Tensor | None = None,
+           out: torch.Tensor | None = None, splits: int = 0) -> torch.Tensor:
+    """O [B, H, D] fp32: softmax attention of Q [B, H, D] (bf16) over the cache
+    rows named by ids [B, k] (or all of the first n_entries rows when ids is
+    None) followed by the window rows [B, W, D], then inverse RoPE on the last
+    rope_dims channels at positions q_pos [B] int64. The window may be a view
+    whose last two dimensions are dense (e.g. the tail of a state span)."""
+    _need_cuda(Q, cache, ids, window, q_pos, cache_scale, window_scale, n_entries, out)
+    _bf16_like(Q, "Q")
+    _dense(Q, "Q"); _dense(cache, "cache")
+    B, H, D = Q.shape
+    if cache.dim() != 3 or cache.shape[0] != B or cache.shape[2] != D:
+        raise ValueError("cache must be [B, rows, D]")
+    cache_fp8 = cache.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if cache_fp8:
+        if cache_scale is None or cache_scale.dtype != torch.float32 or tuple(cache_scale.shape) != tuple(cache.shape[:2]):
+            raise ValueError("an fp8 cache needs cache_scale fp32 [B, rows]")
+        _dense(cache_scale, "cache_scale")
+    else:
+        _bf16_like(cache, "cache")
+    k = 0
+    if ids is not None:
+        if ids.dtype != torch.int32 or ids.dim() != 2 or ids.shape[0] != B or not ids.is_contiguous():
+            raise ValueError("ids must be contiguous int32 [B, k]")
+        k = ids.shape[1]
+    if n_entries is not None and (n_entries.dtype != torch.int32 or n_entries.numel() != B):
+        raise ValueError("n_entries must be int32 [B]")
+    W, wstride, win_fp8 = 0, 0, False
+    if window is not None and window.shape[1] > 0:
+        if window.dim() != 3 or window.shape[0] != B or window.shape[2] != D:
+            raise ValueError("window must be [B, W, D]")
+        if window.stride(2) != 1 or window.stride(1) != D or window.stride(0) % D != 0:
+            raise ValueError("window rows must be dense with a whole-row batch stride")
+        W = window.shape[1]
+        wstride = window.stride(0) // D
+        win_fp8 = window.dtype in (torch.uint8, torch.float8_e4m3fn)
+        if win_fp8:
+            if window_scale is None or window_scale.dtype != torch.float32:
+                raise ValueError("an fp8 window needs window_scale fp32 [B, W]")
+            if window_scale.stride(1) != 1 or window_scale.stride(0) != wstride:
+                raise ValueError("window_scale must share the window's batch stride (in rows)")
+        else:
+            _bf16_like(window, "window")
+    else:
+        window = None
+    if rope_dims and (q_pos is None or q_pos.dtype != torch.int64 or q_pos.numel() != B):
+        raise ValueError("rope_dims > 0 needs q_pos int64 [B]")
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float32, device=Q.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, D) or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [B, H, D]")
+    max_keys = (k if ids is not None else cache.shape[1]) + W
+    nbytes = _lib_attend_ws(B, H, D, max_keys, splits)
+    ws = _workspace(nbytes, Q.device)
+    _check(_lib_attend(_ptr(Q), B, H, D, FP8_E4M3 if cache_fp8 else BF16, _ptr(cache), _ptr(cache_scale),
+                       cache.shape[1], _ptr(ids), k, _ptr(n_entries), FP8_E4M3 if win_fp8 else BF16,
+                       _ptr(window), _ptr(window_scale), W, wstride, rope_dims, rope_base, _ptr(q_pos),
+                       softmax_scale, _ptr(out), splits, _ptr(ws), 0 if ws is None else ws.numel(),
+                       _stream(Q.device)))
+    return out
+
+
+# ------------------------------------------------------------------ codecs
+
+def encode_fp8_rows(x: torch.Tensor):
+    """[rows, D] bf16 or fp32 -> (codes uint8 [rows, D], scale fp32 [rows])."""
+    _need_cuda(x)
+    _dense(x, "x")
+    in_dt = F32 if x.dtype == torch.float32 else BF16
+    if in_dt == BF16:
+        _bf16_like(x, "x")
+    rows, D = x.reshape(-1, x.shape[-1]).shape
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check(_lib_enc8(in_dt, _ptr(x), rows, D, _ptr(codes), _ptr(scale), _stream(x.device)))
+    return codes, scale
+
+
+def decode_fp8_rows(codes: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
+    _need_cuda(codes, scale)
+    _dense(codes, "codes"); _dense(scale, "scale")
+    rows, D = codes.reshape(-1, codes.shape[-1]).shape
+    out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+    _check(_lib_dec8(_ptr(codes), _ptr(scale), rows, D, _ptr(out), _stream(codes.device)))
+    return out
+
+
+def encode_fp4_g16(x: torch.Tensor):
+    """[rows, Di] bf16 or fp32 -> (packed uint8 [rows, Di/2], scales uint8 [rows, Di/16])."""
+    _need_cuda(x)
+    _dense(x, "x")
+    in_dt = F32 if x.dtype == torch.float32 else BF16
+    if in_dt == BF16:
+        _bf16_like(x, "x")
+    Di = x.shape[-1]
+    rows = x.numel() // Di
+    packed = torch.empty(x.shape[:-1] + (Di // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (Di // 16,), dtype=torch.uint8, device=x.device)
+    _check(_lib_enc4(in_dt, _ptr(x), rows, Di, _ptr(packed), _ptr(scales), _stream(x.device)))
+    return packed, scales
+
+
+def decode_fp4_g16(packed: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    _need_cuda(packed, scales)
+    _dense(packed, "packed"); _dense(scales, "scales")
+    Di = packed.shape[-1] * 2
+    rows = packed.numel() // (Di // 2)
+    out = torch.empty(packed.shape[:-1] + (Di,), dtype=torch.float32, device=packed.device)
+    _check(_lib_dec4(_ptr(packed), _ptr(scales), rows, Di, _ptr(out), _stream(packed.device)))
+    return out
+
+
+# ------------------------------------------------------------------ raw access (tests, bench)
+
+def raw():
+    """The ctypes handle of libcskv.so, for tests of the C ABI itself."""
+    return _lib

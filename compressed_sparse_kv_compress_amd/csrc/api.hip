@@ -1,0 +1,273 @@
+// C ABI of libcskv: argument validation, launch planning, error reporting.
+// Everything is checked on the host before any kernel is enqueued.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/cskv.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+cskv_status fail(cskv_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+cskv_status ok() {
+  g_err[0] = '\0';
+  return CSKV_OK;
+}
+
+cskv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CSKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define CHECK(cond, status, ...) \
+  do {                           \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* cskv_status_string(cskv_status s) {
+  switch (s) {
+    case CSKV_OK: return "ok";
+    case CSKV_EINVAL: return "invalid argument";
+    case CSKV_EUNSUPPORTED: return "unsupported";
+    case CSKV_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* cskv_last_error(void) { return g_err; }
+
+int32_t cskv_version(void) { return 100; }
+
+// ------------------------------------------------------------------ compress
+
+cskv_status cskv_compress(int32_t kind, const void* S, const float* gate, int64_t B, int64_t T,
+                          int32_t D, int64_t first_entry, int32_t cache_dtype, void* cache,
+                          float* cache_scale, int64_t cache_rows, void* stream) {
+  CHECK(kind == CSKV_C4A || kind == CSKV_C128A, CSKV_EINVAL, "compress: unknown kind %d", kind);
+  CHECK(B >= 0 && T >= 0 && first_entry >= 0 && cache_rows >= 0, CSKV_EINVAL,
+        "compress: negative size (B=%lld T=%lld first_entry=%lld cache_rows=%lld)", (long long)B,
+        (long long)T, (long long)first_entry, (long long)cache_rows);
+  CHECK(D == 128 || D == 512, CSKV_EUNSUPPORTED, "compress: D=%d (supported: 128, 512)", D);
+  CHECK(cache_dtype == CSKV_BF16 || cache_dtype == CSKV_FP8_E4M3, CSKV_EUNSUPPORTED,
+        "compress: cache dtype %d (supported: bf16, fp8)", cache_dtype);
+  const int64_t w = kind == CSKV_C4A ? 8 : 128, s = kind == CSKV_C4A ? 4 : 128;
+  const int64_t n = T < w ? 0 : (T - w) / s + 1;
+  CHECK(first_entry + n <= cache_rows, CSKV_EINVAL,
+        "compress: entries %lld..%lld do not fit cache_rows=%lld", (long long)first_entry,
+        (long long)(first_entry + n - 1), (long long)cache_rows);
+  if (B == 0 || n == 0) return ok();
+  CHECK(S && gate && cache, CSKV_EINVAL, "compress: null S, gate or cache");
+  CHECK(cache_dtype != CSKV_FP8_E4M3 || cache_scale, CSKV_EINVAL, "compress: fp8 cache needs cache_scale");
+  CHECK(aligned(S, 16) && aligned(cache, 16) && aligned(gate, 4), CSKV_EINVAL,
+        "compress: S and cache must be 16-byte aligned");
+  CHECK(B <= 65535, CSKV_EUNSUPPORTED, "compress: B=%lld > 65535", (long long)B);
+  CHECK(kind == CSKV_C4A || n <= 0x7FFFFFFF, CSKV_EUNSUPPORTED, "compress: too many entries");
+  return hip_status(cskv::launch_compress(kind, reinterpret_cast<const uint16_t*>(S), gate, B, T, D,
+                                          n, first_entry, cache_dtype == CSKV_FP8_E4M3, cache,
+                                          cache_scale, cache_rows,
+                                          reinterpret_cast<hipStream_t>(stream)),
+                    "compress launch");
+}
+
+// ------------------------------------------------------------------ index / top-k
+
+static cskv_status topk_common(int64_t B, int64_t n_max, int32_t Di, int32_t k, int32_t key_dtype,
+                               int32_t chunk, cskv::TopkPlan* plan) {
+  CHECK(B >= 0 && n_max >= 0, CSKV_EINVAL, "index_topk: negative size");
+  CHECK(k >= 1, CSKV_EINVAL, "index_topk: k=%d must be >= 1", k);
+  CHECK(k <= 2048, CSKV_EUNSUPPORTED, "index_topk: k=%d > 2048", k);
+  CHECK(Di == 32 || Di == 128, CSKV_EUNSUPPORTED, "index_topk: Di=%d (supported: 32, 128)", Di);
+  CHECK(key_dtype == CSKV_BF16 || key_dtype == CSKV_FP4_E2M1, CSKV_EUNSUPPORTED,
+        "index_topk: key dtype %d (supported: bf16, fp4)", key_dtype);
+  CHECK(chunk == 0 || (chunk >= 256 && chunk <= 16384 && chunk % 256 == 0), CSKV_EINVAL,
+        "index_topk: chunk=%d must be 0 or a multiple of 256 in [256, 16384]", chunk);
+  CHECK(B <= 65535, CSKV_EUNSUPPORTED, "index_topk: B=%lld > 65535", (long long)B);
+  CHECK(n_max <= 0x7FFFFFFF, CSKV_EUNSUPPORTED, "index_topk: n_max too large for int32 ids");
+  CHECK(cskv::plan_topk(B, n_max, k, chunk, plan), CSKV_EUNSUPPORTED,
+        "index_topk: no selection plan for n_max=%lld k=%d chunk=%d", (long long)n_max, k, chunk);
+  return ok();
+}
+
+size_t cskv_index_topk_workspace(int64_t B, int64_t n_max, int32_t Di, int32_t k, int32_t key_dtype,
+                                 int32_t chunk) {
+  cskv::TopkPlan plan;
+  if (topk_common(B, n_max, Di, k, key_dtype, chunk, &plan) != CSKV_OK) return 0;
+  return plan.bytes;
+}
+
+cskv_status cskv_index_topk(const void* q_idx, int32_t key_dtype, const void* k_idx,
+                            const uint8_t* k_scale, const int32_t* n_entries, int64_t B,
+                            int64_t n_max, int32_t Di, int32_t k, int32_t* ids, int32_t chunk,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  cskv::TopkPlan plan;
+  cskv_status st = topk_common(B, n_max, Di, k, key_dtype, chunk, &plan);
+  if (st != CSKV_OK) return st;
+  if (B == 0) return ok();
+  CHECK(q_idx && ids, CSKV_EINVAL, "index_topk: null q_idx or ids");
+  CHECK(n_max == 0 || k_idx, CSKV_EINVAL, "index_topk: null k_idx");
+  CHECK(key_dtype != CSKV_FP4_E2M1 || n_max == 0 || k_scale, CSKV_EINVAL,
+        "index_topk: fp4 keys need k_scale");
+  CHECK(aligned(q_idx, 16) && (k_idx == nullptr || aligned(k_idx, 16)), CSKV_EINVAL,
+        "index_topk: q_idx and k_idx must be 16-byte aligned");
+  CHECK(k_scale == nullptr || aligned(k_scale, 2), CSKV_EINVAL, "index_topk: k_scale must be 2-byte aligned");
+  CHECK(workspace_bytes >= plan.bytes, CSKV_EINVAL,
+        "index_topk: workspace %zu bytes < %zu required", workspace_bytes, plan.bytes);
+  CHECK(plan.bytes == 0 || (workspace && aligned(workspace, 256)), CSKV_EINVAL,
+        "index_topk: workspace must be non-null and 256-byte aligned");
+  return hip_status(cskv::launch_index_topk(plan, reinterpret_cast<const uint16_t*>(q_idx),
+                                            key_dtype == CSKV_FP4_E2M1, k_idx, k_scale, n_entries,
+                                            B, n_max, Di, k, ids, workspace,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                    "index_topk launch");
+}
+
+// ------------------------------------------------------------------ attend
+
+size_t cskv_attend_workspace(int64_t B, int32_t H, int32_t D, int64_t max_keys, int32_t splits) {
+  cskv::AttendPlan plan;
+  if (B < 0 || H < 1 || H > 64 || !(D == 128 || D == 512) || max_keys < 0 || splits < 0) return 0;
+  if (!cskv::plan_attend(B, H, D, max_keys, splits, &plan)) return 0;
+  return plan.bytes;
+}
+
+cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t cache_dtype,
+                        const void* cache, const float* cache_scale, int64_t cache_rows,
+                        const int32_t* ids, int32_t k, const int32_t* n_entries,
+                        int32_t window_dtype, const void* window, const float* window_scale,
+                        int32_t W, int64_t window_batch_stride, int32_t rope_dims,
+                        float rope_base, const int64_t* q_pos, float softmax_scale, float* O,
+                        int32_t splits, void* workspace, size_t workspace_bytes, void* stream) {
+  CHECK(B >= 0 && cache_rows >= 0 && W >= 0, CSKV_EINVAL, "attend: negative size");
+  CHECK(H >= 1 && H <= 64, CSKV_EUNSUPPORTED, "attend: H=%d (supported: 1..64)", H);
+  CHECK(D == 128 || D == 512, CSKV_EUNSUPPORTED, "attend: D=%d (supported: 128, 512)", D);
+  CHECK(cache_dtype == CSKV_BF16 || cache_dtype == CSKV_FP8_E4M3, CSKV_EUNSUPPORTED,
+        "attend: cache dtype %d (supported: bf16, fp8)", cache_dtype);
+  CHECK(window_dtype == CSKV_BF16 || window_dtype == CSKV_FP8_E4M3, CSKV_EUNSUPPORTED,
+        "attend: window dtype %d (supported: bf16, fp8)", window_dtype);
+  CHECK(ids == nullptr || k >= 0, CSKV_EINVAL, "attend: k=%d must be >= 0", k);
+  CHECK(rope_dims >= 0 && rope_dims <= D && rope_dims % 2 == 0, CSKV_EINVAL,
+        "attend: rope_dims=%d must be even and <= D", rope_dims);
+  CHECK(rope_dims == 0 || rope_base > 0.0f, CSKV_EINVAL, "attend: rope_base must be > 0");
+  CHECK(splits >= 0, CSKV_EINVAL, "attend: splits=%d must be >= 0", splits);
+  CHECK(W == 0 || window_batch_stride >= W, CSKV_EINVAL,
+        "attend: window_batch_stride=%lld < W=%d", (long long)window_batch_stride, W);
+  CHECK(B <= 65535, CSKV_EUNSUPPORTED, "attend: B=%lld > 65535", (long long)B);
+  if (B == 0) return ok();
+  CHECK(Q && O, CSKV_EINVAL, "attend: null Q or O");
+  CHECK(rope_dims == 0 || q_pos, CSKV_EINVAL, "attend: rope_dims > 0 needs q_pos");
+  const int64_t n_sel_max = ids ? (int64_t)k : cache_rows;
+  CHECK(n_sel_max == 0 || cache, CSKV_EINVAL, "attend: null cache");
+  CHECK(cache_dtype != CSKV_FP8_E4M3 || n_sel_max == 0 || cache_scale, CSKV_EINVAL,
+        "attend: fp8 cache needs cache_scale");
+  CHECK(W == 0 || window, CSKV_EINVAL, "attend: null window");
+  CHECK(window_dtype != CSKV_FP8_E4M3 || W == 0 || window_scale, CSKV_EINVAL,
+        "attend: fp8 window needs window_scale");
+  CHECK(aligned(Q, 16) && aligned(O, 4) && (!cache || aligned(cache, 16)) &&
+            (!window || aligned(window, 16)),
+        CSKV_EINVAL, "attend: Q, cache and window must be 16-byte aligned");
+  cskv::AttendPlan plan;
+  const int64_t max_keys = n_sel_max + W;
+  CHECK(cskv::plan_attend(B, H, D, max_keys, splits, &plan), CSKV_EUNSUPPORTED, "attend: no plan");
+  CHECK(workspace_bytes >= plan.bytes, CSKV_EINVAL, "attend: workspace %zu bytes < %zu required",
+        workspace_bytes, plan.bytes);
+  CHECK(plan.bytes == 0 || (workspace && aligned(workspace, 256)), CSKV_EINVAL,
+        "attend: workspace must be non-null and 256-byte aligned");
+  cskv::AttendArgs a;
+  a.Q = reinterpret_cast<const uint16_t*>(Q);
+  a.B = B;
+  a.H = H;
+  a.D = D;
+  a.cache_fp8 = cache_dtype == CSKV_FP8_E4M3;
+  a.cache = cache;
+  a.cache_scale = cache_scale;
+  a.cache_rows = cache_rows;
+  a.ids = ids;
+  a.k = ids ? k : 0;
+  a.n_entries = ids ? nullptr : n_entries;
+  a.win_fp8 = window_dtype == CSKV_FP8_E4M3;
+  a.window = window;
+  a.window_scale = window_scale;
+  a.W = W;
+  a.win_bstride = window_batch_stride;
+  a.rope_dims = rope_dims;
+  a.rope_base = rope_base;
+  a.q_pos = q_pos;
+  a.softmax_scale = softmax_scale;
+  a.O = O;
+  return hip_status(cskv::launch_attend(plan, a, workspace, reinterpret_cast<hipStream_t>(stream)),
+                    "attend launch");
+}
+
+// ------------------------------------------------------------------ codecs
+
+cskv_status cskv_encode_fp8_rows(int32_t in_dtype, const void* x, int64_t rows, int32_t D,
+                                 uint8_t* codes, float* scale, void* stream) {
+  CHECK(in_dtype == CSKV_BF16 || in_dtype == CSKV_F32, CSKV_EUNSUPPORTED,
+        "encode_fp8_rows: input dtype %d (supported: bf16, f32)", in_dtype);
+  CHECK(rows >= 0, CSKV_EINVAL, "encode_fp8_rows: negative rows");
+  CHECK(D >= 64 && D <= 1024 && D % 64 == 0, CSKV_EUNSUPPORTED,
+        "encode_fp8_rows: D=%d must be a multiple of 64 in [64, 1024]", D);
+  if (rows == 0) return ok();
+  CHECK(x && codes && scale, CSKV_EINVAL, "encode_fp8_rows: null pointer");
+  CHECK((rows + 3) / 4 <= 0x7FFFFFFF, CSKV_EUNSUPPORTED, "encode_fp8_rows: too many rows");
+  return hip_status(cskv::launch_encode_fp8_rows(in_dtype == CSKV_BF16, x, rows, D, codes, scale,
+                                                 reinterpret_cast<hipStream_t>(stream)),
+                    "encode_fp8_rows launch");
+}
+
+cskv_status cskv_decode_fp8_rows(const uint8_t* codes, const float* scale, int64_t rows, int32_t D,
+                                 float* out, void* stream) {
+  CHECK(rows >= 0 && D >= 1, CSKV_EINVAL, "decode_fp8_rows: bad size");
+  if (rows == 0) return ok();
+  CHECK(codes && scale && out, CSKV_EINVAL, "decode_fp8_rows: null pointer");
+  CHECK((rows * D + 255) / 256 <= 0x7FFFFFFF, CSKV_EUNSUPPORTED, "decode_fp8_rows: too large");
+  return hip_status(cskv::launch_decode_fp8_rows(codes, scale, rows, D, out,
+                                                 reinterpret_cast<hipStream_t>(stream)),
+                    "decode_fp8_rows launch");
+}
+
+cskv_status cskv_encode_fp4_g16(int32_t in_dtype, const void* x, int64_t rows, int32_t Di,
+                                uint8_t* packed, uint8_t* scales, void* stream) {
+  CHECK(in_dtype == CSKV_BF16 || in_dtype == CSKV_F32, CSKV_EUNSUPPORTED,
+        "encode_fp4_g16: input dtype %d (supported: bf16, f32)", in_dtype);
+  CHECK(rows >= 0 && Di >= 16 && Di % 16 == 0, CSKV_EINVAL,
+        "encode_fp4_g16: Di=%d must be a positive multiple of 16", Di);
+  if (rows == 0) return ok();
+  CHECK(x && packed && scales, CSKV_EINVAL, "encode_fp4_g16: null pointer");
+  CHECK(aligned(packed, 8), CSKV_EINVAL, "encode_fp4_g16: packed must be 8-byte aligned");
+  CHECK((rows * (Di / 16) + 255) / 256 <= 0x7FFFFFFF, CSKV_EUNSUPPORTED, "encode_fp4_g16: too large");
+  return hip_status(cskv::launch_encode_fp4_g16(in_dtype == CSKV_BF16, x, rows, Di, packed, scales,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                    "encode_fp4_g16 launch");
+}
+
+cskv_status cskv_decode_fp4_g16(const uint8_t* packed, const uint8_t* scales, int64_t rows,
+                                int32_t Di, float* out, void* stream) {
+  CHECK(rows >= 0 && Di >= 16 && Di % 16 == 0, CSKV_EINVAL,
+        "decode_fp4_g16: Di=%d must be a positive multiple of 16", Di);
+  if (rows == 0) return ok();
+  CHECK(packed && scales && out, CSKV_EINVAL, "decode_fp4_g16: null pointer");
+  CHECK(aligned(packed, 4), CSKV_EINVAL, "decode_fp4_g16: packed must be 4-byte aligned");
+  CHECK((rows * (Di / 2) + 255) / 256 <= 0x7FFFFFFF, CSKV_EUNSUPPORTED, "decode_fp4_g16: too large");
+  return hip_status(cskv::launch_decode_fp4_g16(packed, scales, rows, Di, out,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                    "decode_fp4_g16 launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,165 @@
+// Device-side helpers shared by the gfx950 kernels: number formats, wave
+// reductions, MFMA operand types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cskv {
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- E4M3 (OCP, "FN")
+// sign | 4-bit exponent (bias 7) | 3-bit mantissa; exponent 0 is subnormal;
+// S.1111.111 is NaN; largest finite 448.
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  const uint32_t e = (code >> 3) & 0xFu, m = code & 7u;
+  float mag = (e == 0) ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  if (e == 0xFu && m == 7u) mag = __uint_as_float(0x7FC00000u);
+  return __uint_as_float(__float_as_uint(mag) | ((code & 0x80u) << 24));
+}
+
+// bf16 bit pattern of an E4M3 value (exact: 3 mantissa bits, exponents -9..8).
+__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t code) {
+  return __float_as_uint(e4m3_to_f32(code)) >> 16;
+}
+
+// Nearest E4M3 code, ties to even mantissa, saturating at 448; NaN -> 0x7F.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __uint_as_float(u & 0x7FFFFFFFu);
+  if (a != a) return 0x7Fu;
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0x1p-6f) {
+    // subnormal range: value = m * 2^-9, m = nearest-even integer of a * 2^9
+    // (m == 8 is the smallest normal, which is also code 8)
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    // keep 3 of the 23 fp32 mantissa bits, rounding to nearest even
+    const uint32_t ua = __float_as_uint(a);
+    const uint32_t r = (ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20;
+    code = r - (120u << 3);
+  }
+  return code | sign;
+}
+
+// ---------------------------------------------------------------- E2M1 (OCP MX FP4)
+// sign | 2-bit exponent (bias 1) | 1-bit mantissa; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
+
+__device__ __forceinline__ float e2m1_to_f32(uint32_t code) {
+  // (e,m) placed as a tiny float whose exponent field is e: times 2^126 this is
+  // exactly the E2M1 value, subnormal (e = 0) included.
+  const float mag = __uint_as_float((code & 7u) << 22) * 0x1p126f;
+  return __uint_as_float(__float_as_uint(mag) | ((code & 8u) << 28));
+}
+
+// Nearest E2M1 code, ties to even, saturating at 6; NaN -> 0.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const float a = __uint_as_float(u & 0x7FFFFFFFu);
+  if (a != a) return 0u;
+  const uint32_t mag = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+  return mag | ((u >> 28) & 8u);
+}
+
+// Two packed E2M1 codes (one byte of `word`, selected by SEL) to a bf16 pair;
+// the low nibble lands in the low half. Uses the gfx950 scaled converter with
+// scale 1.
+template <int SEL>
+__device__ __forceinline__ bf16x2_t fp4x2_to_bf16x2(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, SEL);
+}
+
+// ---------------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// DPP controls (GFX9): quad permutations and rotations within a row of 16 lanes.
+constexpr int kDppQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;   // row_ror:4
+constexpr int kDppRowRor8 = 0x128;   // row_ror:8
+
+// Sum over each aligned group of 4 lanes (every lane of the group gets it).
+__device__ __forceinline__ float sum_quad(float v) {
+  v += dpp_f32<kDppQuadSwap1>(v);
+  v += dpp_f32<kDppQuadSwap2>(v);
+  return v;
+}
+
+// Sum over each row of 16 lanes (every lane of the row gets it).
+__device__ __forceinline__ float sum_row16(float v) {
+  v = sum_quad(v);
+  v += dpp_f32<kDppRowRor4>(v);
+  v += dpp_f32<kDppRowRor8>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Inclusive prefix sum over the wave (lane 0 first).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (lane_id() >= o) v += t;
+  }
+  return v;
+}
+
+// Orderable key of a score: larger score -> larger key; -0 equals +0; NaN -> 0
+// (below every number, -inf included).
+__device__ __forceinline__ uint32_t score_key(float s) {
+  if (s != s) return 0u;
+  s = s + 0.0f;  // -0 + +0 = +0 under round-to-nearest
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace cskv

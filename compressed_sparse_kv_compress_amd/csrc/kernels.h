@@ -1,0 +1,77 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+// Every launcher assumes its arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace cskv {
+
+// ---- compress.hip
+hipError_t launch_compress(int kind, const uint16_t* S, const float* gate, int64_t B, int64_t T,
+                           int D, int64_t n, int64_t first_entry, bool fp8, void* cache,
+                           float* cache_scale, int64_t cache_rows, hipStream_t stream);
+
+// ---- index_topk.hip
+// Plan of the selection tree: level 0 scores `chunk` entries per workgroup and
+// keeps each chunk's best k; every further level merges up to `fanin` lists
+// into one until a single list per sequence remains.
+struct TopkPlan {
+  int64_t chunk;         // entries per level-0 workgroup
+  int64_t lists[8];      // lists per sequence produced by level i (lists[0] = chunks)
+  int levels;            // number of levels (the last one yields 1 list)
+  int fanin;             // lists merged per workgroup above level 0
+  size_t bytes;          // workspace bytes
+  size_t off_key[8], off_idx[8], off_cnt[8];
+};
+bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, TopkPlan* plan);
+hipError_t launch_index_topk(const TopkPlan& plan, const uint16_t* q_idx, bool fp4,
+                             const void* k_idx, const uint8_t* k_scale, const int32_t* n_entries,
+                             int64_t B, int64_t n_max, int Di, int k, int32_t* ids,
+                             void* workspace, hipStream_t stream);
+
+// ---- attend.hip
+struct AttendPlan {
+  int splits;            // key-row splits per sequence
+  int64_t keys_per_split;
+  size_t bytes;          // workspace bytes (partials), 0 when splits == 1
+};
+bool plan_attend(int64_t B, int H, int D, int64_t max_keys, int splits_hint, AttendPlan* plan);
+struct AttendArgs {
+  const uint16_t* Q;
+  int64_t B;
+  int H, D;
+  bool cache_fp8;
+  const void* cache;
+  const float* cache_scale;
+  int64_t cache_rows;
+  const int32_t* ids;
+  int k;
+  const int32_t* n_entries;
+  bool win_fp8;
+  const void* window;
+  const float* window_scale;
+  int W;
+  int64_t win_bstride;
+  int rope_dims;
+  float rope_base;
+  const int64_t* q_pos;
+  float softmax_scale;
+  float* O;
+};
+hipError_t launch_attend(const AttendPlan& plan, const AttendArgs& a, void* workspace,
+                         hipStream_t stream);
+
+// ---- codec.hip
+hipError_t launch_encode_fp8_rows(bool in_bf16, const void* x, int64_t rows, int D,
+                                  uint8_t* codes, float* scale, hipStream_t stream);
+hipError_t launch_decode_fp8_rows(const uint8_t* codes, const float* scale, int64_t rows, int D,
+                                  float* out, hipStream_t stream);
+hipError_t launch_encode_fp4_g16(bool in_bf16, const void* x, int64_t rows, int Di,
+                                 uint8_t* packed, uint8_t* scales, hipStream_t stream);
+hipError_t launch_decode_fp4_g16(const uint8_t* packed, const uint8_t* scales, int64_t rows,
+                                 int Di, float* out, hipStream_t stream);
+
+}  // namespace cskv

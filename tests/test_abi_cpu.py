@@ -1,0 +1,117 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, sizes workspaces, and rejects bad arguments on the host
+before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cskv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from compressed_sparse_kv_compress_amd import _lib
+    return _lib
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cskv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib._lib, n), n
+    assert sorted(lib.EXPORTS) == names
+
+
+def test_version_and_status_strings(lib):
+    assert lib.version() == 100
+    assert lib._lib_status_string(-1) == b"invalid argument"
+    assert lib._lib_status_string(0) == b"ok"
+
+
+def test_topk_workspace_sizes(lib):
+    # 32 x 32767 entries, k = 512: 2048-entry chunks, one merge level
+    ws = lib._lib_topk_ws(32, 32767, 128, 512, lib.BF16, 0)
+    lists = -(-32767 // 2048)
+    assert ws >= 32 * lists * 512 * 8 and ws < 32 * lists * 512 * 8 + 32 * lists * 4 + 4096
+    # one chunk covers everything: no workspace
+    assert lib._lib_topk_ws(1, 511, 32, 64, lib.BF16, 0) == 0
+    # rejected shapes report 0
+    assert lib._lib_topk_ws(1, 100, 64, 8, lib.BF16, 0) == 0
+    assert lib._lib_topk_ws(1, 100, 128, 4096, lib.BF16, 0) == 0
+
+
+def test_attend_workspace_sizes(lib):
+    assert lib._lib_attend_ws(8, 64, 512, 640, 1) == 0
+    assert lib._lib_attend_ws(8, 64, 512, 640, 4) == 8 * 4 * 64 * (512 + 2) * 4
+    assert lib._lib_attend_ws(8, 64, 384, 640, 4) == 0           # unsupported D
+
+
+def test_compress_validation(lib):
+    p = ctypes.c_void_p(16)           # never dereferenced: every call below is rejected first
+    assert lib._lib_compress(7, p, p, 1, 64, 512, 0, lib.BF16, p, None, 100, None) == lib.EINVAL
+    assert lib._lib_compress(0, p, p, 1, 64, 384, 0, lib.BF16, p, None, 100, None) == lib.EUNSUPPORTED
+    assert lib._lib_compress(0, p, p, 1, 64, 512, 0, lib.BF16, p, None, 10, None) == lib.EINVAL   # 15 entries
+    assert b"do not fit" in lib._lib_last_error()
+    assert lib._lib_compress(0, None, p, 1, 64, 512, 0, lib.BF16, p, None, 100, None) == lib.EINVAL
+    assert lib._lib_compress(0, p, p, 1, 64, 512, 0, lib.FP8_E4M3, p, None, 100, None) == lib.EINVAL
+    assert lib._lib_compress(0, ctypes.c_void_p(18), p, 1, 64, 512, 0, lib.BF16, p, None, 100, None) == lib.EINVAL
+    # nothing to do is not an error
+    assert lib._lib_compress(0, None, None, 1, 7, 512, 0, lib.BF16, None, None, 0, None) == lib.OK
+    assert lib._lib_compress(1, None, None, 0, 4096, 512, 0, lib.BF16, None, None, 32, None) == lib.OK
+
+
+def test_topk_validation(lib):
+    p = ctypes.c_void_p(256)
+    f = lib._lib_topk
+    assert f(p, lib.BF16, p, None, None, 1, 100, 128, 0, p, 0, None, 0, None) == lib.EINVAL          # k = 0
+    assert f(p, lib.BF16, p, None, None, 1, 100, 128, 4096, p, 0, None, 0, None) == lib.EUNSUPPORTED
+    assert f(p, lib.BF16, p, None, None, 1, 100, 96, 8, p, 0, None, 0, None) == lib.EUNSUPPORTED      # Di
+    assert f(p, lib.FP4_E2M1, p, None, None, 1, 100, 128, 8, p, 0, None, 0, None) == lib.EINVAL       # no scales
+    assert f(p, lib.BF16, p, None, None, 1, 100, 128, 8, p, 100, None, 0, None) == lib.EINVAL         # chunk
+    assert f(None, lib.BF16, p, None, None, 1, 100, 128, 8, p, 0, None, 0, None) == lib.EINVAL
+    # too small a workspace
+    assert f(p, lib.BF16, p, None, None, 4, 100000, 128, 512, p, 0, p, 16, None) == lib.EINVAL
+    assert b"workspace" in lib._lib_last_error()
+
+
+def test_attend_validation(lib):
+    p = ctypes.c_void_p(256)
+    f = lib._lib_attend
+
+    def call(**kw):
+        a = dict(Q=p, B=1, H=64, D=512, cdt=lib.BF16, cache=p, cs=None, rows=10, ids=p, k=4, ne=None,
+                 wdt=lib.BF16, win=p, ws_=None, W=4, wst=4, R=64, base=10000.0, pos=p, tau=0.1, O=p,
+                 splits=1, work=None, wsb=0, stream=None)
+        a.update(kw)
+        return f(*a.values())
+
+    # only calls rejected on the host are made here (a valid one would launch)
+    assert call(H=65) == lib.EUNSUPPORTED
+    assert call(D=256) == lib.EUNSUPPORTED
+    assert call(R=63) == lib.EINVAL
+    assert call(R=1024) == lib.EINVAL
+    assert call(wst=3) == lib.EINVAL
+    assert call(cdt=lib.FP8_E4M3) == lib.EINVAL            # fp8 cache without scales
+    assert call(wdt=lib.FP8_E4M3) == lib.EINVAL
+    assert call(pos=None) == lib.EINVAL
+    assert call(Q=ctypes.c_void_p(8)) == lib.EINVAL        # misaligned
+    assert call(k=4000, splits=4, work=None, wsb=0) == lib.EINVAL  # needs a workspace
+    assert call(B=0) == lib.OK
+
+
+def test_codec_validation(lib):
+    p = ctypes.c_void_p(256)
+    assert lib._lib_enc8(lib.BF16, p, 4, 100, p, p, None) == lib.EUNSUPPORTED
+    assert lib._lib_enc8(lib.FP8_E4M3, p, 4, 128, p, p, None) == lib.EUNSUPPORTED
+    assert lib._lib_enc4(lib.F32, p, 4, 24, p, p, None) == lib.EINVAL
+    assert lib._lib_dec4(p, p, 4, 24, p, None) == lib.EINVAL
+    assert lib._lib_enc8(lib.F32, None, 0, 128, None, None, None) == lib.OK

@@ -1,0 +1,129 @@
+"""attend parity: GPU output against the oracle's float64 attention + inverse
+RoPE on identical input bytes (row-relative <= 2e-2 bf16, <= 6e-2 fp8)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats as F
+from oracle import method as M
+from tests.helpers import row_rel_err, sorted_ids, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cskv():
+    import compressed_sparse_kv_compress_amd as m
+    return m
+
+
+def _bf16(seed, tensor, shape):
+    return synth.normal_bf16(synth.stream_key(seed, tensor), 0, int(np.prod(shape))).reshape(shape)
+
+
+def _oracle(Q, cache, ids, win, tau, R, base, pos, n_entries=None):
+    B = Q.shape[0]
+    return np.stack([M.attend(Q[b], cache[b], None if ids is None else ids[b],
+                              None if win is None else win[b], tau, R, base, pos[b],
+                              None if n_entries is None else int(n_entries[b])) for b in range(B)])
+
+
+@pytest.mark.parametrize("B,H,D,N,k,W,R", [
+    (1, 8, 128, 511, 64, 32, 32),      # the tiny workload's shape
+    (3, 64, 512, 3000, 512, 128, 64),  # the c4a layer shape
+    (2, 20, 512, 900, 100, 7, 0),      # heads not a multiple of 16, no rotation
+    (2, 64, 128, 300, 37, 0, 16),      # no window
+])
+def test_sparse_bf16_matches_oracle(cskv, B, H, D, N, k, W, R):
+    seed = B * 100 + H
+    Q = _bf16(seed, synth.T_Q, (B, H, D))
+    cache = _bf16(seed, synth.T_CACHE, (B, N, D))
+    win = _bf16(seed, synth.T_WIN, (B, W, D))
+    rng = np.random.default_rng(seed)
+    ids = np.stack([sorted_ids(rng, N, k, n_valid=k - (3 if b == 1 else 0)) for b in range(B)])
+    pos = np.array([1000 + 977 * b for b in range(B)], dtype=np.int64)
+    tau = 1 / np.sqrt(D)
+    ref = _oracle(F.bf16_to_f64(Q), F.bf16_to_f64(cache), ids, F.bf16_to_f64(win), tau, R, 10000.0, pos)
+    for splits in (0, 1, 3):
+        O = cskv.attend(to_dev_bf16(Q), to_dev_bf16(cache), to_dev(ids), to_dev_bf16(win) if W else None,
+                        softmax_scale=tau, rope_dims=R, q_pos=to_dev(pos), splits=splits)
+        err = row_rel_err(O.cpu().numpy(), ref)
+        assert err <= 2e-2, (splits, err)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 5, 40])
+def test_dense_bf16_matches_oracle(cskv, splits):
+    B, H, D, N, W, R = 3, 64, 512, 1500, 128, 64
+    Q = _bf16(1, synth.T_Q, (B, H, D))
+    cache = _bf16(1, synth.T_CACHE, (B, N, D))
+    win = _bf16(1, synth.T_WIN, (B, W, D))
+    nv = np.array([1500, 33, 0], dtype=np.int32)
+    pos = np.array([(1 << 20) - 1, 5, 0], dtype=np.int64)
+    tau = 1 / np.sqrt(D)
+    ref = _oracle(F.bf16_to_f64(Q), F.bf16_to_f64(cache), None, F.bf16_to_f64(win), tau, R, 10000.0, pos, nv)
+    O = cskv.attend(to_dev_bf16(Q), to_dev_bf16(cache), None, to_dev_bf16(win), softmax_scale=tau,
+                    rope_dims=R, q_pos=to_dev(pos), n_entries=to_dev(nv), splits=splits)
+    assert row_rel_err(O.cpu().numpy(), ref) <= 2e-2
+
+
+def test_fp8_cache_and_window_match_oracle(cskv):
+    B, H, D, N, k, W, R = 2, 64, 512, 2000, 512, 128, 64
+    seed = 44
+    Q = _bf16(seed, synth.T_Q, (B, H, D))
+    cc = synth.fp8_codes(synth.stream_key(seed, synth.T_CACHE), 0, B * N * D).reshape(B, N, D)
+    cs = synth.pos_scale(synth.stream_key(seed, synth.T_CACHE_SCALE), 0, B * N).reshape(B, N)
+    wc = synth.fp8_codes(synth.stream_key(seed, synth.T_WIN), 0, B * W * D).reshape(B, W, D)
+    wsc = synth.pos_scale(synth.stream_key(seed, synth.T_WIN_SCALE), 0, B * W).reshape(B, W)
+    rng = np.random.default_rng(seed)
+    ids = np.stack([sorted_ids(rng, N, k) for _ in range(B)])
+    pos = np.array([123456, 7], dtype=np.int64)
+    tau = 1 / np.sqrt(D)
+    ref = _oracle(F.bf16_to_f64(Q), F.decode_fp8_rows(cc, cs), ids, F.decode_fp8_rows(wc, wsc), tau, R,
+                  10000.0, pos)
+    for splits in (0, 1):
+        O = cskv.attend(to_dev_bf16(Q), to_dev(cc), to_dev(ids), to_dev(wc), cache_scale=to_dev(cs),
+                        window_scale=to_dev(wsc), softmax_scale=tau, rope_dims=R, q_pos=to_dev(pos),
+                        splits=splits)
+        assert row_rel_err(O.cpu().numpy(), ref) <= 6e-2
+
+
+def test_window_is_a_view_into_a_span(cskv):
+    B, H, D, N, k, T, W = 2, 64, 512, 600, 64, 132, 128
+    Q = _bf16(2, synth.T_Q, (B, H, D))
+    cache = _bf16(2, synth.T_CACHE, (B, N, D))
+    span = _bf16(2, synth.T_S, (B, T, D))
+    rng = np.random.default_rng(2)
+    ids = np.stack([sorted_ids(rng, N, k) for _ in range(B)])
+    pos = np.array([5000, 6000], dtype=np.int64)
+    span_d = to_dev_bf16(span)
+    O = cskv.attend(to_dev_bf16(Q), to_dev_bf16(cache), to_dev(ids), span_d[:, T - W:, :],
+                    softmax_scale=0.05, rope_dims=64, q_pos=to_dev(pos))
+    ref = _oracle(F.bf16_to_f64(Q), F.bf16_to_f64(cache), ids, F.bf16_to_f64(span[:, T - W:]), 0.05, 64,
+                  10000.0, pos)
+    assert row_rel_err(O.cpu().numpy(), ref) <= 2e-2
+
+
+def test_empty_key_sets(cskv):
+    B, H, D = 2, 16, 128
+    Q = to_dev_bf16(_bf16(3, synth.T_Q, (B, H, D)))
+    cache = to_dev_bf16(_bf16(3, synth.T_CACHE, (B, 10, D)))
+    ids = torch.full((B, 4), -1, dtype=torch.int32, device="cuda")
+    O = cskv.attend(Q, cache, ids, None, softmax_scale=0.1)
+    assert torch.all(O == 0)
+    win = _bf16(3, synth.T_WIN, (B, 5, D))
+    O = cskv.attend(Q, cache, ids, to_dev_bf16(win), softmax_scale=0.1).cpu().numpy()
+    ref = np.stack([M.attention(F.bf16_to_f64(_bf16(3, synth.T_Q, (B, H, D))[b]), F.bf16_to_f64(win[b]), 0.1)
+                    for b in range(B)])
+    assert row_rel_err(O, ref) <= 2e-2
+
+
+def test_attend_deterministic(cskv):
+    B, H, D, N = 2, 64, 512, 5000
+    Q = to_dev_bf16(_bf16(4, synth.T_Q, (B, H, D)))
+    cache = to_dev_bf16(_bf16(4, synth.T_CACHE, (B, N, D)))
+    win = to_dev_bf16(_bf16(4, synth.T_WIN, (B, 128, D)))
+    pos = torch.tensor([1, 2], dtype=torch.int64, device="cuda")
+    a = cskv.attend(Q, cache, None, win, softmax_scale=0.04, rope_dims=64, q_pos=pos).cpu().numpy()
+    b = cskv.attend(Q, cache, None, win, softmax_scale=0.04, rope_dims=64, q_pos=pos).cpu().numpy()
+    assert np.array_equal(a, b)

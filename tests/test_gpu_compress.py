@@ -1,0 +1,114 @@
+"""compress parity: GPU entries against the oracle's float64 entries on the
+same input bytes (row-relative error <= 2e-2 for bf16, <= 6e-2 for fp8)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats as F
+from oracle import method as M
+from tests.helpers import bf16_f64, row_rel_err, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cskv():
+    import compressed_sparse_kv_compress_amd as m
+    return m
+
+
+def _inputs(seed, B, T, D, gate_scale=1.0):
+    kS = synth.stream_key(seed, synth.T_S)
+    kG = synth.stream_key(seed, synth.T_GATE)
+    S = synth.normal_bf16(kS, 0, B * T * D).reshape(B, T, D)
+    g = (synth.normal_f32(kG, 0, B * T) * np.float32(gate_scale)).reshape(B, T)
+    return S, g
+
+
+@pytest.mark.parametrize("kind,B,T,D", [("c4a", 3, 1030, 128), ("c4a", 2, 2054, 512), ("c4a", 1, 8, 512),
+                                        ("c128a", 2, 1000, 512), ("c128a", 3, 384, 128)])
+def test_compress_bf16_matches_oracle(cskv, kind, B, T, D):
+    S, g = _inputs(11 + T, B, T, D, gate_scale=2.0)
+    n = M.entry_count(kind, T)
+    rows = n + 5
+    cache = torch.full((B, rows, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    assert cskv.compress(kind, to_dev_bf16(S), to_dev(g), cache) == n
+    got = bf16_f64(cache)
+    for b in range(B):
+        ref = M.compress(kind, F.bf16_to_f64(S[b]), g[b].astype(np.float64))
+        err = row_rel_err(got[b, :n], ref)
+        assert err <= 2e-2, err
+        assert err <= 4e-3          # bf16 rounding of the entry dominates
+        assert np.all(got[b, n:] == 7.0), "rows past the last complete window were written"
+
+
+@pytest.mark.parametrize("kind,D", [("c4a", 512), ("c4a", 128), ("c128a", 512)])
+def test_compress_fp8_matches_oracle(cskv, kind, D):
+    B, T = 2, 1024 if kind == "c4a" else 1280
+    S, g = _inputs(29, B, T, D)
+    n = M.entry_count(kind, T)
+    codes = torch.zeros((B, n, D), dtype=torch.uint8, device="cuda")
+    scale = torch.zeros((B, n), dtype=torch.float32, device="cuda")
+    cskv.compress(kind, to_dev_bf16(S), to_dev(g), codes, scale)
+    c, s = codes.cpu().numpy(), scale.cpu().numpy()
+    flips = 0
+    for b in range(B):
+        ref = M.compress(kind, F.bf16_to_f64(S[b]), g[b].astype(np.float64))
+        dec = F.decode_fp8_rows(c[b], s[b])
+        assert row_rel_err(dec, ref) <= 6e-2
+        # the encoder itself: the oracle encoding of the oracle rows differs at most by
+        # one code step where the two fp32 sums round differently near a boundary
+        rc, rs = F.encode_fp8_rows(ref.astype(np.float32))
+        np.testing.assert_allclose(s[b], rs, rtol=1e-5)
+        flips += int(np.sum(rc != c[b]))
+    assert flips <= 0.01 * c.size
+
+
+def test_compress_span_continues_a_sequence(cskv):
+    """Compressing a later span (with its carried states) yields the same
+    entries as compressing the whole sequence: decode-time appends."""
+    B, D, L = 2, 512, 4096
+    S, g = _inputs(5, B, L, D)
+    full4 = np.stack([M.compress("c4a", F.bf16_to_f64(S[b]), g[b].astype(np.float64)) for b in range(B)])
+    n4 = full4.shape[1]
+    cache = torch.zeros((B, n4, D), dtype=torch.bfloat16, device="cuda")
+    # prefix: first L-128 states; span: 4 carried + 128 new states
+    cskv.compress("c4a", to_dev_bf16(S[:, : L - 128].copy()), to_dev(g[:, : L - 128].copy()), cache)
+    first = (L - 128 - 4) // 4
+    span = S[:, L - 132:].copy()
+    wrote = cskv.compress("c4a", to_dev_bf16(span), to_dev(g[:, L - 132:].copy()), cache, first_entry=first)
+    assert wrote == 32 and first + wrote == n4
+    assert row_rel_err(bf16_f64(cache), full4) <= 4e-3
+    full128 = np.stack([M.compress("c128a", F.bf16_to_f64(S[b]), g[b].astype(np.float64)) for b in range(B)])
+    c128 = torch.zeros((B, L // 128, D), dtype=torch.bfloat16, device="cuda")
+    cskv.compress("c128a", to_dev_bf16(S[:, : L - 128].copy()), to_dev(g[:, : L - 128].copy()), c128)
+    cskv.compress("c128a", to_dev_bf16(S[:, L - 128:].copy()), to_dev(g[:, L - 128:].copy()), c128,
+                  first_entry=L // 128 - 1)
+    assert row_rel_err(bf16_f64(c128), full128) <= 4e-3
+
+
+def test_compress_short_span_writes_nothing(cskv):
+    S, g = _inputs(3, 1, 7, 128)
+    cache = torch.full((1, 4, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    assert cskv.compress("c4a", to_dev_bf16(S), to_dev(g), cache) == 0
+    assert cskv.compress("c128a", to_dev_bf16(S), to_dev(g), cache) == 0
+    torch.cuda.synchronize()
+    assert torch.all(cache == 3.0)
+
+
+def test_compress_rejects_overflowing_cache(cskv):
+    S, g = _inputs(3, 1, 64, 128)
+    cache = torch.zeros((1, 10, 128), dtype=torch.bfloat16, device="cuda")   # needs 15 rows
+    with pytest.raises(cskv.CskvError):
+        cskv.compress("c4a", to_dev_bf16(S), to_dev(g), cache)
+
+
+def test_compress_deterministic(cskv):
+    S, g = _inputs(9, 2, 2048, 512)
+    outs = []
+    for _ in range(2):
+        cache = torch.zeros((2, 511, 512), dtype=torch.bfloat16, device="cuda")
+        cskv.compress("c4a", to_dev_bf16(S), to_dev(g), cache)
+        outs.append(cache.view(torch.int16).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
