@@ -1,0 +1,458 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the compressed sparse KV attention path on one MI355X.
+
+One step = one decode token for every sequence of the batch through one layer:
+index_topk (indexer scores + exact top-512) and attend (gather attention over
+the selected c4a entries + the 128-row window, inverse RoPE) for c4a layers;
+attend alone (dense over every entry + window) for c128a layers; the 61-layer
+workload also compresses each layer's 128 new states first. Inputs are
+synthetic, generated on the device, and resident in HBM before timing starts;
+caches are built by the library's own compress kernel. Timed steps rotate over
+several disjoint input sets so that the 256 MB last-level cache cannot serve
+them.
+
+Prints one JSON line: decode tokens/s per layer (whole batch / step time), the
+achieved HBM bandwidth of the dominant kernel call against the 8 TB/s peak, and
+the CPU oracle's rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4a_128k_bf16",
+                    choices=["c4a_128k_bf16", "c128a_1m_bf16", "c4a_1m_fp8_fp4", "mixed61_256k_bf16", "tiny_c4a_2k"])
+    ap.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0 = automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--chunk", type=int, default=0, help="index_topk chunk override")
+    ap.add_argument("--splits", type=int, default=0, help="attend splits override")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ workloads
+
+class Workload:
+    """Device inputs for one or more sets, a step function and byte accounting."""
+
+    def __init__(self, cfg, args, torch, cskv, sd, synth):
+        self.cfg, self.args, self.torch, self.cskv, self.sd, self.synth = cfg, args, torch, cskv, sd, synth
+        self.dev = torch.device("cuda:0")
+
+    def key(self, set_i, tensor, layer=0):
+        return self.synth.stream_key(self.cfg.seed + 1000 * set_i, tensor, layer)
+
+
+class C4aLayer(Workload):
+    """One c4a layer: index_topk over every entry, then sparse attend."""
+
+    def setup(self, n_sets):
+        torch, cskv, sd, s = self.torch, self.cskv, self.sd, self.synth
+        c = self.cfg
+        B, L, D, H, Di, W = c.B, c.L, c.D, c.H, c.Di, c.W
+        N = c.n_entries
+        fp8 = c.cache_dtype == "fp8"
+        fp4 = c.key_dtype == "fp4"
+        self.sets = []
+        for i in range(n_sets):
+            log(f"setup: c4a input set {i + 1}/{n_sets}")
+            st = {}
+            cache = torch.empty((B, N, D), dtype=torch.uint8 if fp8 else torch.bfloat16, device=self.dev)
+            cscale = torch.empty((B, N), dtype=torch.float32, device=self.dev) if fp8 else None
+            win = torch.empty((B, W, D), dtype=torch.uint8 if fp8 else torch.bfloat16, device=self.dev)
+            wscale = torch.empty((B, W), dtype=torch.float32, device=self.dev) if fp8 else None
+            # the cache is compressed from the states, one sequence at a time (bounded scratch)
+            for b in range(B):
+                S = torch.empty((1, L, D), dtype=torch.bfloat16, device=self.dev)
+                g = torch.empty((1, L), dtype=torch.float32, device=self.dev)
+                sd.fill(S, s.KIND_NORMAL_BF16, self.key(i, s.T_S), offset=b * L * D)
+                sd.fill(g, s.KIND_NORMAL_F32, self.key(i, s.T_GATE), offset=b * L)
+                cskv.compress("c4a", S, g, cache[b:b + 1], None if cscale is None else cscale[b:b + 1])
+                tail = S[0, L - W:].contiguous()
+                if fp8:
+                    wc, ws_ = cskv.encode_fp8_rows(tail)
+                    win[b].copy_(wc)
+                    wscale[b].copy_(ws_)
+                else:
+                    win[b].copy_(tail)
+                del S, g
+            if fp4:
+                kidx = sd.new((B, N, Di // 2), s.KIND_BYTES, self.key(i, s.T_KIDX), device=self.dev)
+                kscale = sd.new((B, N, Di // 16), s.KIND_POW2_E4M3, self.key(i, s.T_KIDX_SCALE), device=self.dev,
+                                emin=-2, emax=2)
+            else:
+                kidx = sd.new((B, N, Di), s.KIND_INT_BF16, self.key(i, s.T_KIDX), device=self.dev, a=c.idx_range)
+                kscale = None
+            st.update(cache=cache, cscale=cscale, win=win, wscale=wscale, kidx=kidx, kscale=kscale,
+                      qidx=sd.new((B, Di), s.KIND_INT_BF16, self.key(i, s.T_QIDX), device=self.dev, a=c.idx_range),
+                      Q=sd.new((B, H, D), s.KIND_NORMAL_BF16, self.key(i, s.T_Q), device=self.dev),
+                      ids=torch.empty((B, c.k), dtype=torch.int32, device=self.dev),
+                      O=torch.empty((B, H, D), dtype=torch.float32, device=self.dev),
+                      pos=torch.full((B,), c.q_pos, dtype=torch.int64, device=self.dev))
+            self.sets.append(st)
+        torch.cuda.synchronize()
+
+    def dominant(self, st):
+        self.cskv.index_topk(st["qidx"], st["kidx"], self.cfg.k, k_scale=st["kscale"], ids=st["ids"],
+                             chunk=self.args.chunk)
+
+    def rest(self, st):
+        c = self.cfg
+        self.cskv.attend(st["Q"], st["cache"], st["ids"], st["win"], cache_scale=st["cscale"],
+                         window_scale=st["wscale"], softmax_scale=c.tau, rope_dims=c.R, rope_base=c.rope_base,
+                         q_pos=st["pos"], out=st["O"], splits=self.args.splits)
+
+    def bytes(self):
+        c = self.cfg
+        N = c.n_entries
+        key_b = (c.Di // 2 + c.Di // 16) if c.key_dtype == "fp4" else c.Di * 2
+        row_b = (c.D + 4) if c.cache_dtype == "fp8" else c.D * 2
+        dom = c.B * (N * key_b + c.Di * 2 + c.k * 4)
+        rest = c.B * ((c.k + c.W) * row_b + c.k * 4 + c.H * c.D * 2 + c.H * c.D * 4)
+        return dom, rest
+
+    def flops(self):
+        c = self.cfg
+        return c.B * (2 * c.n_entries * c.Di + 4 * c.H * c.D * (c.k + c.W))
+
+
+class C128aLayer(Workload):
+    """One c128a layer: dense attend over every entry plus the window."""
+
+    def setup(self, n_sets):
+        torch, cskv, sd, s = self.torch, self.cskv, self.sd, self.synth
+        c = self.cfg
+        B, L, D, H, W = c.B, c.L, c.D, c.H, c.W
+        N = c.n_entries
+        self.sets = []
+        for i in range(n_sets):
+            log(f"setup: c128a input set {i + 1}/{n_sets}")
+            cache = torch.empty((B, N, D), dtype=torch.bfloat16, device=self.dev)
+            win = torch.empty((B, W, D), dtype=torch.bfloat16, device=self.dev)
+            for b in range(B):
+                S = torch.empty((1, L, D), dtype=torch.bfloat16, device=self.dev)
+                g = torch.empty((1, L), dtype=torch.float32, device=self.dev)
+                sd.fill(S, s.KIND_NORMAL_BF16, self.key(i, s.T_S), offset=b * L * D)
+                sd.fill(g, s.KIND_NORMAL_F32, self.key(i, s.T_GATE), offset=b * L)
+                cskv.compress("c128a", S, g, cache[b:b + 1])
+                win[b].copy_(S[0, L - W:])
+                del S, g
+            self.sets.append(dict(cache=cache, win=win,
+                                  Q=sd.new((B, H, D), s.KIND_NORMAL_BF16, self.key(i, s.T_Q), device=self.dev),
+                                  O=torch.empty((B, H, D), dtype=torch.float32, device=self.dev),
+                                  pos=torch.full((B,), c.q_pos, dtype=torch.int64, device=self.dev)))
+        torch.cuda.synchronize()
+
+    def dominant(self, st):
+        c = self.cfg
+        self.cskv.attend(st["Q"], st["cache"], None, st["win"], softmax_scale=c.tau, rope_dims=c.R,
+                         rope_base=c.rope_base, q_pos=st["pos"], out=st["O"], splits=self.args.splits)
+
+    def rest(self, st):
+        pass
+
+    def bytes(self):
+        c = self.cfg
+        return c.B * ((c.n_entries + c.W) * c.D * 2 + c.H * c.D * 2 + c.H * c.D * 4), 0
+
+    def flops(self):
+        c = self.cfg
+        return c.B * 4 * c.H * c.D * (c.n_entries + c.W)
+
+
+class Mixed61(Workload):
+    """61 layers (c128a on even, c4a on odd): per layer compress 128 new states
+    into the cache, then (c4a) index_topk, then attend."""
+
+    def setup(self, n_sets):
+        torch, cskv, sd, s = self.torch, self.cskv, self.sd, self.synth
+        c = self.cfg
+        B, L, D, H, W, Di = c.B, c.L, c.D, c.H, c.W, c.Di
+        from synth.configs import c128a_entries, c4a_entries
+        self.N4, self.N128 = c4a_entries(L), c128a_entries(L)
+        self.layers = []
+        i = 0
+        for layer in range(c.layers):
+            if layer % 10 == 0:
+                log(f"setup: layer {layer + 1}/{c.layers}")
+            kind = c.layer_kind(layer)
+            lay = {"kind": kind}
+            span_T = 132 if kind == "c4a" else 128
+            lay["span"] = sd.new((B, span_T, D), s.KIND_NORMAL_BF16, self.key(i, s.T_S, layer), device=self.dev)
+            lay["gate"] = sd.new((B, span_T), s.KIND_NORMAL_F32, self.key(i, s.T_GATE, layer), device=self.dev)
+            lay["Q"] = sd.new((B, H, D), s.KIND_NORMAL_BF16, self.key(i, s.T_Q, layer), device=self.dev)
+            lay["O"] = torch.empty((B, H, D), dtype=torch.float32, device=self.dev)
+            if kind == "c4a":
+                lay["cache"] = sd.new((B, self.N4, D), s.KIND_NORMAL_BF16, self.key(i, s.T_CACHE, layer), device=self.dev)
+                lay["kidx"] = sd.new((B, self.N4, Di), s.KIND_INT_BF16, self.key(i, s.T_KIDX, layer), device=self.dev,
+                                     a=c.idx_range)
+                lay["qidx"] = sd.new((B, Di), s.KIND_INT_BF16, self.key(i, s.T_QIDX, layer), device=self.dev,
+                                     a=c.idx_range)
+                lay["ids"] = torch.empty((B, c.k), dtype=torch.int32, device=self.dev)
+                lay["first"] = (L - 132) // 4
+                lay["win"] = lay["span"][:, 4:, :]
+            else:
+                lay["cache"] = sd.new((B, self.N128, D), s.KIND_NORMAL_BF16, self.key(i, s.T_CACHE, layer),
+                                      device=self.dev)
+                lay["first"] = L // 128 - 1
+                lay["win"] = lay["span"]
+            self.layers.append(lay)
+        self.pos = torch.full((B,), c.q_pos, dtype=torch.int64, device=self.dev)
+        self.sets = [None]
+        torch.cuda.synchronize()
+
+    def step_layers(self, timer=None):
+        c, cskv = self.cfg, self.cskv
+        for lay in self.layers:
+            cskv.compress(lay["kind"], lay["span"], lay["gate"], lay["cache"], first_entry=lay["first"])
+            if lay["kind"] == "c4a":
+                if timer:
+                    timer.start()
+                cskv.index_topk(lay["qidx"], lay["kidx"], c.k, ids=lay["ids"], chunk=self.args.chunk)
+                if timer:
+                    timer.stop()
+                ids = lay["ids"]
+            else:
+                ids = None
+            cskv.attend(lay["Q"], lay["cache"], ids, lay["win"], softmax_scale=c.tau, rope_dims=c.R,
+                        rope_base=c.rope_base, q_pos=self.pos, out=lay["O"], splits=self.args.splits)
+
+    def bytes(self):
+        c = self.cfg
+        n4 = sum(1 for l in range(c.layers) if c.layer_kind(l) == "c4a")
+        n128 = c.layers - n4
+        dom = n4 * c.B * (self.N4 * c.Di * 2 + c.Di * 2 + c.k * 4)
+        qo = c.H * c.D * 6
+        c4_rest = c.B * (132 * c.D * 2 + 132 * 4 + 32 * c.D * 2 + (c.k + c.W) * c.D * 2 + c.k * 4 + qo)
+        c128 = c.B * (128 * c.D * 2 + 128 * 4 + c.D * 2 + (self.N128 + c.W) * c.D * 2 + qo)
+        return dom, n4 * c4_rest + n128 * c128
+
+    def flops(self):
+        c = self.cfg
+        n4 = sum(1 for l in range(c.layers) if c.layer_kind(l) == "c4a")
+        n128 = c.layers - n4
+        return c.B * (n4 * (2 * self.N4 * c.Di + 4 * c.H * c.D * (c.k + c.W)) +
+                      n128 * 4 * c.H * c.D * (self.N128 + c.W))
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+def cpu_baseline(cfg, seconds):
+    """The oracle, as it is, on a bounded sample of the same workload: a few
+    sequences of one layer (inputs regenerated on the host, outside the timed
+    region), run repeatedly for about `seconds`. Returns a dict for the JSON."""
+    import numpy as np
+    import synth
+    from oracle import formats as F
+    from oracle import method as M
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    kind = cfg.layer_kind(1) if cfg.kind == "mixed" else cfg.kind
+    from synth.configs import c128a_entries, c4a_entries
+    N = c4a_entries(cfg.L) if kind == "c4a" else c128a_entries(cfg.L)
+    n_seq = 2
+    seqs = []
+    for b in range(n_seq):
+        key = lambda t: synth.stream_key(cfg.seed, t, 1)  # noqa: E731
+        Q = F.bf16_to_f64(synth.normal_bf16(key(synth.T_Q), b * cfg.H * cfg.D, cfg.H * cfg.D).reshape(cfg.H, cfg.D))
+        win = F.bf16_to_f64(synth.normal_bf16(key(synth.T_WIN), b * cfg.W * cfg.D, cfg.W * cfg.D).reshape(cfg.W, cfg.D))
+        # only the rows a query can read are filled: every row for c128a, the
+        # rows the oracle's own top-k picks for c4a (filled after selection)
+        cache = np.zeros((N, cfg.D), dtype=np.float64)
+        st = {"Q": Q, "win": win, "cache": cache}
+        if kind == "c4a":
+            st["qidx"] = F.bf16_to_f64(synth.int_bf16(key(synth.T_QIDX), b * cfg.Di, cfg.Di, cfg.idx_range))
+            if cfg.key_dtype == "fp4":
+                codes = synth.random_bytes(key(synth.T_KIDX), b * N * cfg.Di // 2, N * cfg.Di // 2).reshape(N, cfg.Di // 2)
+                sc = synth.pow2_e4m3(key(synth.T_KIDX_SCALE), b * N * cfg.Di // 16, N * cfg.Di // 16, -2, 2
+                                     ).reshape(N, cfg.Di // 16)
+                st["kidx_codes"], st["kidx_scales"] = codes, sc
+            else:
+                st["kidx"] = F.bf16_to_f64(synth.int_bf16(key(synth.T_KIDX), b * N * cfg.Di, N * cfg.Di,
+                                                          cfg.idx_range).reshape(N, cfg.Di))
+            ids = M.topk_ids(M.index_scores(st["qidx"], st["kidx"] if "kidx" in st else
+                                            F.decode_fp4_g16(st["kidx_codes"], st["kidx_scales"])), cfg.k)
+            rows = ids[ids >= 0]
+        else:
+            rows = np.arange(N)
+        cache[rows] = F.bf16_to_f64(synth.normal_bf16(key(synth.T_CACHE), 0, rows.size * cfg.D)
+                                    .reshape(rows.size, cfg.D))
+        seqs.append(st)
+
+    def one(st):
+        if kind == "c4a":
+            keys = st["kidx"] if "kidx" in st else F.decode_fp4_g16(st["kidx_codes"], st["kidx_scales"])
+            M.c4a_decode(st["Q"], st["qidx"], keys, st["cache"], st["win"], cfg.k, cfg.tau, cfg.R,
+                         cfg.rope_base, cfg.q_pos)
+        else:
+            M.c128a_decode(st["Q"], st["cache"], st["win"], cfg.tau, cfg.R, cfg.rope_base, cfg.q_pos)
+
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        one(seqs[done % n_seq])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done / el, "unit": "decode tokens/s per layer", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} single-sequence {kind} layer decodes ({n_seq} distinct sequences of the "
+                      f"{cfg.name} workload, inputs generated before timing) in {el:.1f} s"}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by "
+              "sequence with no communication, so N GPUs run N independent copies)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import compressed_sparse_kv_compress_amd as cskv
+    import synth
+    from synth import configs
+    from synth import device as sd
+
+    cfg = configs.BY_NAME[args.workload]
+    cls = {"c4a": C4aLayer, "c128a": C128aLayer, "mixed": Mixed61}[cfg.kind]
+    wl = cls(cfg, args, torch, cskv, sd, synth)
+    n_sets = args.sets or (1 if cfg.kind == "mixed" else 4)
+    t_setup = time.perf_counter()
+    wl.setup(n_sets)
+    setup_s = time.perf_counter() - t_setup
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    class Timer:
+        def __init__(self, n):
+            self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(n)]
+            self.i = 0
+
+        def start(self):
+            self.ev[self.i][0].record()
+
+        def stop(self):
+            self.ev[self.i][1].record()
+            self.i += 1
+
+        def total_ms(self):
+            return sum(a.elapsed_time(b) for a, b in self.ev[: self.i])
+
+    mixed = cfg.kind == "mixed"
+    n4 = sum(1 for l in range(cfg.layers) if cfg.layer_kind(l) == "c4a") if mixed else 1
+    for i in range(args.warmup):
+        if mixed:
+            wl.step_layers()
+        else:
+            st = wl.sets[i % n_sets]
+            wl.dominant(st)
+            wl.rest(st)
+    torch.cuda.synchronize()
+    log(f"setup {setup_s:.1f} s, warmup done; timing {args.steps} steps")
+
+    timer = Timer(args.steps * n4)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        if mixed:
+            wl.step_layers(timer)
+        else:
+            st = wl.sets[i % n_sets]
+            timer.start()
+            wl.dominant(st)
+            timer.stop()
+            wl.rest(st)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    dom_ms = timer.total_ms() / timer.i
+
+    dom_bytes, rest_bytes = wl.bytes()
+    dom_bytes_launch = dom_bytes / n4
+    achieved = dom_bytes_launch / (dom_ms * 1e-3) / 1e9
+    tokens = cfg.B / (ms_step * 1e-3)
+    if mixed:
+        metric = "decode tokens/s per 61-layer step"
+    else:
+        metric = "decode tokens/s per layer"
+    out = {
+        "metric": metric,
+        "value": round(tokens, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.cache_dtype == "bf16" and cfg.key_dtype == "bf16" else "fp8+fp4 (bf16 MFMA, fp32 accumulate)",
+        "data": "synthetic (SplitMix64 streams; caches built by the library's compress kernel)" if not mixed
+                else "synthetic (SplitMix64 streams; prefix caches drawn directly, new states compressed in the step)",
+        "config": {"workload": cfg.name, "batch": cfg.B, "context": cfg.L, "heads": cfg.H, "D": cfg.D,
+                   "rotary": cfg.R, "window": cfg.W, "top_k": cfg.k or None, "indexer_dim": cfg.Di or None,
+                   "cache": cfg.cache_dtype, "indexer_keys": cfg.key_dtype if cfg.k else None,
+                   "layers": cfg.layers, "input_sets_rotated": n_sets},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "index_topk (k_index_chunk + k_topk_merge)" if (cfg.kind != "c128a") else
+                      "attend (k_attend + k_attend_merge)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": int(dom_bytes_launch),
+            "avg_launch_ms": round(dom_ms, 5),
+        },
+        "step_bandwidth_gbs": round((dom_bytes + rest_bytes) / (ms_step * 1e-3) / 1e9, 1),
+        "algorithmic_bytes_per_step": int(dom_bytes + rest_bytes),
+        "tflops_per_s": round(wl.flops() / (ms_step * 1e-3) / 1e12, 2),
+        "setup_s": round(setup_s, 1),
+    }
+    log(f"timed: {ms_step:.4f} ms/step")
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        if mixed:
+            # the oracle sample is one c4a layer; a 61-layer step costs about 61 of them
+            out["cpu_baseline"]["value"] /= cfg.layers
+            out["cpu_baseline"]["unit"] = "decode tokens/s per 61-layer step (sampled c4a layer rate / 61)"
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
