@@ -101,16 +101,20 @@ def _dense(t, name):
 _workspaces: dict = {}
 
 
-def _workspace(nbytes: int, device) -> torch.Tensor | None:
-    """A zero-initialised scratch buffer per device, grown on demand. Calls on
-    one device are ordered on its current stream, so they can share it."""
+def _workspace(purpose: str, nbytes: int, device, layout=None) -> torch.Tensor | None:
+    """A scratch buffer per (purpose, device), grown on demand. Calls on one
+    device are ordered on its current stream, so calls of one purpose can share
+    it. ``layout`` names the argument set a stateful workspace was last used
+    with: the buffer is zero-filled (a fill kernel) whenever it changes."""
     if nbytes == 0:
         return None
-    key = torch.device(device).index
-    buf = _workspaces.get(key)
+    key = (purpose, torch.device(device).index)
+    buf, last = _workspaces.get(key, (None, None))
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
-        _workspaces[key] = buf
+    elif layout is not None and layout != last:
+        buf.zero_()
+    _workspaces[key] = (buf, layout)
     return buf
 
 
@@ -178,7 +182,7 @@ def index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, k: int, k_scale: torch.
     elif ids.dtype != torch.int32 or tuple(ids.shape) != (B, k) or not ids.is_contiguous():
         raise ValueError("ids must be contiguous int32 [B, k]")
     nbytes = _lib_topk_ws(B, N, Di, k, key_dtype, chunk)   # 0 also when the call will reject
-    ws = _workspace(nbytes, q_idx.device)
+    ws = _workspace("index_topk", nbytes, q_idx.device, layout=(B, N, Di, k, key_dtype, chunk))
     _check(_lib_topk(_ptr(q_idx), key_dtype, _ptr(k_idx), _ptr(k_scale), _ptr(n_entries), B, N, Di, k,
                      _ptr(ids), chunk, _ptr(ws), 0 if ws is None else ws.numel(), _stream(q_idx.device)))
     return ids
@@ -242,7 +246,7 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
         raise ValueError("out must be contiguous fp32 [B, H, D]")
     max_keys = (k if ids is not None else cache.shape[1]) + W
     nbytes = _lib_attend_ws(B, H, D, max_keys, splits)
-    ws = _workspace(nbytes, Q.device)
+    ws = _workspace("attend", nbytes, Q.device)
     _check(_lib_attend(_ptr(Q), B, H, D, FP8_E4M3 if cache_fp8 else BF16, _ptr(cache), _ptr(cache_scale),
                        cache.shape[1], _ptr(ids), k, _ptr(n_entries), FP8_E4M3 if win_fp8 else BF16,
                        _ptr(window), _ptr(window_scale), W, wstride, rope_dims, rope_base, _ptr(q_pos),

@@ -7,166 +7,187 @@
 // sliding window": the newest 128 states are read exactly, in the same
 // softmax. [P1] "Shared key and value": inverse RoPE on the attention output.
 //
-// All heads of a sequence share the key rows, so QK^T and PV are dense
-// contractions of [heads x D] against [keys x D]: they run on 16x16x32 bf16
-// MFMA. A workgroup (4 waves) owns one sequence and a contiguous split of its
-// key slots; per 32-slot tile it
-//   1. gathers the rows (bf16, or fp8 codes decoded exactly to bf16 with the
-//      row scale folded into logits and probabilities) from HBM into
-//      registers one tile ahead, then stores them to LDS twice: row-major for
-//      QK^T and channel-major (8x8 register transposes) for PV;
-//   2. QK^T: wave w computes S^T[32 keys x 16 heads] for heads 16w..16w+15
-//      with its Q fragment held in registers;
-//   3. online softmax (exp2 domain) per head, P to LDS as bf16;
-//   4. PV: wave w accumulates O[heads x D/4 channels] for its channel quarter.
-// With one split the epilogue normalises, applies inverse RoPE and stores O;
-// otherwise partial (max, sum, unnormalised O) go to the workspace and
-// k_attend_merge combines them (log-sum-exp) and applies inverse RoPE.
+// All heads of a sequence share the key rows, so both contractions are dense
+// and run on 16x16x32 bf16 MFMA. A workgroup (4 waves) owns one sequence and a
+// contiguous split of its key slots; wave w owns heads 16w .. 16w+15. Per tile
+// of 32 key slots:
+//   1. the rows (bf16, or fp8 codes widened exactly to bf16; an fp8 row's
+//      scale is folded into its logits and probabilities) are gathered from
+//      HBM into registers one tile ahead and stored row-major into one of two
+//      LDS buffers (one barrier per tile);
+//   2. S^T[32 keys x 16 heads] = K Q^T with Q held in registers;
+//   3. online softmax per head in the exp2 domain; the running maximum is
+//      raised only when a logit exceeds it by more than 2^8, so the
+//      accumulators are rescaled rarely;
+//   4. O^T[D x 16 heads] += K^T P^T: the probabilities stay in the registers
+//      the QK^T product left them in (they are exactly the B operand, for a
+//      matching order of the 32 keys), and K^T comes from the row-major tile
+//      through gfx950's transposing LDS reads.
+// Each lane ends with 4 consecutive channels of one head: rotary pairs sit in
+// one lane. With one split the epilogue normalises, applies inverse RoPE and
+// stores O; otherwise partials (max, sum, unnormalised O) go to the workspace
+// and k_attend_merge combines them with a log-sum-exp merge.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace cskv {
 
 constexpr int kAttThreads = 256;
 constexpr int kTK = 32;        // key slots per tile
-constexpr int kHMax = 64;      // heads per workgroup (padded to 16s)
+constexpr int kHMax = 64;      // heads per workgroup (4 waves x 16)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyRescale = 8.0f;   // log2 headroom before the running max is raised
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct AttLayout {
-  static constexpr int KROW = D + 8;        // bf16 per row-major key row (padding vs bank conflicts)
-  static constexpr int KCOL = kTK + 8;      // bf16 per channel-major row
-  static constexpr int PST = kTK + 8;       // bf16 per P row
-  static constexpr size_t off_krow = 0;
-  static constexpr size_t off_kcol = off_krow + (size_t)kTK * KROW * 2;
-  static constexpr size_t off_p = off_kcol + (size_t)D * KCOL * 2;
-  static constexpr size_t off_alpha = off_p + (size_t)kHMax * PST * 2;
-  static constexpr size_t off_rs = off_alpha + kHMax * 4;      // per-slot logit factor
-  static constexpr size_t off_ps = off_rs + kTK * 4;           // per-slot value scale (< 0 = masked)
-  static constexpr size_t off_m = off_ps + kTK * 4;
-  static constexpr size_t off_l = off_m + kHMax * 4;
-  static constexpr size_t off_cos = off_l + kHMax * 4;
+  // row stride in bf16: D + 24 makes the stride 12 (mod 64) dwords, so the
+  // 16-byte row reads of QK^T and the transposing reads of PV are free of
+  // bank conflicts within each 16-lane group
+  static constexpr int KROW = D + 24;
+  static constexpr size_t tile_bytes = (size_t)kTK * KROW * 2;
+  static constexpr size_t off_tile0 = 0;
+  static constexpr size_t off_tile1 = tile_bytes;
+  static constexpr size_t off_rs = 2 * tile_bytes;             // [2][kTK] logit factor per slot
+  static constexpr size_t off_ps = off_rs + 2 * kTK * 4;       // [2][kTK] value scale (-inf: masked)
+  static constexpr size_t off_cos = off_ps + 2 * kTK * 4;
   static constexpr size_t off_sin = off_cos + (D / 2) * 4;
   static constexpr size_t bytes = off_sin + (D / 2) * 4;
 };
 
-// 8 fp8 codes -> 8 bf16 (exact), packed like a bf16 row load.
-__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 c) {
-  uint4 r;
-  r.x = e4m3_to_bf16_bits(c.x & 0xFFu) | (e4m3_to_bf16_bits((c.x >> 8) & 0xFFu) << 16);
-  r.y = e4m3_to_bf16_bits((c.x >> 16) & 0xFFu) | (e4m3_to_bf16_bits(c.x >> 24) << 16);
-  r.z = e4m3_to_bf16_bits(c.y & 0xFFu) | (e4m3_to_bf16_bits((c.y >> 8) & 0xFFu) << 16);
-  r.w = e4m3_to_bf16_bits((c.y >> 16) & 0xFFu) | (e4m3_to_bf16_bits(c.y >> 24) << 16);
-  return r;
+// Where a tile's rows come from: the slot's row pointer (nullptr for an
+// empty slot: an id out of range, or past the last key) and whether it is fp8.
+struct SlotRow {
+  const uint8_t* ptr;
+  const float* scale;   // fp8 row scale, nullptr for bf16
+};
+
+template <int D, bool CFP8, bool WFP8>
+__device__ __forceinline__ SlotRow slot_row(const AttendArgs& a, int64_t b, int64_t slot, int64_t n_sel,
+                                            int64_t n_keys, bool dense) {
+  SlotRow sr{nullptr, nullptr};
+  if (slot >= n_keys) return sr;
+  if (slot < n_sel) {
+    const int64_t row = dense ? slot : (int64_t)a.ids[b * a.k + slot];
+    if (row < 0 || row >= a.cache_rows) return sr;
+    const int64_t r = b * a.cache_rows + row;
+    sr.ptr = reinterpret_cast<const uint8_t*>(a.cache) + r * D * (CFP8 ? 1 : 2);
+    sr.scale = CFP8 ? a.cache_scale + r : nullptr;
+  } else {
+    const int64_t r = b * a.win_bstride + (slot - n_sel);
+    sr.ptr = reinterpret_cast<const uint8_t*>(a.window) + r * D * (WFP8 ? 1 : 2);
+    sr.scale = WFP8 ? a.window_scale + r : nullptr;
+  }
+  return sr;
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+// Per-slot factors of a tile: logit factor (value scale * tau * log2 e) and
+// value scale (-inf marks an empty slot).
+__device__ __forceinline__ void put_slot(uint8_t* lds, size_t off_rs, size_t off_ps, int buf, int j,
+                                         float vs, float tau_log2e) {
+  float* rs = reinterpret_cast<float*>(lds + off_rs) + buf * kTK;
+  float* ps = reinterpret_cast<float*>(lds + off_ps) + buf * kTK;
+  rs[j] = vs != -INFINITY ? vs * tau_log2e : 0.0f;
+  ps[j] = vs;
 }
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
 
-// One thread's share of a tile: rows 8*kb .. 8*kb+7, channels 8*cb .. 8*cb+7.
+// Direct HBM -> LDS fill of a bf16 tile with D = 512: every wave instruction
+// moves one 1 KiB row (16 bytes per lane) into its padded LDS row, no
+// registers involved. Wave w fills rows 8w .. 8w+7; empty slots are zeroed.
+template <int D, bool CFP8, bool WFP8>
+__device__ __forceinline__ void dma_tile(const AttendArgs& a, int64_t b, int64_t slot0, int64_t n_sel,
+                                         int64_t n_keys, bool dense, uint8_t* lds, int buf, float tau_log2e,
+                                         int wave, int lane) {
+  using L = AttLayout<D>;
+  static_assert(D * 2 == kWave * 16, "one wave instruction moves one row");
+  uint8_t* tile = lds + (buf ? L::off_tile1 : L::off_tile0);
+  uint64_t p = 0;
+  if (lane < 8) {
+    const SlotRow sr = slot_row<D, CFP8, WFP8>(a, b, slot0 + 8 * wave + lane, n_sel, n_keys, dense);
+    p = reinterpret_cast<uint64_t>(sr.ptr);
+    put_slot(lds, L::off_rs, L::off_ps, buf, 8 * wave + lane, sr.ptr ? 1.0f : -INFINITY, tau_log2e);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lo32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)p, i);
+    const uint32_t hi32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(p >> 32), i);
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(((uint64_t)hi32 << 32) | lo32);
+    uint8_t* row = tile + (size_t)(8 * wave + i) * L::KROW * 2;
+    if (src) {
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + 16 * lane),
+                                       (__attribute__((address_space(3))) void*)row, 16, 0, 0);
+    } else {
+      *reinterpret_cast<uint4*>(row + 16 * lane) = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Register-staged fill (fp8 rows, mixed dtypes, or D = 128): one thread's
+// share is rows 8*kb .. 8*kb+7, channels 8*cb .. 8*cb+7. When every row is
+// fp8 the codes are kept as loaded (8 bytes) and widened to bf16 when written
+// to LDS; otherwise each row is held as 8 bf16.
+template <bool RAW_FP8>
 struct TileRegs {
-  uint4 r[8];
-  float vs[8];     // value scale of the row (1 for bf16)
-  bool ok[8];      // slot holds a real key row
+  typename std::conditional<RAW_FP8, uint2, uint4>::type r[8];
+  float vs[8];     // value scale of the row (1 for bf16), or -inf for an empty slot
 };
 
 template <int D, bool CFP8, bool WFP8>
 __device__ __forceinline__ void load_tile(const AttendArgs& a, int64_t b, int64_t slot0, int64_t n_sel,
-                                          int64_t n_keys, bool dense, int kb, int cb, TileRegs& t) {
+                                          int64_t n_keys, bool dense, int kb, int cb,
+                                          TileRegs<CFP8 && WFP8>& t) {
+  constexpr bool RAW = CFP8 && WFP8;
   const bool active_c = cb * 8 < D;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int64_t slot = slot0 + 8 * kb + i;
-    t.r[i] = make_uint4(0, 0, 0, 0);
-    t.vs[i] = 0.0f;
-    t.ok[i] = false;
-    if (slot >= n_keys) continue;
-    if (slot < n_sel) {
-      const int64_t row = dense ? slot : (int64_t)a.ids[b * a.k + slot];
-      if (row < 0 || row >= a.cache_rows) continue;
-      const int64_t r = b * a.cache_rows + row;
-      t.ok[i] = true;
-      if constexpr (CFP8) {
-        t.vs[i] = a.cache_scale[r];
-        if (active_c) t.r[i] = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(
-                          reinterpret_cast<const uint8_t*>(a.cache) + r * D + cb * 8));
-      } else {
-        t.vs[i] = 1.0f;
-        if (active_c) t.r[i] = *reinterpret_cast<const uint4*>(
-                          reinterpret_cast<const uint16_t*>(a.cache) + r * D + cb * 8);
-      }
+    if constexpr (RAW) t.r[i] = make_uint2(0, 0);
+    else t.r[i] = make_uint4(0, 0, 0, 0);
+    t.vs[i] = -INFINITY;
+    const SlotRow sr = slot_row<D, CFP8, WFP8>(a, b, slot0 + 8 * kb + i, n_sel, n_keys, dense);
+    if (!sr.ptr) continue;
+    t.vs[i] = sr.scale ? *sr.scale : 1.0f;
+    if (!active_c) continue;
+    if (sr.scale) {
+      const uint2 c = *reinterpret_cast<const uint2*>(sr.ptr + cb * 8);
+      if constexpr (RAW) t.r[i] = c;
+      else t.r[i] = fp8x8_to_bf16x8(c);
     } else {
-      const int64_t r = b * a.win_bstride + (slot - n_sel);
-      t.ok[i] = true;
-      if constexpr (WFP8) {
-        t.vs[i] = a.window_scale[r];
-        if (active_c) t.r[i] = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(
-                          reinterpret_cast<const uint8_t*>(a.window) + r * D + cb * 8));
-      } else {
-        t.vs[i] = 1.0f;
-        if (active_c) t.r[i] = *reinterpret_cast<const uint4*>(
-                          reinterpret_cast<const uint16_t*>(a.window) + r * D + cb * 8);
-      }
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(uint8_t* lds, int kb, int cb, const TileRegs& t,
-                                           float tau_log2e) {
-  using L = AttLayout<D>;
-  uint16_t* krow = reinterpret_cast<uint16_t*>(lds + L::off_krow);
-  uint16_t* kcol = reinterpret_cast<uint16_t*>(lds + L::off_kcol);
-  if (cb * 8 < D) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<uint4*>(krow + (8 * kb + i) * L::KROW + 8 * cb) = t.r[i];
-    // transpose the 8x8 bf16 block: channel c of keys 0..7
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint32_t w[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = word_of(t.r[i], c >> 1);
-      uint4 o;
-      if ((c & 1) == 0) {
-        o.x = lo_pair(w[0], w[1]); o.y = lo_pair(w[2], w[3]);
-        o.z = lo_pair(w[4], w[5]); o.w = lo_pair(w[6], w[7]);
-      } else {
-        o.x = hi_pair(w[0], w[1]); o.y = hi_pair(w[2], w[3]);
-        o.z = hi_pair(w[4], w[5]); o.w = hi_pair(w[6], w[7]);
-      }
-      *reinterpret_cast<uint4*>(kcol + (8 * cb + c) * L::KCOL + 8 * kb) = o;
-    }
-  }
-  if (cb == 0) {
-    float* rs = reinterpret_cast<float*>(lds + L::off_rs);
-    float* ps = reinterpret_cast<float*>(lds + L::off_ps);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      rs[8 * kb + i] = t.ok[i] ? t.vs[i] * tau_log2e : 0.0f;
-      ps[8 * kb + i] = t.ok[i] ? t.vs[i] : -1.0f;   // < 0 marks a masked slot
+      if constexpr (!RAW) t.r[i] = *reinterpret_cast<const uint4*>(sr.ptr + cb * 16);
     }
   }
 }
 
 template <int D, bool CFP8, bool WFP8>
-__global__ __launch_bounds__(kAttThreads) void k_attend(AttendArgs a, int splits, int64_t keys_per_split,
-                                                       float* __restrict__ ws_acc,
-                                                       float* __restrict__ ws_ml) {
+__device__ __forceinline__ void store_tile(uint8_t* lds, int buf, int kb, int cb,
+                                           const TileRegs<CFP8 && WFP8>& t, float tau_log2e) {
+  using L = AttLayout<D>;
+  uint16_t* tile = reinterpret_cast<uint16_t*>(lds + (buf ? L::off_tile1 : L::off_tile0));
+  if (cb * 8 < D) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint4 v;
+      if constexpr (CFP8 && WFP8) v = fp8x8_to_bf16x8(t.r[i]);
+      else v = t.r[i];
+      *reinterpret_cast<uint4*>(tile + (8 * kb + i) * L::KROW + 8 * cb) = v;
+    }
+  }
+  if (cb == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) put_slot(lds, L::off_rs, L::off_ps, buf, 8 * kb + i, t.vs[i], tau_log2e);
+  }
+}
+
+template <int D, bool CFP8, bool WFP8>
+__global__ __launch_bounds__(kAttThreads, 2) void k_attend(AttendArgs a, int splits,
+                                                          int64_t keys_per_split,
+                                                          float* __restrict__ ws_acc,
+                                                          float* __restrict__ ws_ml) {
   using L = AttLayout<D>;
   constexpr int KS = D / 32;          // k-steps of QK^T
-  constexpr int CTW = D / 64;         // 16-channel tiles per wave in PV
+  constexpr int CT = D / 16;          // 16-channel tiles of O^T
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint16_t* krow = reinterpret_cast<uint16_t*>(lds + L::off_krow);
-  uint16_t* kcol = reinterpret_cast<uint16_t*>(lds + L::off_kcol);
-  uint16_t* pl = reinterpret_cast<uint16_t*>(lds + L::off_p);
-  float* alpha_l = reinterpret_cast<float*>(lds + L::off_alpha);
-  float* rs_l = reinterpret_cast<float*>(lds + L::off_rs);
-  float* ps_l = reinterpret_cast<float*>(lds + L::off_ps);
-  float* m_l = reinterpret_cast<float*>(lds + L::off_m);
-  float* l_l = reinterpret_cast<float*>(lds + L::off_l);
   float* cos_l = reinterpret_cast<float*>(lds + L::off_cos);
   float* sin_l = reinterpret_cast<float*>(lds + L::off_sin);
 
@@ -174,7 +195,6 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(AttendArgs a, int splits
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t b = blockIdx.y;
   const int s = blockIdx.x;
-  const int HT = (a.H + 15) / 16;
   const bool dense = a.ids == nullptr;
   int64_t n_sel;
   if (dense) {
@@ -187,6 +207,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(AttendArgs a, int splits
   const int64_t lo = (int64_t)s * keys_per_split;
   const int64_t hi = lo + keys_per_split < n_keys ? lo + keys_per_split : n_keys;
   const float tau_log2e = a.softmax_scale * kLog2e;
+  const int h = 16 * wave + l16;            // this lane's head
+  const bool wave_on = 16 * wave < a.H;     // wave-uniform
 
   // rotary tables (fp64 angles), used by the single-split epilogue
   if (splits == 1 && t < a.rope_dims / 2) {
@@ -196,11 +218,10 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(AttendArgs a, int splits
     sin_l[t] = (float)sin(ang);
   }
 
-  // Q fragment: B operand of S^T = K Q^T; lane holds Q[16w + l16][32ks + 8g .. +7]
+  // Q fragment: B operand of S^T = K Q^T; lane holds Q[h][32ks + 8g .. +7]
   bf16x8_t qf[KS];
   {
-    const int h = 16 * wave + l16;
-    const bool qok = wave < HT && h < a.H;
+    const bool qok = wave_on && h < a.H;
     const uint16_t* qrow = a.Q + (b * a.H + (qok ? h : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -209,150 +230,161 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(AttendArgs a, int splits
     }
   }
 
-  f32x4_t acc[4][CTW];
+  f32x4_t acc[CT];
 #pragma unroll
-  for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-    for (int ct = 0; ct < CTW; ++ct) acc[ht][ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
+  // transposing-read addresses (bf16 offsets within a tile): lane src = l16 of
+  // group g fetches 4 channels of row kbase + l16/4, so that lane l16 receives
+  // channel l16 of rows kbase .. kbase+3
+  const int tr_row = l16 >> 2, tr_col = 4 * (l16 & 3);
+  const int tr_off0 = (4 * g + tr_row) * L::KROW + tr_col;
+  const int tr_off1 = (16 + 4 * g + tr_row) * L::KROW + tr_col;
+
+  constexpr bool kDma = D == 512 && !CFP8 && !WFP8;
   const int kb = t >> 6, cb = t & 63;
-  TileRegs tr;
-  if (lo < hi) load_tile<D, CFP8, WFP8>(a, b, lo, n_sel, n_keys, dense, kb, cb, tr);
+  TileRegs<CFP8 && WFP8> tr;
+  if (lo < hi) {
+    if constexpr (kDma) {
+      dma_tile<D, CFP8, WFP8>(a, b, lo, n_sel, n_keys, dense, lds, 0, tau_log2e, wave, lane);
+    } else {
+      load_tile<D, CFP8, WFP8>(a, b, lo, n_sel, n_keys, dense, kb, cb, tr);
+      store_tile<D, CFP8, WFP8>(lds, 0, kb, cb, tr, tau_log2e);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
+  int buf = 0;
   for (int64_t tile = lo; tile < hi; tile += kTK) {
-    __syncthreads();                        // previous tile fully consumed
-    store_tile<D>(lds, kb, cb, tr, tau_log2e);
-    __syncthreads();
-    if (tile + kTK < hi) load_tile<D, CFP8, WFP8>(a, b, tile + kTK, n_sel, n_keys, dense, kb, cb, tr);
+    const bool more = tile + kTK < hi;
+    if (more) {
+      // the other buffer was last read before the previous barrier
+      if constexpr (kDma) dma_tile<D, CFP8, WFP8>(a, b, tile + kTK, n_sel, n_keys, dense, lds, buf ^ 1, tau_log2e, wave, lane);
+      else load_tile<D, CFP8, WFP8>(a, b, tile + kTK, n_sel, n_keys, dense, kb, cb, tr);
+    }
 
-    if (wave < HT) {
+    if (wave_on) {
+      const uint16_t* kt = reinterpret_cast<const uint16_t*>(lds + (buf ? L::off_tile1 : L::off_tile0));
+      const float* rs = reinterpret_cast<const float*>(lds + L::off_rs) + buf * kTK;
+      const float* ps = reinterpret_cast<const float*>(lds + L::off_ps) + buf * kTK;
       f32x4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(krow + l16 * L::KROW + 32 * ks + 8 * g);
-        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(krow + (16 + l16) * L::KROW + 32 * ks + 8 * g);
+        const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kt + l16 * L::KROW + 32 * ks + 8 * g);
+        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kt + (16 + l16) * L::KROW + 32 * ks + 8 * g);
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
+        if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the loads kept in flight
       }
-      // lane holds logits of head 16w + l16 for slots 4g+i and 16+4g+i
-      float x[8];
+      // lane holds the logits of head h for key slots 4g+i (s0) and 16+4g+i (s1)
+      float x[8], vsc[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j0 = 4 * g + i, j1 = 16 + 4 * g + i;
-        x[i] = ps_l[j0] >= 0.0f ? s0[i] * rs_l[j0] : -INFINITY;
-        x[4 + i] = ps_l[j1] >= 0.0f ? s1[i] * rs_l[j1] : -INFINITY;
+        vsc[i] = ps[j0];
+        vsc[4 + i] = ps[j1];
+        x[i] = vsc[i] != -INFINITY ? s0[i] * rs[j0] : -INFINITY;
+        x[4 + i] = vsc[4 + i] != -INFINITY ? s1[i] * rs[j1] : -INFINITY;
       }
       float mx = x[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
+      const bool raise = mx > m_run + kLazyRescale || (m_run == -INFINITY && mx != -INFINITY);
+      if (__ballot(raise)) {
+        const float alpha = raise ? (m_run == -INFINITY ? 0.0f : exp2f(m_run - mx)) : 1.0f;
+        if (raise) m_run = mx;
+        l_run *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[ct][i] *= alpha;
+        }
+      }
       float p[8], lsum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = (x[i] == -INFINITY) ? 0.0f : exp2f(x[i] - m_new);
+        p[i] = x[i] == -INFINITY ? 0.0f : exp2f(x[i] - m_run);
         lsum += p[i];
       }
       lsum += __shfl_xor(lsum, 16, kWave);
       lsum += __shfl_xor(lsum, 32, kWave);
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-      const int h = 16 * wave + l16;
-      uint16_t* prow = pl + h * L::PST;
-      uint2 w0, w1;
-      {
-        float v[8];
+      l_run += lsum;
+      // P^T as the B operand: k-slot j of group g is key 4g+j (j < 4) or 16+4g+j-4
+      uint4 pw;
+      float pv[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = p[i] * fmaxf(ps_l[4 * g + i], 0.0f);
-          v[4 + i] = p[4 + i] * fmaxf(ps_l[16 + 4 * g + i], 0.0f);
-        }
-        w0.x = pack_bf16x2(v[0], v[1]); w0.y = pack_bf16x2(v[2], v[3]);
-        w1.x = pack_bf16x2(v[4], v[5]); w1.y = pack_bf16x2(v[6], v[7]);
+      for (int i = 0; i < 8; ++i) pv[i] = p[i] == 0.0f ? 0.0f : p[i] * vsc[i];
+      pw.x = pack_bf16x2(pv[0], pv[1]);
+      pw.y = pack_bf16x2(pv[2], pv[3]);
+      pw.z = pack_bf16x2(pv[4], pv[5]);
+      pw.w = pack_bf16x2(pv[6], pv[7]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+      typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+      const uint16_t* ktc = kt;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const v4i16_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(ktc + tr_off0 + 16 * ct));
+        const v4i16_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(ktc + tr_off1 + 16 * ct));
+        const v4i16_t kk[2] = {r0, r1};
+        const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, kk);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, pb, acc[ct], 0, 0, 0);
+        if ((ct & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
-      *reinterpret_cast<uint2*>(prow + 4 * g) = w0;
-      *reinterpret_cast<uint2*>(prow + 16 + 4 * g) = w1;
-      if (g == 0) alpha_l[h] = alpha;
     }
+    if constexpr (!kDma) {
+      if (more) store_tile<D, CFP8, WFP8>(lds, buf ^ 1, kb, cb, tr, tau_log2e);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the next tile's rows have landed in LDS
     __syncthreads();
-
-    // PV: O[heads][channels of this wave] += P[heads][32 slots] x K[32 slots][channels]
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      if (ht < HT) {
-        float al[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = alpha_l[16 * ht + 4 * g + i];
-        const bf16x8_t pa = *reinterpret_cast<const bf16x8_t*>(pl + (16 * ht + l16) * L::PST + 8 * g);
-#pragma unroll
-        for (int ct = 0; ct < CTW; ++ct) {
-          const int ch = wave * (D / 4) + 16 * ct + l16;
-          const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(kcol + ch * L::KCOL + 8 * g);
-          f32x4_t c = acc[ht][ct];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) c[i] *= al[i];
-          acc[ht][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, kv, c, 0, 0, 0);
-        }
-      }
-    }
+    buf ^= 1;
   }
 
-  // per-head softmax state -> LDS
-  if (wave < HT && g == 0) {
-    m_l[16 * wave + l16] = m_run;
-    l_l[16 * wave + l16] = l_run;
-  }
-  __syncthreads();
-
+  if (!wave_on) return;
+  // lane holds O^T[16ct + 4g + i][h]: channels 16ct+4g .. 16ct+4g+3 of head h
   if (splits == 1) {
     const int R = a.rope_dims;
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    if (h < a.H) {
+      float* orow = a.O + (b * a.H + h) * D;
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      if (ht >= HT) continue;
-#pragma unroll
-      for (int ct = 0; ct < CTW; ++ct) {
-        const int ch = wave * (D / 4) + 16 * ct + l16;
-        const bool rot = ch >= D - R;
-        const int j = (ch - (D - R)) >> 1;
-        const float cs = rot ? cos_l[j] : 1.0f, sn = rot ? sin_l[j] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int h = 16 * ht + 4 * g + i;
-          const float lh = l_l[h];
-          const float v = lh > 0.0f ? acc[ht][ct][i] / lh : 0.0f;
-          const float pv = __shfl_xor(v, 1, kWave);
-          float o = v;
-          if (rot) o = (ch & 1) == 0 ? v * cs - pv * sn : pv * sn + v * cs;
-          if (h < a.H) a.O[(b * a.H + h) * D + ch] = o;
+      for (int ct = 0; ct < CT; ++ct) {
+        const int c = 16 * ct + 4 * g;
+        float4 o = make_float4(acc[ct][0] * inv, acc[ct][1] * inv, acc[ct][2] * inv, acc[ct][3] * inv);
+        if (c >= D - R) {
+          const int j = (c - (D - R)) >> 1;
+          const float c0 = cos_l[j], s0 = sin_l[j];
+          o = make_float4(o.x * c0 - o.y * s0, o.x * s0 + o.y * c0, o.z, o.w);
         }
+        if (c + 2 >= D - R) {
+          const int j = (c + 2 - (D - R)) >> 1;
+          const float c1 = cos_l[j], s1 = sin_l[j];
+          o = make_float4(o.x, o.y, o.z * c1 - o.w * s1, o.z * s1 + o.w * c1);
+        }
+        *reinterpret_cast<float4*>(orow + c) = o;
       }
     }
   } else {
     const int64_t part = b * splits + s;
+    if (h < a.H) {
+      float* arow = ws_acc + (part * kHMax + h) * D;
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      if (ht >= HT) continue;
-#pragma unroll
-      for (int ct = 0; ct < CTW; ++ct) {
-        const int ch = wave * (D / 4) + 16 * ct + l16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int h = 16 * ht + 4 * g + i;
-          if (h < a.H) ws_acc[(part * kHMax + h) * D + ch] = acc[ht][ct][i];
-        }
+      for (int ct = 0; ct < CT; ++ct) {
+        const int c = 16 * ct + 4 * g;
+        *reinterpret_cast<float4*>(arow + c) = make_float4(acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
       }
-    }
-    if (t < a.H) {
-      ws_ml[(part * kHMax + t) * 2 + 0] = m_l[t];
-      ws_ml[(part * kHMax + t) * 2 + 1] = l_l[t];
+      if (g == 0) *reinterpret_cast<float2*>(ws_ml + (part * kHMax + h) * 2) = make_float2(m_run, l_run);
     }
   }
 }
 
 // Log-sum-exp merge of the splits of one (sequence, head), then inverse RoPE.
+// Thread t owns channels 4t .. 4t+3.
 template <int D>
 __global__ __launch_bounds__(128) void k_attend_merge(AttendArgs a, int splits,
                                                       const float* __restrict__ ws_acc,
@@ -360,55 +392,73 @@ __global__ __launch_bounds__(128) void k_attend_merge(AttendArgs a, int splits,
   const int64_t b = blockIdx.y;
   const int h = blockIdx.x;
   const int t = threadIdx.x;
+  if (4 * t >= D) return;
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml) + (b * splits) * kHMax + h;
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ws_ml[((b * splits + s) * kHMax + h) * 2]);
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[(int64_t)s * kHMax].x);
   float Lsum = 0.0f;
+  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if (M != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const float* ml = ws_ml + ((b * splits + s) * kHMax + h) * 2;
-      if (ml[0] != -INFINITY) Lsum += ml[1] * exp2f(ml[0] - M);
-    }
-  }
-  const int R = a.rope_dims;
-  for (int pr = t; pr < D / 2; pr += 128) {
-    const int c0 = 2 * pr;
-    float x = 0.0f, y = 0.0f;
-    if (Lsum > 0.0f) {
-      for (int s = 0; s < splits; ++s) {
-        const float* ml = ws_ml + ((b * splits + s) * kHMax + h) * 2;
-        if (ml[0] == -INFINITY) continue;
-        const float w = exp2f(ml[0] - M);
-        const float* acc = ws_acc + ((b * splits + s) * kHMax + h) * D;
-        x = fmaf(acc[c0], w, x);
-        y = fmaf(acc[c0 + 1], w, y);
+    const float* base = ws_acc + ((b * splits) * kHMax + h) * D + 4 * t;
+    constexpr int U = 8;
+    for (int s0 = 0; s0 < splits; s0 += U) {
+      float4 v[U];
+      float w[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int s = s0 + u;
+        w[u] = 0.0f;
+        v[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (s < splits) {
+          const float2 p = ml[(int64_t)s * kHMax];
+          if (p.x != -INFINITY) {
+            w[u] = exp2f(p.x - M);
+            Lsum += p.y * w[u];
+            v[u] = *reinterpret_cast<const float4*>(base + (int64_t)s * kHMax * D);
+          }
+        }
       }
-      x /= Lsum;
-      y /= Lsum;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        o.x = fmaf(v[u].x, w[u], o.x);
+        o.y = fmaf(v[u].y, w[u], o.y);
+        o.z = fmaf(v[u].z, w[u], o.z);
+        o.w = fmaf(v[u].w, w[u], o.w);
+      }
     }
-    if (c0 >= D - R) {
-      const int j = (c0 - (D - R)) >> 1;
-      const double theta = pow((double)a.rope_base, -2.0 * (double)j / (double)R);
-      const double ang = -(double)a.q_pos[b] * theta;
-      const float cs = (float)cos(ang), sn = (float)sin(ang);
-      const float xr = x * cs - y * sn, yr = x * sn + y * cs;
-      x = xr;
-      y = yr;
-    }
-    float* o = a.O + (b * a.H + h) * D + c0;
-    o[0] = x;
-    o[1] = y;
   }
+  const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+  o = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  const int R = a.rope_dims;
+  const int c = 4 * t;
+  if (c >= D - R) {
+    const int j = (c - (D - R)) >> 1;
+    const double th = pow((double)a.rope_base, -2.0 * (double)j / (double)R);
+    const double ang = -(double)a.q_pos[b] * th;
+    const float c0 = (float)cos(ang), s0 = (float)sin(ang);
+    o = make_float4(o.x * c0 - o.y * s0, o.x * s0 + o.y * c0, o.z, o.w);
+  }
+  if (c + 2 >= D - R) {
+    const int j = (c + 2 - (D - R)) >> 1;
+    const double th = pow((double)a.rope_base, -2.0 * (double)j / (double)R);
+    const double ang = -(double)a.q_pos[b] * th;
+    const float c1 = (float)cos(ang), s1 = (float)sin(ang);
+    o = make_float4(o.x, o.y, o.z * c1 - o.w * s1, o.z * s1 + o.w * c1);
+  }
+  *reinterpret_cast<float4*>(a.O + (b * a.H + h) * D + c) = o;
 }
 
 // ------------------------------------------------------------- planning / launch
 
 bool plan_attend(int64_t B, int H, int D, int64_t max_keys, int splits_hint, AttendPlan* p) {
   (void)H;
+  (void)D;
   const int64_t tiles = max_keys <= 0 ? 1 : (max_keys + kTK - 1) / kTK;
   int64_t splits = splits_hint;
   if (splits <= 0) {
-    int64_t want = (512 + B - 1) / B;
-    int64_t cap = tiles / 4;
+    // about two workgroups per compute unit, at least 4 tiles per split
+    const int64_t want = (512 + B - 1) / B;
+    const int64_t cap = tiles / 4;
     splits = want < cap ? want : cap;
     if (splits < 1) splits = 1;
     if (splits > 64) splits = 64;
@@ -428,15 +478,17 @@ static hipError_t launch_attend_t(const AttendPlan& p, const AttendArgs& a, void
                                   hipStream_t stream) {
   using L = AttLayout<D>;
   auto kern = k_attend<D, CFP8, WFP8>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
-  if (e != hipSuccess) return e;
+  if (L::bytes > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
+    if (e != hipSuccess) return e;
+  }
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = p.splits > 1 ? ws_acc + (size_t)a.B * p.splits * kHMax * D : nullptr;
   dim3 grid((unsigned)p.splits, (unsigned)a.B);
   hipLaunchKernelGGL(kern, grid, dim3(kAttThreads), L::bytes, stream, a, p.splits,
                      p.keys_per_split, ws_acc, ws_ml);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   hipLaunchKernelGGL((k_attend_merge<D>), dim3((unsigned)a.H, (unsigned)a.B), dim3(128), 0, stream,
                      a, p.splits, ws_acc, ws_ml);

@@ -29,11 +29,14 @@ __global__ __launch_bounds__(256) void k_encode_fp8_rows(const void* __restrict_
   if (lane == 0) scale[row] = sc;
 }
 
+// One thread per code; the decode goes through the same converter the
+// attention kernel uses on its loads (then exact to fp32, times the scale).
 __global__ void k_decode_fp8_rows(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
                                   int64_t rows, int D, float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows * D) return;
-  out[i] = e4m3_to_f32(codes[i]) * scale[i / D];
+  const uint32_t bits = fp8x2_to_bf16x2<false>((uint32_t)codes[i]);
+  out[i] = bf16_lo(bits) * scale[i / D];
 }
 
 // One thread per group of 16 channels.

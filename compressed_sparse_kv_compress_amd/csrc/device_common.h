@@ -99,6 +99,20 @@ __device__ __forceinline__ bf16x2_t fp4x2_to_bf16x2(uint32_t word) {
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, SEL);
 }
 
+// Two E4M3 codes (one 16-bit half of `word`, selected by HI) to a bf16 pair,
+// exactly (3 mantissa bits and exponents 2^-9 .. 2^8 fit bf16), through the
+// gfx950 scaled converter with scale 1; the lower code lands in the low half.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, HI));
+}
+
+// 8 E4M3 codes -> 8 bf16, packed like a 16-byte bf16 row load.
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 c) {
+  return make_uint4(fp8x2_to_bf16x2<false>(c.x), fp8x2_to_bf16x2<true>(c.x), fp8x2_to_bf16x2<false>(c.y),
+                    fp8x2_to_bf16x2<true>(c.y));
+}
+
 // ---------------------------------------------------------------- wave helpers
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }

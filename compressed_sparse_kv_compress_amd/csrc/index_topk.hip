@@ -4,63 +4,105 @@
 // compressed entries per query (default k = 512). [P2] Step 5: a learned
 // indexer scores every compressed block; the query reads only the chosen ones.
 //
-// Level 0 (k_index_chunk): one workgroup scores a chunk of entries - a GEMV of
-// the query's indexer vector against bf16 or fp4 keys streamed from HBM with
-// 16-byte coalesced loads, reduced across lanes with DPP - writes each score's
-// orderable 32-bit key to LDS, then selects the chunk's k best with a radix
-// select in LDS and writes them in entry order.
-// Levels >= 1 (k_topk_merge): one workgroup merges up to `fanin` lists of one
-// sequence into its k best, again in entry order. The global top-k under the
-// total order (score desc, entry asc) is contained in the union of the chunks'
-// top-k, so every level is exact; the last level writes the ids, -1 padded.
+// Three kernels:
+//   k_index_score  (grid: chunks x sequences) streams the indexer keys once
+//     from HBM with 16-byte coalesced loads (bf16, or fp4 codes + E4M3 group
+//     scales dequantised in registers), computes each entry's score as a GEMV
+//     against the query's indexer vector, turns it into an order-preserving
+//     32-bit key, writes the keys to the workspace (4 B per entry, coalesced)
+//     and adds the chunk's histogram of the top 12 key bits into a
+//     per-sequence histogram.
+//   k_topk_filter  (grid: slices x sequences) finds, from that histogram, the
+//     bin holding the k-th largest key and keeps the entries of its slice
+//     whose bin is at or above it, in entry order (about k plus one bin's
+//     worth per sequence).
+//   k_topk_final   (grid: sequences) gathers those candidates, resolves the
+//     remaining 20 key bits by radix select in LDS, writes the ids in
+//     ascending entry order (ties go to the lower entry) and clears the
+//     histogram for the next call.
+// The selection is exact: every entry of a bin above the threshold bin is in
+// the top k, and the threshold bin is resolved on full keys.
 #include "kernels.h"
 
 namespace cskv {
 
 constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kHistPad = 257;               // per-wave histogram copies, bank-shifted
-constexpr int kMaxChunk = 16384;            // LDS keys of one chunk
-constexpr int kMaxMerge = 16384;            // candidates one merge workgroup holds
-constexpr int kAutoChunkMax = 8192;
+constexpr int kHistBits = 12;
+constexpr int kHistBins = 1 << kHistBits;   // per-sequence histogram of the top key bits
+constexpr int kBinShift = 32 - kHistBits;
+constexpr int kRadixPad = 257;              // per-wave radix histograms, bank-shifted
+constexpr int kCandCap = 4096;              // candidates the final select holds in LDS
+constexpr int kSliceUnit = 2048;            // keys a select workgroup filters per round
+constexpr int kMaxSlices = 2048;
 constexpr int kMisc = 16;
 
-// ------------------------------------------------------------- selection core
+// ------------------------------------------------------------- block helpers
 
-// k-th largest of keys[0..n) (1 <= k <= n) by 4 passes of 8-bit radix select.
-// Returns the key T and how many keys equal to T belong to the top k.
-__device__ void block_kth(const uint32_t* keys, int n, int k, uint32_t* hist, int* misc,
-                          uint32_t& T_out, int& need_eq_out) {
+// Exclusive prefix sum over the block in thread order; also returns the total.
+__device__ int block_exclusive_scan(int v, int* scratch, int& total) {
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
-  uint32_t prefix = 0;
-  int remaining = k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = t; i < kTopkWaves * kHistPad; i += kTopkThreads) hist[i] = 0u;
+  const int incl = wave_inclusive_scan(v);
+  if (lane == kWave - 1) scratch[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const int s = scratch[w];
+    if (w < wave) before += s;
+    total += s;
+  }
+  __syncthreads();
+  return before + incl - v;
+}
+
+// Radix select on the low `low_bits` bits: among keys[0..n) whose bits above
+// `low_bits` equal those of `prefix`, finds the rem-th largest (1 <= rem <=
+// their count). Returns the full key T and how many keys equal to T are
+// needed. `keys` may be in LDS or global memory; `hist` is LDS.
+__device__ void radix_select(const uint32_t* keys, int n, int rem, uint32_t prefix, int low_bits,
+                             uint32_t* hist, int* misc, uint32_t& T_out, int& need_eq_out) {
+  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  int hi = low_bits;
+  while (hi > 0) {
+    const int w = hi < 8 ? hi : 8;
+    const int shift = hi - w;
+    const uint32_t dmask = (1u << w) - 1u;
+    for (int i = t; i < kTopkWaves * kRadixPad; i += kTopkThreads) hist[i] = 0u;
     __syncthreads();
-    uint32_t* h = hist + wave * kHistPad;
-    for (int i = t; i < n; i += kTopkThreads) {
-      const uint32_t key = keys[i];
-      const bool match = (pass == 0) || (((key ^ prefix) >> (shift + 8)) == 0u);
-      if (match) atomicAdd(&h[(key >> shift) & 255u], 1u);
+    uint32_t* h = hist + wave * kRadixPad;
+    for (int i0 = 0; i0 < n; i0 += 4 * kTopkThreads) {
+      uint32_t kv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kTopkThreads + t;
+        kv[u] = i < n ? keys[i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kTopkThreads + t;
+        const bool match = hi >= 32 || ((kv[u] ^ prefix) >> hi) == 0u;
+        if (i < n && match) atomicAdd(&h[(kv[u] >> shift) & dmask], 1u);
+      }
     }
     __syncthreads();
     if (wave == 0) {
-      // lane l covers digits 255-4l .. 252-4l, so the scan runs from the top digit down
+      // lane l covers digits 255-4l .. 252-4l: the scan runs from the top digit down
       int c[4], s = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 255 - 4 * lane - j;
         int v = 0;
 #pragma unroll
-        for (int w = 0; w < kTopkWaves; ++w) v += (int)hist[w * kHistPad + d];
+        for (int ww = 0; ww < kTopkWaves; ++ww) v += (int)hist[ww * kRadixPad + d];
         c[j] = v;
         s += v;
       }
       int above = wave_inclusive_scan(s) - s;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (above < remaining && remaining <= above + c[j]) {
+        if (above < rem && rem <= above + c[j]) {
           misc[0] = 255 - 4 * lane - j;
           misc[1] = above;
         }
@@ -68,20 +110,20 @@ __device__ void block_kth(const uint32_t* keys, int n, int k, uint32_t* hist, in
       }
     }
     __syncthreads();
-    prefix |= (uint32_t)misc[0] << shift;
-    remaining -= misc[1];
+    prefix = (prefix & ~(dmask << shift)) | ((uint32_t)misc[0] << shift);
+    rem -= misc[1];
+    hi = shift;
     __syncthreads();
   }
   T_out = prefix;
-  need_eq_out = remaining;
+  need_eq_out = rem;
 }
 
 // Emits, in index order, every key > T plus the first need_eq keys == T (or
-// every key when `all`). Writes key (if out_key) and id = idx_map[i] (if
-// idx_map) else idx_base + i. Returns the number emitted (same in all threads).
-__device__ int block_emit(const uint32_t* keys, int n, bool all, uint32_t T, int need_eq,
-                          int* misc, uint32_t* out_key, int32_t* out_idx, int out_cap,
-                          const int32_t* idx_map, int32_t idx_base) {
+// every key when `all`): writes out_idx[p] = idx_map[i] (or idx_base + i).
+// Returns the number emitted (same in all threads).
+__device__ int block_emit(const uint32_t* keys, int n, bool all, uint32_t T, int need_eq, int* misc,
+                          int32_t* out_idx, int out_cap, const int32_t* idx_map, int32_t idx_base) {
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int per = (((n + kTopkWaves - 1) / kTopkWaves) + kWave - 1) & ~(kWave - 1);
   const int lo = wave * per;
@@ -128,10 +170,7 @@ __device__ int block_emit(const uint32_t* keys, int n, bool all, uint32_t T, int
     const uint64_t selm = __ballot(sel);
     if (sel) {
       const int p = pos + __popcll(selm & lanemask_lt());
-      if (p < out_cap) {   // always true when the selection is consistent; guards the store
-        if (out_key) out_key[p] = key;
-        out_idx[p] = idx_map ? idx_map[i] : idx_base + i;
-      }
+      if (p < out_cap) out_idx[p] = idx_map ? idx_map[i] : idx_base + i;
     }
     eq_run += __popcll(eqm);
     pos += __popcll(selm);
@@ -140,12 +179,20 @@ __device__ int block_emit(const uint32_t* keys, int n, bool all, uint32_t T, int
   return total < out_cap ? total : out_cap;
 }
 
-// ------------------------------------------------------------- level 0
+// ------------------------------------------------------------- scoring
 
-// bf16 keys: LPE = DI/8 lanes read one 16-byte slice each of an entry; a
+// Records one scored entry: its order key in LDS and in the chunk histogram.
+__device__ __forceinline__ void put_key(uint32_t* keys, uint32_t* hist, int e, float score) {
+  const uint32_t key = score_key(score);
+  keys[e] = key;
+  atomicAdd(&hist[key >> kBinShift], 1u);
+}
+
+// bf16 keys: LPE = DI/8 lanes read one 16-byte slice each of an entry; one
 // wave-wide load covers 64/LPE consecutive entries (1 KiB contiguous).
 template <int DI>
-__device__ void score_chunk_bf16(const uint16_t* q, const uint16_t* keys_g, int n, uint32_t* keys) {
+__device__ void score_chunk_bf16(const uint16_t* q, const uint16_t* keys_g, int n, uint32_t* keys,
+                                 uint32_t* hist) {
   constexpr int LPE = DI / 8;
   constexpr int EPL = kWave / LPE;
   constexpr int U = 8;
@@ -172,16 +219,17 @@ __device__ void score_chunk_bf16(const uint16_t* q, const uint16_t* keys_g, int 
       if constexpr (LPE == 16) p = sum_row16(p);
       else if constexpr (LPE == 4) p = sum_quad(p);
       const int e = (g0 + kTopkWaves * u) * EPL + sub;
-      if (cg == 0 && e < n) keys[e] = score_key(p);
+      if (cg == 0 && e < n) put_key(keys, hist, e, p);
     }
   }
 }
 
 // fp4 keys: each lane reads 16 code bytes (32 channels = two 16-channel groups)
-// and the two matching E4M3 group scales; LPE = DI/32 lanes per entry.
+// and the two matching E4M3 group scales; LPE = DI/32 lanes per entry. The
+// E2M1 codes are widened to bf16 exactly by the gfx950 converter.
 template <int DI>
 __device__ void score_chunk_fp4(const uint16_t* q, const uint8_t* codes_g, const uint8_t* scales_g,
-                                int n, uint32_t* keys) {
+                                int n, uint32_t* keys, uint32_t* hist) {
   constexpr int LPE = DI / 32;
   constexpr int EPL = kWave / LPE;
   constexpr int U = 8;
@@ -233,110 +281,273 @@ __device__ void score_chunk_fp4(const uint16_t* q, const uint8_t* codes_g, const
       float p = fmaf(g1s, e4m3_to_f32(s[u] >> 8), g0s * e4m3_to_f32(s[u] & 0xFFu));
       if constexpr (LPE == 4) p = sum_quad(p);
       const int e = (g0 + kTopkWaves * u) * EPL + sub;
-      if (part == 0 && e < n) keys[e] = score_key(p);
+      if (part == 0 && e < n) put_key(keys, hist, e, p);
     }
   }
 }
 
 template <int DI, bool FP4>
-__global__ __launch_bounds__(kTopkThreads) void k_index_chunk(
+__global__ __launch_bounds__(kTopkThreads) void k_index_score(
     const uint16_t* __restrict__ q_idx, const void* __restrict__ k_idx,
     const uint8_t* __restrict__ k_scale, const int32_t* __restrict__ n_entries, int64_t n_max,
-    int chunk, int k, int64_t n_lists, uint32_t* __restrict__ out_key,
-    int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt, int32_t* __restrict__ final_ids) {
+    int chunk, int64_t key_stride, uint32_t* __restrict__ ws_keys, uint32_t* __restrict__ ws_hist) {
   extern __shared__ uint32_t lds[];
-  uint32_t* keys = lds;
-  uint32_t* hist = lds + chunk;
-  int* misc = reinterpret_cast<int*>(hist + kTopkWaves * kHistPad);
+  uint32_t* hist = lds;
+  uint32_t* keys = lds + kHistBins;
+  const int t = threadIdx.x;
   const int64_t b = blockIdx.y;
-  const int64_t c = blockIdx.x;
   int64_t nv = n_entries ? (int64_t)n_entries[b] : n_max;
   nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
-  const int64_t start = c * chunk;
+  const int64_t start = (int64_t)blockIdx.x * chunk;
   const int64_t rem = nv - start;
-  const int n = rem <= 0 ? 0 : (rem > chunk ? chunk : (int)rem);
-  const int64_t list = b * n_lists + c;
+  if (rem <= 0) return;
+  const int n = rem > chunk ? chunk : (int)rem;
 
-  if (n > 0) {
-    const uint16_t* q = q_idx + b * DI;
-    if constexpr (FP4) {
-      const uint8_t* codes = reinterpret_cast<const uint8_t*>(k_idx) + (b * n_max + start) * (DI / 2);
-      const uint8_t* scales = k_scale + (b * n_max + start) * (DI / 16);
-      score_chunk_fp4<DI>(q, codes, scales, n, keys);
-    } else {
-      const uint16_t* kk = reinterpret_cast<const uint16_t*>(k_idx) + (b * n_max + start) * DI;
-      score_chunk_bf16<DI>(q, kk, n, keys);
-    }
+  for (int i = t; i < kHistBins; i += kTopkThreads) hist[i] = 0u;
+  __syncthreads();
+  const uint16_t* q = q_idx + b * DI;
+  if constexpr (FP4) {
+    const uint8_t* codes = reinterpret_cast<const uint8_t*>(k_idx) + (b * n_max + start) * (DI / 2);
+    const uint8_t* scales = k_scale + (b * n_max + start) * (DI / 16);
+    score_chunk_fp4<DI>(q, codes, scales, n, keys, hist);
+  } else {
+    const uint16_t* kk = reinterpret_cast<const uint16_t*>(k_idx) + (b * n_max + start) * DI;
+    score_chunk_bf16<DI>(q, kk, n, keys, hist);
   }
   __syncthreads();
-  const bool all = n <= k;
-  uint32_t T = 0u;
-  int need = 0;
-  if (!all) block_kth(keys, n, k, hist, misc, T, need);
-  int cnt = 0;
-  if (final_ids) {
-    int32_t* ids = final_ids + b * k;
-    if (n > 0) cnt = block_emit(keys, n, all, T, need, misc, nullptr, ids, k, nullptr, (int32_t)start);
-    for (int i = cnt + threadIdx.x; i < k; i += kTopkThreads) ids[i] = -1;
-  } else {
-    if (n > 0)
-      cnt = block_emit(keys, n, all, T, need, misc, out_key + list * k, out_idx + list * k, k, nullptr,
-                       (int32_t)start);
-    if (threadIdx.x == 0) out_cnt[list] = cnt;
+  // keys -> workspace (start and key_stride are multiples of 4: 16-byte stores)
+  uint32_t* dst = ws_keys + b * key_stride + start;
+  for (int i = 4 * t; i < n; i += 4 * kTopkThreads) {
+    if (i + 4 <= n) {
+      *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(keys + i);
+    } else {
+      for (int j = i; j < n; ++j) dst[j] = keys[j];
+    }
+  }
+  uint32_t* gh = ws_hist + b * kHistBins;
+  for (int i = t; i < kHistBins; i += kTopkThreads) {
+    const uint32_t h = hist[i];
+    if (h) atomicAdd(&gh[i], h);
   }
 }
 
-// ------------------------------------------------------------- levels >= 1
+// ------------------------------------------------------------- selection
 
-__global__ __launch_bounds__(kTopkThreads) void k_topk_merge(
-    const uint32_t* __restrict__ in_key, const int32_t* __restrict__ in_idx,
-    const int32_t* __restrict__ in_cnt, int64_t in_lists, int fanin, int k,
-    uint32_t* __restrict__ out_key, int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt,
-    int64_t out_lists, int32_t* __restrict__ final_ids) {
-  extern __shared__ uint32_t lds[];
-  const int cap = fanin * k;
-  uint32_t* keys = lds;
-  int32_t* idx = reinterpret_cast<int32_t*>(lds + cap);
-  uint32_t* hist = lds + 2 * cap;
-  int* misc = reinterpret_cast<int*>(hist + kTopkWaves * kHistPad);
-  int* offs = misc + kMisc;  // [fanin + 1]
-  const int64_t b = blockIdx.y;
-  const int64_t node = blockIdx.x;
-  const int64_t l0 = node * fanin;
-  const int m = (int)((l0 + fanin <= in_lists ? l0 + fanin : in_lists) - l0);
+struct SelectLds {
+  uint32_t ckey[kCandCap];
+  int32_t cidx[kCandCap];
+  uint32_t rhist[kTopkWaves * kRadixPad];
+  int pre[kMaxSlices + 1];
+  int misc[kMisc];
+  int scan[kTopkWaves];
+};
+
+// The bin of the k-th largest key of a sequence (1 <= k < total) and the
+// number of keys in the bins above it, from the global histogram.
+__device__ void threshold_bin(const uint32_t* gh, int k, int* scan, int* misc, int& tbin, int& above) {
   const int t = threadIdx.x;
-  if (t < kWave) {
-    const int cnt = t < m ? in_cnt[b * in_lists + l0 + t] : 0;
-    const int incl = wave_inclusive_scan(cnt);
-    if (t < m) offs[t + 1] = incl;
-    if (t == 0) offs[0] = 0;
+  constexpr int PER = kHistBins / kTopkThreads;   // 16 bins per thread, thread 0 the top ones
+  const int top = kHistBins - 1 - PER * t;
+  const uint4* p = reinterpret_cast<const uint4*>(gh + top - (PER - 1));
+  uint32_t h[PER];
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i) {
+    const uint4 v = p[i];
+    h[4 * i] = v.x; h[4 * i + 1] = v.y; h[4 * i + 2] = v.z; h[4 * i + 3] = v.w;
   }
-  __syncthreads();
-  const int total = offs[m];
-  for (int i = t; i < m * k; i += kTopkThreads) {
-    const int j = i / k, s = i - j * k;
-    if (s < offs[j + 1] - offs[j] && offs[j] + s < cap) {
-      const int64_t src = (b * in_lists + l0 + j) * k + s;
-      keys[offs[j] + s] = in_key[src];
-      idx[offs[j] + s] = in_idx[src];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s += (int)h[i];
+  int total;
+  int run = block_exclusive_scan(s, scan, total);
+  if (run < k && k <= run + s) {
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {   // h[PER-1] is this thread's top bin
+      const int c = (int)h[i];
+      if (run < k && k <= run + c) {
+        misc[0] = top - (PER - 1 - i);
+        misc[1] = run;
+      }
+      run += c;
     }
   }
   __syncthreads();
-  const bool all = total <= k;
-  uint32_t T = 0u;
-  int need = 0;
-  if (!all) block_kth(keys, total, k, hist, misc, T, need);
-  int cnt = 0;
-  if (final_ids) {
-    int32_t* ids = final_ids + b * k;
-    if (total > 0) cnt = block_emit(keys, total, all, T, need, misc, nullptr, ids, k, idx, 0);
-    for (int i = cnt + t; i < k; i += kTopkThreads) ids[i] = -1;
-  } else {
-    const int64_t list = b * out_lists + node;
-    if (total > 0)
-      cnt = block_emit(keys, total, all, T, need, misc, out_key + list * k, out_idx + list * k, k, idx, 0);
-    if (t == 0) out_cnt[list] = cnt;
+  tbin = misc[0];
+  above = misc[1];
+  __syncthreads();
+}
+
+// One workgroup per slice of a sequence: keeps the keys whose histogram bin
+// is at or above the threshold bin, in entry order, with their entry numbers.
+__global__ __launch_bounds__(kTopkThreads) void k_topk_filter(
+    const uint32_t* __restrict__ ws_keys, int64_t key_stride, const int32_t* __restrict__ n_entries,
+    int64_t n_max, int k, int slice, int n_slices, const uint32_t* __restrict__ ws_hist,
+    uint32_t* __restrict__ ws_ckey, int32_t* __restrict__ ws_cidx, int32_t* __restrict__ ws_cnt) {
+  __shared__ int scan[kTopkWaves];
+  __shared__ int misc[kMisc];
+  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  const int64_t b = blockIdx.y;
+  const int s = blockIdx.x;
+  int64_t nv = n_entries ? (int64_t)n_entries[b] : n_max;
+  nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
+  const int n_here = (int)min((int64_t)slice, max((int64_t)0, nv - (int64_t)s * slice));
+  int tbin = 0, above = 0;
+  if (nv > k && n_here > 0) threshold_bin(ws_hist + b * kHistBins, k, scan, misc, tbin, above);
+
+  const int64_t cand_base = (b * n_slices + s) * (int64_t)slice;
+  const uint32_t* src = ws_keys + b * key_stride + (int64_t)s * slice;
+  int written = 0;
+  for (int r0 = 0; r0 < n_here; r0 += kSliceUnit) {
+    const int rn = min(kSliceUnit, n_here - r0);
+    // wave w owns keys [r0 + 512w, r0 + 512w + 512) of the round, lane-strided
+    constexpr int PER = kSliceUnit / kTopkThreads;   // 8
+    uint32_t kv[PER];
+    bool keep[PER];
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = wave * (PER * kWave) + u * kWave + lane;
+      kv[u] = i < rn ? src[r0 + i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = wave * (PER * kWave) + u * kWave + lane;
+      keep[u] = i < rn && (int)(kv[u] >> kBinShift) >= tbin;
+      cnt += __popcll(__ballot(keep[u]));
+    }
+    if (lane == 0) scan[wave] = cnt;
+    __syncthreads();
+    int pos = written, round_total = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) {
+      const int c = scan[w];
+      if (w < wave) pos += c;
+      round_total += c;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const uint64_t m = __ballot(keep[u]);
+      if (keep[u]) {
+        const int p = pos + __popcll(m & lanemask_lt());
+        const int i = wave * (PER * kWave) + u * kWave + lane;
+        ws_ckey[cand_base + p] = kv[u];
+        ws_cidx[cand_base + p] = (int32_t)((int64_t)s * slice + r0 + i);
+      }
+      pos += __popcll(m);
+    }
+    written += round_total;
   }
+  if (t == 0) ws_cnt[b * n_slices + s] = written;
+}
+
+// One workgroup per sequence: gathers the slices' candidates, resolves the
+// threshold bin on full keys, writes the ids (ascending, -1 padded) and
+// clears the sequence's histogram for the next call.
+__global__ __launch_bounds__(kTopkThreads) void k_topk_final(
+    const int32_t* __restrict__ n_entries, int64_t n_max, int k, int slice, int n_slices,
+    uint32_t* __restrict__ ws_hist, uint32_t* __restrict__ ws_ckey, int32_t* __restrict__ ws_cidx,
+    const int32_t* __restrict__ ws_cnt, int32_t* __restrict__ ids) {
+  __shared__ SelectLds L;
+  const int t = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  int64_t nv = n_entries ? (int64_t)n_entries[b] : n_max;
+  nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
+  uint32_t* gh = ws_hist + b * kHistBins;
+  const bool take_all = nv <= k;
+  int tbin = 0, above = 0;
+  if (!take_all) threshold_bin(gh, k, L.scan, L.misc, tbin, above);
+
+  // slice offsets of the candidates
+  int32_t* out = ids + b * k;
+  const int32_t* cnt_b = ws_cnt + b * n_slices;
+  int total = 0;
+  for (int s0 = 0; s0 < n_slices; s0 += kTopkThreads) {
+    const int c = s0 + t < n_slices ? cnt_b[s0 + t] : 0;
+    int part_total;
+    const int ex = block_exclusive_scan(c, L.scan, part_total);
+    if (s0 + t < n_slices) L.pre[s0 + t] = total + ex;
+    total += part_total;
+  }
+  if (t == 0) L.pre[n_slices] = total;
+  __syncthreads();
+
+  const uint32_t* keys;
+  const int32_t* idxs;
+  if (total <= kCandCap) {
+    // gather into LDS, 8 loads in flight per thread
+    for (int j0 = 0; j0 < total; j0 += 8 * kTopkThreads) {
+      uint32_t kk[8];
+      int32_t ii[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * kTopkThreads + t;
+        kk[u] = 0u;
+        ii[u] = 0;
+        if (j < total) {
+          int lo = 0, hi = n_slices - 1;          // last slice with pre <= j
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (L.pre[mid] <= j) lo = mid; else hi = mid - 1;
+          }
+          const int64_t off = (b * n_slices + lo) * (int64_t)slice + (j - L.pre[lo]);
+          kk[u] = ws_ckey[off];
+          ii[u] = ws_cidx[off];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * kTopkThreads + t;
+        if (j < total) {
+          L.ckey[j] = kk[u];
+          L.cidx[j] = ii[u];
+        }
+      }
+    }
+    __syncthreads();
+    keys = L.ckey;
+    idxs = L.cidx;
+  } else {
+    // more candidates than LDS holds (heavily tied scores): compact the slices
+    // in place in global memory and select there (reads never overtake writes:
+    // a slice's destination offset is at most its source offset)
+    uint32_t* ck = ws_ckey + b * n_slices * (int64_t)slice;
+    int32_t* ci = ws_cidx + b * n_slices * (int64_t)slice;
+    for (int s1 = 1; s1 < n_slices; ++s1) {
+      const int c = L.pre[s1 + 1] - L.pre[s1];
+      const int64_t from = (int64_t)s1 * slice, to = L.pre[s1];
+      for (int j0 = 0; j0 < c; j0 += kTopkThreads) {
+        const int j = j0 + t;
+        uint32_t kk = 0u;
+        int32_t ii = 0;
+        if (j < c) { kk = ck[from + j]; ii = ci[from + j]; }
+        __syncthreads();
+        if (j < c) { ck[to + j] = kk; ci[to + j] = ii; }
+        __syncthreads();
+      }
+    }
+    __threadfence_block();
+    __syncthreads();
+    keys = ck;
+    idxs = ci;
+  }
+
+  int cnt = 0;
+  if (total > 0) {
+    if (take_all) {
+      cnt = block_emit(keys, total, true, 0u, 0, L.misc, out, k, idxs, 0);
+    } else {
+      uint32_t T;
+      int need_eq;
+      radix_select(keys, total, k - above, (uint32_t)tbin << kBinShift, kBinShift, L.rhist, L.misc, T,
+                   need_eq);
+      cnt = block_emit(keys, total, false, T, need_eq, L.misc, out, k, idxs, 0);
+    }
+  }
+  for (int i = cnt + t; i < k; i += kTopkThreads) out[i] = -1;
+
+  // leave the histogram clear for the next call
+  for (int i = t; i < kHistBins; i += kTopkThreads) gh[i] = 0u;
 }
 
 // ------------------------------------------------------------- planning / launch
@@ -344,59 +555,50 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_merge(
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, TopkPlan* p) {
+  (void)k;
   int64_t chunk = chunk_hint;
   if (chunk == 0) {
-    // aim at ~512 level-0 workgroups over the whole batch
-    int64_t want = (B * n_max + 511) / 512;
-    chunk = 1024;
-    while (chunk < want && chunk < kAutoChunkMax) chunk *= 2;
+    // about 1500 scoring workgroups over the batch, chunks of 512 .. 8192 entries
+    const int64_t want = (B * n_max + 1535) / 1536;
+    chunk = 512;
+    while (chunk < want && chunk < 8192) chunk *= 2;
   }
-  if (chunk < 256 || chunk > kMaxChunk || chunk % 256 != 0) return false;
+  if (chunk < 256 || chunk > 16384 || chunk % 256 != 0) return false;
   p->chunk = chunk;
-  p->fanin = kMaxMerge / k < 64 ? kMaxMerge / k : 64;
-  if (p->fanin < 2) return false;
-  int64_t lists = n_max <= 0 ? 1 : (n_max + chunk - 1) / chunk;
-  int lv = 0;
-  p->lists[lv++] = lists;
-  while (lists > 1) {
-    if (lv >= 8) return false;
-    lists = (lists + p->fanin - 1) / p->fanin;
-    p->lists[lv++] = lists;
-  }
-  p->levels = lv;
+  p->n_chunks = n_max <= 0 ? 1 : (n_max + chunk - 1) / chunk;
+  int64_t slice = kSliceUnit;
+  while ((n_max + slice - 1) / slice > kMaxSlices) slice *= 2;
+  if (slice > (int64_t)1 << 24) return false;
+  p->slice = slice;
+  p->n_slices = n_max <= 0 ? 1 : (n_max + slice - 1) / slice;
+  p->key_stride = (n_max + 3) & ~(int64_t)3;
+  const size_t nb = (size_t)B;
   size_t off = 0;
-  for (int i = 0; i < lv; ++i) {
-    p->off_key[i] = p->off_idx[i] = p->off_cnt[i] = 0;
-    if (i == lv - 1) break;  // the last level writes the caller's ids
-    const size_t n = (size_t)B * (size_t)p->lists[i];
-    p->off_key[i] = off; off = align256(off + n * (size_t)k * 4);
-    p->off_idx[i] = off; off = align256(off + n * (size_t)k * 4);
-    p->off_cnt[i] = off; off = align256(off + n * 4);
-  }
+  p->off_hist = off; off = align256(off + nb * kHistBins * 4);
+  p->zero_bytes = off;
+  p->off_cnt = off; off = align256(off + nb * (size_t)p->n_slices * 4);
+  p->off_keys = off; off = align256(off + nb * (size_t)p->key_stride * 4);
+  p->off_ckey = off; off = align256(off + nb * (size_t)p->n_slices * (size_t)slice * 4);
+  p->off_cidx = off; off = align256(off + nb * (size_t)p->n_slices * (size_t)slice * 4);
   p->bytes = off;
   return true;
 }
 
 template <int DI, bool FP4>
-static hipError_t launch_level0(const TopkPlan& p, const uint16_t* q_idx, const void* k_idx,
-                                const uint8_t* k_scale, const int32_t* n_entries, int64_t B,
-                                int64_t n_max, int k, int32_t* ids, uint8_t* ws,
-                                hipStream_t stream) {
-  const size_t shmem = (size_t)p.chunk * 4 + kTopkWaves * kHistPad * 4 + kMisc * 4;
-  auto kern = k_index_chunk<DI, FP4>;
+static hipError_t launch_score(const TopkPlan& p, const uint16_t* q_idx, const void* k_idx,
+                               const uint8_t* k_scale, const int32_t* n_entries, int64_t B,
+                               int64_t n_max, uint8_t* ws, hipStream_t stream) {
+  const size_t shmem = (size_t)kHistBins * 4 + (size_t)p.chunk * 4;
+  auto kern = k_index_score<DI, FP4>;
   if (shmem > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  const bool final_level = p.levels == 1;
-  dim3 grid((unsigned)p.lists[0], (unsigned)B);
-  hipLaunchKernelGGL(kern, grid, dim3(kTopkThreads), shmem, stream, q_idx, k_idx, k_scale,
-                     n_entries, n_max, (int)p.chunk, k, p.lists[0],
-                     final_level ? nullptr : reinterpret_cast<uint32_t*>(ws + p.off_key[0]),
-                     final_level ? nullptr : reinterpret_cast<int32_t*>(ws + p.off_idx[0]),
-                     final_level ? nullptr : reinterpret_cast<int32_t*>(ws + p.off_cnt[0]),
-                     final_level ? ids : nullptr);
+  dim3 grid((unsigned)p.n_chunks, (unsigned)B);
+  hipLaunchKernelGGL(kern, grid, dim3(kTopkThreads), shmem, stream, q_idx, k_idx, k_scale, n_entries,
+                     n_max, (int)p.chunk, p.key_stride, reinterpret_cast<uint32_t*>(ws + p.off_keys),
+                     reinterpret_cast<uint32_t*>(ws + p.off_hist));
   return hipGetLastError();
 }
 
@@ -405,38 +607,30 @@ hipError_t launch_index_topk(const TopkPlan& p, const uint16_t* q_idx, bool fp4,
                              int64_t n_max, int Di, int k, int32_t* ids, void* workspace,
                              hipStream_t stream) {
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  hipError_t e;
-  if (fp4) {
-    e = Di == 128 ? launch_level0<128, true>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream)
-                  : launch_level0<32, true>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream);
-  } else {
-    e = Di == 128 ? launch_level0<128, false>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream)
-                  : launch_level0<32, false>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream);
+  hipError_t e = hipSuccess;
+  if (n_max > 0) {
+    if (fp4) {
+      e = Di == 128 ? launch_score<128, true>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, ws, stream)
+                    : launch_score<32, true>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, ws, stream);
+    } else {
+      e = Di == 128 ? launch_score<128, false>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, ws, stream)
+                    : launch_score<32, false>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, ws, stream);
+    }
+    if (e != hipSuccess) return e;
   }
+  dim3 grid((unsigned)p.n_slices, (unsigned)B);
+  hipLaunchKernelGGL(k_topk_filter, grid, dim3(kTopkThreads), 0, stream,
+                     reinterpret_cast<const uint32_t*>(ws + p.off_keys), p.key_stride, n_entries, n_max,
+                     k, (int)p.slice, (int)p.n_slices, reinterpret_cast<const uint32_t*>(ws + p.off_hist),
+                     reinterpret_cast<uint32_t*>(ws + p.off_ckey), reinterpret_cast<int32_t*>(ws + p.off_cidx),
+                     reinterpret_cast<int32_t*>(ws + p.off_cnt));
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t shmem = (size_t)p.fanin * k * 8 + kTopkWaves * kHistPad * 4 + kMisc * 4 +
-                       ((size_t)p.fanin + 1) * 4;
-  if (p.levels > 1 && shmem > 65536) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_merge),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    if (e != hipSuccess) return e;
-  }
-  for (int lv = 1; lv < p.levels; ++lv) {
-    const bool final_level = lv == p.levels - 1;
-    dim3 grid((unsigned)p.lists[lv], (unsigned)B);
-    hipLaunchKernelGGL(k_topk_merge, grid, dim3(kTopkThreads), shmem, stream,
-                       reinterpret_cast<const uint32_t*>(ws + p.off_key[lv - 1]),
-                       reinterpret_cast<const int32_t*>(ws + p.off_idx[lv - 1]),
-                       reinterpret_cast<const int32_t*>(ws + p.off_cnt[lv - 1]), p.lists[lv - 1],
-                       p.fanin, k,
-                       final_level ? nullptr : reinterpret_cast<uint32_t*>(ws + p.off_key[lv]),
-                       final_level ? nullptr : reinterpret_cast<int32_t*>(ws + p.off_idx[lv]),
-                       final_level ? nullptr : reinterpret_cast<int32_t*>(ws + p.off_cnt[lv]),
-                       p.lists[lv], final_level ? ids : nullptr);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  hipLaunchKernelGGL(k_topk_final, dim3((unsigned)B), dim3(kTopkThreads), 0, stream, n_entries, n_max, k,
+                     (int)p.slice, (int)p.n_slices, reinterpret_cast<uint32_t*>(ws + p.off_hist),
+                     reinterpret_cast<uint32_t*>(ws + p.off_ckey), reinterpret_cast<int32_t*>(ws + p.off_cidx),
+                     reinterpret_cast<const int32_t*>(ws + p.off_cnt), ids);
+  return hipGetLastError();
 }
 
 }  // namespace cskv

@@ -15,16 +15,19 @@ hipError_t launch_compress(int kind, const uint16_t* S, const float* gate, int64
                            float* cache_scale, int64_t cache_rows, hipStream_t stream);
 
 // ---- index_topk.hip
-// Plan of the selection tree: level 0 scores `chunk` entries per workgroup and
-// keeps each chunk's best k; every further level merges up to `fanin` lists
-// into one until a single list per sequence remains.
+// Plan of the indexer: k_index_score scores `chunk` entries per workgroup,
+// k_topk_filter filters `slice` keys per workgroup, k_topk_final finishes one
+// sequence per workgroup. Workspace regions (byte offsets): the per-sequence
+// histogram comes first (it must be zero when a call starts and every call
+// leaves it zero), then the slice candidate counts, the order keys and the
+// candidate keys / entry numbers.
 struct TopkPlan {
-  int64_t chunk;         // entries per level-0 workgroup
-  int64_t lists[8];      // lists per sequence produced by level i (lists[0] = chunks)
-  int levels;            // number of levels (the last one yields 1 list)
-  int fanin;             // lists merged per workgroup above level 0
-  size_t bytes;          // workspace bytes
-  size_t off_key[8], off_idx[8], off_cnt[8];
+  int64_t chunk, n_chunks;     // entries per scoring workgroup, workgroups per sequence
+  int64_t slice, n_slices;     // keys per selection workgroup, workgroups per sequence
+  int64_t key_stride;          // order keys per sequence row (a multiple of 4)
+  size_t off_hist, off_cnt, off_keys, off_ckey, off_cidx;
+  size_t zero_bytes;           // leading bytes that must be zero between calls
+  size_t bytes;                // workspace bytes
 };
 bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, TopkPlan* plan);
 hipError_t launch_index_topk(const TopkPlan& plan, const uint16_t* q_idx, bool fp4,

@@ -20,9 +20,10 @@
  *     describes the problem. A fault inside a kernel is reported by the HIP
  *     runtime at the caller's next synchronisation, not by these calls.
  *   - Workspaces are caller-provided device buffers of at least the size the
- *     matching *_workspace() query returns (for the same arguments). They must
- *     be zero-filled before their first use; every completed call leaves them
- *     reusable. Two calls that share a workspace must be stream-ordered.
+ *     matching *_workspace() query returns (for the same arguments), 256-byte
+ *     aligned. Two calls that share a workspace must be stream-ordered. The
+ *     index_topk workspace carries state between calls (see there); the
+ *     attend workspace does not.
  */
 #ifndef CSKV_H
 #define CSKV_H
@@ -106,7 +107,14 @@ cskv_status cskv_compress(int32_t kind, const void* S, const float* gate, int64_
  *   ids       [B, k] int32
  *   chunk     entries scored per workgroup: 0 = automatic, else a multiple
  *             of 256 in [256, 16384]
- * EUNSUPPORTED if the entry count needs more than three selection levels.
+ *   workspace cskv_index_topk_workspace() bytes. Its leading region holds a
+ *             per-sequence histogram and completion counter that must be zero
+ *             when a call starts: zero-fill the workspace before the first
+ *             call, and again before a call with different B, n_max, k or
+ *             chunk or after the buffer served another purpose. Every completed
+ *             call leaves that region zero, so calls with the same arguments
+ *             can reuse the workspace as it is.
+ * EUNSUPPORTED if n_max needs selection slices longer than 2^24 entries.
  */
 size_t cskv_index_topk_workspace(int64_t B, int64_t n_max, int32_t Di, int32_t k,
                                  int32_t key_dtype, int32_t chunk);

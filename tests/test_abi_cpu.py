@@ -38,12 +38,16 @@ def test_version_and_status_strings(lib):
 
 
 def test_topk_workspace_sizes(lib):
-    # 32 x 32767 entries, k = 512: 2048-entry chunks, one merge level
-    ws = lib._lib_topk_ws(32, 32767, 128, 512, lib.BF16, 0)
-    lists = -(-32767 // 2048)
-    assert ws >= 32 * lists * 512 * 8 and ws < 32 * lists * 512 * 8 + 32 * lists * 4 + 4096
-    # one chunk covers everything: no workspace
-    assert lib._lib_topk_ws(1, 511, 32, 64, lib.BF16, 0) == 0
+    # 32 x 32767 entries, k = 512: a 4096-bin histogram per sequence, one order
+    # key per entry and room for every entry as a candidate (key + entry number)
+    B, N = 32, 32767
+    ws = lib._lib_topk_ws(B, N, 128, 512, lib.BF16, 0)
+    need = B * (4096 * 4 + N * 4 + 2 * N * 4)
+    assert need <= ws <= need + B * (8 * 2048 * 4 + 64) + 64 * 1024
+    # a single entry still needs the histogram and counter
+    assert lib._lib_topk_ws(1, 1, 32, 64, lib.BF16, 0) >= 4096 * 4 + 4
+    # the size grows with the batch
+    assert lib._lib_topk_ws(64, N, 128, 512, lib.BF16, 0) > ws
     # rejected shapes report 0
     assert lib._lib_topk_ws(1, 100, 64, 8, lib.BF16, 0) == 0
     assert lib._lib_topk_ws(1, 100, 128, 4096, lib.BF16, 0) == 0

@@ -38,7 +38,7 @@ def _oracle_ids(q, kk, k, n_valid=None):
     (1, 511, 32, 64, 4, 0),          # the tiny workload's shape
     (3, 5000, 128, 512, 8, 1024),    # several chunks and a ragged tail
     (2, 33000, 128, 512, 8, 0),      # automatic chunking
-    (2, 25600, 128, 64, 8, 256),     # three selection levels (100 chunks -> 2 lists -> 1)
+    (2, 25600, 128, 64, 8, 256),     # 100 scoring chunks, 13 selection slices per sequence
     (4, 777, 128, 2048, 8, 256),     # k larger than N: -1 padding
     (2, 4096, 32, 100, 1, 512),      # values in [-1, 1]: massive ties
 ])
@@ -106,3 +106,75 @@ def test_topk_rejects_bad_arguments(cskv):
     q64 = np.zeros((1, 64), dtype=np.uint16)
     with pytest.raises(cskv.CskvError):
         cskv.index_topk(to_dev_bf16(q64), to_dev_bf16(np.zeros((1, 10, 64), dtype=np.uint16)), 4)
+
+
+def test_topk_ties_beyond_lds_capacity(cskv):
+    """More than 4096 entries share the threshold bin: the selection runs from
+    global memory instead of LDS and must still be exact."""
+    B, N, Di, k = 2, 40000, 128, 512
+    q = np.full((B, Di), F.f32_to_bf16(np.float32(1.0)), dtype=np.uint16)
+    kk = np.zeros((B, N, Di), dtype=np.uint16)
+    one = F.f32_to_bf16(np.float32(1.0))
+    kk[0, 39000:39100, 0] = one                    # 100 entries score 1, the rest 0
+    kk[1, 5:9, 0] = F.f32_to_bf16(np.float32(-1.0))
+    ids = cskv.index_topk(to_dev_bf16(q), to_dev_bf16(kk), k).cpu().numpy()
+    assert np.array_equal(ids, _oracle_ids(q, kk, k))
+    assert np.array_equal(ids[0], np.concatenate([np.arange(412), np.arange(39000, 39100)]).astype(np.int32))
+
+
+def test_topk_workspace_reuse_across_shapes(cskv):
+    """Calls with changing shapes and interleaved attend calls: every result
+    must match the oracle (the workspace state is rebuilt when the shape changes)."""
+    shapes = [(2, 5000, 128, 512), (3, 9000, 128, 512), (2, 5000, 128, 512), (1, 70000, 32, 64),
+              (2, 5000, 128, 512)]
+    for i, (B, N, Di, k) in enumerate(shapes):
+        q, kk = _bf16_case(900 + i, B, N, Di, 8)
+        ids = cskv.index_topk(to_dev_bf16(q), to_dev_bf16(kk), k).cpu().numpy()
+        assert np.array_equal(ids, _oracle_ids(q, kk, k)), (i, B, N)
+        Q = torch.zeros((B, 16, 128), dtype=torch.bfloat16, device="cuda")
+        cache = torch.zeros((B, 700, 128), dtype=torch.bfloat16, device="cuda")
+        cskv.attend(Q, cache, None, None, softmax_scale=0.1, splits=4)
+
+
+def _device_int_keys(seed, B, N, Di, a):
+    from synth import device as sd
+    q = sd.new((B, Di), synth.KIND_INT_BF16, synth.stream_key(seed, synth.T_QIDX), a=a)
+    kk = sd.new((B, N, Di), synth.KIND_INT_BF16, synth.stream_key(seed, synth.T_KIDX), a=a)
+    return q, kk
+
+
+@pytest.mark.slow
+def test_topk_full_size_c4a_128k_bf16(cskv):
+    """The 128K bf16 workload at full size (32 sequences x 32767 entries, Di 128,
+    top-512), in the launch configuration the benchmark uses; sampled sequences
+    are regenerated on the host for the oracle."""
+    from synth.configs import C4A_128K as w
+    B, N, Di = w.B, w.n_entries, w.Di
+    q_d, kk_d = _device_int_keys(w.seed, B, N, Di, w.idx_range)
+    ids = cskv.index_topk(q_d, kk_d, w.k).cpu().numpy()
+    kq, kk_ = synth.stream_key(w.seed, synth.T_QIDX), synth.stream_key(w.seed, synth.T_KIDX)
+    for b in (0, 13, B - 1):
+        q = F.bf16_to_f64(synth.int_bf16(kq, b * Di, Di, w.idx_range))
+        keys = F.bf16_to_f64(synth.int_bf16(kk_, b * N * Di, N * Di, w.idx_range).reshape(N, Di))
+        assert np.array_equal(ids[b], M.topk_ids(M.index_scores(q, keys), w.k)), b
+    assert np.all(np.diff(ids, axis=1) > 0)
+
+
+@pytest.mark.slow
+def test_topk_full_size_c4a_1m_fp4(cskv):
+    """The 1M-context fp4 workload at full size (8 sequences x 262143 entries)."""
+    from synth import device as sd
+    from synth.configs import C4A_1M_Q as w
+    B, N, Di = w.B, w.n_entries, w.Di
+    kq = synth.stream_key(w.seed, synth.T_QIDX)
+    kc = synth.stream_key(w.seed, synth.T_KIDX)
+    ks = synth.stream_key(w.seed, synth.T_KIDX_SCALE)
+    q_d = sd.new((B, Di), synth.KIND_INT_BF16, kq, a=w.idx_range)
+    codes_d = sd.new((B, N, Di // 2), synth.KIND_BYTES, kc)
+    sc_d = sd.new((B, N, Di // 16), synth.KIND_POW2_E4M3, ks, emin=-2, emax=2)
+    ids = cskv.index_topk(q_d, codes_d, w.k, k_scale=sc_d).cpu().numpy()
+    for b in (0, B - 1):
+        q = F.bf16_to_f64(synth.int_bf16(kq, b * Di, Di, w.idx_range))
+        codes = synth.random_bytes(kc, b * N * Di // 2, N * Di // 2).reshape(N, Di // 2)
+        sc = synth.pow2_e4m3(ks, b * N * Di // 16, N * Di // 16, -2, 2).reshape(N, Di // 16)
+        assert np.array_equal(ids[b], M.topk_ids(M.index_scores(q, F.decode_fp4_g16(codes, sc)), w.k)), b
