@@ -11,10 +11,12 @@
 // and run on 16x16x32 bf16 MFMA. A workgroup (4 waves) owns one sequence and a
 // contiguous split of its key slots; wave w owns heads 16w .. 16w+15. Per tile
 // of 32 key slots:
-//   1. the rows (bf16, or fp8 codes widened exactly to bf16; an fp8 row's
-//      scale is folded into its logits and probabilities) are gathered from
-//      HBM into registers one tile ahead and stored row-major into one of two
-//      LDS buffers (one barrier per tile);
+//   1. the rows reach LDS one tile ahead of their use: bf16 rows of 1 KiB by
+//      direct HBM->LDS DMA (non-temporal, no registers), fp8 rows by DMA into
+//      a staging buffer and one cooperative pass that widens the codes to bf16
+//      exactly (an fp8 row's scale is folded into its logits and
+//      probabilities); other shapes through registers. Entry ids of sparse
+//      reads are fetched one tile earlier still, so no DMA waits on an id;
 //   2. S^T[32 keys x 16 heads] = K Q^T with Q held in registers;
 //   3. online softmax per head in the exp2 domain; the running maximum is
 //      raised only when a logit exceeds it by more than 2^8, so the
@@ -23,6 +25,9 @@
 //      the QK^T product left them in (they are exactly the B operand, for a
 //      matching order of the 32 keys), and K^T comes from the row-major tile
 //      through gfx950's transposing LDS reads.
+// Tile rows are padded to a stride of 8 (mod 64) dwords and their 16-byte
+// chunks are XOR-swizzled by (row / 8) mod 4, which keeps both the row reads of
+// QK^T and the transposing reads of PV free of LDS bank conflicts.
 // Each lane ends with 4 consecutive channels of one head: rotary pairs sit in
 // one lane. With one split the epilogue normalises, applies inverse RoPE and
 // stores O; otherwise partials (max, sum, unnormalised O) go to the workspace
@@ -38,41 +43,47 @@ constexpr int kTK = 32;        // key slots per tile
 constexpr int kHMax = 64;      // heads per workgroup (4 waves x 16)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRescale = 8.0f;   // log2 headroom before the running max is raised
+constexpr int kCachePolicyStream = 2;  // non-temporal loads for rows read once
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-template <int D>
+// Swizzle of a tile row's 16-byte chunks.
+__device__ __forceinline__ int chunk_swz(int row) { return (row >> 3) & 3; }
+
+template <int D, bool CFP8, bool WFP8>
 struct AttLayout {
-  // row stride in bf16: D + 24 makes the stride 12 (mod 64) dwords, so the
-  // 16-byte row reads of QK^T and the transposing reads of PV are free of
-  // bank conflicts within each 16-lane group
-  static constexpr int KROW = D + 24;
+  static constexpr bool kAllFp8 = CFP8 && WFP8;
+  static constexpr bool kDma = D == 512 && !CFP8 && !WFP8;      // bf16 rows by DMA
+  static constexpr bool kDmaFp8 = D == 512 && kAllFp8;          // fp8 rows by DMA + widening pass
+  static constexpr int KROW = D + 16;                           // bf16 per tile row
+  static constexpr int NBUF = kDmaFp8 ? 1 : 2;                  // bf16 tiles
   static constexpr size_t tile_bytes = (size_t)kTK * KROW * 2;
-  static constexpr size_t off_tile0 = 0;
-  static constexpr size_t off_tile1 = tile_bytes;
-  static constexpr size_t off_rs = 2 * tile_bytes;             // [2][kTK] logit factor per slot
-  static constexpr size_t off_ps = off_rs + 2 * kTK * 4;       // [2][kTK] value scale (-inf: masked)
+  static constexpr size_t stage_bytes = kDmaFp8 ? (size_t)kTK * D : 0;   // fp8 rows, unpadded
+  static constexpr size_t off_tile = 0;
+  static constexpr size_t off_stage = NBUF * tile_bytes;                 // [2] staging tiles
+  static constexpr size_t off_rs = off_stage + 2 * stage_bytes;          // [2][kTK] logit factor per slot
+  static constexpr size_t off_ps = off_rs + 2 * kTK * 4;                 // [2][kTK] value scale (-inf: empty)
   static constexpr size_t off_cos = off_ps + 2 * kTK * 4;
   static constexpr size_t off_sin = off_cos + (D / 2) * 4;
   static constexpr size_t bytes = off_sin + (D / 2) * 4;
 };
 
-// Where a tile's rows come from: the slot's row pointer (nullptr for an
-// empty slot: an id out of range, or past the last key) and whether it is fp8.
+// Where a slot's row lives: pointer (nullptr for an empty slot - an id out of
+// range, or past the last key) and its fp8 row scale (nullptr for bf16).
 struct SlotRow {
   const uint8_t* ptr;
-  const float* scale;   // fp8 row scale, nullptr for bf16
+  const float* scale;
 };
 
 template <int D, bool CFP8, bool WFP8>
-__device__ __forceinline__ SlotRow slot_row(const AttendArgs& a, int64_t b, int64_t slot, int64_t n_sel,
-                                            int64_t n_keys, bool dense) {
+__device__ __forceinline__ SlotRow slot_row(const AttendArgs& a, int64_t b, int64_t slot, int64_t row_id,
+                                            int64_t n_sel, int64_t n_keys) {
   SlotRow sr{nullptr, nullptr};
   if (slot >= n_keys) return sr;
   if (slot < n_sel) {
-    const int64_t row = dense ? slot : (int64_t)a.ids[b * a.k + slot];
-    if (row < 0 || row >= a.cache_rows) return sr;
-    const int64_t r = b * a.cache_rows + row;
+    if (row_id < 0 || row_id >= a.cache_rows) return sr;
+    const int64_t r = b * a.cache_rows + row_id;
     sr.ptr = reinterpret_cast<const uint8_t*>(a.cache) + r * D * (CFP8 ? 1 : 2);
     sr.scale = CFP8 ? a.cache_scale + r : nullptr;
   } else {
@@ -83,8 +94,13 @@ __device__ __forceinline__ SlotRow slot_row(const AttendArgs& a, int64_t b, int6
   return sr;
 }
 
-// Per-slot factors of a tile: logit factor (value scale * tau * log2 e) and
-// value scale (-inf marks an empty slot).
+// Entry id of a slot (sparse: from ids; dense: the slot itself).
+__device__ __forceinline__ int64_t slot_id(const AttendArgs& a, int64_t b, int64_t slot, int64_t n_sel,
+                                           bool dense) {
+  if (dense || slot >= n_sel || slot < 0) return slot;
+  return (int64_t)a.ids[b * a.k + slot];
+}
+
 __device__ __forceinline__ void put_slot(uint8_t* lds, size_t off_rs, size_t off_ps, int buf, int j,
                                          float vs, float tau_log2e) {
   float* rs = reinterpret_cast<float*>(lds + off_rs) + buf * kTK;
@@ -93,84 +109,136 @@ __device__ __forceinline__ void put_slot(uint8_t* lds, size_t off_rs, size_t off
   ps[j] = vs;
 }
 
-// Direct HBM -> LDS fill of a bf16 tile with D = 512: every wave instruction
-// moves one 1 KiB row (16 bytes per lane) into its padded LDS row, no
-// registers involved. Wave w fills rows 8w .. 8w+7; empty slots are zeroed.
+__device__ __forceinline__ const uint8_t* lane_ptr(uint64_t p, int lane) {
+  const uint32_t lo32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)p, lane);
+  const uint32_t hi32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(p >> 32), lane);
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi32 << 32) | lo32);
+}
+
+// A tile row as lane j < 8 of wave w holds it for row 8w + j: its address and
+// value scale (-inf for an empty slot), resolved one tile before its DMA so that
+// issuing the DMA never waits on an id or scale load.
+struct RowRef {
+  uint64_t ptr;
+  float vs;
+};
+
 template <int D, bool CFP8, bool WFP8>
-__device__ __forceinline__ void dma_tile(const AttendArgs& a, int64_t b, int64_t slot0, int64_t n_sel,
-                                         int64_t n_keys, bool dense, uint8_t* lds, int buf, float tau_log2e,
-                                         int wave, int lane) {
-  using L = AttLayout<D>;
-  static_assert(D * 2 == kWave * 16, "one wave instruction moves one row");
-  uint8_t* tile = lds + (buf ? L::off_tile1 : L::off_tile0);
-  uint64_t p = 0;
-  if (lane < 8) {
-    const SlotRow sr = slot_row<D, CFP8, WFP8>(a, b, slot0 + 8 * wave + lane, n_sel, n_keys, dense);
-    p = reinterpret_cast<uint64_t>(sr.ptr);
-    put_slot(lds, L::off_rs, L::off_ps, buf, 8 * wave + lane, sr.ptr ? 1.0f : -INFINITY, tau_log2e);
-  }
+__device__ __forceinline__ RowRef resolve_row(const AttendArgs& a, int64_t b, int64_t slot, int64_t row_id,
+                                              int64_t n_sel, int64_t n_keys) {
+  const SlotRow sr = slot_row<D, CFP8, WFP8>(a, b, slot, row_id, n_sel, n_keys);
+  RowRef r;
+  r.ptr = reinterpret_cast<uint64_t>(sr.ptr);
+  r.vs = !sr.ptr ? -INFINITY : (sr.scale ? *sr.scale : 1.0f);
+  return r;
+}
+
+// DMA fill of one tile: wave w moves rows 8w .. 8w+7 whose references lanes
+// 0-7 hold. bf16 rows (1 KiB) go straight into their swizzled LDS row; fp8
+// rows (512 B, two per wave instruction) go into the staging tile. Empty bf16
+// rows are zeroed here, empty fp8 rows by the widening pass.
+template <int D, bool CFP8, bool WFP8>
+__device__ __forceinline__ void dma_tile(const RowRef& ref, uint8_t* lds, int buf, float tau_log2e, int wave,
+                                         int lane) {
+  using L = AttLayout<D, CFP8, WFP8>;
+  const uint64_t p = lane < 8 ? ref.ptr : 0;
+  if (lane < 8) put_slot(lds, L::off_rs, L::off_ps, buf, 8 * wave + lane, ref.vs, tau_log2e);
+  if constexpr (L::kDma) {
+    uint8_t* tile = lds + L::off_tile + buf * L::tile_bytes;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t lo32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)p, i);
-    const uint32_t hi32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(p >> 32), i);
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(((uint64_t)hi32 << 32) | lo32);
-    uint8_t* row = tile + (size_t)(8 * wave + i) * L::KROW * 2;
-    if (src) {
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + 16 * lane),
-                                       (__attribute__((address_space(3))) void*)row, 16, 0, 0);
-    } else {
-      *reinterpret_cast<uint4*>(row + 16 * lane) = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * wave + i;
+      const uint8_t* src = lane_ptr(p, i);
+      uint8_t* row = tile + (size_t)r * L::KROW * 2;
+      // lane l fills chunk position l, which holds logical chunk l ^ swz(r)
+      if (src) {
+        __builtin_amdgcn_global_load_lds(
+            (__attribute__((address_space(1))) void*)(src + 16 * (lane ^ chunk_swz(r))),
+            (__attribute__((address_space(3))) void*)row, 16, 0, kCachePolicyStream);
+      } else {
+        *reinterpret_cast<uint4*>(row + 16 * lane) = make_uint4(0, 0, 0, 0);
+      }
+    }
+  } else {
+    static_assert(L::kDmaFp8, "DMA fill needs bf16 or fp8 rows of D = 512");
+    uint8_t* stage = lds + L::off_stage + buf * L::stage_bytes;
+    const int half = lane >> 5, hl = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // lanes 0-31 move row 2i, lanes 32-63 row 2i+1 (readlane needs a uniform lane)
+      const uint8_t* src_even = lane_ptr(p, 2 * i);
+      const uint8_t* src_odd = lane_ptr(p, 2 * i + 1);
+      const uint8_t* src = half ? src_odd : src_even;
+      if (src) {
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + 16 * hl),
+                                         (__attribute__((address_space(3))) void*)(stage + (8 * wave + 2 * i) * D),
+                                         16, 0, kCachePolicyStream);
+      }
     }
   }
 }
 
-// Register-staged fill (fp8 rows, mixed dtypes, or D = 128): one thread's
-// share is rows 8*kb .. 8*kb+7, channels 8*cb .. 8*cb+7. When every row is
-// fp8 the codes are kept as loaded (8 bytes) and widened to bf16 when written
-// to LDS; otherwise each row is held as 8 bf16.
-template <bool RAW_FP8>
+// Widens a staged fp8 tile into the bf16 tile: thread t converts 64 codes of
+// row t/8 (logical chunks 8(t%8) .. 8(t%8)+7); empty slots become zeros.
+template <int D>
+__device__ __forceinline__ void widen_tile(uint8_t* lds, int buf) {
+  using L = AttLayout<D, true, true>;
+  const int t = threadIdx.x;
+  const int r = t >> 3, part = t & 7;
+  const uint8_t* stage = lds + L::off_stage + buf * L::stage_bytes + r * D + part * 64;
+  const float* ps = reinterpret_cast<const float*>(lds + L::off_ps) + buf * kTK;
+  const bool empty = ps[r] == -INFINITY;
+  uint4 c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c[j] = *reinterpret_cast<const uint4*>(stage + 16 * j);
+  uint16_t* row = reinterpret_cast<uint16_t*>(lds + L::off_tile) + r * L::KROW;
+  const int swz = chunk_swz(r);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint4 lo = fp8x8_to_bf16x8(make_uint2(c[j].x, c[j].y));
+    uint4 hi = fp8x8_to_bf16x8(make_uint2(c[j].z, c[j].w));
+    if (empty) lo = hi = make_uint4(0, 0, 0, 0);
+    const int ch0 = 8 * part + 2 * j;          // logical chunks ch0, ch0 + 1
+    *reinterpret_cast<uint4*>(row + 8 * (ch0 ^ swz)) = lo;
+    *reinterpret_cast<uint4*>(row + 8 * ((ch0 + 1) ^ swz)) = hi;
+  }
+}
+
+// Register-staged fill (mixed cache/window dtypes, or D = 128): one thread's
+// share is rows 8*kb .. 8*kb+7, logical chunk cb (8 channels), held as bf16.
 struct TileRegs {
-  typename std::conditional<RAW_FP8, uint2, uint4>::type r[8];
+  uint4 r[8];
   float vs[8];     // value scale of the row (1 for bf16), or -inf for an empty slot
 };
 
 template <int D, bool CFP8, bool WFP8>
 __device__ __forceinline__ void load_tile(const AttendArgs& a, int64_t b, int64_t slot0, int64_t n_sel,
-                                          int64_t n_keys, bool dense, int kb, int cb,
-                                          TileRegs<CFP8 && WFP8>& t) {
-  constexpr bool RAW = CFP8 && WFP8;
+                                          int64_t n_keys, bool dense, int kb, int cb, TileRegs& t) {
   const bool active_c = cb * 8 < D;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    if constexpr (RAW) t.r[i] = make_uint2(0, 0);
-    else t.r[i] = make_uint4(0, 0, 0, 0);
+    t.r[i] = make_uint4(0, 0, 0, 0);
     t.vs[i] = -INFINITY;
-    const SlotRow sr = slot_row<D, CFP8, WFP8>(a, b, slot0 + 8 * kb + i, n_sel, n_keys, dense);
+    const int64_t slot = slot0 + 8 * kb + i;
+    const SlotRow sr = slot_row<D, CFP8, WFP8>(a, b, slot, slot_id(a, b, slot, n_sel, dense), n_sel, n_keys);
     if (!sr.ptr) continue;
     t.vs[i] = sr.scale ? *sr.scale : 1.0f;
     if (!active_c) continue;
-    if (sr.scale) {
-      const uint2 c = *reinterpret_cast<const uint2*>(sr.ptr + cb * 8);
-      if constexpr (RAW) t.r[i] = c;
-      else t.r[i] = fp8x8_to_bf16x8(c);
-    } else {
-      if constexpr (!RAW) t.r[i] = *reinterpret_cast<const uint4*>(sr.ptr + cb * 16);
-    }
+    if (sr.scale) t.r[i] = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(sr.ptr + cb * 8));
+    else t.r[i] = *reinterpret_cast<const uint4*>(sr.ptr + cb * 16);
   }
 }
 
 template <int D, bool CFP8, bool WFP8>
-__device__ __forceinline__ void store_tile(uint8_t* lds, int buf, int kb, int cb,
-                                           const TileRegs<CFP8 && WFP8>& t, float tau_log2e) {
-  using L = AttLayout<D>;
-  uint16_t* tile = reinterpret_cast<uint16_t*>(lds + (buf ? L::off_tile1 : L::off_tile0));
+__device__ __forceinline__ void store_tile(uint8_t* lds, int buf, int kb, int cb, const TileRegs& t,
+                                           float tau_log2e) {
+  using L = AttLayout<D, CFP8, WFP8>;
+  uint16_t* tile = reinterpret_cast<uint16_t*>(lds + L::off_tile + buf * L::tile_bytes);
   if (cb * 8 < D) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint4 v;
-      if constexpr (CFP8 && WFP8) v = fp8x8_to_bf16x8(t.r[i]);
-      else v = t.r[i];
-      *reinterpret_cast<uint4*>(tile + (8 * kb + i) * L::KROW + 8 * cb) = v;
+      const int r = 8 * kb + i;
+      *reinterpret_cast<uint4*>(tile + r * L::KROW + 8 * (cb ^ chunk_swz(r))) = t.r[i];
     }
   }
   if (cb == 0) {
@@ -184,7 +252,8 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_attend(AttendArgs a, int spl
                                                           int64_t keys_per_split,
                                                           float* __restrict__ ws_acc,
                                                           float* __restrict__ ws_ml) {
-  using L = AttLayout<D>;
+  using L = AttLayout<D, CFP8, WFP8>;
+  constexpr bool kAnyDma = L::kDma || L::kDmaFp8;
   constexpr int KS = D / 32;          // k-steps of QK^T
   constexpr int CT = D / 16;          // 16-channel tiles of O^T
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -218,6 +287,24 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_attend(AttendArgs a, int spl
     sin_l[t] = (float)sin(ang);
   }
 
+  // DMA paths: lane j < 8 of wave w tracks row 8w + j of the coming tiles:
+  // ref1 (address and scale) for the next tile to fill, id2 for the one after.
+  RowRef ref1{0, -INFINITY};
+  int64_t id2 = 0;
+  auto row_slot = [&](int64_t tile0) { return tile0 + 8 * wave + lane; };
+  if (kAnyDma && lane < 8) {
+    ref1 = resolve_row<D, CFP8, WFP8>(a, b, row_slot(lo), slot_id(a, b, row_slot(lo), n_sel, dense), n_sel,
+                                      n_keys);
+    id2 = slot_id(a, b, row_slot(lo + kTK), n_sel, dense);
+  }
+  // after a DMA of tile0 + kTK's predecessor: resolve tile0 + kTK, fetch the id of tile0 + 2 kTK
+  auto advance = [&](int64_t tile0) {
+    if (lane < 8) {
+      ref1 = resolve_row<D, CFP8, WFP8>(a, b, row_slot(tile0 + kTK), id2, n_sel, n_keys);
+      id2 = slot_id(a, b, row_slot(tile0 + 2 * kTK), n_sel, dense);
+    }
+  };
+
   // Q fragment: B operand of S^T = K Q^T; lane holds Q[h][32ks + 8g .. +7]
   bf16x8_t qf[KS];
   {
@@ -235,19 +322,30 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_attend(AttendArgs a, int spl
   for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // transposing-read addresses (bf16 offsets within a tile): lane src = l16 of
-  // group g fetches 4 channels of row kbase + l16/4, so that lane l16 receives
-  // channel l16 of rows kbase .. kbase+3
-  const int tr_row = l16 >> 2, tr_col = 4 * (l16 & 3);
-  const int tr_off0 = (4 * g + tr_row) * L::KROW + tr_col;
-  const int tr_off1 = (16 + 4 * g + tr_row) * L::KROW + tr_col;
+  // LDS read offsets (bf16 elements) that do not depend on the tile.
+  // QK^T A operand: row l16 (and 16 + l16), logical chunk 4ks + g.
+  const int qk_off0 = l16 * L::KROW + 8 * (g ^ chunk_swz(l16));
+  const int qk_off1 = (16 + l16) * L::KROW + 8 * (g ^ chunk_swz(16 + l16));
+  // PV A operand by transposing reads: lane l16 of group g supplies 4 channels
+  // c0 + 4(l16 % 4) .. +3 of row kbase + l16/4, so that lane l16 receives
+  // channel c0 + l16 of rows kbase .. kbase+3 (kbase = 4g, then 16 + 4g).
+  const int tq = l16 & 3, tr_r = l16 >> 2;
+  const int tr_row0 = 4 * g + tr_r, tr_row1 = 16 + 4 * g + tr_r;
+  // logical chunk of channel 16ct + 4tq is 2ct + (tq >> 1); with ct = 2m + e the
+  // swizzled chunk is 4m + ((2e + (tq >> 1)) ^ swz(row))
+  int tr_base0[2], tr_base1[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    tr_base0[e] = tr_row0 * L::KROW + 8 * ((2 * e + (tq >> 1)) ^ chunk_swz(tr_row0)) + 4 * (tq & 1);
+    tr_base1[e] = tr_row1 * L::KROW + 8 * ((2 * e + (tq >> 1)) ^ chunk_swz(tr_row1)) + 4 * (tq & 1);
+  }
 
-  constexpr bool kDma = D == 512 && !CFP8 && !WFP8;
   const int kb = t >> 6, cb = t & 63;
-  TileRegs<CFP8 && WFP8> tr;
+  TileRegs tr;
   if (lo < hi) {
-    if constexpr (kDma) {
-      dma_tile<D, CFP8, WFP8>(a, b, lo, n_sel, n_keys, dense, lds, 0, tau_log2e, wave, lane);
+    if constexpr (kAnyDma) {
+      dma_tile<D, CFP8, WFP8>(ref1, lds, 0, tau_log2e, wave, lane);
+      advance(lo);
     } else {
       load_tile<D, CFP8, WFP8>(a, b, lo, n_sel, n_keys, dense, kb, cb, tr);
       store_tile<D, CFP8, WFP8>(lds, 0, kb, cb, tr, tau_log2e);
@@ -255,25 +353,34 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_attend(AttendArgs a, int spl
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if constexpr (L::kDmaFp8) {
+    if (lo < hi) widen_tile<D>(lds, 0);
+    __syncthreads();
+  }
 
   int buf = 0;
   for (int64_t tile = lo; tile < hi; tile += kTK) {
     const bool more = tile + kTK < hi;
     if (more) {
       // the other buffer was last read before the previous barrier
-      if constexpr (kDma) dma_tile<D, CFP8, WFP8>(a, b, tile + kTK, n_sel, n_keys, dense, lds, buf ^ 1, tau_log2e, wave, lane);
-      else load_tile<D, CFP8, WFP8>(a, b, tile + kTK, n_sel, n_keys, dense, kb, cb, tr);
+      if constexpr (kAnyDma) {
+        dma_tile<D, CFP8, WFP8>(ref1, lds, buf ^ 1, tau_log2e, wave, lane);
+        advance(tile + kTK);
+      } else {
+        load_tile<D, CFP8, WFP8>(a, b, tile + kTK, n_sel, n_keys, dense, kb, cb, tr);
+      }
     }
 
     if (wave_on) {
-      const uint16_t* kt = reinterpret_cast<const uint16_t*>(lds + (buf ? L::off_tile1 : L::off_tile0));
+      const int cur = L::kDmaFp8 ? 0 : buf;
+      const uint16_t* kt = reinterpret_cast<const uint16_t*>(lds + L::off_tile + cur * L::tile_bytes);
       const float* rs = reinterpret_cast<const float*>(lds + L::off_rs) + buf * kTK;
       const float* ps = reinterpret_cast<const float*>(lds + L::off_ps) + buf * kTK;
       f32x4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kt + l16 * L::KROW + 32 * ks + 8 * g);
-        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kt + (16 + l16) * L::KROW + 32 * ks + 8 * g);
+        const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kt + qk_off0 + 32 * ks);
+        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kt + qk_off1 + 32 * ks);
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
         if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the loads kept in flight
@@ -314,34 +421,35 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_attend(AttendArgs a, int spl
       lsum += __shfl_xor(lsum, 32, kWave);
       l_run += lsum;
       // P^T as the B operand: k-slot j of group g is key 4g+j (j < 4) or 16+4g+j-4
-      uint4 pw;
       float pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) pv[i] = p[i] == 0.0f ? 0.0f : p[i] * vsc[i];
+      uint4 pw;
       pw.x = pack_bf16x2(pv[0], pv[1]);
       pw.y = pack_bf16x2(pv[2], pv[3]);
       pw.z = pack_bf16x2(pv[4], pv[5]);
       pw.w = pack_bf16x2(pv[6], pv[7]);
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
-      typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
-      const uint16_t* ktc = kt;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const v4i16_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16*)(ktc + tr_off0 + 16 * ct));
-        const v4i16_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16*)(ktc + tr_off1 + 16 * ct));
+        const int e = ct & 1, m = ct >> 1;
+        const v4i16_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kt + tr_base0[e] + 32 * m));
+        const v4i16_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kt + tr_base1[e] + 32 * m));
         const v4i16_t kk[2] = {r0, r1};
         const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, kk);
         acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, pb, acc[ct], 0, 0, 0);
         if ((ct & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if constexpr (!kDma) {
+    if constexpr (!kAnyDma) {
       if (more) store_tile<D, CFP8, WFP8>(lds, buf ^ 1, kb, cb, tr, tau_log2e);
     }
     __builtin_amdgcn_s_waitcnt(0);   // the next tile's rows have landed in LDS
     __syncthreads();
+    if constexpr (L::kDmaFp8) {
+      if (more) widen_tile<D>(lds, buf ^ 1);
+      __syncthreads();
+    }
     buf ^= 1;
   }
 
@@ -476,7 +584,7 @@ bool plan_attend(int64_t B, int H, int D, int64_t max_keys, int splits_hint, Att
 template <int D, bool CFP8, bool WFP8>
 static hipError_t launch_attend_t(const AttendPlan& p, const AttendArgs& a, void* workspace,
                                   hipStream_t stream) {
-  using L = AttLayout<D>;
+  using L = AttLayout<D, CFP8, WFP8>;
   auto kern = k_attend<D, CFP8, WFP8>;
   if (L::bytes > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

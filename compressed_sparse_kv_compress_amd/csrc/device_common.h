@@ -28,8 +28,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// Two fp32 values to a bf16 pair (round to nearest even), one gfx950
+// conversion instruction; the first value lands in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------- E4M3 (OCP, "FN")
@@ -111,6 +115,20 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 c) {
   return make_uint4(fp8x2_to_bf16x2<false>(c.x), fp8x2_to_bf16x2<true>(c.x), fp8x2_to_bf16x2<false>(c.y),
                     fp8x2_to_bf16x2<true>(c.y));
+}
+
+// ---------------------------------------------------------------- streaming loads
+// Data read exactly once (indexer keys, cache rows) is loaded non-temporally so
+// that it does not displace reusable lines from the caches.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t load_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(p);
 }
 
 // ---------------------------------------------------------------- wave helpers

@@ -208,7 +208,7 @@ __device__ void score_chunk_bf16(const uint16_t* q, const uint16_t* keys_g, int 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int e = (g0 + kTopkWaves * u) * EPL + sub;
-      v[u] = e < n ? kp[(int64_t)e * LPE + cg] : make_uint4(0, 0, 0, 0);
+      v[u] = e < n ? load_stream(kp + (int64_t)e * LPE + cg) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -256,8 +256,8 @@ __device__ void score_chunk_fp4(const uint16_t* q, const uint8_t* codes_g, const
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int e = (g0 + kTopkWaves * u) * EPL + sub;
-      v[u] = e < n ? cp[(int64_t)e * LPE + part] : make_uint4(0, 0, 0, 0);
-      s[u] = e < n ? (uint32_t)sp[(int64_t)e * LPE + part] : 0u;
+      v[u] = e < n ? load_stream(cp + (int64_t)e * LPE + part) : make_uint4(0, 0, 0, 0);
+      s[u] = e < n ? load_stream(sp + (int64_t)e * LPE + part) : 0u;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -342,30 +342,35 @@ struct SelectLds {
   int scan[kTopkWaves];
 };
 
-// The bin of the k-th largest key of a sequence (1 <= k < total) and the
-// number of keys in the bins above it, from the global histogram.
-__device__ void threshold_bin(const uint32_t* gh, int k, int* scan, int* misc, int& tbin, int& above) {
-  const int t = threadIdx.x;
-  constexpr int PER = kHistBins / kTopkThreads;   // 16 bins per thread, thread 0 the top ones
-  const int top = kHistBins - 1 - PER * t;
-  const uint4* p = reinterpret_cast<const uint4*>(gh + top - (PER - 1));
-  uint32_t h[PER];
+// A thread's 16 bins of a sequence histogram, thread 0 holding the top ones
+// (h[15] is the thread's highest bin).
+constexpr int kBinsPerThread = kHistBins / kTopkThreads;
+__device__ __forceinline__ void load_hist16(const uint32_t* gh, uint32_t (&h)[kBinsPerThread]) {
+  const int top = kHistBins - 1 - kBinsPerThread * (int)threadIdx.x;
+  const uint4* p = reinterpret_cast<const uint4*>(gh + top - (kBinsPerThread - 1));
 #pragma unroll
-  for (int i = 0; i < PER / 4; ++i) {
+  for (int i = 0; i < kBinsPerThread / 4; ++i) {
     const uint4 v = p[i];
     h[4 * i] = v.x; h[4 * i + 1] = v.y; h[4 * i + 2] = v.z; h[4 * i + 3] = v.w;
   }
+}
+
+// The bin of the k-th largest key of a sequence (1 <= k < total) and the
+// number of keys in the bins above it, from the histogram slices of load_hist16.
+__device__ void threshold_bin(const uint32_t (&h)[kBinsPerThread], int k, int* scan, int* misc, int& tbin,
+                              int& above) {
+  const int top = kHistBins - 1 - kBinsPerThread * (int)threadIdx.x;
   int s = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) s += (int)h[i];
+  for (int i = 0; i < kBinsPerThread; ++i) s += (int)h[i];
   int total;
   int run = block_exclusive_scan(s, scan, total);
   if (run < k && k <= run + s) {
 #pragma unroll
-    for (int i = PER - 1; i >= 0; --i) {   // h[PER-1] is this thread's top bin
+    for (int i = kBinsPerThread - 1; i >= 0; --i) {
       const int c = (int)h[i];
       if (run < k && k <= run + c) {
-        misc[0] = top - (PER - 1 - i);
+        misc[0] = top - (kBinsPerThread - 1 - i);
         misc[1] = run;
       }
       run += c;
@@ -392,7 +397,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_filter(
   nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
   const int n_here = (int)min((int64_t)slice, max((int64_t)0, nv - (int64_t)s * slice));
   int tbin = 0, above = 0;
-  if (nv > k && n_here > 0) threshold_bin(ws_hist + b * kHistBins, k, scan, misc, tbin, above);
+  bool have_tbin = nv <= k;
 
   const int64_t cand_base = (b * n_slices + s) * (int64_t)slice;
   const uint32_t* src = ws_keys + b * key_stride + (int64_t)s * slice;
@@ -408,6 +413,12 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_filter(
     for (int u = 0; u < PER; ++u) {
       const int i = wave * (PER * kWave) + u * kWave + lane;
       kv[u] = i < rn ? src[r0 + i] : 0u;
+    }
+    if (!have_tbin) {   // the histogram is read while the keys are in flight
+      uint32_t h[kBinsPerThread];
+      load_hist16(ws_hist + b * kHistBins, h);
+      threshold_bin(h, k, scan, misc, tbin, above);
+      have_tbin = true;
     }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -455,19 +466,34 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_final(
   nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
   uint32_t* gh = ws_hist + b * kHistBins;
   const bool take_all = nv <= k;
+  int32_t* out = ids + b * k;
+
+  // slice counts (thread t owns slices 8t .. 8t+7) and histogram, loaded together
+  constexpr int CPT = kMaxSlices / kTopkThreads;   // 8
+  const int32_t* cnt_b = ws_cnt + b * n_slices;
+  int c[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int si = CPT * t + j;
+    c[j] = si < n_slices ? cnt_b[si] : 0;
+  }
+  uint32_t h[kBinsPerThread];
+  if (!take_all) load_hist16(gh, h);
+
   int tbin = 0, above = 0;
-  if (!take_all) threshold_bin(gh, k, L.scan, L.misc, tbin, above);
+  if (!take_all) threshold_bin(h, k, L.scan, L.misc, tbin, above);
 
   // slice offsets of the candidates
-  int32_t* out = ids + b * k;
-  const int32_t* cnt_b = ws_cnt + b * n_slices;
-  int total = 0;
-  for (int s0 = 0; s0 < n_slices; s0 += kTopkThreads) {
-    const int c = s0 + t < n_slices ? cnt_b[s0 + t] : 0;
-    int part_total;
-    const int ex = block_exclusive_scan(c, L.scan, part_total);
-    if (s0 + t < n_slices) L.pre[s0 + t] = total + ex;
-    total += part_total;
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) mine += c[j];
+  int total;
+  int run = block_exclusive_scan(mine, L.scan, total);
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int si = CPT * t + j;
+    if (si < n_slices) L.pre[si] = run;
+    run += c[j];
   }
   if (t == 0) L.pre[n_slices] = total;
   __syncthreads();
