@@ -47,6 +47,9 @@ def parse():
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--chunk", type=int, default=0, help="index_topk chunk override")
     ap.add_argument("--splits", type=int, default=0, help="attend splits override")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.md from the counter_collection.csv files of a "
+                         "FETCH_SIZE run and a WRITE_SIZE run of this bench (with --copy-calibration), then exit")
     return ap.parse_args()
 
 
@@ -323,6 +326,104 @@ def cpu_baseline(cfg, seconds):
                       f"{cfg.name} workload, inputs generated before timing) in {el:.1f} s"}
 
 
+# ------------------------------------------------------------------ HBM traffic from counters
+#
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read for
+# the 1 GiB device copy that --copy-calibration adds, so that the figure is in
+# bytes that actually crossed the HBM interface. The summary records a digest of
+# the kernel sources; the bench reports the figure only while that digest still
+# matches, since a changed kernel makes old counters meaningless.
+
+CSRC = os.path.join(ROOT, "compressed_sparse_kv_compress_amd", "csrc")
+COPY_BYTES = 1 << 30
+
+
+def dominant_kernels(kind):
+    return ("k_index_score", "k_topk_filter", "k_topk_final") if kind != "c128a" else ("k_attend", "k_attend_merge")
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+
+
+def summarize_traffic(cfg, fetch_csv, write_csv):
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        vals = defaultdict(list)
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+                    vals[name].append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copy = "__amd_rocclr_copyBuffer"
+    # the 1 GiB copy is the dispatch with the largest reading among copyBuffer dispatches
+    f_scale = COPY_BYTES / (max(fetch[copy]) * 1024.0)
+    w_scale = COPY_BYTES / (max(write[copy]) * 1024.0)
+    dom = dominant_kernels(cfg.kind)
+    rows, total = [], 0.0
+    for name in sorted(set(fetch) | set(write)):
+        if not name.startswith("cskv::"):
+            continue
+        fk = sum(fetch.get(name, [0])) / max(1, len(fetch.get(name, [])))
+        wk = sum(write.get(name, [0])) / max(1, len(write.get(name, [])))
+        fb, wb = fk * 1024 * f_scale, wk * 1024 * w_scale
+        is_dom = name.split("<")[0].split("::")[-1] in dom
+        if is_dom:
+            total += fb + wb
+        rows.append((name, len(fetch.get(name, [])), fk, wk, fb, wb, is_dom))
+    lines = [
+        f"# HBM traffic per dispatch: {cfg.name}",
+        "",
+        "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the run's dispatches),",
+        "each from its own rocprofv3 --pmc run of `python3 bench.py --workload "
+        f"{cfg.name} --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration`, scaled by the",
+        f"reading for the 1 GiB device copy: FETCH_SIZE x {f_scale:.4f}, WRITE_SIZE x {w_scale:.4f}.",
+        "",
+        "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes | written bytes | dominant call |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    for name, n, fk, wk, fb, wb, d in rows:
+        lines.append(f"| {name} | {n} | {fk:.1f} | {wk:.1f} | {fb:.4g} | {wb:.4g} | {'yes' if d else ''} |")
+    lines += [
+        "",
+        f"traffic_bytes_per_dominant_call: {int(total)}",
+        f"kernel_source_digest: {kernel_source_digest()}",
+        "",
+    ]
+    with open(traffic_path(cfg.name), "w") as f:
+        f.write("\n".join(lines))
+    log(f"wrote {traffic_path(cfg.name)}: {int(total)} bytes per dominant call")
+
+
+def recorded_traffic(workload):
+    """Counter-measured bytes per dominant call, or None when absent or stale."""
+    try:
+        with open(traffic_path(workload)) as f:
+            text = f.read()
+    except OSError:
+        return None
+    kv = dict(l.split(": ", 1) for l in text.splitlines() if l.startswith(("traffic_bytes", "kernel_source")))
+    if kv.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return int(kv["traffic_bytes_per_dominant_call"])
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -331,14 +432,18 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by "
               "sequence with no communication, so N GPUs run N independent copies)", file=sys.stderr)
         sys.exit(2)
+    from synth import configs
+    cfg = configs.BY_NAME[args.workload]
+    if args.summarize_traffic:
+        summarize_traffic(cfg, *args.summarize_traffic)
+        return
+
     import torch
 
     import compressed_sparse_kv_compress_amd as cskv
     import synth
-    from synth import configs
     from synth import device as sd
 
-    cfg = configs.BY_NAME[args.workload]
     cls = {"c4a": C4aLayer, "c128a": C128aLayer, "mixed": Mixed61}[cfg.kind]
     wl = cls(cfg, args, torch, cskv, sd, synth)
     n_sets = args.sets or (1 if cfg.kind == "mixed" else 4)
@@ -428,13 +533,13 @@ def main():
                    "layers": cfg.layers, "input_sets_rotated": n_sets},
         "roofline": {
             "bound": "hbm",
-            "kernel": "index_topk (k_index_chunk + k_topk_merge)" if (cfg.kind != "c128a") else
+            "kernel": "index_topk (k_index_score + k_topk_filter + k_topk_final)" if (cfg.kind != "c128a") else
                       "attend (k_attend + k_attend_merge)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(cfg.name),
             "algorithmic_bytes_per_launch": int(dom_bytes_launch),
             "avg_launch_ms": round(dom_ms, 5),
         },

@@ -142,8 +142,11 @@ cskv_status cskv_index_topk(const void* q_idx, int32_t key_dtype, const void* k_
 size_t cskv_attend_workspace(int64_t B, int32_t H, int32_t D, int64_t max_keys, int32_t splits) {
   cskv::AttendPlan plan;
   if (B < 0 || H < 1 || H > 64 || !(D == 128 || D == 512) || max_keys < 0 || splits < 0) return 0;
-  if (!cskv::plan_attend(B, H, D, max_keys, splits, &plan)) return 0;
-  return plan.bytes;
+  // the larger of the dense and the sparse plan, whichever the call will use
+  size_t bytes = 0;
+  if (cskv::plan_attend(B, H, D, max_keys, false, splits, &plan)) bytes = plan.bytes;
+  if (cskv::plan_attend(B, H, D, max_keys, true, splits, &plan) && plan.bytes > bytes) bytes = plan.bytes;
+  return bytes;
 }
 
 cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t cache_dtype,
@@ -183,7 +186,8 @@ cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t 
         CSKV_EINVAL, "attend: Q, cache and window must be 16-byte aligned");
   cskv::AttendPlan plan;
   const int64_t max_keys = n_sel_max + W;
-  CHECK(cskv::plan_attend(B, H, D, max_keys, splits, &plan), CSKV_EUNSUPPORTED, "attend: no plan");
+  CHECK(cskv::plan_attend(B, H, D, max_keys, ids != nullptr, splits, &plan), CSKV_EUNSUPPORTED,
+        "attend: no plan for %lld key slots (sparse reads support at most 524288)", (long long)max_keys);
   CHECK(workspace_bytes >= plan.bytes, CSKV_EINVAL, "attend: workspace %zu bytes < %zu required",
         workspace_bytes, plan.bytes);
   CHECK(plan.bytes == 0 || (workspace && aligned(workspace, 256)), CSKV_EINVAL,

@@ -25,8 +25,8 @@
 //     from the reads of another and never serialises them;
 //   - S^T[32 keys x 16 heads] = K Q^T with Q held in registers;
 //   - online softmax per head in the exp2 domain; the running maximum is raised
-//     only when a logit exceeds it by more than 2^8, so the accumulators are
-//     rescaled rarely;
+//     only when a logit exceeds it by more than 2^16 (probabilities stay within
+//     bf16 and fp32 range), so the accumulators are rescaled rarely;
 //   - O^T[D x 16 heads] += K^T P^T: the probabilities stay in the registers the
 //     QK^T product left them in (they are exactly the B operand, for a matching
 //     order of the 32 keys), and K^T comes from the row-major tile through
@@ -50,7 +50,7 @@ constexpr int kNStage = 4;       // tiles in the LDS ring
 constexpr int kHMax = 64;        // heads per workgroup (4 waves x 16)
 constexpr int kMaxSplitIds = 2048;   // entry ids of a sparse split staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazyRescale = 8.0f;     // log2 headroom before the running max is raised
+constexpr float kLazyRescale = 16.0f;    // log2 headroom before the running max is raised
 constexpr int kCachePolicyStream = 2;    // non-temporal loads for rows read once
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -372,10 +372,12 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const bool raise = mx > m_run + kLazyRescale || (m_run == -INFINITY && mx != -INFINITY);
+    // raise the running max when a logit passes it by more than the headroom;
+    // accumulators that are still empty (m_run = -inf) need no rescale
+    const bool first = m_run == -INFINITY && mx != -INFINITY;
+    const bool raise = mx > m_run + kLazyRescale && !first;
     if (__ballot(raise)) {
-      const float alpha = raise ? (m_run == -INFINITY ? 0.0f : exp2f(m_run - mx)) : 1.0f;
-      if (raise) m_run = mx;
+      const float alpha = raise ? exp2f(m_run - mx) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
@@ -383,6 +385,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
         for (int i = 0; i < 4; ++i) acc[ct][i] *= alpha;
       }
     }
+    if (raise || first) m_run = mx;
     float p[8], lsum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -478,49 +481,68 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
 }
 
 // Log-sum-exp merge of the splits of one (sequence, head), then inverse RoPE.
-// Thread t owns channels 4t .. 4t+3.
+// The splits' (max, sum) pairs are staged in LDS; thread t owns channels
+// 4t .. 4t+3 and issues the loads of all splits' partials together.
+constexpr int kMergeMaxSplits = 256;
+
 template <int D>
 __global__ __launch_bounds__(128) void k_attend_merge(AttendArgs a, int splits,
                                                       const float* __restrict__ ws_acc,
                                                       const float* __restrict__ ws_ml) {
+  __shared__ float w_l[kMergeMaxSplits];
+  __shared__ float lsum_l;
   const int64_t b = blockIdx.y;
   const int h = blockIdx.x;
   const int t = threadIdx.x;
-  if (4 * t >= D) return;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml) + (b * splits) * kHMax + h;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[(int64_t)s * kHMax].x);
-  float Lsum = 0.0f;
+  // max over splits: wave 0 reduces, writes the split weights and their sum
+  if (t < kWave) {
+    float mloc[kMergeMaxSplits / kWave], lloc[kMergeMaxSplits / kWave];
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMergeMaxSplits / kWave; ++j) {
+      const int sp = t + kWave * j;
+      const float2 p = sp < splits ? ml[(int64_t)sp * kHMax] : make_float2(-INFINITY, 0.0f);
+      mloc[j] = p.x;
+      lloc[j] = p.y;
+      M = fmaxf(M, p.x);
+    }
+    M = wave_max(M);
+    float L = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMergeMaxSplits / kWave; ++j) {
+      const int sp = t + kWave * j;
+      const float w = (mloc[j] == -INFINITY || M == -INFINITY) ? 0.0f : exp2f(mloc[j] - M);
+      if (sp < splits) w_l[sp] = w;
+      L += w * lloc[j];
+    }
+    L = wave_sum(L);
+    if (t == 0) lsum_l = L;
+  }
+  __syncthreads();
+  if (4 * t >= D) return;
+  const float* base = ws_acc + ((b * splits) * kHMax + h) * D + 4 * t;
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  if (M != -INFINITY) {
-    const float* base = ws_acc + ((b * splits) * kHMax + h) * D + 4 * t;
-    constexpr int U = 8;
-    for (int s0 = 0; s0 < splits; s0 += U) {
-      float4 v[U];
-      float w[U];
+  constexpr int U = 16;
+  for (int s0 = 0; s0 < splits; s0 += U) {
+    float4 v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = s0 + u;
-        w[u] = 0.0f;
-        v[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (s < splits) {
-          const float2 p = ml[(int64_t)s * kHMax];
-          if (p.x != -INFINITY) {
-            w[u] = exp2f(p.x - M);
-            Lsum += p.y * w[u];
-            v[u] = *reinterpret_cast<const float4*>(base + (int64_t)s * kHMax * D);
-          }
-        }
-      }
+    for (int u = 0; u < U; ++u) {
+      const int sp = s0 + u;
+      v[u] = sp < splits ? *reinterpret_cast<const float4*>(base + (int64_t)sp * kHMax * D)
+                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        o.x = fmaf(v[u].x, w[u], o.x);
-        o.y = fmaf(v[u].y, w[u], o.y);
-        o.z = fmaf(v[u].z, w[u], o.z);
-        o.w = fmaf(v[u].w, w[u], o.w);
-      }
+    for (int u = 0; u < U; ++u) {
+      const int sp = s0 + u;
+      const float w = sp < splits ? w_l[sp] : 0.0f;
+      o.x = fmaf(v[u].x, w, o.x);
+      o.y = fmaf(v[u].y, w, o.y);
+      o.z = fmaf(v[u].z, w, o.z);
+      o.w = fmaf(v[u].w, w, o.w);
     }
   }
+  const float Lsum = lsum_l;
   const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
   o = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
   const int R = a.rope_dims;
@@ -544,7 +566,7 @@ __global__ __launch_bounds__(128) void k_attend_merge(AttendArgs a, int splits,
 
 // ------------------------------------------------------------- planning / launch
 
-bool plan_attend(int64_t B, int H, int D, int64_t max_keys, int splits_hint, AttendPlan* p) {
+bool plan_attend(int64_t B, int H, int D, int64_t max_keys, bool sparse, int splits_hint, AttendPlan* p) {
   (void)H;
   (void)D;
   const int64_t tiles = max_keys <= 0 ? 1 : (max_keys + kTK - 1) / kTK;
@@ -554,9 +576,13 @@ bool plan_attend(int64_t B, int H, int D, int64_t max_keys, int splits_hint, Att
     splits = (256 + B - 1) / B;
     if (splits > 64) splits = 64;
   }
-  // a split stages at most kMaxSplitIds entry ids (sparse reads)
-  const int64_t min_splits = (tiles + kMaxSplitIds / kTK - 1) / (kMaxSplitIds / kTK);
-  if (splits < min_splits) splits = min_splits;
+  if (sparse) {
+    // a sparse split stages at most kMaxSplitIds entry ids in LDS
+    const int64_t min_splits = (tiles + kMaxSplitIds / kTK - 1) / (kMaxSplitIds / kTK);
+    if (min_splits > kMergeMaxSplits) return false;
+    if (splits < min_splits) splits = min_splits;
+  }
+  if (splits > kMergeMaxSplits) splits = kMergeMaxSplits;
   if (splits > tiles) splits = tiles;
   if (splits < 1) splits = 1;
   const int64_t tiles_per = (tiles + splits - 1) / splits;

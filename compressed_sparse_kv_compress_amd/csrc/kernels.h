@@ -41,7 +41,9 @@ struct AttendPlan {
   int64_t keys_per_split;
   size_t bytes;          // workspace bytes (partials), 0 when splits == 1
 };
-bool plan_attend(int64_t B, int H, int D, int64_t max_keys, int splits_hint, AttendPlan* plan);
+// Plans the key-slot splits of an attend call; sparse calls stage their entry
+// ids in LDS, which bounds a split's length. False if no plan exists.
+bool plan_attend(int64_t B, int H, int D, int64_t max_keys, bool sparse, int splits_hint, AttendPlan* plan);
 struct AttendArgs {
   const uint16_t* Q;
   int64_t B;

@@ -147,7 +147,11 @@ cskv_status cskv_index_topk(const void* q_idx, int32_t key_dtype, const void* k_
  *                window_scale at window_scale + b*window_batch_stride)
  *   rope_dims    even, <= D (0 = no rotation);  q_pos [B] int64 device positions
  *   O            [B, H, D] fp32
- *   splits       key-row splits per sequence: 0 = automatic, else >= 1
+ *   splits       key-row splits per sequence: 0 = automatic, else >= 1 (sparse
+ *                reads split further so that a split covers at most 2048 ids)
+ *   workspace    cskv_attend_workspace() bytes (the query covers both dense and
+ *                sparse use of the same sizes); no state is kept in it
+ * EUNSUPPORTED for sparse reads of more than 524288 key slots.
  */
 size_t cskv_attend_workspace(int64_t B, int32_t H, int32_t D, int64_t max_keys, int32_t splits);
 cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t cache_dtype,
