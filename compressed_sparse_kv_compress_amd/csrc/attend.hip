@@ -24,9 +24,14 @@
 //     unrolled over the ring, so the compiler can tell the DMA into one buffer
 //     from the reads of another and never serialises them;
 //   - S^T[32 keys x 16 heads] = K Q^T with Q held in registers;
-//   - online softmax per head in the exp2 domain; the running maximum is raised
-//     only when a logit exceeds it by more than 2^16 (probabilities stay within
-//     bf16 and fp32 range), so the accumulators are rescaled rarely;
+//   - softmax per head in the exp2 domain against a reference maximum that is
+//     fixed for the whole split (0 at first). Each lane also tracks the largest
+//     logit it saw; if at the end a head's true maximum lies more than 64
+//     (log2 units) above or below the reference, the split is run a second time
+//     with the true maximum as reference. Probabilities therefore stay within
+//     [2^-64, 2^64] of the largest one (inside bf16 and fp32 range) and the
+//     accumulators are never rescaled, so the loop holds them in the MFMA
+//     accumulator registers without moving them;
 //   - O^T[D x 16 heads] += K^T P^T: the probabilities stay in the registers the
 //     QK^T product left them in (they are exactly the B operand, for a matching
 //     order of the 32 keys), and K^T comes from the row-major tile through
@@ -50,16 +55,16 @@ constexpr int kNStage = 4;       // tiles in the LDS ring
 constexpr int kHMax = 64;        // heads per workgroup (4 waves x 16)
 constexpr int kMaxSplitIds = 2048;   // entry ids of a sparse split staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazyRescale = 16.0f;    // log2 headroom before the running max is raised
+constexpr float kHeadroom = 64.0f;       // log2 distance allowed between reference and true maximum
 constexpr int kCachePolicyStream = 2;    // non-temporal loads for rows read once
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-// DMA sources of empty slots: a zero row and a -inf row scale (file-local, so
+// DMA sources of empty slots: a zero row and a zero row scale (file-local, so
 // their addresses are PC-relative constants rather than loads).
 static __device__ __attribute__((aligned(16))) uint8_t g_zero_row[1024];
-static __device__ float g_empty_scale = -INFINITY;
+static __device__ float g_empty_scale = 0.0f;
 
 // Swizzle of a tile row's 16-byte chunks.
 __device__ __forceinline__ int chunk_swz(int row) { return (row >> 3) & 3; }
@@ -69,6 +74,7 @@ struct AttCfg {
   static constexpr bool kDma = D == 512 && !CFP8 && !WFP8;      // bf16 rows by DMA
   static constexpr bool kDmaFp8 = D == 512 && CFP8 && WFP8;     // fp8 rows by DMA + widening pass
   static constexpr bool kReg = !kDma && !kDmaFp8;               // register-staged fill
+  static constexpr bool kScaled = CFP8 || WFP8;                 // rows carry a value scale
   static constexpr int KROW = D + 16;                           // bf16 per tile row
   static constexpr int kTileElems = kTK * KROW;                 // bf16 per tile
   static constexpr int kStageBytes = kDmaFp8 ? kTK * D : 16;    // fp8 staging tile
@@ -147,26 +153,29 @@ __device__ __forceinline__ void slot_source(const RowSrc& rs, int64_t slot, int6
 
 // Issues the fill of one tile (slots tile0 .. tile0+31): wave w handles rows
 // 8w .. 8w+7, lane j < 8 resolving row 8w + j. `tile` is the bf16 buffer
-// (DMA and register paths), `stage` the fp8 staging buffer, `ps` the per-slot
-// value scale (-inf: empty slot).
+// (DMA and register paths), `stage` the fp8 staging buffer; per slot, `pb` is
+// the logit bias (0, or -inf for an empty slot) and `vs` the row's value scale
+// (fp8 rows: the row scale; bf16 rows: 1; empty slots: 0).
 template <int D, bool CFP8, bool WFP8>
 __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, int64_t lo,
                                            int64_t n_sel, int64_t n_keys, bool dense, const int32_t* ids_l,
-                                           uint16_t* tile, uint8_t* stage, float* ps, int wave, int lane) {
+                                           uint16_t* tile, uint8_t* stage, float* pb, float* vs, int wave,
+                                           int lane) {
   using C = AttCfg<D, CFP8, WFP8>;
   if constexpr (C::kReg) {
     // thread (kb, cb): rows 8kb .. 8kb+7, logical chunk cb (8 channels)
     const int t = threadIdx.x, kb = t >> 6, cb = t & 63;
     const bool active_c = cb * 8 < D;
     uint4 r[8];
-    float vs[8];
+    float sc[8], bias[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint8_t* p;
       const float* sp;
       slot_source<D, CFP8, WFP8>(rsrc, tile0 + 8 * kb + i, lo, n_sel, n_keys, dense, ids_l, p, sp);
       r[i] = make_uint4(0, 0, 0, 0);
-      vs[i] = p ? (sp ? *sp : 1.0f) : -INFINITY;
+      sc[i] = p ? (sp ? *sp : 1.0f) : 0.0f;
+      bias[i] = p ? 0.0f : -INFINITY;
       if (p && active_c) {
         if (sp) r[i] = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(p + cb * 8));
         else r[i] = *reinterpret_cast<const uint4*>(p + cb * 16);
@@ -181,15 +190,18 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
     }
     if (cb == 0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ps[8 * kb + i] = vs[i];
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (C::kScaled) vs[8 * kb + i] = sc[i];   // vs has kTK slots only for scaled rows
+        pb[8 * kb + i] = bias[i];
+      }
     }
   } else {
     const uint8_t* p = nullptr;
     const float* sp = nullptr;
     if (lane < 8) slot_source<D, CFP8, WFP8>(rsrc, tile0 + 8 * wave + lane, lo, n_sel, n_keys, dense, ids_l, p, sp);
     const uint64_t src_l = reinterpret_cast<uint64_t>(p ? p : g_zero_row);
+    if (lane < 8) pb[8 * wave + lane] = p ? 0.0f : -INFINITY;
     if constexpr (C::kDma) {
-      if (lane < 8) ps[8 * wave + lane] = p ? 1.0f : -INFINITY;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int row = 8 * wave + i;
@@ -200,11 +212,11 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
             (__attribute__((address_space(3))) void*)(tile + row * C::KROW), 16, 0, kCachePolicyStream);
       }
     } else {
-      // row scales: lanes 0-7 move one dword each into ps[8w .. 8w+7]
+      // row scales: lanes 0-7 move one dword each into vs[8w .. 8w+7]
       if (lane < 8) {
         const float* s = p ? sp : &g_empty_scale;
         __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)s,
-                                         (__attribute__((address_space(3))) void*)(ps + 8 * wave), 4, 0, 0);
+                                         (__attribute__((address_space(3))) void*)(vs + 8 * wave), 4, 0, 0);
       }
       // fp8 rows of 512 B: lanes 0-31 move row 2i, lanes 32-63 row 2i+1
       const int half = lane >> 5, hl = lane & 31;
@@ -254,8 +266,12 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   __shared__ __attribute__((aligned(16))) uint16_t tile3[C::kDmaFp8 ? 8 : C::kTileElems];
   __shared__ __attribute__((aligned(16))) uint8_t stage0[C::kStageBytes], stage1[C::kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t stage2[C::kStageBytes], stage3[C::kStageBytes];
-  __shared__ __attribute__((aligned(16))) float ps0[kTK], ps1[kTK], ps2[kTK], ps3[kTK];
+  // per slot: logit bias (0 or -inf) and value scale (scaled rows only)
+  __shared__ __attribute__((aligned(16))) float pb0[kTK], pb1[kTK], pb2[kTK], pb3[kTK];
+  __shared__ __attribute__((aligned(16))) float vs0[C::kScaled ? kTK : 4], vs1[C::kScaled ? kTK : 4];
+  __shared__ __attribute__((aligned(16))) float vs2[C::kScaled ? kTK : 4], vs3[C::kScaled ? kTK : 4];
   __shared__ int32_t ids_l[kMaxSplitIds];
+  __shared__ int redo_l;
   __shared__ float cos_l[D / 2], sin_l[D / 2];
 
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
@@ -300,13 +316,9 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
     cos_l[t] = (float)cos(ang);
     sin_l[t] = (float)sin(ang);
   }
+  if (t == 0) redo_l = 0;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-
-  f32x4_t acc[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY, l_run = 0.0f;
 
   // LDS read offsets (bf16 elements) that do not depend on the tile.
   // QK^T A operand: row l16 (and 16 + l16), logical chunk 4ks + g.
@@ -338,82 +350,99 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
     constexpr int S = decltype(sc)::value;
     return S == 0 ? stage0 : (S == 1 ? stage1 : (S == 2 ? stage2 : stage3));
   };
-  auto ps_of = [&](auto sc) __attribute__((always_inline)) -> float* {
+  auto pb_of = [&](auto sc) __attribute__((always_inline)) -> float* {
     constexpr int S = decltype(sc)::value;
-    return S == 0 ? ps0 : (S == 1 ? ps1 : (S == 2 ? ps2 : ps3));
+    return S == 0 ? pb0 : (S == 1 ? pb1 : (S == 2 ? pb2 : pb3));
+  };
+  auto vs_of = [&](auto sc) __attribute__((always_inline)) -> float* {
+    constexpr int S = decltype(sc)::value;
+    return S == 0 ? vs0 : (S == 1 ? vs1 : (S == 2 ? vs2 : vs3));
   };
   auto issue = [&](auto sc, int i) __attribute__((always_inline)) {
     issue_tile<D, CFP8, WFP8>(rsrc, lo + (int64_t)i * kTK, lo, n_sel, n_keys, dense, ids_l, tile_of(sc),
-                              stage_of(sc), ps_of(sc), wave, lane);
+                              stage_of(sc), pb_of(sc), vs_of(sc), wave, lane);
   };
 
-  // tile compute on a ready bf16 tile with its slot scales
-  auto compute = [&](const uint16_t* kt, const float* ps) __attribute__((always_inline)) {
+  // Softmax state of head h: probabilities are exp2(logit - m_ref) with m_ref
+  // fixed for a pass; m_seen is the largest logit this lane saw and l_run the
+  // sum of this lane's probabilities (the four lanes of a head are summed at
+  // the end).
+  float m_ref = 0.0f, m_seen, l_run;
+  f32x4_t acc[CT];
+
+  // tile compute on a ready bf16 tile with its slot biases and value scales
+  auto compute = [&](const uint16_t* kt, const float* pbv, const float* vsv) __attribute__((always_inline)) {
+    // slot metadata of keys 4g .. 4g+3 and 16+4g .. 16+4g+3 (same for all heads)
+    const float4 b_lo = *reinterpret_cast<const float4*>(pbv + 4 * g);
+    const float4 b_hi = *reinterpret_cast<const float4*>(pbv + 16 + 4 * g);
+    float4 v_lo = make_float4(1.0f, 1.0f, 1.0f, 1.0f), v_hi = v_lo;
+    if constexpr (C::kScaled) {
+      v_lo = *reinterpret_cast<const float4*>(vsv + 4 * g);
+      v_hi = *reinterpret_cast<const float4*>(vsv + 16 + 4 * g);
+    }
+    // S^T = K Q^T, with the LDS reads of the key rows kQD k-steps ahead of use
+    constexpr int kQD = 4;
+    bf16x8_t ka0[KS], ka1[KS];
+#pragma unroll
+    for (int ks = 0; ks < kQD; ++ks) {
+      ka0[ks] = *reinterpret_cast<const bf16x8_t*>(kt + qk_off0 + 32 * ks);
+      ka1[ks] = *reinterpret_cast<const bf16x8_t*>(kt + qk_off1 + 32 * ks);
+    }
     f32x4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kt + qk_off0 + 32 * ks);
-      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kt + qk_off1 + 32 * ks);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
-      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the loads kept in flight
+      if (ks + kQD < KS) {
+        ka0[ks + kQD] = *reinterpret_cast<const bf16x8_t*>(kt + qk_off0 + 32 * (ks + kQD));
+        ka1[ks + kQD] = *reinterpret_cast<const bf16x8_t*>(kt + qk_off1 + 32 * (ks + kQD));
+      }
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[ks], qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[ks], qf[ks], s1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // K^T operands of PV: the first kPD channel tiles are read while the
+    // softmax runs
+    constexpr int kPD = 4;
+    v4i16_t kr0[CT], kr1[CT];
+    auto read_kt = [&](int ct) __attribute__((always_inline)) {
+      const int e = ct & 1, m = ct >> 1;
+      kr0[ct] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kt + tr_base0[e] + 32 * m));
+      kr1[ct] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kt + tr_base1[e] + 32 * m));
+    };
+#pragma unroll
+    for (int ct = 0; ct < kPD; ++ct) read_kt(ct);
+    __builtin_amdgcn_sched_barrier(0);
     // lane holds the logits of head h for key slots 4g+i (s0) and 16+4g+i (s1)
-    float x[8], vsc[8];
+    const float bb[8] = {b_lo.x, b_lo.y, b_lo.z, b_lo.w, b_hi.x, b_hi.y, b_hi.z, b_hi.w};
+    const float vv[8] = {v_lo.x, v_lo.y, v_lo.z, v_lo.w, v_hi.x, v_hi.y, v_hi.z, v_hi.w};
+    float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      vsc[i] = ps[4 * g + i];
-      vsc[4 + i] = ps[16 + 4 * g + i];
-      x[i] = vsc[i] != -INFINITY ? s0[i] * (vsc[i] * tau_log2e) : -INFINITY;
-      x[4 + i] = vsc[4 + i] != -INFINITY ? s1[i] * (vsc[4 + i] * tau_log2e) : -INFINITY;
+      x[i] = C::kScaled ? fmaf(s0[i] * vv[i], tau_log2e, bb[i]) : fmaf(s0[i], tau_log2e, bb[i]);
+      x[4 + i] = C::kScaled ? fmaf(s1[i] * vv[4 + i], tau_log2e, bb[4 + i]) : fmaf(s1[i], tau_log2e, bb[4 + i]);
     }
-    float mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    // raise the running max when a logit passes it by more than the headroom;
-    // accumulators that are still empty (m_run = -inf) need no rescale
-    const bool first = m_run == -INFINITY && mx != -INFINITY;
-    const bool raise = mx > m_run + kLazyRescale && !first;
-    if (__ballot(raise)) {
-      const float alpha = raise ? exp2f(m_run - mx) : 1.0f;
-      l_run *= alpha;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[ct][i] *= alpha;
-      }
-    }
-    if (raise || first) m_run = mx;
-    float p[8], lsum = 0.0f;
+    m_seen = fmaxf(m_seen, fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                 fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
+    float p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      p[i] = x[i] == -INFINITY ? 0.0f : exp2f(x[i] - m_run);
-      lsum += p[i];
+      p[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);   // exp2(-inf) = 0 for empty slots
+      l_run += p[i];
+      if constexpr (C::kScaled) p[i] *= vv[i];
     }
-    lsum += __shfl_xor(lsum, 16, kWave);
-    lsum += __shfl_xor(lsum, 32, kWave);
-    l_run += lsum;
     // P^T as the B operand: k-slot j of group g is key 4g+j (j < 4) or 16+4g+j-4
-    float pv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pv[i] = p[i] == 0.0f ? 0.0f : p[i] * vsc[i];
     uint4 pw;
-    pw.x = pack_bf16x2(pv[0], pv[1]);
-    pw.y = pack_bf16x2(pv[2], pv[3]);
-    pw.z = pack_bf16x2(pv[4], pv[5]);
-    pw.w = pack_bf16x2(pv[6], pv[7]);
-    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+    pw.x = pack_bf16x2(p[0], p[1]);
+    pw.y = pack_bf16x2(p[2], p[3]);
+    pw.z = pack_bf16x2(p[4], p[5]);
+    pw.w = pack_bf16x2(p[6], p[7]);
+    const bf16x8_t pbf = __builtin_bit_cast(bf16x8_t, pw);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      const int e = ct & 1, m = ct >> 1;
-      const v4i16_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kt + tr_base0[e] + 32 * m));
-      const v4i16_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kt + tr_base1[e] + 32 * m));
-      const v4i16_t kk[2] = {r0, r1};
-      const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, kk);
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, pb, acc[ct], 0, 0, 0);
-      if ((ct & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      if (ct + kPD < CT) read_kt(ct + kPD);
+      const v4i16_t kk[2] = {kr0[ct], kr1[ct]};
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk), pbf, acc[ct], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -428,19 +457,39 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
       widen_tile<D>(stage_of(sc), tile_of(sc));
       lds_barrier();
     }
-    if (wave_on) compute(tile_of(sc), ps_of(sc));
+    if (wave_on) compute(tile_of(sc), pb_of(sc), vs_of(sc));
   };
 
-  // prologue: the first three tiles
-  if (n_tiles > 0) issue(std::integral_constant<int, 0>{}, 0);
-  if (n_tiles > 1) issue(std::integral_constant<int, 1>{}, 1);
-  if (n_tiles > 2) issue(std::integral_constant<int, 2>{}, 2);
-  for (int i = 0; i < n_tiles; i += kNStage) {
-    step(std::integral_constant<int, 0>{}, i);
-    step(std::integral_constant<int, 1>{}, i + 1);
-    step(std::integral_constant<int, 2>{}, i + 2);
-    step(std::integral_constant<int, 3>{}, i + 3);
+  // At most two passes over the split: the second only when some head's true
+  // maximum lies too far from the reference maximum of the first.
+#pragma nounroll
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m_seen = -INFINITY;
+    l_run = 0.0f;
+    // prologue: the first three tiles
+    if (n_tiles > 0) issue(std::integral_constant<int, 0>{}, 0);
+    if (n_tiles > 1) issue(std::integral_constant<int, 1>{}, 1);
+    if (n_tiles > 2) issue(std::integral_constant<int, 2>{}, 2);
+    for (int i = 0; i < n_tiles; i += kNStage) {
+      step(std::integral_constant<int, 0>{}, i);
+      step(std::integral_constant<int, 1>{}, i + 1);
+      step(std::integral_constant<int, 2>{}, i + 2);
+      step(std::integral_constant<int, 3>{}, i + 3);
+    }
+    // the head's largest logit over the split (every tile has landed: no DMA in flight)
+    float mh = fmaxf(m_seen, __shfl_xor(m_seen, 16, kWave));
+    mh = fmaxf(mh, __shfl_xor(mh, 32, kWave));
+    const bool redo = pass == 0 && wave_on && mh != -INFINITY &&
+                      (mh > m_ref + kHeadroom || mh < m_ref - kHeadroom);
+    if (__ballot(redo) && lane == 0) redo_l = 1;
+    lds_barrier();   // votes visible; every wave is done with the ring
+    if (redo_l == 0 || pass > 0) break;
+    m_ref = mh != -INFINITY ? mh : 0.0f;
   }
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
 
   if (!wave_on) return;
   // lane holds O^T[16ct + 4g + i][h]: channels 16ct+4g .. 16ct+4g+3 of head h
@@ -475,7 +524,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
         const int c = 16 * ct + 4 * g;
         *reinterpret_cast<float4*>(arow + c) = make_float4(acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
       }
-      if (g == 0) *reinterpret_cast<float2*>(ws_ml + (part * kHMax + h) * 2) = make_float2(m_run, l_run);
+      if (g == 0) *reinterpret_cast<float2*>(ws_ml + (part * kHMax + h) * 2) = make_float2(m_ref, l_run);
     }
   }
 }

@@ -127,3 +127,60 @@ def test_attend_deterministic(cskv):
     a = cskv.attend(Q, cache, None, win, softmax_scale=0.04, rope_dims=64, q_pos=pos).cpu().numpy()
     b = cskv.attend(Q, cache, None, win, softmax_scale=0.04, rope_dims=64, q_pos=pos).cpu().numpy()
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("case", ["large", "negative", "mixed"])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_logits_far_from_zero(cskv, case, sparse):
+    """Logit ranges far above or below zero (in log2 units, beyond the 64 of
+    headroom around the first pass's reference maximum) take the second pass;
+    heads of one sequence may need it while others do not."""
+    B, H, D, N, k, W, R = 2, 64, 512, 1200, 256, 40, 64
+    seed = {"large": 61, "negative": 62, "mixed": 63}[case]
+    Q = F.bf16_to_f64(_bf16(seed, synth.T_Q, (B, H, D)))
+    cache = F.bf16_to_f64(_bf16(seed, synth.T_CACHE, (B, N, D)))
+    win = F.bf16_to_f64(_bf16(seed, synth.T_WIN, (B, W, D)))
+    tau = 1 / np.sqrt(D)
+    if case == "large":
+        tau = 3.0                          # logits with a spread of hundreds
+    else:
+        # rows near a common direction u; heads pointing against it see only
+        # very negative logits
+        cache = 1.0 + 0.1 * cache
+        win = 1.0 + 0.1 * win
+        # mixed: heads against u, along u, and across it (ordinary logits)
+        sign = -np.ones(H) if case == "negative" else np.array([-1.0, 1.0, 0.0])[np.arange(H) % 3]
+        Q = sign[None, :, None] + 0.1 * Q
+        tau = 0.2
+    Qb, cb, wb = (F.f32_to_bf16(x.astype(np.float32)) for x in (Q, cache, win))
+    rng = np.random.default_rng(seed)
+    ids = np.stack([sorted_ids(rng, N, k) for _ in range(B)]) if sparse else None
+    pos = np.array([77, 1 << 19], dtype=np.int64)
+    ref = _oracle(F.bf16_to_f64(Qb), F.bf16_to_f64(cb), ids, F.bf16_to_f64(wb), tau, R, 10000.0, pos)
+    for splits in (0, 1, 4):
+        O = cskv.attend(to_dev_bf16(Qb), to_dev_bf16(cb), None if ids is None else to_dev(ids), to_dev_bf16(wb),
+                        softmax_scale=tau, rope_dims=R, q_pos=to_dev(pos), splits=splits)
+        err = row_rel_err(O.cpu().numpy(), ref)
+        assert err <= 2e-2, (splits, err)
+
+
+def test_fp8_logits_far_from_zero(cskv):
+    """The second pass on the scaled (fp8) rows path."""
+    B, H, D, N, k, W, R = 1, 64, 512, 700, 512, 128, 64
+    seed = 64
+    Q = _bf16(seed, synth.T_Q, (B, H, D))
+    cc = synth.fp8_codes(synth.stream_key(seed, synth.T_CACHE), 0, B * N * D).reshape(B, N, D)
+    cs = synth.pos_scale(synth.stream_key(seed, synth.T_CACHE_SCALE), 0, B * N).reshape(B, N)
+    wc = synth.fp8_codes(synth.stream_key(seed, synth.T_WIN), 0, B * W * D).reshape(B, W, D)
+    wsc = synth.pos_scale(synth.stream_key(seed, synth.T_WIN_SCALE), 0, B * W).reshape(B, W)
+    rng = np.random.default_rng(seed)
+    ids = np.stack([sorted_ids(rng, N, k) for _ in range(B)])
+    pos = np.array([4242], dtype=np.int64)
+    tau = 4.0
+    ref = _oracle(F.bf16_to_f64(Q), F.decode_fp8_rows(cc, cs), ids, F.decode_fp8_rows(wc, wsc), tau, R,
+                  10000.0, pos)
+    for splits in (0, 1):
+        O = cskv.attend(to_dev_bf16(Q), to_dev(cc), to_dev(ids), to_dev(wc), cache_scale=to_dev(cs),
+                        window_scale=to_dev(wsc), softmax_scale=tau, rope_dims=R, q_pos=to_dev(pos),
+                        splits=splits)
+        assert row_rel_err(O.cpu().numpy(), ref) <= 6e-2
