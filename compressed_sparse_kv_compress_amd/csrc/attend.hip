@@ -32,17 +32,21 @@
 //     [2^-64, 2^64] of the largest one (inside bf16 and fp32 range) and the
 //     accumulators are never rescaled, so the loop holds them in the MFMA
 //     accumulator registers without moving them;
-//   - O^T[D x 16 heads] += K^T P^T: the probabilities stay in the registers the
-//     QK^T product left them in (they are exactly the B operand, for a matching
-//     order of the 32 keys), and K^T comes from the row-major tile through
-//     gfx950's transposing LDS reads.
+//   - the probabilities of all 64 heads meet in a 4 KiB LDS buffer (each lane
+//     writes its 8 values as one 16-byte store, already in the key order the
+//     next product consumes), and wave w computes O^T[D/4 channels x 64 heads]
+//     += K^T P^T for its quarter of the channels, so each K element is read
+//     from LDS once by QK^T's wave and once, transposed, for PV; K^T comes from
+//     the row-major tile through gfx950's transposing LDS reads.
 // Tile rows are padded to a stride of 8 (mod 64) dwords and their 16-byte
 // chunks are XOR-swizzled by (row / 8) mod 4, which keeps both the row reads of
 // QK^T and the transposing reads of PV free of LDS bank conflicts.
 // Each lane ends with 4 consecutive channels of one head: rotary pairs sit in
 // one lane. With one split the epilogue normalises, applies inverse RoPE and
-// stores O; otherwise partials (max, sum, unnormalised O) go to the workspace
-// and k_attend_merge combines them with a log-sum-exp merge.
+// stores O; otherwise partials (reference maximum, sum, unnormalised O, the
+// latter in the accumulators' register order so that every store writes 1 KiB
+// contiguously) go to the workspace and k_attend_merge combines them with a
+// log-sum-exp merge.
 #include <type_traits>
 
 #include "kernels.h"
@@ -77,7 +81,8 @@ struct AttCfg {
   static constexpr bool kScaled = CFP8 || WFP8;                 // rows carry a value scale
   static constexpr int KROW = D + 16;                           // bf16 per tile row
   static constexpr int kTileElems = kTK * KROW;                 // bf16 per tile
-  static constexpr int kStageBytes = kDmaFp8 ? kTK * D : 16;    // fp8 staging tile
+  // fp8 staging tile: the rows' codes, then their 32 scales (one DMA target per slot)
+  static constexpr int kStageBytes = kDmaFp8 ? kTK * D + kTK * 4 : 16;
   static constexpr int kOpsPerTile = kDma ? 8 : (kDmaFp8 ? 5 : 0);   // DMA instructions per wave
 };
 
@@ -258,7 +263,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
                                                           float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
   using C = AttCfg<D, CFP8, WFP8>;
   constexpr int KS = D / 32;          // k-steps of QK^T
-  constexpr int CT = D / 16;          // 16-channel tiles of O^T
+  constexpr int CTW = D / 64;         // 16-channel tiles of O^T per wave (a quarter of D)
   constexpr int KROW = C::KROW;
   // ring buffers: separate LDS objects so DMA targets and reads never alias
   __shared__ __attribute__((aligned(16))) uint16_t tile0[C::kTileElems], tile1[C::kTileElems];
@@ -268,10 +273,17 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   __shared__ __attribute__((aligned(16))) uint8_t stage2[C::kStageBytes], stage3[C::kStageBytes];
   // per slot: logit bias (0 or -inf) and value scale (scaled rows only)
   __shared__ __attribute__((aligned(16))) float pb0[kTK], pb1[kTK], pb2[kTK], pb3[kTK];
-  __shared__ __attribute__((aligned(16))) float vs0[C::kScaled ? kTK : 4], vs1[C::kScaled ? kTK : 4];
-  __shared__ __attribute__((aligned(16))) float vs2[C::kScaled ? kTK : 4], vs3[C::kScaled ? kTK : 4];
+  constexpr int kVsLen = C::kScaled && !C::kDmaFp8 ? kTK : 4;   // the fp8 DMA path keeps them in stage
+  __shared__ __attribute__((aligned(16))) float vs0[kVsLen], vs1[kVsLen], vs2[kVsLen], vs3[kVsLen];
   __shared__ int32_t ids_l[kMaxSplitIds];
+  // probabilities of the tile, row h: key slots in the k order of the PV product
+  __shared__ __attribute__((aligned(16))) uint16_t p_l[kHMax * kTK];
+  __shared__ float mref_l[kHMax], lsum_l[kHMax];
   __shared__ int redo_l;
+  // target of one DMA issued before any tile: the compiler's bookkeeping of
+  // LDS DMA targets treats the first target it meets as aliasing later DMA,
+  // so that role goes to a buffer the loop never reads
+  __shared__ __attribute__((aligned(16))) uint8_t dma_first_l[16 * kWave];
   __shared__ float cos_l[D / 2], sin_l[D / 2];
 
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
@@ -317,6 +329,8 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
     sin_l[t] = (float)sin(ang);
   }
   if (t == 0) redo_l = 0;
+  // rows of heads without a computing wave stay zero
+  for (int j = t; j < kHMax * kTK / 8; j += kAttThreads) reinterpret_cast<uint4*>(p_l)[j] = make_uint4(0, 0, 0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -331,12 +345,15 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   // the swizzled chunk is 4m + ((2e + (tq >> 1)) ^ swz(row)).
   const int tq = l16 & 3, tr_r = l16 >> 2;
   const int tr_row0 = 4 * g + tr_r, tr_row1 = 16 + 4 * g + tr_r;
+  // this wave's channel tiles are ct = CTW * wave + j, j < CTW
   int tr_base0[2], tr_base1[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    tr_base0[e] = tr_row0 * KROW + 8 * ((2 * e + (tq >> 1)) ^ chunk_swz(tr_row0)) + 4 * (tq & 1);
-    tr_base1[e] = tr_row1 * KROW + 8 * ((2 * e + (tq >> 1)) ^ chunk_swz(tr_row1)) + 4 * (tq & 1);
+    tr_base0[e] = tr_row0 * KROW + 8 * ((2 * e + (tq >> 1)) ^ chunk_swz(tr_row0)) + 4 * (tq & 1) + 16 * CTW * wave;
+    tr_base1[e] = tr_row1 * KROW + 8 * ((2 * e + (tq >> 1)) ^ chunk_swz(tr_row1)) + 4 * (tq & 1) + 16 * CTW * wave;
   }
+  // P^T B operand of head tile ht: lane (l16, g) reads row 16 ht + l16, slots 8g .. 8g+7
+  const int p_off = l16 * kTK + 8 * g;
 
   const RowSrc rsrc = row_src<D, CFP8, WFP8>(a, b);
 
@@ -356,22 +373,23 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   };
   auto vs_of = [&](auto sc) __attribute__((always_inline)) -> float* {
     constexpr int S = decltype(sc)::value;
-    return S == 0 ? vs0 : (S == 1 ? vs1 : (S == 2 ? vs2 : vs3));
+    if constexpr (C::kDmaFp8) return reinterpret_cast<float*>(stage_of(sc) + kTK * D);
+    else return S == 0 ? vs0 : (S == 1 ? vs1 : (S == 2 ? vs2 : vs3));
   };
   auto issue = [&](auto sc, int i) __attribute__((always_inline)) {
     issue_tile<D, CFP8, WFP8>(rsrc, lo + (int64_t)i * kTK, lo, n_sel, n_keys, dense, ids_l, tile_of(sc),
                               stage_of(sc), pb_of(sc), vs_of(sc), wave, lane);
   };
-
   // Softmax state of head h: probabilities are exp2(logit - m_ref) with m_ref
   // fixed for a pass; m_seen is the largest logit this lane saw and l_run the
   // sum of this lane's probabilities (the four lanes of a head are summed at
   // the end).
   float m_ref = 0.0f, m_seen, l_run;
-  f32x4_t acc[CT];
+  f32x4_t acc[CTW][4];   // O^T[16 (CTW wave + j) + 4g + i][16 ht + l16]
 
-  // tile compute on a ready bf16 tile with its slot biases and value scales
-  auto compute = [&](const uint16_t* kt, const float* pbv, const float* vsv) __attribute__((always_inline)) {
+  // QK^T and softmax of this wave's 16 heads on a ready bf16 tile with its slot
+  // biases and value scales; the probabilities go to p_l
+  auto qk_softmax = [&](const uint16_t* kt, const float* pbv, const float* vsv) __attribute__((always_inline)) {
     // slot metadata of keys 4g .. 4g+3 and 16+4g .. 16+4g+3 (same for all heads)
     const float4 b_lo = *reinterpret_cast<const float4*>(pbv + 4 * g);
     const float4 b_hi = *reinterpret_cast<const float4*>(pbv + 16 + 4 * g);
@@ -399,18 +417,6 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[ks], qf[ks], s1, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // K^T operands of PV: the first kPD channel tiles are read while the
-    // softmax runs
-    constexpr int kPD = 4;
-    v4i16_t kr0[CT], kr1[CT];
-    auto read_kt = [&](int ct) __attribute__((always_inline)) {
-      const int e = ct & 1, m = ct >> 1;
-      kr0[ct] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kt + tr_base0[e] + 32 * m));
-      kr1[ct] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kt + tr_base1[e] + 32 * m));
-    };
-#pragma unroll
-    for (int ct = 0; ct < kPD; ++ct) read_kt(ct);
-    __builtin_amdgcn_sched_barrier(0);
     // lane holds the logits of head h for key slots 4g+i (s0) and 16+4g+i (s1)
     const float bb[8] = {b_lo.x, b_lo.y, b_lo.z, b_lo.w, b_hi.x, b_hi.y, b_hi.z, b_hi.w};
     const float vv[8] = {v_lo.x, v_lo.y, v_lo.z, v_lo.w, v_hi.x, v_hi.y, v_hi.z, v_hi.w};
@@ -429,19 +435,38 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
       l_run += p[i];
       if constexpr (C::kScaled) p[i] *= vv[i];
     }
-    // P^T as the B operand: k-slot j of group g is key 4g+j (j < 4) or 16+4g+j-4
+    // k slot j of group g is key 4g+j (j < 4) or 16+4g+j-4: the lane's 8 values in order
     uint4 pw;
     pw.x = pack_bf16x2(p[0], p[1]);
     pw.y = pack_bf16x2(p[2], p[3]);
     pw.z = pack_bf16x2(p[4], p[5]);
     pw.w = pack_bf16x2(p[6], p[7]);
-    const bf16x8_t pbf = __builtin_bit_cast(bf16x8_t, pw);
+    *reinterpret_cast<uint4*>(p_l + 16 * wave * kTK + p_off) = pw;
+  };
+
+  // O^T[this wave's channels x 64 heads] += K^T P^T on a ready tile whose
+  // probabilities are in p_l
+  auto pv = [&](const uint16_t* kt) __attribute__((always_inline)) {
+    bf16x8_t pb[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) pb[ht] = *reinterpret_cast<const bf16x8_t*>(p_l + 16 * ht * kTK + p_off);
+    constexpr int kPD = CTW < 3 ? CTW : 3;   // channel tiles read ahead
+    v4i16_t kr0[CTW], kr1[CTW];
+    auto read_kt = [&](int j) __attribute__((always_inline)) {
+      const int e = j & 1, m = j >> 1;
+      kr0[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kt + tr_base0[e] + 32 * m));
+      kr1[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kt + tr_base1[e] + 32 * m));
+    };
+#pragma unroll
+    for (int j = 0; j < kPD; ++j) read_kt(j);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      if (ct + kPD < CT) read_kt(ct + kPD);
-      const v4i16_t kk[2] = {kr0[ct], kr1[ct]};
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk), pbf, acc[ct], 0, 0, 0);
+    for (int j = 0; j < CTW; ++j) {
+      if (j + kPD < CTW) read_kt(j + kPD);
+      const v4i16_t kk[2] = {kr0[j], kr1[j]};
+      const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, kk);
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) acc[j][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, pb[ht], acc[j][ht], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -457,15 +482,23 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
       widen_tile<D>(stage_of(sc), tile_of(sc));
       lds_barrier();
     }
-    if (wave_on) compute(tile_of(sc), pb_of(sc), vs_of(sc));
+    if (wave_on) qk_softmax(tile_of(sc), pb_of(sc), vs_of(sc));
+    lds_barrier();   // probabilities of all heads visible
+    pv(tile_of(sc));
   };
 
   // At most two passes over the split: the second only when some head's true
   // maximum lies too far from the reference maximum of the first.
+  // (still in flight when the first tile wait retires it with everything older)
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g_zero_row + 16 * lane),
+                                   (__attribute__((address_space(3))) void*)dma_first_l, 16, 0, 0);
 #pragma nounroll
   for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < CTW; ++j) {
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) acc[j][ht] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     m_seen = -INFINITY;
     l_run = 0.0f;
     // prologue: the first three tiles
@@ -490,127 +523,145 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   }
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
-
-  if (!wave_on) return;
-  // lane holds O^T[16ct + 4g + i][h]: channels 16ct+4g .. 16ct+4g+3 of head h
+  // every wave holds channels of all heads: share each head's reference and sum
+  if (g == 0) {
+    mref_l[h] = m_ref;
+    lsum_l[h] = wave_on ? l_run : 0.0f;
+  }
+  __syncthreads();
+  // for head tile ht, the lane holds channels 16 (CTW wave + j) + 4g .. +3 of
+  // head 16 ht + l16
   if (splits == 1) {
     const int R = a.rope_dims;
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    if (h < a.H) {
-      float* orow = a.O + (b * a.H + h) * D;
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const int c = 16 * ct + 4 * g;
-        float4 o = make_float4(acc[ct][0] * inv, acc[ct][1] * inv, acc[ct][2] * inv, acc[ct][3] * inv);
+    for (int ht = 0; ht < 4; ++ht) {
+      const int hh = 16 * ht + l16;
+      if (hh >= a.H) continue;
+      const float L = lsum_l[hh];
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      float* orow = a.O + (b * a.H + hh) * D;
+#pragma unroll
+      for (int j = 0; j < CTW; ++j) {
+        const int c = 16 * (CTW * wave + j) + 4 * g;
+        const f32x4_t v = acc[j][ht];
+        float4 o = make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
         if (c >= D - R) {
-          const int j = (c - (D - R)) >> 1;
-          const float c0 = cos_l[j], s0 = sin_l[j];
+          const int q = (c - (D - R)) >> 1;
+          const float c0 = cos_l[q], s0 = sin_l[q];
           o = make_float4(o.x * c0 - o.y * s0, o.x * s0 + o.y * c0, o.z, o.w);
         }
         if (c + 2 >= D - R) {
-          const int j = (c + 2 - (D - R)) >> 1;
-          const float c1 = cos_l[j], s1 = sin_l[j];
+          const int q = (c + 2 - (D - R)) >> 1;
+          const float c1 = cos_l[q], s1 = sin_l[q];
           o = make_float4(o.x, o.y, o.z * c1 - o.w * s1, o.z * s1 + o.w * c1);
         }
         *reinterpret_cast<float4*>(orow + c) = o;
       }
     }
   } else {
+    // partial of (sequence, split): float4 blocks [wave][j][ht][lane], each store 1 KiB contiguous
     const int64_t part = b * splits + s;
-    if (h < a.H) {
-      float* arow = ws_acc + (part * kHMax + h) * D;
+    float4* dst = reinterpret_cast<float4*>(ws_acc) + (part * 4 + wave) * (CTW * 4 * kWave) + lane;
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const int c = 16 * ct + 4 * g;
-        *reinterpret_cast<float4*>(arow + c) = make_float4(acc[ct][0], acc[ct][1], acc[ct][2], acc[ct][3]);
+    for (int j = 0; j < CTW; ++j) {
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        const f32x4_t v = acc[j][ht];
+        dst[(j * 4 + ht) * kWave] = make_float4(v[0], v[1], v[2], v[3]);
       }
-      if (g == 0) *reinterpret_cast<float2*>(ws_ml + (part * kHMax + h) * 2) = make_float2(m_ref, l_run);
     }
+    if (t < kHMax) reinterpret_cast<float2*>(ws_ml)[part * kHMax + t] = make_float2(mref_l[t], lsum_l[t]);
   }
 }
 
-// Log-sum-exp merge of the splits of one (sequence, head), then inverse RoPE.
-// The splits' (max, sum) pairs are staged in LDS; thread t owns channels
-// 4t .. 4t+3 and issues the loads of all splits' partials together.
+// Log-sum-exp merge of a sequence's splits, then inverse RoPE. Workgroup
+// (q, b) combines partial block q (a 16-channel tile of every head, 256
+// float4): thread t owns float4 t of the block, i.e. head 16 (t / 64) + t % 16
+// and channels 16q + 4 ((t % 64) / 16) .. +3. Per head, the reference maxima
+// and sums of all splits are first reduced to (M, L) by four groups of 64
+// threads; split s then weighs its partial by exp2(m_s - M).
 constexpr int kMergeMaxSplits = 256;
 
 template <int D>
-__global__ __launch_bounds__(128) void k_attend_merge(AttendArgs a, int splits,
+__global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
                                                       const float* __restrict__ ws_acc,
                                                       const float* __restrict__ ws_ml) {
-  __shared__ float w_l[kMergeMaxSplits];
-  __shared__ float lsum_l;
+  constexpr int CTW = D / 64;
+  __shared__ float mq_l[4][kHMax], lq_l[4][kHMax];
   const int64_t b = blockIdx.y;
-  const int h = blockIdx.x;
+  const int q = blockIdx.x;                 // 16-channel tile: wave slice q / CTW, j = q % CTW
   const int t = threadIdx.x;
-  const float2* ml = reinterpret_cast<const float2*>(ws_ml) + (b * splits) * kHMax + h;
-  // max over splits: wave 0 reduces, writes the split weights and their sum
-  if (t < kWave) {
-    float mloc[kMergeMaxSplits / kWave], lloc[kMergeMaxSplits / kWave];
-    float M = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kMergeMaxSplits / kWave; ++j) {
-      const int sp = t + kWave * j;
-      const float2 p = sp < splits ? ml[(int64_t)sp * kHMax] : make_float2(-INFINITY, 0.0f);
-      mloc[j] = p.x;
-      lloc[j] = p.y;
-      M = fmaxf(M, p.x);
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml) + b * splits * kHMax;
+  {
+    const int hh = t & 63, grp = t >> 6;
+    float M = -INFINITY, L = 0.0f;
+    for (int sp = grp; sp < splits; sp += 4) {
+      const float2 v = ml[(int64_t)sp * kHMax + hh];
+      if (v.x > M) {
+        L = (M == -INFINITY ? 0.0f : L * exp2f(M - v.x)) + v.y;
+        M = v.x;
+      } else {
+        L += v.y * exp2f(v.x - M);
+      }
     }
-    M = wave_max(M);
-    float L = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMergeMaxSplits / kWave; ++j) {
-      const int sp = t + kWave * j;
-      const float w = (mloc[j] == -INFINITY || M == -INFINITY) ? 0.0f : exp2f(mloc[j] - M);
-      if (sp < splits) w_l[sp] = w;
-      L += w * lloc[j];
-    }
-    L = wave_sum(L);
-    if (t == 0) lsum_l = L;
+    mq_l[grp][hh] = M;
+    lq_l[grp][hh] = L;
   }
   __syncthreads();
-  if (4 * t >= D) return;
-  const float* base = ws_acc + ((b * splits) * kHMax + h) * D + 4 * t;
+  const int ht = t >> 6, lane = t & 63;
+  const int hh = 16 * ht + (lane & 15);
+  float M = -INFINITY;
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) M = fmaxf(M, mq_l[grp][hh]);
+  float L = 0.0f;
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    const float mg = mq_l[grp][hh];
+    if (mg != -INFINITY) L += lq_l[grp][hh] * exp2f(mg - M);
+  }
+  const int w = q / CTW, j = q % CTW;
+  const float4* src = reinterpret_cast<const float4*>(ws_acc) + (((b * splits) * 4 + w) * CTW + j) * (4 * kWave) + t;
+  const int64_t pstride = 4 * CTW * 4 * kWave;   // float4 per partial
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  constexpr int U = 16;
+  constexpr int U = 8;
   for (int s0 = 0; s0 < splits; s0 += U) {
     float4 v[U];
+    float ms[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int sp = s0 + u;
-      v[u] = sp < splits ? *reinterpret_cast<const float4*>(base + (int64_t)sp * kHMax * D)
-                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      const int sp = s0 + u < splits ? s0 + u : splits - 1;
+      v[u] = src[(int64_t)sp * pstride];
+      ms[u] = ml[(int64_t)sp * kHMax + hh].x;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int sp = s0 + u;
-      const float w = sp < splits ? w_l[sp] : 0.0f;
-      o.x = fmaf(v[u].x, w, o.x);
-      o.y = fmaf(v[u].y, w, o.y);
-      o.z = fmaf(v[u].z, w, o.z);
-      o.w = fmaf(v[u].w, w, o.w);
+      const float wgt = s0 + u < splits ? exp2f(ms[u] - M) : 0.0f;
+      o.x = fmaf(v[u].x, wgt, o.x);
+      o.y = fmaf(v[u].y, wgt, o.y);
+      o.z = fmaf(v[u].z, wgt, o.z);
+      o.w = fmaf(v[u].w, wgt, o.w);
     }
   }
-  const float Lsum = lsum_l;
-  const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+  if (hh >= a.H) return;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   o = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
   const int R = a.rope_dims;
-  const int c = 4 * t;
+  const int c = 16 * q + 4 * (lane >> 4);
   if (c >= D - R) {
-    const int j = (c - (D - R)) >> 1;
-    const double th = pow((double)a.rope_base, -2.0 * (double)j / (double)R);
+    const int jj = (c - (D - R)) >> 1;
+    const double th = pow((double)a.rope_base, -2.0 * (double)jj / (double)R);
     const double ang = -(double)a.q_pos[b] * th;
     const float c0 = (float)cos(ang), s0 = (float)sin(ang);
     o = make_float4(o.x * c0 - o.y * s0, o.x * s0 + o.y * c0, o.z, o.w);
   }
   if (c + 2 >= D - R) {
-    const int j = (c + 2 - (D - R)) >> 1;
-    const double th = pow((double)a.rope_base, -2.0 * (double)j / (double)R);
+    const int jj = (c + 2 - (D - R)) >> 1;
+    const double th = pow((double)a.rope_base, -2.0 * (double)jj / (double)R);
     const double ang = -(double)a.q_pos[b] * th;
     const float c1 = (float)cos(ang), s1 = (float)sin(ang);
     o = make_float4(o.x, o.y, o.z * c1 - o.w * s1, o.z * s1 + o.w * c1);
   }
-  *reinterpret_cast<float4*>(a.O + (b * a.H + h) * D + c) = o;
+  *reinterpret_cast<float4*>(a.O + (b * a.H + hh) * D + c) = o;
 }
 
 // ------------------------------------------------------------- planning / launch
@@ -653,7 +704,7 @@ static hipError_t launch_attend_t(const AttendPlan& p, const AttendArgs& a, void
                      p.keys_per_split, ws_acc, ws_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((k_attend_merge<D>), dim3((unsigned)a.H, (unsigned)a.B), dim3(128), 0, stream,
+  hipLaunchKernelGGL((k_attend_merge<D>), dim3((unsigned)(D / 16), (unsigned)a.B), dim3(256), 0, stream,
                      a, p.splits, ws_acc, ws_ml);
   return hipGetLastError();
 }
