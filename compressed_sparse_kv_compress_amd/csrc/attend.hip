@@ -260,7 +260,7 @@ __device__ __forceinline__ void widen_tile(const uint8_t* stage, uint16_t* tile)
 
 template <int D, bool CFP8, bool WFP8>
 __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int splits, int64_t keys_per_split,
-                                                          float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
+                                                          uint16_t* __restrict__ ws_acc, float* __restrict__ ws_ml) {
   using C = AttCfg<D, CFP8, WFP8>;
   constexpr int KS = D / 32;          // k-steps of QK^T
   constexpr int CTW = D / 64;         // 16-channel tiles of O^T per wave (a quarter of D)
@@ -317,16 +317,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
       qf[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
-  // the split's entry ids (sparse), and the rotary table of a single split
+  // the split's entry ids (sparse)
   if (!dense) {
     const int64_t n_ids = min(hi, n_sel) - lo;
     for (int64_t j = t; j < n_ids; j += kAttThreads) ids_l[j] = a.ids[b * a.k + lo + j];
-  }
-  if (splits == 1 && t < a.rope_dims / 2) {
-    const double theta = pow((double)a.rope_base, -2.0 * (double)t / (double)a.rope_dims);
-    const double ang = -(double)a.q_pos[b] * theta;
-    cos_l[t] = (float)cos(ang);
-    sin_l[t] = (float)sin(ang);
   }
   if (t == 0) redo_l = 0;
   // rows of heads without a computing wave stay zero
@@ -505,6 +499,13 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
     if (n_tiles > 0) issue(std::integral_constant<int, 0>{}, 0);
     if (n_tiles > 1) issue(std::integral_constant<int, 1>{}, 1);
     if (n_tiles > 2) issue(std::integral_constant<int, 2>{}, 2);
+    if (pass == 0 && splits == 1 && t < a.rope_dims / 2) {
+      // the rotary table of a single split, while the first tiles are in flight
+      const double theta = pow((double)a.rope_base, -2.0 * (double)t / (double)a.rope_dims);
+      const double ang = -(double)a.q_pos[b] * theta;
+      cos_l[t] = (float)cos(ang);
+      sin_l[t] = (float)sin(ang);
+    }
     for (int i = 0; i < n_tiles; i += kNStage) {
       step(std::integral_constant<int, 0>{}, i);
       step(std::integral_constant<int, 1>{}, i + 1);
@@ -559,15 +560,19 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
       }
     }
   } else {
-    // partial of (sequence, split): float4 blocks [wave][j][ht][lane], each store 1 KiB contiguous
+    // partial of (sequence, split), normalised by its own sum (a convex
+    // combination of key rows) and rounded to bf16: 4-channel blocks
+    // [wave][j][ht][lane] of 8 bytes, each store 512 B contiguous
     const int64_t part = b * splits + s;
-    float4* dst = reinterpret_cast<float4*>(ws_acc) + (part * 4 + wave) * (CTW * 4 * kWave) + lane;
+    uint2* dst = reinterpret_cast<uint2*>(ws_acc) + (part * 4 + wave) * (CTW * 4 * kWave) + lane;
 #pragma unroll
-    for (int j = 0; j < CTW; ++j) {
+    for (int ht = 0; ht < 4; ++ht) {
+      const float L = lsum_l[16 * ht + l16];
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
+      for (int j = 0; j < CTW; ++j) {
         const f32x4_t v = acc[j][ht];
-        dst[(j * 4 + ht) * kWave] = make_float4(v[0], v[1], v[2], v[3]);
+        dst[(j * 4 + ht) * kWave] = make_uint2(pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv));
       }
     }
     if (t < kHMax) reinterpret_cast<float2*>(ws_ml)[part * kHMax + t] = make_float2(mref_l[t], lsum_l[t]);
@@ -575,28 +580,54 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
 }
 
 // Log-sum-exp merge of a sequence's splits, then inverse RoPE. Workgroup
-// (q, b) combines partial block q (a 16-channel tile of every head, 256
-// float4): thread t owns float4 t of the block, i.e. head 16 (t / 64) + t % 16
-// and channels 16q + 4 ((t % 64) / 16) .. +3. Per head, the reference maxima
-// and sums of all splits are first reduced to (M, L) by four groups of 64
-// threads; split s then weighs its partial by exp2(m_s - M).
+// (q, b) combines partial block q (a 16-channel tile of every head: 256
+// blocks of 4 channels): thread t owns block t, i.e. head 16 (t / 64) + t % 16
+// and channels 16q + 4 ((t % 64) / 16) .. +3. First, per head, the splits'
+// reference maxima and sums are reduced to (M, L) by four groups of 64
+// threads and each split's weight exp2(m_s - M) l_s / L is stored in LDS (the
+// partials are normalised by their own sums l_s); then every thread loads its
+// block of all splits at once and sums them weighted.
 constexpr int kMergeMaxSplits = 256;
 
 template <int D>
 __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
-                                                      const float* __restrict__ ws_acc,
+                                                      const uint16_t* __restrict__ ws_acc,
                                                       const float* __restrict__ ws_ml) {
   constexpr int CTW = D / 64;
+  extern __shared__ float w_l[];            // [splits][kHMax] weights
   __shared__ float mq_l[4][kHMax], lq_l[4][kHMax];
+  __shared__ float cs_l[2][8];              // rotary cos/sin of this tile's (up to 8) pairs
   const int64_t b = blockIdx.y;
   const int q = blockIdx.x;                 // 16-channel tile: wave slice q / CTW, j = q % CTW
   const int t = threadIdx.x;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml) + b * splits * kHMax;
+  const int R = a.rope_dims;
+  // rotary pairs of channels 16q .. 16q+15 that lie in the last R channels
+  if (t < 8) {
+    const int c = 16 * q + 2 * t;
+    if (c >= D - R) {
+      const int jj = (c - (D - R)) >> 1;
+      const double th = pow((double)a.rope_base, -2.0 * (double)jj / (double)R);
+      const double ang = -(double)a.q_pos[b] * th;
+      cs_l[0][t] = (float)cos(ang);
+      cs_l[1][t] = (float)sin(ang);
+    }
+  }
+  // the first 16 splits' blocks are loaded before the weights are known
+  constexpr int U = 16;
+  const int ht = t >> 6, lane = t & 63;
+  const int hh = 16 * ht + (lane & 15);
+  const int w = q / CTW, j = q % CTW;
+  const uint2* src = reinterpret_cast<const uint2*>(ws_acc) + (((b * splits) * 4 + w) * CTW + j) * (4 * kWave) + t;
+  const int64_t pstride = 4 * CTW * 4 * kWave;   // 4-channel blocks per partial
+  uint2 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) v[u] = src[(int64_t)(u < splits ? u : splits - 1) * pstride];
+  const int hh0 = t & 63, grp = t >> 6;
   {
-    const int hh = t & 63, grp = t >> 6;
     float M = -INFINITY, L = 0.0f;
     for (int sp = grp; sp < splits; sp += 4) {
-      const float2 v = ml[(int64_t)sp * kHMax + hh];
+      const float2 v = ml[(int64_t)sp * kHMax + hh0];
       if (v.x > M) {
         L = (M == -INFINITY ? 0.0f : L * exp2f(M - v.x)) + v.y;
         M = v.x;
@@ -604,61 +635,56 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
         L += v.y * exp2f(v.x - M);
       }
     }
-    mq_l[grp][hh] = M;
-    lq_l[grp][hh] = L;
+    mq_l[grp][hh0] = M;
+    lq_l[grp][hh0] = L;
   }
   __syncthreads();
-  const int ht = t >> 6, lane = t & 63;
-  const int hh = 16 * ht + (lane & 15);
-  float M = -INFINITY;
+  {
+    float M = -INFINITY;
 #pragma unroll
-  for (int grp = 0; grp < 4; ++grp) M = fmaxf(M, mq_l[grp][hh]);
-  float L = 0.0f;
+    for (int gg = 0; gg < 4; ++gg) M = fmaxf(M, mq_l[gg][hh0]);
+    float L = 0.0f;
 #pragma unroll
-  for (int grp = 0; grp < 4; ++grp) {
-    const float mg = mq_l[grp][hh];
-    if (mg != -INFINITY) L += lq_l[grp][hh] * exp2f(mg - M);
+    for (int gg = 0; gg < 4; ++gg) {
+      const float mg = mq_l[gg][hh0];
+      if (mg != -INFINITY) L += lq_l[gg][hh0] * exp2f(mg - M);
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    for (int sp = grp; sp < splits; sp += 4) {
+      const float2 v = ml[(int64_t)sp * kHMax + hh0];
+      w_l[sp * kHMax + hh0] = v.x == -INFINITY ? 0.0f : exp2f(v.x - M) * v.y * inv;
+    }
   }
-  const int w = q / CTW, j = q % CTW;
-  const float4* src = reinterpret_cast<const float4*>(ws_acc) + (((b * splits) * 4 + w) * CTW + j) * (4 * kWave) + t;
-  const int64_t pstride = 4 * CTW * 4 * kWave;   // float4 per partial
+  __syncthreads();
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  constexpr int U = 8;
   for (int s0 = 0; s0 < splits; s0 += U) {
-    float4 v[U];
-    float ms[U];
+    if (s0 > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int sp = s0 + u < splits ? s0 + u : splits - 1;
-      v[u] = src[(int64_t)sp * pstride];
-      ms[u] = ml[(int64_t)sp * kHMax + hh].x;
+      for (int u = 0; u < U; ++u) {
+        const int sp = s0 + u < splits ? s0 + u : splits - 1;
+        v[u] = src[(int64_t)sp * pstride];
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float wgt = s0 + u < splits ? exp2f(ms[u] - M) : 0.0f;
-      o.x = fmaf(v[u].x, wgt, o.x);
-      o.y = fmaf(v[u].y, wgt, o.y);
-      o.z = fmaf(v[u].z, wgt, o.z);
-      o.w = fmaf(v[u].w, wgt, o.w);
+      const float wgt = s0 + u < splits ? w_l[(s0 + u) * kHMax + hh] : 0.0f;
+      o.x = fmaf(__uint_as_float(v[u].x << 16), wgt, o.x);
+      o.y = fmaf(__uint_as_float(v[u].x & 0xFFFF0000u), wgt, o.y);
+      o.z = fmaf(__uint_as_float(v[u].y << 16), wgt, o.z);
+      o.w = fmaf(__uint_as_float(v[u].y & 0xFFFF0000u), wgt, o.w);
     }
   }
   if (hh >= a.H) return;
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  o = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-  const int R = a.rope_dims;
   const int c = 16 * q + 4 * (lane >> 4);
+  // (the weights already divide by L)
   if (c >= D - R) {
-    const int jj = (c - (D - R)) >> 1;
-    const double th = pow((double)a.rope_base, -2.0 * (double)jj / (double)R);
-    const double ang = -(double)a.q_pos[b] * th;
-    const float c0 = (float)cos(ang), s0 = (float)sin(ang);
+    const int pr = (c - 16 * q) >> 1;
+    const float c0 = cs_l[0][pr], s0 = cs_l[1][pr];
     o = make_float4(o.x * c0 - o.y * s0, o.x * s0 + o.y * c0, o.z, o.w);
   }
   if (c + 2 >= D - R) {
-    const int jj = (c + 2 - (D - R)) >> 1;
-    const double th = pow((double)a.rope_base, -2.0 * (double)jj / (double)R);
-    const double ang = -(double)a.q_pos[b] * th;
-    const float c1 = (float)cos(ang), s1 = (float)sin(ang);
+    const int pr = (c + 2 - 16 * q) >> 1;
+    const float c1 = cs_l[0][pr], s1 = cs_l[1][pr];
     o = make_float4(o.x, o.y, o.z * c1 - o.w * s1, o.z * s1 + o.w * c1);
   }
   *reinterpret_cast<float4*>(a.O + (b * a.H + hh) * D + c) = o;
@@ -689,7 +715,8 @@ bool plan_attend(int64_t B, int H, int D, int64_t max_keys, bool sparse, int spl
   splits = (tiles + tiles_per - 1) / tiles_per;
   p->splits = (int)splits;
   p->keys_per_split = tiles_per * kTK;
-  p->bytes = splits > 1 ? (size_t)B * splits * kHMax * ((size_t)D + 2) * 4 : 0;
+  // bf16 partials, then an fp32 (reference maximum, sum) pair per head
+  p->bytes = splits > 1 ? (size_t)B * splits * kHMax * ((size_t)D * 2 + 8) : 0;
   return true;
 }
 
@@ -697,15 +724,15 @@ template <int D, bool CFP8, bool WFP8>
 static hipError_t launch_attend_t(const AttendPlan& p, const AttendArgs& a, void* workspace,
                                   hipStream_t stream) {
   auto kern = k_attend<D, CFP8, WFP8>;
-  float* ws_acc = reinterpret_cast<float*>(workspace);
-  float* ws_ml = p.splits > 1 ? ws_acc + (size_t)a.B * p.splits * kHMax * D : nullptr;
+  uint16_t* ws_acc = reinterpret_cast<uint16_t*>(workspace);
+  float* ws_ml = p.splits > 1 ? reinterpret_cast<float*>(ws_acc + (size_t)a.B * p.splits * kHMax * D) : nullptr;
   dim3 grid((unsigned)p.splits, (unsigned)a.B);
   hipLaunchKernelGGL(kern, grid, dim3(kAttThreads), 0, stream, a, p.splits,
                      p.keys_per_split, ws_acc, ws_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((k_attend_merge<D>), dim3((unsigned)(D / 16), (unsigned)a.B), dim3(256), 0, stream,
-                     a, p.splits, ws_acc, ws_ml);
+  hipLaunchKernelGGL((k_attend_merge<D>), dim3((unsigned)(D / 16), (unsigned)a.B), dim3(256),
+                     (size_t)p.splits * kHMax * sizeof(float), stream, a, p.splits, ws_acc, ws_ml);
   return hipGetLastError();
 }
 

@@ -55,7 +55,8 @@ def test_topk_workspace_sizes(lib):
 
 def test_attend_workspace_sizes(lib):
     assert lib._lib_attend_ws(8, 64, 512, 640, 1) == 0
-    assert lib._lib_attend_ws(8, 64, 512, 640, 4) == 8 * 4 * 64 * (512 + 2) * 4
+    # bf16 partials plus an fp32 (max, sum) pair per head and split
+    assert lib._lib_attend_ws(8, 64, 512, 640, 4) == 8 * 4 * 64 * (512 * 2 + 8)
     assert lib._lib_attend_ws(8, 64, 384, 640, 4) == 0           # unsupported D
 
 
