@@ -15,11 +15,14 @@
 //   k_topk_filter  (grid: slices x sequences) finds, from that histogram, the
 //     bin holding the k-th largest key and keeps the entries of its slice
 //     whose bin is at or above it, in entry order (about k plus one bin's
-//     worth per sequence).
-//   k_topk_final   (grid: sequences) gathers those candidates, resolves the
-//     remaining 20 key bits by radix select in LDS, writes the ids in
-//     ascending entry order (ties go to the lower entry) and clears the
-//     histogram for the next call.
+//     worth per sequence). It also adds a histogram of the next 8 key bits of
+//     the threshold bin's keys into a per-sequence 256-bin histogram, and the
+//     first slice records the threshold bin and the count of keys above it.
+//   k_topk_final   (grid: sequences) finds from the 256-bin histogram the
+//     20-bit prefix of the k-th largest key, gathers the candidates, resolves
+//     the remaining 12 key bits by radix select in LDS, writes the ids in
+//     ascending entry order (ties go to the lower entry) and clears both
+//     histograms for the next call.
 // The selection is exact: every entry of a bin above the threshold bin is in
 // the top k, and the threshold bin is resolved on full keys.
 #include "kernels.h"
@@ -36,6 +39,9 @@ constexpr int kCandCap = 4096;              // candidates the final select holds
 constexpr int kSliceUnit = 2048;            // keys a select workgroup filters per round
 constexpr int kMaxSlices = 2048;
 constexpr int kMisc = 16;
+constexpr int kSubBits = 8;                 // key bits below the threshold bin resolved by the filter
+constexpr int kSubBins = 1 << kSubBits;
+constexpr int kLowBits = kBinShift - kSubBits;   // 12 bits left to the final select
 
 // ------------------------------------------------------------- block helpers
 
@@ -336,6 +342,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_index_score(
 struct SelectLds {
   uint32_t ckey[kCandCap];
   int32_t cidx[kCandCap];
+  uint16_t slice_of[kCandCap];   // slice of each gathered candidate
   uint32_t rhist[kTopkWaves * kRadixPad];
   int pre[kMaxSlices + 1];
   int misc[kMisc];
@@ -387,9 +394,11 @@ __device__ void threshold_bin(const uint32_t (&h)[kBinsPerThread], int k, int* s
 __global__ __launch_bounds__(kTopkThreads) void k_topk_filter(
     const uint32_t* __restrict__ ws_keys, int64_t key_stride, const int32_t* __restrict__ n_entries,
     int64_t n_max, int k, int slice, int n_slices, const uint32_t* __restrict__ ws_hist,
-    uint32_t* __restrict__ ws_ckey, int32_t* __restrict__ ws_cidx, int32_t* __restrict__ ws_cnt) {
+    uint32_t* __restrict__ ws_hist2, int2* __restrict__ ws_thr, uint32_t* __restrict__ ws_ckey,
+    int32_t* __restrict__ ws_cidx, int32_t* __restrict__ ws_cnt) {
   __shared__ int scan[kTopkWaves];
   __shared__ int misc[kMisc];
+  __shared__ uint32_t h2[kSubBins];       // next 8 bits of this slice's threshold-bin keys
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int64_t b = blockIdx.y;
   const int s = blockIdx.x;
@@ -398,6 +407,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_filter(
   const int n_here = (int)min((int64_t)slice, max((int64_t)0, nv - (int64_t)s * slice));
   int tbin = 0, above = 0;
   bool have_tbin = nv <= k;
+  const bool take_all = have_tbin;
+  for (int i = t; i < kSubBins; i += kTopkThreads) h2[i] = 0u;
+  __syncthreads();
 
   const int64_t cand_base = (b * n_slices + s) * (int64_t)slice;
   const uint32_t* src = ws_keys + b * key_stride + (int64_t)s * slice;
@@ -425,6 +437,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_filter(
       const int i = wave * (PER * kWave) + u * kWave + lane;
       keep[u] = i < rn && (int)(kv[u] >> kBinShift) >= tbin;
       cnt += __popcll(__ballot(keep[u]));
+      if (!take_all && i < rn && (int)(kv[u] >> kBinShift) == tbin)
+        atomicAdd(&h2[(kv[u] >> kLowBits) & (kSubBins - 1)], 1u);
     }
     if (lane == 0) scan[wave] = cnt;
     __syncthreads();
@@ -450,25 +464,37 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_filter(
     written += round_total;
   }
   if (t == 0) ws_cnt[b * n_slices + s] = written;
+  if (!take_all) {
+    if (s == 0 && t == 0) ws_thr[b] = make_int2(tbin, above);   // (nv > k: slice 0 holds keys)
+    __syncthreads();
+    for (int i = t; i < kSubBins; i += kTopkThreads) {
+      const uint32_t c = h2[i];
+      if (c) atomicAdd(&ws_hist2[b * kSubBins + i], c);
+    }
+  }
 }
 
-// One workgroup per sequence: gathers the slices' candidates, resolves the
-// threshold bin on full keys, writes the ids (ascending, -1 padded) and
-// clears the sequence's histogram for the next call.
+// One workgroup per sequence: finds the 20-bit prefix of the k-th largest key
+// from the filter's threshold bin and 256-bin histogram, gathers the slices'
+// candidates, resolves the remaining 12 bits on full keys, writes the ids
+// (ascending, -1 padded) and clears both histograms for the next call.
 __global__ __launch_bounds__(kTopkThreads) void k_topk_final(
     const int32_t* __restrict__ n_entries, int64_t n_max, int k, int slice, int n_slices,
-    uint32_t* __restrict__ ws_hist, uint32_t* __restrict__ ws_ckey, int32_t* __restrict__ ws_cidx,
-    const int32_t* __restrict__ ws_cnt, int32_t* __restrict__ ids) {
+    uint32_t* __restrict__ ws_hist, uint32_t* __restrict__ ws_hist2, const int2* __restrict__ ws_thr,
+    uint32_t* __restrict__ ws_ckey, int32_t* __restrict__ ws_cidx, const int32_t* __restrict__ ws_cnt,
+    int32_t* __restrict__ ids) {
   __shared__ SelectLds L;
   const int t = threadIdx.x;
   const int64_t b = blockIdx.x;
   int64_t nv = n_entries ? (int64_t)n_entries[b] : n_max;
   nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
   uint32_t* gh = ws_hist + b * kHistBins;
+  uint32_t* gh2 = ws_hist2 + b * kSubBins;
   const bool take_all = nv <= k;
   int32_t* out = ids + b * k;
 
-  // slice counts (thread t owns slices 8t .. 8t+7) and histogram, loaded together
+  // slice counts (thread t owns slices 8t .. 8t+7), the threshold record and
+  // the sub-bin histogram (thread t owns sub-bin 255 - t), loaded together
   constexpr int CPT = kMaxSlices / kTopkThreads;   // 8
   const int32_t* cnt_b = ws_cnt + b * n_slices;
   int c[CPT];
@@ -477,11 +503,12 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_final(
     const int si = CPT * t + j;
     c[j] = si < n_slices ? cnt_b[si] : 0;
   }
-  uint32_t h[kBinsPerThread];
-  if (!take_all) load_hist16(gh, h);
-
-  int tbin = 0, above = 0;
-  if (!take_all) threshold_bin(h, k, L.scan, L.misc, tbin, above);
+  int2 thr = make_int2(0, 0);
+  uint32_t h2v = 0u;
+  if (!take_all) {
+    thr = ws_thr[b];
+    h2v = gh2[kSubBins - 1 - t];
+  }
 
   // slice offsets of the candidates
   int mine = 0;
@@ -496,12 +523,33 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_final(
     run += c[j];
   }
   if (t == 0) L.pre[n_slices] = total;
+
+  // the sub-bin holding the k-th largest key: sub-bins from the top down
+  uint32_t prefix = 0u;
+  int rem = 0;
+  if (!take_all) {
+    const int need = k - thr.y;                  // keys still to take from the threshold bin
+    int sub_total;
+    const int above2 = block_exclusive_scan((int)h2v, L.scan, sub_total);   // keys in higher sub-bins
+    if (above2 < need && need <= above2 + (int)h2v) {
+      L.misc[0] = kSubBins - 1 - t;
+      L.misc[1] = need - above2;
+    }
+  }
   __syncthreads();
+  if (!take_all) {
+    prefix = ((uint32_t)thr.x << kBinShift) | ((uint32_t)L.misc[0] << kLowBits);
+    rem = L.misc[1];
+  }
 
   const uint32_t* keys;
   const int32_t* idxs;
   if (total <= kCandCap) {
-    // gather into LDS, 8 loads in flight per thread
+    // each candidate position's slice, then the gather into LDS
+    for (int si = t; si < n_slices; si += kTopkThreads) {
+      for (int j = L.pre[si]; j < L.pre[si + 1]; ++j) L.slice_of[j] = (uint16_t)si;
+    }
+    __syncthreads();
     for (int j0 = 0; j0 < total; j0 += 8 * kTopkThreads) {
       uint32_t kk[8];
       int32_t ii[8];
@@ -511,12 +559,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_final(
         kk[u] = 0u;
         ii[u] = 0;
         if (j < total) {
-          int lo = 0, hi = n_slices - 1;          // last slice with pre <= j
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (L.pre[mid] <= j) lo = mid; else hi = mid - 1;
-          }
-          const int64_t off = (b * n_slices + lo) * (int64_t)slice + (j - L.pre[lo]);
+          const int sl = L.slice_of[j];
+          const int64_t off = (b * n_slices + sl) * (int64_t)slice + (j - L.pre[sl]);
           kk[u] = ws_ckey[off];
           ii[u] = ws_cidx[off];
         }
@@ -540,15 +584,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_final(
     uint32_t* ck = ws_ckey + b * n_slices * (int64_t)slice;
     int32_t* ci = ws_cidx + b * n_slices * (int64_t)slice;
     for (int s1 = 1; s1 < n_slices; ++s1) {
-      const int c = L.pre[s1 + 1] - L.pre[s1];
+      const int cs = L.pre[s1 + 1] - L.pre[s1];
       const int64_t from = (int64_t)s1 * slice, to = L.pre[s1];
-      for (int j0 = 0; j0 < c; j0 += kTopkThreads) {
+      for (int j0 = 0; j0 < cs; j0 += kTopkThreads) {
         const int j = j0 + t;
         uint32_t kk = 0u;
         int32_t ii = 0;
-        if (j < c) { kk = ck[from + j]; ii = ci[from + j]; }
+        if (j < cs) { kk = ck[from + j]; ii = ci[from + j]; }
         __syncthreads();
-        if (j < c) { ck[to + j] = kk; ci[to + j] = ii; }
+        if (j < cs) { ck[to + j] = kk; ci[to + j] = ii; }
         __syncthreads();
       }
     }
@@ -565,15 +609,17 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_final(
     } else {
       uint32_t T;
       int need_eq;
-      radix_select(keys, total, k - above, (uint32_t)tbin << kBinShift, kBinShift, L.rhist, L.misc, T,
-                   need_eq);
+      radix_select(keys, total, rem, prefix, kLowBits, L.rhist, L.misc, T, need_eq);
       cnt = block_emit(keys, total, false, T, need_eq, L.misc, out, k, idxs, 0);
     }
   }
   for (int i = cnt + t; i < k; i += kTopkThreads) out[i] = -1;
 
-  // leave the histogram clear for the next call
-  for (int i = t; i < kHistBins; i += kTopkThreads) gh[i] = 0u;
+  // leave the histograms clear for the next call
+  if (!take_all) {
+    for (int i = t; i < kHistBins; i += kTopkThreads) gh[i] = 0u;
+    for (int i = t; i < kSubBins; i += kTopkThreads) gh2[i] = 0u;
+  }
 }
 
 // ------------------------------------------------------------- planning / launch
@@ -601,7 +647,9 @@ bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, TopkPlan* p) {
   const size_t nb = (size_t)B;
   size_t off = 0;
   p->off_hist = off; off = align256(off + nb * kHistBins * 4);
+  p->off_hist2 = off; off = align256(off + nb * kSubBins * 4);
   p->zero_bytes = off;
+  p->off_thr = off; off = align256(off + nb * 8);
   p->off_cnt = off; off = align256(off + nb * (size_t)p->n_slices * 4);
   p->off_keys = off; off = align256(off + nb * (size_t)p->key_stride * 4);
   p->off_ckey = off; off = align256(off + nb * (size_t)p->n_slices * (size_t)slice * 4);
@@ -648,12 +696,14 @@ hipError_t launch_index_topk(const TopkPlan& p, const uint16_t* q_idx, bool fp4,
   hipLaunchKernelGGL(k_topk_filter, grid, dim3(kTopkThreads), 0, stream,
                      reinterpret_cast<const uint32_t*>(ws + p.off_keys), p.key_stride, n_entries, n_max,
                      k, (int)p.slice, (int)p.n_slices, reinterpret_cast<const uint32_t*>(ws + p.off_hist),
+                     reinterpret_cast<uint32_t*>(ws + p.off_hist2), reinterpret_cast<int2*>(ws + p.off_thr),
                      reinterpret_cast<uint32_t*>(ws + p.off_ckey), reinterpret_cast<int32_t*>(ws + p.off_cidx),
                      reinterpret_cast<int32_t*>(ws + p.off_cnt));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_topk_final, dim3((unsigned)B), dim3(kTopkThreads), 0, stream, n_entries, n_max, k,
                      (int)p.slice, (int)p.n_slices, reinterpret_cast<uint32_t*>(ws + p.off_hist),
+                     reinterpret_cast<uint32_t*>(ws + p.off_hist2), reinterpret_cast<const int2*>(ws + p.off_thr),
                      reinterpret_cast<uint32_t*>(ws + p.off_ckey), reinterpret_cast<int32_t*>(ws + p.off_cidx),
                      reinterpret_cast<const int32_t*>(ws + p.off_cnt), ids);
   return hipGetLastError();

@@ -25,7 +25,7 @@ struct TopkPlan {
   int64_t chunk, n_chunks;     // entries per scoring workgroup, workgroups per sequence
   int64_t slice, n_slices;     // keys per selection workgroup, workgroups per sequence
   int64_t key_stride;          // order keys per sequence row (a multiple of 4)
-  size_t off_hist, off_cnt, off_keys, off_ckey, off_cidx;
+  size_t off_hist, off_hist2, off_thr, off_cnt, off_keys, off_ckey, off_cidx;
   size_t zero_bytes;           // leading bytes that must be zero between calls
   size_t bytes;                // workspace bytes
 };

@@ -107,13 +107,13 @@ cskv_status cskv_compress(int32_t kind, const void* S, const float* gate, int64_
  *   ids       [B, k] int32
  *   chunk     entries scored per workgroup: 0 = automatic, else a multiple
  *             of 256 in [256, 16384]
- *   workspace cskv_index_topk_workspace() bytes. Its leading region holds a
- *             per-sequence histogram and completion counter that must be zero
- *             when a call starts: zero-fill the workspace before the first
- *             call, and again before a call with different B, n_max, k or
- *             chunk or after the buffer served another purpose. Every completed
- *             call leaves that region zero, so calls with the same arguments
- *             can reuse the workspace as it is.
+ *   workspace cskv_index_topk_workspace() bytes. Its leading region holds
+ *             per-sequence histograms that must be zero when a call starts:
+ *             zero-fill the workspace before the first call, and again before a
+ *             call with different B, n_max, k or chunk or after the buffer
+ *             served another purpose. Every completed call leaves that region
+ *             zero, so calls with the same arguments can reuse the workspace as
+ *             it is.
  * EUNSUPPORTED if n_max needs selection slices longer than 2^24 entries.
  */
 size_t cskv_index_topk_workspace(int64_t B, int64_t n_max, int32_t Di, int32_t k,

@@ -38,11 +38,12 @@ def test_version_and_status_strings(lib):
 
 
 def test_topk_workspace_sizes(lib):
-    # 32 x 32767 entries, k = 512: a 4096-bin histogram per sequence, one order
-    # key per entry and room for every entry as a candidate (key + entry number)
+    # 32 x 32767 entries, k = 512: a 4096-bin and a 256-bin histogram and a
+    # threshold record per sequence, one order key per entry and room for every
+    # entry as a candidate (key + entry number)
     B, N = 32, 32767
     ws = lib._lib_topk_ws(B, N, 128, 512, lib.BF16, 0)
-    need = B * (4096 * 4 + N * 4 + 2 * N * 4)
+    need = B * (4096 * 4 + 256 * 4 + 8 + N * 4 + 2 * N * 4)
     assert need <= ws <= need + B * (8 * 2048 * 4 + 64) + 64 * 1024
     # a single entry still needs the histogram and counter
     assert lib._lib_topk_ws(1, 1, 32, 64, lib.BF16, 0) >= 4096 * 4 + 4
