@@ -201,6 +201,41 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
       }
     }
   } else {
+    if constexpr (C::kDma) {
+      // dense rows that all come from the cache: contiguous, so the row
+      // addresses are scalar arithmetic and the swizzle (which depends on
+      // row / 8 = wave only) is one lane offset for all 8 rows
+      const int wv = __builtin_amdgcn_readfirstlane(wave);   // scalar, so LDS targets are too
+      const int64_t row0 = tile0 + 8 * wv;
+      if (dense && row0 + 8 <= n_sel) {
+        if (lane < 8) pb[8 * wv + lane] = 0.0f;
+        const uint8_t* src = rsrc.cache + row0 * (D * 2) + 16 * (lane ^ chunk_swz(8 * wv));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + i * (D * 2)),
+                                           (__attribute__((address_space(3))) void*)(tile + (8 * wv + i) * C::KROW),
+                                           16, 0, kCachePolicyStream);
+        }
+        return;
+      }
+      if (!dense && row0 + 8 <= n_sel) {
+        // selected entries only: each lane < 8 reads one id, each row takes it
+        // with one readlane; rows of invalid ids read the zero row
+        const int myid = lane < 8 ? ids_l[row0 - lo + lane] : 0;
+        const bool ok = myid >= 0 && (int64_t)myid < rsrc.cache_rows;
+        if (lane < 8) pb[8 * wv + lane] = ok ? 0.0f : -INFINITY;
+        const int lane_off = 16 * (lane ^ chunk_swz(8 * wv));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int id = __builtin_amdgcn_readlane(myid, i);
+          const uint8_t* rowp = id >= 0 && (int64_t)id < rsrc.cache_rows ? rsrc.cache + (int64_t)id * (D * 2) : g_zero_row;
+          __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(rowp + lane_off),
+                                           (__attribute__((address_space(3))) void*)(tile + (8 * wv + i) * C::KROW),
+                                           16, 0, kCachePolicyStream);
+        }
+        return;
+      }
+    }
     const uint8_t* p = nullptr;
     const float* sp = nullptr;
     if (lane < 8) slot_source<D, CFP8, WFP8>(rsrc, tile0 + 8 * wave + lane, lo, n_sel, n_keys, dense, ids_l, p, sp);
