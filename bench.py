@@ -342,7 +342,7 @@ COPY_BYTES = 1 << 30
 
 
 def dominant_kernels(kind):
-    return ("k_index_score", "k_topk_filter", "k_topk_final") if kind != "c128a" else ("k_attend", "k_attend_merge")
+    return ("k_index_score", "k_topk_final") if kind != "c128a" else ("k_attend", "k_attend_merge")
 
 
 def kernel_source_digest():
@@ -574,7 +574,7 @@ def main():
                    "launch": "eager" if graphs is None else "hip_graph"},
         "roofline": {
             "bound": "hbm",
-            "kernel": "index_topk (k_index_score + k_topk_filter + k_topk_final)" if (cfg.kind != "c128a") else
+            "kernel": "index_topk (k_index_score + k_topk_final)" if (cfg.kind != "c128a") else
                       "attend (k_attend + k_attend_merge)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

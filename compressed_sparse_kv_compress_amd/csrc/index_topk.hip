@@ -4,48 +4,52 @@
 // compressed entries per query (default k = 512). [P2] Step 5: a learned
 // indexer scores every compressed block; the query reads only the chosen ones.
 //
-// Three kernels:
+// Two kernels:
 //   k_index_score  (grid: chunks x sequences) streams the indexer keys once
 //     from HBM with 16-byte coalesced loads (bf16, or fp4 codes + E4M3 group
 //     scales dequantised in registers), computes each entry's score as a GEMV
-//     against the query's indexer vector, turns it into an order-preserving
-//     32-bit key, writes the keys to the workspace (4 B per entry, coalesced)
-//     and adds the chunk's histogram of the top 12 key bits into a
-//     per-sequence histogram.
-//   k_topk_filter  (grid: slices x sequences) finds, from that histogram, the
-//     bin holding the k-th largest key and keeps the entries of its slice
-//     whose bin is at or above it, in entry order (about k plus one bin's
-//     worth per sequence). It also adds a histogram of the next 8 key bits of
-//     the threshold bin's keys into a per-sequence 256-bin histogram, and the
-//     first slice records the threshold bin and the count of keys above it.
-//   k_topk_final   (grid: sequences) finds from the 256-bin histogram the
-//     20-bit prefix of the k-th largest key, gathers the candidates, resolves
-//     the remaining 12 key bits by radix select in LDS, writes the ids in
-//     ascending entry order (ties go to the lower entry) and clears both
-//     histograms for the next call.
+//     against the query's indexer vector and turns it into an order-preserving
+//     32-bit key, kept in LDS. It adds the chunk's histogram of the top 12 key
+//     bits into a per-sequence histogram with returning atomics. The counts
+//     returned (plus the chunk's own) never exceed the final ones, so the bin
+//     they place the k-th largest key in is at or below the true one. The chunk
+//     keeps its entries in that bin or above as candidates (key and entry
+//     number, in entry order): a superset of its share of the top k.
+//   k_topk_final   (grid: sequences, 1024 threads) finds the true threshold
+//     bin from the complete histogram and gathers into LDS the candidates at
+//     or above it, counting the next 8 key bits of the threshold bin's keys on
+//     the way. That fixes the 20-bit prefix of the k-th largest key; the few
+//     keys sharing it are ranked against each other (a radix select on the
+//     last 12 bits when there are many). It writes the ids in ascending entry
+//     order (ties go to the lower entry) and clears the histogram for the next
+//     call.
 // The selection is exact: every entry of a bin above the threshold bin is in
 // the top k, and the threshold bin is resolved on full keys.
 #include "kernels.h"
 
 namespace cskv {
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 256;            // scoring workgroups
 constexpr int kTopkWaves = kTopkThreads / kWave;
+constexpr int kFinalThreads = 1024;          // selection workgroups (one per sequence)
+constexpr int kFinalWaves = kFinalThreads / kWave;
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;   // per-sequence histogram of the top key bits
 constexpr int kBinShift = 32 - kHistBits;
 constexpr int kRadixPad = 257;              // per-wave radix histograms, bank-shifted
-constexpr int kCandCap = 4096;              // candidates the final select holds in LDS
-constexpr int kSliceUnit = 2048;            // keys a select workgroup filters per round
-constexpr int kMaxSlices = 2048;
-constexpr int kMisc = 16;
-constexpr int kSubBits = 8;                 // key bits below the threshold bin resolved by the filter
+constexpr int kCandCap = 8192;              // candidates the final select holds in LDS
+constexpr int kRound = 2048;                // keys a scoring workgroup compacts per round
+constexpr int kMaxChunks = 4096;            // scoring chunks per sequence
+constexpr int kMisc = 4 + 2 * kFinalWaves;   // block_emit keeps two counts per wave after 4 words
+constexpr int kSubBits = 8;                 // key bits below the threshold bin counted while gathering
 constexpr int kSubBins = 1 << kSubBits;
-constexpr int kLowBits = kBinShift - kSubBits;   // 12 bits left to the final select
+constexpr int kLowBits = kBinShift - kSubBits;   // 12 bits below the 20-bit prefix
+constexpr int kTieCap = 256;                // keys sharing the k-th key's 20-bit prefix ranked pairwise
 
 // ------------------------------------------------------------- block helpers
 
 // Exclusive prefix sum over the block in thread order; also returns the total.
+template <int NT>
 __device__ int block_exclusive_scan(int v, int* scratch, int& total) {
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int incl = wave_inclusive_scan(v);
@@ -54,7 +58,7 @@ __device__ int block_exclusive_scan(int v, int* scratch, int& total) {
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
+  for (int w = 0; w < (NT / kWave); ++w) {
     const int s = scratch[w];
     if (w < wave) before += s;
     total += s;
@@ -67,6 +71,7 @@ __device__ int block_exclusive_scan(int v, int* scratch, int& total) {
 // `low_bits` equal those of `prefix`, finds the rem-th largest (1 <= rem <=
 // their count). Returns the full key T and how many keys equal to T are
 // needed. `keys` may be in LDS or global memory; `hist` is LDS.
+template <int NT>
 __device__ void radix_select(const uint32_t* keys, int n, int rem, uint32_t prefix, int low_bits,
                              uint32_t* hist, int* misc, uint32_t& T_out, int& need_eq_out) {
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
@@ -75,19 +80,19 @@ __device__ void radix_select(const uint32_t* keys, int n, int rem, uint32_t pref
     const int w = hi < 8 ? hi : 8;
     const int shift = hi - w;
     const uint32_t dmask = (1u << w) - 1u;
-    for (int i = t; i < kTopkWaves * kRadixPad; i += kTopkThreads) hist[i] = 0u;
+    for (int i = t; i < (NT / kWave) * kRadixPad; i += NT) hist[i] = 0u;
     __syncthreads();
     uint32_t* h = hist + wave * kRadixPad;
-    for (int i0 = 0; i0 < n; i0 += 4 * kTopkThreads) {
+    for (int i0 = 0; i0 < n; i0 += 4 * NT) {
       uint32_t kv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * kTopkThreads + t;
+        const int i = i0 + u * NT + t;
         kv[u] = i < n ? keys[i] : 0u;
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * kTopkThreads + t;
+        const int i = i0 + u * NT + t;
         const bool match = hi >= 32 || ((kv[u] ^ prefix) >> hi) == 0u;
         if (i < n && match) atomicAdd(&h[(kv[u] >> shift) & dmask], 1u);
       }
@@ -101,7 +106,7 @@ __device__ void radix_select(const uint32_t* keys, int n, int rem, uint32_t pref
         const int d = 255 - 4 * lane - j;
         int v = 0;
 #pragma unroll
-        for (int ww = 0; ww < kTopkWaves; ++ww) v += (int)hist[ww * kRadixPad + d];
+        for (int ww = 0; ww < (NT / kWave); ++ww) v += (int)hist[ww * kRadixPad + d];
         c[j] = v;
         s += v;
       }
@@ -128,10 +133,11 @@ __device__ void radix_select(const uint32_t* keys, int n, int rem, uint32_t pref
 // Emits, in index order, every key > T plus the first need_eq keys == T (or
 // every key when `all`): writes out_idx[p] = idx_map[i] (or idx_base + i).
 // Returns the number emitted (same in all threads).
+template <int NT>
 __device__ int block_emit(const uint32_t* keys, int n, bool all, uint32_t T, int need_eq, int* misc,
                           int32_t* out_idx, int out_cap, const int32_t* idx_map, int32_t idx_base) {
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
-  const int per = (((n + kTopkWaves - 1) / kTopkWaves) + kWave - 1) & ~(kWave - 1);
+  const int per = (((n + (NT / kWave) - 1) / (NT / kWave)) + kWave - 1) & ~(kWave - 1);
   const int lo = wave * per;
   const int hi = min(lo + per, n);
   int gt = 0, eq = 0;
@@ -144,15 +150,15 @@ __device__ int block_emit(const uint32_t* keys, int n, bool all, uint32_t T, int
   }
   if (lane == 0) {
     misc[4 + wave] = gt;
-    misc[4 + kTopkWaves + wave] = eq;
+    misc[4 + (NT / kWave) + wave] = eq;
   }
   __syncthreads();
   int eq_before = 0, sel_before = 0, total = 0;
   {
     int eb = 0;
 #pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) {
-      const int e = misc[4 + kTopkWaves + w];
+    for (int w = 0; w < (NT / kWave); ++w) {
+      const int e = misc[4 + (NT / kWave) + w];
       const int take = min(max(need_eq - eb, 0), e);
       const int sel = misc[4 + w] + take;
       if (w < wave) {
@@ -292,21 +298,81 @@ __device__ void score_chunk_fp4(const uint16_t* q, const uint8_t* codes_g, const
   }
 }
 
+// A thread's 16 bins of a sequence histogram, thread 0 holding the top ones
+// (h[15] is the thread's highest bin).
+constexpr int kBinsPerThread = kHistBins / kTopkThreads;
+template <int NT>
+__device__ __forceinline__ void load_hist16(const uint32_t* gh, uint32_t (&h)[kHistBins / NT]) {
+  constexpr int BPT = kHistBins / NT;
+  const int top = kHistBins - 1 - BPT * (int)threadIdx.x;
+  const uint4* p = reinterpret_cast<const uint4*>(gh + top - (BPT - 1));
+#pragma unroll
+  for (int i = 0; i < BPT / 4; ++i) {
+    const uint4 v = p[i];
+    h[4 * i] = v.x; h[4 * i + 1] = v.y; h[4 * i + 2] = v.z; h[4 * i + 3] = v.w;
+  }
+}
+
+// The bin of the k-th largest key of a sequence, the number of keys in the
+// bins above it and in the bin itself, from the histogram slices of
+// load_hist16. When the histogram holds fewer than k keys the result is bin 0
+// with 0 above.
+template <int NT>
+__device__ void threshold_bin(const uint32_t (&h)[kHistBins / NT], int k, int* scan, int* misc, int& tbin,
+                              int& above, int& tcount) {
+  constexpr int BPT = kHistBins / NT;
+  const int top = kHistBins - 1 - BPT * (int)threadIdx.x;
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) s += (int)h[i];
+  if (threadIdx.x == 0) {
+    misc[0] = 0;
+    misc[1] = 0;
+    misc[2] = 0;
+  }
+  int total;
+  int run = block_exclusive_scan<NT>(s, scan, total);   // (its barriers order the misc stores)
+  if (run < k && k <= run + s) {
+#pragma unroll
+    for (int i = BPT - 1; i >= 0; --i) {
+      const int c = (int)h[i];
+      if (run < k && k <= run + c) {
+        misc[0] = top - (BPT - 1 - i);
+        misc[1] = run;
+        misc[2] = c;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  tbin = misc[0];
+  above = misc[1];
+  tcount = misc[2];
+  __syncthreads();
+}
+
 template <int DI, bool FP4>
 __global__ __launch_bounds__(kTopkThreads) void k_index_score(
     const uint16_t* __restrict__ q_idx, const void* __restrict__ k_idx,
     const uint8_t* __restrict__ k_scale, const int32_t* __restrict__ n_entries, int64_t n_max,
-    int chunk, int64_t key_stride, uint32_t* __restrict__ ws_keys, uint32_t* __restrict__ ws_hist) {
-  extern __shared__ uint32_t lds[];
+    int chunk, int n_chunks, int k, uint32_t* __restrict__ ws_hist, uint32_t* __restrict__ ws_ckey,
+    int32_t* __restrict__ ws_cidx, int32_t* __restrict__ ws_cnt) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  __shared__ int scan[kTopkWaves];
+  __shared__ int misc[kMisc];
   uint32_t* hist = lds;
   uint32_t* keys = lds + kHistBins;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int64_t b = blockIdx.y;
+  const int c = blockIdx.x;
   int64_t nv = n_entries ? (int64_t)n_entries[b] : n_max;
   nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
-  const int64_t start = (int64_t)blockIdx.x * chunk;
+  const int64_t start = (int64_t)c * chunk;
   const int64_t rem = nv - start;
-  if (rem <= 0) return;
+  if (rem <= 0) {
+    if (t == 0) ws_cnt[b * n_chunks + c] = 0;
+    return;
+  }
   const int n = rem > chunk ? chunk : (int)rem;
 
   for (int i = t; i < kHistBins; i += kTopkThreads) hist[i] = 0u;
@@ -321,133 +387,50 @@ __global__ __launch_bounds__(kTopkThreads) void k_index_score(
     score_chunk_bf16<DI>(q, kk, n, keys, hist);
   }
   __syncthreads();
-  // keys -> workspace (start and key_stride are multiples of 4: 16-byte stores)
-  uint32_t* dst = ws_keys + b * key_stride + start;
-  for (int i = 4 * t; i < n; i += 4 * kTopkThreads) {
-    if (i + 4 <= n) {
-      *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(keys + i);
-    } else {
-      for (int j = i; j < n; ++j) dst[j] = keys[j];
-    }
-  }
+
+  // Add the chunk histogram into the sequence's. A bin's returned count plus
+  // the chunk's own is at most its final count; untouched bins count 0.
   uint32_t* gh = ws_hist + b * kHistBins;
-  for (int i = t; i < kHistBins; i += kTopkThreads) {
-    const uint32_t h = hist[i];
-    if (h) atomicAdd(&gh[i], h);
-  }
-}
-
-// ------------------------------------------------------------- selection
-
-struct SelectLds {
-  uint32_t ckey[kCandCap];
-  int32_t cidx[kCandCap];
-  uint16_t slice_of[kCandCap];   // slice of each gathered candidate
-  uint32_t rhist[kTopkWaves * kRadixPad];
-  int pre[kMaxSlices + 1];
-  int misc[kMisc];
-  int scan[kTopkWaves];
-};
-
-// A thread's 16 bins of a sequence histogram, thread 0 holding the top ones
-// (h[15] is the thread's highest bin).
-constexpr int kBinsPerThread = kHistBins / kTopkThreads;
-__device__ __forceinline__ void load_hist16(const uint32_t* gh, uint32_t (&h)[kBinsPerThread]) {
-  const int top = kHistBins - 1 - kBinsPerThread * (int)threadIdx.x;
-  const uint4* p = reinterpret_cast<const uint4*>(gh + top - (kBinsPerThread - 1));
+  uint32_t now[kBinsPerThread];
 #pragma unroll
-  for (int i = 0; i < kBinsPerThread / 4; ++i) {
-    const uint4 v = p[i];
-    h[4 * i] = v.x; h[4 * i + 1] = v.y; h[4 * i + 2] = v.z; h[4 * i + 3] = v.w;
+  for (int u = 0; u < kBinsPerThread; ++u) {
+    const uint32_t h = hist[t + u * kTopkThreads];
+    now[u] = h ? atomicAdd(&gh[t + u * kTopkThreads], h) + h : 0u;
   }
-}
-
-// The bin of the k-th largest key of a sequence (1 <= k < total) and the
-// number of keys in the bins above it, from the histogram slices of load_hist16.
-__device__ void threshold_bin(const uint32_t (&h)[kBinsPerThread], int k, int* scan, int* misc, int& tbin,
-                              int& above) {
-  const int top = kHistBins - 1 - kBinsPerThread * (int)threadIdx.x;
-  int s = 0;
 #pragma unroll
-  for (int i = 0; i < kBinsPerThread; ++i) s += (int)h[i];
-  int total;
-  int run = block_exclusive_scan(s, scan, total);
-  if (run < k && k <= run + s) {
-#pragma unroll
-    for (int i = kBinsPerThread - 1; i >= 0; --i) {
-      const int c = (int)h[i];
-      if (run < k && k <= run + c) {
-        misc[0] = top - (kBinsPerThread - 1 - i);
-        misc[1] = run;
-      }
-      run += c;
-    }
+  for (int u = 0; u < kBinsPerThread; ++u) hist[t + u * kTopkThreads] = now[u];
+  __syncthreads();
+  int tb, above, tcount;
+  {
+    uint32_t h[kBinsPerThread];
+    load_hist16<kTopkThreads>(hist, h);
+    threshold_bin<kTopkThreads>(h, k, scan, misc, tb, above, tcount);   // at or below the final threshold bin
   }
-  __syncthreads();
-  tbin = misc[0];
-  above = misc[1];
-  __syncthreads();
-}
 
-// One workgroup per slice of a sequence: keeps the keys whose histogram bin
-// is at or above the threshold bin, in entry order, with their entry numbers.
-__global__ __launch_bounds__(kTopkThreads) void k_topk_filter(
-    const uint32_t* __restrict__ ws_keys, int64_t key_stride, const int32_t* __restrict__ n_entries,
-    int64_t n_max, int k, int slice, int n_slices, const uint32_t* __restrict__ ws_hist,
-    uint32_t* __restrict__ ws_hist2, int2* __restrict__ ws_thr, uint32_t* __restrict__ ws_ckey,
-    int32_t* __restrict__ ws_cidx, int32_t* __restrict__ ws_cnt) {
-  __shared__ int scan[kTopkWaves];
-  __shared__ int misc[kMisc];
-  __shared__ uint32_t h2[kSubBins];       // next 8 bits of this slice's threshold-bin keys
-  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
-  const int64_t b = blockIdx.y;
-  const int s = blockIdx.x;
-  int64_t nv = n_entries ? (int64_t)n_entries[b] : n_max;
-  nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
-  const int n_here = (int)min((int64_t)slice, max((int64_t)0, nv - (int64_t)s * slice));
-  int tbin = 0, above = 0;
-  bool have_tbin = nv <= k;
-  const bool take_all = have_tbin;
-  for (int i = t; i < kSubBins; i += kTopkThreads) h2[i] = 0u;
-  __syncthreads();
-
-  const int64_t cand_base = (b * n_slices + s) * (int64_t)slice;
-  const uint32_t* src = ws_keys + b * key_stride + (int64_t)s * slice;
+  // keep the chunk's entries at or above that bin, in entry order
+  const int64_t cbase = ((int64_t)b * n_chunks + c) * chunk;
   int written = 0;
-  for (int r0 = 0; r0 < n_here; r0 += kSliceUnit) {
-    const int rn = min(kSliceUnit, n_here - r0);
-    // wave w owns keys [r0 + 512w, r0 + 512w + 512) of the round, lane-strided
-    constexpr int PER = kSliceUnit / kTopkThreads;   // 8
+  for (int r0 = 0; r0 < n; r0 += kRound) {
+    const int rn = min(kRound, n - r0);
+    constexpr int PER = kRound / kTopkThreads;   // wave w owns keys [512w, 512w + 512) of the round
     uint32_t kv[PER];
     bool keep[PER];
     int cnt = 0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int i = wave * (PER * kWave) + u * kWave + lane;
-      kv[u] = i < rn ? src[r0 + i] : 0u;
-    }
-    if (!have_tbin) {   // the histogram is read while the keys are in flight
-      uint32_t h[kBinsPerThread];
-      load_hist16(ws_hist + b * kHistBins, h);
-      threshold_bin(h, k, scan, misc, tbin, above);
-      have_tbin = true;
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int i = wave * (PER * kWave) + u * kWave + lane;
-      keep[u] = i < rn && (int)(kv[u] >> kBinShift) >= tbin;
+      kv[u] = i < rn ? keys[r0 + i] : 0u;
+      keep[u] = i < rn && (int)(kv[u] >> kBinShift) >= tb;
       cnt += __popcll(__ballot(keep[u]));
-      if (!take_all && i < rn && (int)(kv[u] >> kBinShift) == tbin)
-        atomicAdd(&h2[(kv[u] >> kLowBits) & (kSubBins - 1)], 1u);
     }
     if (lane == 0) scan[wave] = cnt;
     __syncthreads();
     int pos = written, round_total = 0;
 #pragma unroll
     for (int w = 0; w < kTopkWaves; ++w) {
-      const int c = scan[w];
-      if (w < wave) pos += c;
-      round_total += c;
+      const int cw = scan[w];
+      if (w < wave) pos += cw;
+      round_total += cw;
     }
     __syncthreads();
 #pragma unroll
@@ -456,137 +439,244 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_filter(
       if (keep[u]) {
         const int p = pos + __popcll(m & lanemask_lt());
         const int i = wave * (PER * kWave) + u * kWave + lane;
-        ws_ckey[cand_base + p] = kv[u];
-        ws_cidx[cand_base + p] = (int32_t)((int64_t)s * slice + r0 + i);
+        ws_ckey[cbase + p] = kv[u];
+        ws_cidx[cbase + p] = (int32_t)(start + r0 + i);
       }
       pos += __popcll(m);
     }
     written += round_total;
   }
-  if (t == 0) ws_cnt[b * n_slices + s] = written;
-  if (!take_all) {
-    if (s == 0 && t == 0) ws_thr[b] = make_int2(tbin, above);   // (nv > k: slice 0 holds keys)
-    __syncthreads();
-    for (int i = t; i < kSubBins; i += kTopkThreads) {
-      const uint32_t c = h2[i];
-      if (c) atomicAdd(&ws_hist2[b * kSubBins + i], c);
-    }
-  }
+  if (t == 0) ws_cnt[b * n_chunks + c] = written;
 }
 
-// One workgroup per sequence: finds the 20-bit prefix of the k-th largest key
-// from the filter's threshold bin and 256-bin histogram, gathers the slices'
-// candidates, resolves the remaining 12 bits on full keys, writes the ids
-// (ascending, -1 padded) and clears both histograms for the next call.
-__global__ __launch_bounds__(kTopkThreads) void k_topk_final(
-    const int32_t* __restrict__ n_entries, int64_t n_max, int k, int slice, int n_slices,
-    uint32_t* __restrict__ ws_hist, uint32_t* __restrict__ ws_hist2, const int2* __restrict__ ws_thr,
-    uint32_t* __restrict__ ws_ckey, int32_t* __restrict__ ws_cidx, const int32_t* __restrict__ ws_cnt,
-    int32_t* __restrict__ ids) {
-  __shared__ SelectLds L;
+// ------------------------------------------------------------- selection
+
+struct SelectLds {
+  uint32_t ckey[kCandCap];
+  int32_t cidx[kCandCap];
+  uint8_t chosen[kCandCap];      // tie keys taken
+  uint32_t rhist[kFinalWaves * kRadixPad];
+  uint32_t h2[kSubBins];         // next 8 bits of the threshold bin's keys
+  uint32_t tkey[kTieCap];        // keys sharing the k-th key's 20-bit prefix
+  int tpos[kTieCap];             // ... and their candidate positions
+  int pre[kMaxChunks + 1];
+  int misc[kMisc];
+  int scan[kFinalWaves];
+};
+
+// Writes, in candidate order, the ids of the candidates whose key's top 20
+// bits exceed `pstar`, or equal it with `chosen` set (every candidate when
+// `all`). Thread t handles one contiguous run of positions. Returns the number
+// written (same in all threads).
+template <int NT>
+__device__ int ordered_emit(const uint32_t* keys, const int32_t* idxs, const uint8_t* chosen, int n, bool all,
+                            uint32_t pstar, int* scan, int32_t* out, int out_cap) {
   const int t = threadIdx.x;
+  const int per = (n + NT - 1) / NT;
+  const int lo = min(t * per, n), hi = min(lo + per, n);
+  auto taken = [&](int i) {
+    const uint32_t p = keys[i] >> kLowBits;
+    return all || p > pstar || (p == pstar && chosen[i]);
+  };
+  int cnt = 0;
+  for (int i = lo; i < hi; ++i) cnt += taken(i) ? 1 : 0;
+  int total;
+  int pos = block_exclusive_scan<NT>(cnt, scan, total);
+  for (int i = lo; i < hi; ++i) {
+    if (taken(i)) {
+      if (pos < out_cap) out[pos] = idxs[i];
+      ++pos;
+    }
+  }
+  return total < out_cap ? total : out_cap;
+}
+
+// One workgroup per sequence: finds the threshold bin from the complete
+// histogram, gathers the chunks' candidates at or above it, resolves the
+// remaining 20 bits on full keys, writes the ids (ascending, -1 padded) and
+// clears the histogram for the next call.
+__global__ __launch_bounds__(kFinalThreads) void k_topk_final(
+    const int32_t* __restrict__ n_entries, int64_t n_max, int k, int chunk, int n_chunks,
+    uint32_t* __restrict__ ws_hist, uint32_t* __restrict__ ws_ckey, int32_t* __restrict__ ws_cidx,
+    const int32_t* __restrict__ ws_cnt, int32_t* __restrict__ ids) {
+  __shared__ SelectLds L;
+  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int64_t b = blockIdx.x;
   int64_t nv = n_entries ? (int64_t)n_entries[b] : n_max;
   nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
   uint32_t* gh = ws_hist + b * kHistBins;
-  uint32_t* gh2 = ws_hist2 + b * kSubBins;
   const bool take_all = nv <= k;
   int32_t* out = ids + b * k;
+  if (nv == 0) {   // no entry was scored (the chunk counts may not even exist)
+    for (int i = t; i < k; i += kFinalThreads) out[i] = -1;
+    return;
+  }
 
-  // slice counts (thread t owns slices 8t .. 8t+7), the threshold record and
-  // the sub-bin histogram (thread t owns sub-bin 255 - t), loaded together
-  constexpr int CPT = kMaxSlices / kTopkThreads;   // 8
-  const int32_t* cnt_b = ws_cnt + b * n_slices;
+  // chunk counts (thread t owns chunks CPT*t ..) and the histogram, loaded together
+  constexpr int CPT = kMaxChunks / kFinalThreads;   // 4
+  const int32_t* cnt_b = ws_cnt + b * n_chunks;
   int c[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     const int si = CPT * t + j;
-    c[j] = si < n_slices ? cnt_b[si] : 0;
+    c[j] = si < n_chunks ? cnt_b[si] : 0;
   }
-  int2 thr = make_int2(0, 0);
-  uint32_t h2v = 0u;
-  if (!take_all) {
-    thr = ws_thr[b];
-    h2v = gh2[kSubBins - 1 - t];
-  }
+  uint32_t h[kHistBins / kFinalThreads];
+  load_hist16<kFinalThreads>(gh, h);
+  for (int i = t; i < kSubBins; i += kFinalThreads) L.h2[i] = 0u;
 
-  // slice offsets of the candidates
+  // chunk offsets of the candidates
   int mine = 0;
 #pragma unroll
   for (int j = 0; j < CPT; ++j) mine += c[j];
   int total;
-  int run = block_exclusive_scan(mine, L.scan, total);
+  int run = block_exclusive_scan<kFinalThreads>(mine, L.scan, total);
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     const int si = CPT * t + j;
-    if (si < n_slices) L.pre[si] = run;
+    if (si < n_chunks) L.pre[si] = run;
     run += c[j];
   }
-  if (t == 0) L.pre[n_slices] = total;
-
-  // the sub-bin holding the k-th largest key: sub-bins from the top down
-  uint32_t prefix = 0u;
-  int rem = 0;
-  if (!take_all) {
-    const int need = k - thr.y;                  // keys still to take from the threshold bin
-    int sub_total;
-    const int above2 = block_exclusive_scan((int)h2v, L.scan, sub_total);   // keys in higher sub-bins
-    if (above2 < need && need <= above2 + (int)h2v) {
-      L.misc[0] = kSubBins - 1 - t;
-      L.misc[1] = need - above2;
-    }
-  }
+  if (t == 0) L.pre[n_chunks] = total;
+  int tbin = 0, above = 0, tcount = 0;
+  if (!take_all) threshold_bin<kFinalThreads>(h, k, L.scan, L.misc, tbin, above, tcount);
   __syncthreads();
-  if (!take_all) {
-    prefix = ((uint32_t)thr.x << kBinShift) | ((uint32_t)L.misc[0] << kLowBits);
-    rem = L.misc[1];
-  }
+  // candidates at or above the threshold bin: every key there is one
+  const int kept = take_all ? total : above + tcount;
 
-  const uint32_t* keys;
-  const int32_t* idxs;
-  if (total <= kCandCap) {
-    // each candidate position's slice, then the gather into LDS
-    for (int si = t; si < n_slices; si += kTopkThreads) {
-      for (int j = L.pre[si]; j < L.pre[si + 1]; ++j) L.slice_of[j] = (uint16_t)si;
-    }
-    __syncthreads();
-    for (int j0 = 0; j0 < total; j0 += 8 * kTopkThreads) {
-      uint32_t kk[8];
-      int32_t ii[8];
+  int cnt = 0;
+  if (kept <= kCandCap) {
+    // Gather into LDS, in candidate order, the ones at or above the threshold
+    // bin, counting the next 8 bits of the threshold bin's keys on the way.
+    // Each position's chunk comes from a search over the chunk offsets with
+    // the same trip count in every lane; the loads follow all the searches.
+    constexpr int PER = 4;
+    constexpr int ROUND = PER * kFinalThreads;
+    int n_sel = 0;
+    for (int j0 = 0; j0 < total; j0 += ROUND) {
+      int jj[PER], base[PER], start[PER];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = j0 + u * kTopkThreads + t;
-        kk[u] = 0u;
-        ii[u] = 0;
-        if (j < total) {
-          const int sl = L.slice_of[j];
-          const int64_t off = (b * n_slices + sl) * (int64_t)slice + (j - L.pre[sl]);
-          kk[u] = ws_ckey[off];
-          ii[u] = ws_cidx[off];
+      for (int u = 0; u < PER; ++u) {
+        jj[u] = min(j0 + wave * (PER * kWave) + u * kWave + lane, total - 1);
+        base[u] = 0;
+        start[u] = 0;
+      }
+      for (int n = n_chunks + 1; n > 1;) {
+        const int half = n >> 1;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          const int v = L.pre[base[u] + half];
+          if (v <= jj[u]) {
+            base[u] += half;
+            start[u] = v;
+          }
         }
+        n -= half;
+      }
+      uint32_t kk[PER];
+      int32_t ii[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int64_t off = (b * n_chunks + base[u]) * (int64_t)chunk + (jj[u] - start[u]);
+        kk[u] = ws_ckey[off];
+        ii[u] = ws_cidx[off];
+      }
+      bool keep[PER];
+      int cw = 0;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const bool valid = j0 + wave * (PER * kWave) + u * kWave + lane < total;
+        const int bin = (int)(kk[u] >> kBinShift);
+        keep[u] = valid && (take_all || bin >= tbin);
+        cw += __popcll(__ballot(keep[u]));
+        if (!take_all && valid && bin == tbin) atomicAdd(&L.h2[(kk[u] >> kLowBits) & (kSubBins - 1)], 1u);
+      }
+      if (lane == 0) L.scan[wave] = cw;
+      __syncthreads();
+      int pos = n_sel, round_total = 0;
+#pragma unroll
+      for (int w = 0; w < kFinalWaves; ++w) {
+        const int x = L.scan[w];
+        if (w < wave) pos += x;
+        round_total += x;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = j0 + u * kTopkThreads + t;
-        if (j < total) {
-          L.ckey[j] = kk[u];
-          L.cidx[j] = ii[u];
+      for (int u = 0; u < PER; ++u) {
+        const uint64_t m = __ballot(keep[u]);
+        const int p = pos + __popcll(m & lanemask_lt());
+        if (keep[u] && p < kCandCap) {   // (p < kept always holds for a zeroed workspace)
+          L.ckey[p] = kk[u];
+          L.cidx[p] = ii[u];
         }
+        pos += __popcll(m);
+      }
+      n_sel += round_total;
+      __syncthreads();
+    }
+    n_sel = min(n_sel, kCandCap);
+
+    if (take_all) {
+      cnt = ordered_emit<kFinalThreads>(L.ckey, L.cidx, L.chosen, n_sel, true, 0u, L.scan, out, k);
+    } else {
+      // the sub-bin holding the k-th largest key: sub-bins from the top down
+      const int need = k - above;                  // keys still to take from the threshold bin
+      const int h2v = t < kSubBins ? (int)L.h2[kSubBins - 1 - t] : 0;
+      if (t == 0) L.misc[3] = 0;                   // tie counter
+      int sub_total;
+      const int above2 = block_exclusive_scan<kFinalThreads>(h2v, L.scan, sub_total);   // keys in higher sub-bins
+      if (above2 < need && need <= above2 + h2v) {
+        L.misc[0] = kSubBins - 1 - t;
+        L.misc[1] = need - above2;
+        L.misc[2] = h2v;
+      }
+      __syncthreads();
+      const uint32_t pstar = ((uint32_t)tbin << kSubBits) | (uint32_t)L.misc[0];   // 20-bit prefix
+      const int rem = L.misc[1];                   // keys to take among those with that prefix
+      const int m = L.misc[2];                     // keys with that prefix
+      if (m <= kTieCap) {
+        // rank the keys sharing the prefix against each other (descending key,
+        // then ascending entry, which candidate order gives)
+        for (int i = t; i < n_sel; i += kFinalThreads) {
+          const uint32_t key = L.ckey[i];
+          if ((key >> kLowBits) == pstar) {
+            const int slot = atomicAdd(&L.misc[3], 1);
+            if (slot < kTieCap) {   // (there are exactly m of them)
+              L.tkey[slot] = key;
+              L.tpos[slot] = i;
+            }
+          }
+        }
+        __syncthreads();
+        if (t < m) {
+          const uint32_t key = L.tkey[t];
+          const int pos = L.tpos[t];
+          int rank = 0;
+          for (int s2 = 0; s2 < m; ++s2) {
+            const uint32_t ks = L.tkey[s2];
+            rank += (ks > key || (ks == key && L.tpos[s2] < pos)) ? 1 : 0;
+          }
+          L.chosen[pos] = rank < rem ? 1 : 0;
+        }
+        __syncthreads();
+        cnt = ordered_emit<kFinalThreads>(L.ckey, L.cidx, L.chosen, n_sel, false, pstar, L.scan, out, k);
+      } else {
+        uint32_t T;
+        int need_eq;
+        radix_select<kFinalThreads>(L.ckey, n_sel, rem, pstar << kLowBits, kLowBits, L.rhist, L.misc, T, need_eq);
+        cnt = block_emit<kFinalThreads>(L.ckey, n_sel, false, T, need_eq, L.misc, out, k, L.cidx, 0);
       }
     }
-    __syncthreads();
-    keys = L.ckey;
-    idxs = L.cidx;
   } else {
-    // more candidates than LDS holds (heavily tied scores): compact the slices
-    // in place in global memory and select there (reads never overtake writes:
-    // a slice's destination offset is at most its source offset)
-    uint32_t* ck = ws_ckey + b * n_slices * (int64_t)slice;
-    int32_t* ci = ws_cidx + b * n_slices * (int64_t)slice;
-    for (int s1 = 1; s1 < n_slices; ++s1) {
+    // more keys at or above the threshold bin than LDS holds (heavily tied
+    // scores): compact the chunks' lists in place in global memory and select
+    // there (reads never overtake writes: a list's destination offset is at
+    // most its source offset)
+    uint32_t* ck = ws_ckey + b * n_chunks * (int64_t)chunk;
+    int32_t* ci = ws_cidx + b * n_chunks * (int64_t)chunk;
+    for (int s1 = 1; s1 < n_chunks; ++s1) {
       const int cs = L.pre[s1 + 1] - L.pre[s1];
-      const int64_t from = (int64_t)s1 * slice, to = L.pre[s1];
-      for (int j0 = 0; j0 < cs; j0 += kTopkThreads) {
+      const int64_t from = (int64_t)s1 * chunk, to = L.pre[s1];
+      for (int j0 = 0; j0 < cs; j0 += kFinalThreads) {
         const int j = j0 + t;
         uint32_t kk = 0u;
         int32_t ii = 0;
@@ -598,28 +688,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_final(
     }
     __threadfence_block();
     __syncthreads();
-    keys = ck;
-    idxs = ci;
+    uint32_t T;
+    int need_eq;
+    radix_select<kFinalThreads>(ck, total, k - above, (uint32_t)tbin << kBinShift, kBinShift, L.rhist, L.misc, T, need_eq);
+    cnt = block_emit<kFinalThreads>(ck, total, false, T, need_eq, L.misc, out, k, ci, 0);
   }
+  for (int i = cnt + t; i < k; i += kFinalThreads) out[i] = -1;
 
-  int cnt = 0;
-  if (total > 0) {
-    if (take_all) {
-      cnt = block_emit(keys, total, true, 0u, 0, L.misc, out, k, idxs, 0);
-    } else {
-      uint32_t T;
-      int need_eq;
-      radix_select(keys, total, rem, prefix, kLowBits, L.rhist, L.misc, T, need_eq);
-      cnt = block_emit(keys, total, false, T, need_eq, L.misc, out, k, idxs, 0);
-    }
-  }
-  for (int i = cnt + t; i < k; i += kTopkThreads) out[i] = -1;
-
-  // leave the histograms clear for the next call
-  if (!take_all) {
-    for (int i = t; i < kHistBins; i += kTopkThreads) gh[i] = 0u;
-    for (int i = t; i < kSubBins; i += kTopkThreads) gh2[i] = 0u;
-  }
+  // leave the histogram clear for the next call
+  for (int i = t; i < kHistBins; i += kFinalThreads) gh[i] = 0u;
 }
 
 // ------------------------------------------------------------- planning / launch
@@ -631,29 +708,24 @@ bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, TopkPlan* p) {
   int64_t chunk = chunk_hint;
   if (chunk == 0) {
     // about 1500 scoring workgroups over the batch, chunks of 512 .. 8192 entries
+    // (more when a sequence would need more chunks than the final select tracks)
     const int64_t want = (B * n_max + 1535) / 1536;
     chunk = 512;
     while (chunk < want && chunk < 8192) chunk *= 2;
+    while ((n_max + chunk - 1) / chunk > kMaxChunks && chunk < 16384) chunk *= 2;
   }
   if (chunk < 256 || chunk > 16384 || chunk % 256 != 0) return false;
   p->chunk = chunk;
   p->n_chunks = n_max <= 0 ? 1 : (n_max + chunk - 1) / chunk;
-  int64_t slice = kSliceUnit;
-  while ((n_max + slice - 1) / slice > kMaxSlices) slice *= 2;
-  if (slice > (int64_t)1 << 24) return false;
-  p->slice = slice;
-  p->n_slices = n_max <= 0 ? 1 : (n_max + slice - 1) / slice;
-  p->key_stride = (n_max + 3) & ~(int64_t)3;
+  if (p->n_chunks > kMaxChunks) return false;
   const size_t nb = (size_t)B;
+  const size_t slots = nb * (size_t)p->n_chunks * (size_t)chunk;
   size_t off = 0;
   p->off_hist = off; off = align256(off + nb * kHistBins * 4);
-  p->off_hist2 = off; off = align256(off + nb * kSubBins * 4);
   p->zero_bytes = off;
-  p->off_thr = off; off = align256(off + nb * 8);
-  p->off_cnt = off; off = align256(off + nb * (size_t)p->n_slices * 4);
-  p->off_keys = off; off = align256(off + nb * (size_t)p->key_stride * 4);
-  p->off_ckey = off; off = align256(off + nb * (size_t)p->n_slices * (size_t)slice * 4);
-  p->off_cidx = off; off = align256(off + nb * (size_t)p->n_slices * (size_t)slice * 4);
+  p->off_cnt = off; off = align256(off + nb * (size_t)p->n_chunks * 4);
+  p->off_ckey = off; off = align256(off + slots * 4);
+  p->off_cidx = off; off = align256(off + slots * 4);
   p->bytes = off;
   return true;
 }
@@ -661,7 +733,7 @@ bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, TopkPlan* p) {
 template <int DI, bool FP4>
 static hipError_t launch_score(const TopkPlan& p, const uint16_t* q_idx, const void* k_idx,
                                const uint8_t* k_scale, const int32_t* n_entries, int64_t B,
-                               int64_t n_max, uint8_t* ws, hipStream_t stream) {
+                               int64_t n_max, int k, uint8_t* ws, hipStream_t stream) {
   const size_t shmem = (size_t)kHistBins * 4 + (size_t)p.chunk * 4;
   auto kern = k_index_score<DI, FP4>;
   if (shmem > 65536) {
@@ -671,8 +743,9 @@ static hipError_t launch_score(const TopkPlan& p, const uint16_t* q_idx, const v
   }
   dim3 grid((unsigned)p.n_chunks, (unsigned)B);
   hipLaunchKernelGGL(kern, grid, dim3(kTopkThreads), shmem, stream, q_idx, k_idx, k_scale, n_entries,
-                     n_max, (int)p.chunk, p.key_stride, reinterpret_cast<uint32_t*>(ws + p.off_keys),
-                     reinterpret_cast<uint32_t*>(ws + p.off_hist));
+                     n_max, (int)p.chunk, (int)p.n_chunks, k, reinterpret_cast<uint32_t*>(ws + p.off_hist),
+                     reinterpret_cast<uint32_t*>(ws + p.off_ckey), reinterpret_cast<int32_t*>(ws + p.off_cidx),
+                     reinterpret_cast<int32_t*>(ws + p.off_cnt));
   return hipGetLastError();
 }
 
@@ -684,26 +757,16 @@ hipError_t launch_index_topk(const TopkPlan& p, const uint16_t* q_idx, bool fp4,
   hipError_t e = hipSuccess;
   if (n_max > 0) {
     if (fp4) {
-      e = Di == 128 ? launch_score<128, true>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, ws, stream)
-                    : launch_score<32, true>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, ws, stream);
+      e = Di == 128 ? launch_score<128, true>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ws, stream)
+                    : launch_score<32, true>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ws, stream);
     } else {
-      e = Di == 128 ? launch_score<128, false>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, ws, stream)
-                    : launch_score<32, false>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, ws, stream);
+      e = Di == 128 ? launch_score<128, false>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ws, stream)
+                    : launch_score<32, false>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ws, stream);
     }
     if (e != hipSuccess) return e;
   }
-  dim3 grid((unsigned)p.n_slices, (unsigned)B);
-  hipLaunchKernelGGL(k_topk_filter, grid, dim3(kTopkThreads), 0, stream,
-                     reinterpret_cast<const uint32_t*>(ws + p.off_keys), p.key_stride, n_entries, n_max,
-                     k, (int)p.slice, (int)p.n_slices, reinterpret_cast<const uint32_t*>(ws + p.off_hist),
-                     reinterpret_cast<uint32_t*>(ws + p.off_hist2), reinterpret_cast<int2*>(ws + p.off_thr),
-                     reinterpret_cast<uint32_t*>(ws + p.off_ckey), reinterpret_cast<int32_t*>(ws + p.off_cidx),
-                     reinterpret_cast<int32_t*>(ws + p.off_cnt));
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_topk_final, dim3((unsigned)B), dim3(kTopkThreads), 0, stream, n_entries, n_max, k,
-                     (int)p.slice, (int)p.n_slices, reinterpret_cast<uint32_t*>(ws + p.off_hist),
-                     reinterpret_cast<uint32_t*>(ws + p.off_hist2), reinterpret_cast<const int2*>(ws + p.off_thr),
+  hipLaunchKernelGGL(k_topk_final, dim3((unsigned)B), dim3(kFinalThreads), 0, stream, n_entries, n_max, k,
+                     (int)p.chunk, (int)p.n_chunks, reinterpret_cast<uint32_t*>(ws + p.off_hist),
                      reinterpret_cast<uint32_t*>(ws + p.off_ckey), reinterpret_cast<int32_t*>(ws + p.off_cidx),
                      reinterpret_cast<const int32_t*>(ws + p.off_cnt), ids);
   return hipGetLastError();

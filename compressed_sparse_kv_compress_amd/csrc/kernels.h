@@ -15,17 +15,15 @@ hipError_t launch_compress(int kind, const uint16_t* S, const float* gate, int64
                            float* cache_scale, int64_t cache_rows, hipStream_t stream);
 
 // ---- index_topk.hip
-// Plan of the indexer: k_index_score scores `chunk` entries per workgroup,
-// k_topk_filter filters `slice` keys per workgroup, k_topk_final finishes one
-// sequence per workgroup. Workspace regions (byte offsets): the per-sequence
-// histogram comes first (it must be zero when a call starts and every call
-// leaves it zero), then the slice candidate counts, the order keys and the
-// candidate keys / entry numbers.
+// Plan of the indexer: k_index_score scores `chunk` entries per workgroup and
+// writes the chunk's candidates, k_topk_final finishes one sequence per
+// workgroup. Workspace regions (byte offsets): the per-sequence histogram
+// comes first (it must be zero when a call starts and every call leaves it
+// zero), then the chunks' candidate counts and their candidate keys / entry
+// numbers (room for every entry).
 struct TopkPlan {
   int64_t chunk, n_chunks;     // entries per scoring workgroup, workgroups per sequence
-  int64_t slice, n_slices;     // keys per selection workgroup, workgroups per sequence
-  int64_t key_stride;          // order keys per sequence row (a multiple of 4)
-  size_t off_hist, off_hist2, off_thr, off_cnt, off_keys, off_ckey, off_cidx;
+  size_t off_hist, off_cnt, off_ckey, off_cidx;
   size_t zero_bytes;           // leading bytes that must be zero between calls
   size_t bytes;                // workspace bytes
 };

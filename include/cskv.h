@@ -112,9 +112,10 @@ cskv_status cskv_compress(int32_t kind, const void* S, const float* gate, int64_
  *             zero-fill the workspace before the first call, and again before a
  *             call with different B, n_max, k or chunk or after the buffer
  *             served another purpose. Every completed call leaves that region
- *             zero, so calls with the same arguments can reuse the workspace as
- *             it is.
- * EUNSUPPORTED if n_max needs selection slices longer than 2^24 entries.
+ *             zero (whatever n_entries held), so calls with the same arguments
+ *             can reuse the workspace as it is.
+ * EUNSUPPORTED if a sequence would need more than 4096 chunks (n_max > 4096 *
+ * chunk; with automatic chunking, n_max > 67108864).
  */
 size_t cskv_index_topk_workspace(int64_t B, int64_t n_max, int32_t Di, int32_t k,
                                  int32_t key_dtype, int32_t chunk);

@@ -38,7 +38,7 @@ def _oracle_ids(q, kk, k, n_valid=None):
     (1, 511, 32, 64, 4, 0),          # the tiny workload's shape
     (3, 5000, 128, 512, 8, 1024),    # several chunks and a ragged tail
     (2, 33000, 128, 512, 8, 0),      # automatic chunking
-    (2, 25600, 128, 64, 8, 256),     # 100 scoring chunks, 13 selection slices per sequence
+    (2, 25600, 128, 64, 8, 256),     # 100 scoring chunks per sequence
     (4, 777, 128, 2048, 8, 256),     # k larger than N: -1 padding
     (2, 4096, 32, 100, 1, 512),      # values in [-1, 1]: massive ties
 ])
@@ -67,6 +67,26 @@ def test_topk_ragged_entry_counts(cskv):
     nv = np.array([9000, 0, 100, 512, 8191, 4097], dtype=np.int32)
     ids = cskv.index_topk(to_dev_bf16(q), to_dev_bf16(kk), k, n_entries=to_dev(nv), chunk=1024).cpu().numpy()
     assert np.array_equal(ids, _oracle_ids(q, kk, k, nv))
+
+
+def test_topk_short_sequences_leave_workspace_clear(cskv):
+    """Calls on one workspace where some sequences hold no more than k entries,
+    followed by calls where they hold more: every call must match the oracle
+    (each call leaves the per-sequence histograms clear for the next)."""
+    B, N, Di, k = 4, 6000, 128, 512
+    q, kk = _bf16_case(11, B, N, Di, 8)
+    for nv in ([512, 100, 6000, 0], [6000] * 4, [3000, 6000, 511, 513], [6000] * 4):
+        nv = np.array(nv, dtype=np.int32)
+        ids = cskv.index_topk(to_dev_bf16(q), to_dev_bf16(kk), k, n_entries=to_dev(nv), chunk=1024).cpu().numpy()
+        assert np.array_equal(ids, _oracle_ids(q, kk, k, nv)), nv
+
+
+def test_topk_no_entries(cskv):
+    """n_max = 0: nothing is scored and every id is -1."""
+    q, _ = _bf16_case(2, 2, 10, 128, 8)
+    kk = np.zeros((2, 0, 128), dtype=np.uint16)
+    ids = cskv.index_topk(to_dev_bf16(q), to_dev_bf16(kk), 16).cpu().numpy()
+    assert ids.shape == (2, 16) and (ids == -1).all()
 
 
 def test_topk_all_equal_and_nan(cskv):
@@ -109,7 +129,7 @@ def test_topk_rejects_bad_arguments(cskv):
 
 
 def test_topk_ties_beyond_lds_capacity(cskv):
-    """More than 4096 entries share the threshold bin: the selection runs from
+    """More than 8192 entries share the threshold bin: the selection runs from
     global memory instead of LDS and must still be exact."""
     B, N, Di, k = 2, 40000, 128, 512
     q = np.full((B, Di), F.f32_to_bf16(np.float32(1.0)), dtype=np.uint16)
