@@ -12,9 +12,10 @@
 //     32-bit key, kept in LDS. It adds the chunk's histogram of the top 12 key
 //     bits into a per-sequence histogram with returning atomics. The counts
 //     returned (plus the chunk's own) never exceed the final ones, so the bin
-//     they place the k-th largest key in is at or below the true one. The chunk
-//     keeps its entries in that bin or above as candidates (key and entry
-//     number, in entry order): a superset of its share of the top k.
+//     they place the k-th largest key in is at or below the true one. Each
+//     wave keeps the entries of its quarter of the chunk in that bin or above
+//     as candidates (key and entry number, in entry order) in a list of its
+//     own: together a superset of the chunk's share of the top k.
 //   k_topk_final   (grid: sequences, 1024 threads) finds the true threshold
 //     bin from the complete histogram and gathers into LDS the candidates at
 //     or above it, counting the next 8 key bits of the threshold bin's keys on
@@ -38,13 +39,14 @@ constexpr int kHistBins = 1 << kHistBits;   // per-sequence histogram of the top
 constexpr int kBinShift = 32 - kHistBits;
 constexpr int kRadixPad = 257;              // per-wave radix histograms, bank-shifted
 constexpr int kCandCap = 8192;              // candidates the final select holds in LDS
-constexpr int kRound = 2048;                // keys a scoring workgroup compacts per round
-constexpr int kMaxChunks = 4096;            // scoring chunks per sequence
+constexpr int kMaxChunks = 2048;            // scoring chunks per sequence
+constexpr int kMaxLists = kMaxChunks * kTopkWaves;   // candidate lists per sequence (one per chunk and wave)
 constexpr int kMisc = 4 + 2 * kFinalWaves;   // block_emit keeps two counts per wave after 4 words
 constexpr int kSubBits = 8;                 // key bits below the threshold bin counted while gathering
 constexpr int kSubBins = 1 << kSubBits;
 constexpr int kLowBits = kBinShift - kSubBits;   // 12 bits below the 20-bit prefix
 constexpr int kTieCap = 256;                // keys sharing the k-th key's 20-bit prefix ranked pairwise
+constexpr int kTbCap = 2048;                // threshold-bin keys the final select lists apart
 
 // ------------------------------------------------------------- block helpers
 
@@ -200,11 +202,15 @@ __device__ __forceinline__ void put_key(uint32_t* keys, uint32_t* hist, int e, f
   atomicAdd(&hist[key >> kBinShift], 1u);
 }
 
+// Entry groups [g_begin, g_end) of a chunk of n entries, a group being the
+// 64/LPE consecutive entries one wave-wide load covers; g_end - g_begin is a
+// multiple of 4 waves x 8 unrolled groups, or g_end is the chunk's last group.
+//
 // bf16 keys: LPE = DI/8 lanes read one 16-byte slice each of an entry; one
 // wave-wide load covers 64/LPE consecutive entries (1 KiB contiguous).
 template <int DI>
-__device__ void score_chunk_bf16(const uint16_t* q, const uint16_t* keys_g, int n, uint32_t* keys,
-                                 uint32_t* hist) {
+__device__ void score_chunk_bf16(const uint16_t* q, const uint16_t* keys_g, int n, int g_begin, int g_end,
+                                 uint32_t* keys, uint32_t* hist) {
   constexpr int LPE = DI / 8;
   constexpr int EPL = kWave / LPE;
   constexpr int U = 8;
@@ -214,8 +220,7 @@ __device__ void score_chunk_bf16(const uint16_t* q, const uint16_t* keys_g, int 
   const bf16x2_t q0 = __builtin_bit_cast(bf16x2_t, qv.x), q1 = __builtin_bit_cast(bf16x2_t, qv.y);
   const bf16x2_t q2 = __builtin_bit_cast(bf16x2_t, qv.z), q3 = __builtin_bit_cast(bf16x2_t, qv.w);
   const uint4* kp = reinterpret_cast<const uint4*>(keys_g);
-  const int n_groups = (n + EPL - 1) / EPL;
-  for (int g0 = wave; g0 < n_groups; g0 += kTopkWaves * U) {
+  for (int g0 = g_begin + wave; g0 < g_end; g0 += kTopkWaves * U) {
     uint4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -241,7 +246,7 @@ __device__ void score_chunk_bf16(const uint16_t* q, const uint16_t* keys_g, int 
 // E2M1 codes are widened to bf16 exactly by the gfx950 converter.
 template <int DI>
 __device__ void score_chunk_fp4(const uint16_t* q, const uint8_t* codes_g, const uint8_t* scales_g,
-                                int n, uint32_t* keys, uint32_t* hist) {
+                                int n, int g_begin, int g_end, uint32_t* keys, uint32_t* hist) {
   constexpr int LPE = DI / 32;
   constexpr int EPL = kWave / LPE;
   constexpr int U = 8;
@@ -261,8 +266,7 @@ __device__ void score_chunk_fp4(const uint16_t* q, const uint8_t* codes_g, const
   }
   const uint4* cp = reinterpret_cast<const uint4*>(codes_g);
   const uint16_t* sp = reinterpret_cast<const uint16_t*>(scales_g);
-  const int n_groups = (n + EPL - 1) / EPL;
-  for (int g0 = wave; g0 < n_groups; g0 += kTopkWaves * U) {
+  for (int g0 = g_begin + wave; g0 < g_end; g0 += kTopkWaves * U) {
     uint4 v[U];
     uint32_t s[U];
 #pragma unroll
@@ -298,57 +302,38 @@ __device__ void score_chunk_fp4(const uint16_t* q, const uint8_t* codes_g, const
   }
 }
 
-// A thread's 16 bins of a sequence histogram, thread 0 holding the top ones
-// (h[15] is the thread's highest bin).
 constexpr int kBinsPerThread = kHistBins / kTopkThreads;
-template <int NT>
-__device__ __forceinline__ void load_hist16(const uint32_t* gh, uint32_t (&h)[kHistBins / NT]) {
-  constexpr int BPT = kHistBins / NT;
-  const int top = kHistBins - 1 - BPT * (int)threadIdx.x;
-  const uint4* p = reinterpret_cast<const uint4*>(gh + top - (BPT - 1));
-#pragma unroll
-  for (int i = 0; i < BPT / 4; ++i) {
-    const uint4 v = p[i];
-    h[4 * i] = v.x; h[4 * i + 1] = v.y; h[4 * i + 2] = v.z; h[4 * i + 3] = v.w;
-  }
-}
 
-// The bin of the k-th largest key of a sequence, the number of keys in the
-// bins above it and in the bin itself, from the histogram slices of
-// load_hist16. When the histogram holds fewer than k keys the result is bin 0
-// with 0 above.
-template <int NT>
-__device__ void threshold_bin(const uint32_t (&h)[kHistBins / NT], int k, int* scan, int* misc, int& tbin,
-                              int& above, int& tcount) {
-  constexpr int BPT = kHistBins / NT;
-  const int top = kHistBins - 1 - BPT * (int)threadIdx.x;
+// The bin of the k-th largest key under the counts hist[0 .. 4096) in LDS, or
+// 0 when they hold fewer than k keys, found by one wave alone: lane l sums the
+// 64 bins of segment l (bins 4095 - 64l down to 4032 - 64l), a scan over the
+// lanes finds the segment where the count from the top reaches k, and a scan
+// over that segment's bins finds the bin. Also gives the number of keys in
+// the bins above it and in the bin itself (both 0 with bin 0 when fewer than k).
+__device__ int wave_threshold_bin(const uint32_t* hist, int k, int& above, int& count) {
+  const int lane = lane_id();
+  const uint4* seg = reinterpret_cast<const uint4*>(hist + kHistBins - 64 * (lane + 1));
   int s = 0;
 #pragma unroll
-  for (int i = 0; i < BPT; ++i) s += (int)h[i];
-  if (threadIdx.x == 0) {
-    misc[0] = 0;
-    misc[1] = 0;
-    misc[2] = 0;
+  for (int i = 0; i < 16; ++i) {
+    const uint4 v = seg[(i + lane) & 15];   // rotated so that lanes spread over the banks
+    s += (int)(v.x + v.y + v.z + v.w);
   }
-  int total;
-  int run = block_exclusive_scan<NT>(s, scan, total);   // (its barriers order the misc stores)
-  if (run < k && k <= run + s) {
-#pragma unroll
-    for (int i = BPT - 1; i >= 0; --i) {
-      const int c = (int)h[i];
-      if (run < k && k <= run + c) {
-        misc[0] = top - (BPT - 1 - i);
-        misc[1] = run;
-        misc[2] = c;
-      }
-      run += c;
-    }
-  }
-  __syncthreads();
-  tbin = misc[0];
-  above = misc[1];
-  tcount = misc[2];
-  __syncthreads();
+  const int incl = wave_inclusive_scan(s);   // keys in segments 0 .. lane
+  const uint64_t m = __ballot(incl - s < k && k <= incl);
+  above = 0;
+  count = 0;
+  if (m == 0) return 0;
+  const int L = __ffsll((unsigned long long)m) - 1;
+  const int seg_above = __shfl(incl - s, L);
+  const int top = kHistBins - 1 - 64 * L;
+  const int cnt = (int)hist[top - lane];
+  const int incl2 = wave_inclusive_scan(cnt) + seg_above;
+  const uint64_t m2 = __ballot(incl2 - cnt < k && k <= incl2);
+  const int F = __ffsll((unsigned long long)m2) - 1;
+  above = __shfl(incl2 - cnt, F);
+  count = __shfl(cnt, F);
+  return top - F;
 }
 
 template <int DI, bool FP4>
@@ -358,19 +343,18 @@ __global__ __launch_bounds__(kTopkThreads) void k_index_score(
     int chunk, int n_chunks, int k, uint32_t* __restrict__ ws_hist, uint32_t* __restrict__ ws_ckey,
     int32_t* __restrict__ ws_cidx, int32_t* __restrict__ ws_cnt) {
   extern __shared__ __align__(16) uint32_t lds[];
-  __shared__ int scan[kTopkWaves];
-  __shared__ int misc[kMisc];
   uint32_t* hist = lds;
   uint32_t* keys = lds + kHistBins;
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int64_t b = blockIdx.y;
   const int c = blockIdx.x;
+  const int64_t list = ((int64_t)b * n_chunks + c) * kTopkWaves + wave;   // this wave's candidate list
   int64_t nv = n_entries ? (int64_t)n_entries[b] : n_max;
   nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
   const int64_t start = (int64_t)c * chunk;
   const int64_t rem = nv - start;
   if (rem <= 0) {
-    if (t == 0) ws_cnt[b * n_chunks + c] = 0;
+    if (lane == 0) ws_cnt[list] = 0;
     return;
   }
   const int n = rem > chunk ? chunk : (int)rem;
@@ -378,13 +362,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_index_score(
   for (int i = t; i < kHistBins; i += kTopkThreads) hist[i] = 0u;
   __syncthreads();
   const uint16_t* q = q_idx + b * DI;
+  constexpr int EPL = FP4 ? kWave / (DI / 32) : kWave / (DI / 8);   // entries per wave-wide load
+  const int n_groups = (n + EPL - 1) / EPL;
   if constexpr (FP4) {
     const uint8_t* codes = reinterpret_cast<const uint8_t*>(k_idx) + (b * n_max + start) * (DI / 2);
     const uint8_t* scales = k_scale + (b * n_max + start) * (DI / 16);
-    score_chunk_fp4<DI>(q, codes, scales, n, keys, hist);
+    score_chunk_fp4<DI>(q, codes, scales, n, 0, n_groups, keys, hist);
   } else {
     const uint16_t* kk = reinterpret_cast<const uint16_t*>(k_idx) + (b * n_max + start) * DI;
-    score_chunk_bf16<DI>(q, kk, n, keys, hist);
+    score_chunk_bf16<DI>(q, kk, n, 0, n_groups, keys, hist);
   }
   __syncthreads();
 
@@ -400,68 +386,55 @@ __global__ __launch_bounds__(kTopkThreads) void k_index_score(
 #pragma unroll
   for (int u = 0; u < kBinsPerThread; ++u) hist[t + u * kTopkThreads] = now[u];
   __syncthreads();
-  int tb, above, tcount;
-  {
-    uint32_t h[kBinsPerThread];
-    load_hist16<kTopkThreads>(hist, h);
-    threshold_bin<kTopkThreads>(h, k, scan, misc, tb, above, tcount);   // at or below the final threshold bin
-  }
+  int tb_above, tb_count;
+  const int tb = wave_threshold_bin(hist, k, tb_above, tb_count);   // at or below the final threshold bin
 
-  // keep the chunk's entries at or above that bin, in entry order
-  const int64_t cbase = ((int64_t)b * n_chunks + c) * chunk;
+  // Wave w keeps the entries of its quarter of the chunk at or above that bin,
+  // in entry order, in its own list.
+  const int quarter = chunk / kTopkWaves;
+  const int lo = wave * quarter, hi = min(lo + quarter, n);
+  uint32_t* ck = ws_ckey + list * quarter;
+  int32_t* ci = ws_cidx + list * quarter;
   int written = 0;
-  for (int r0 = 0; r0 < n; r0 += kRound) {
-    const int rn = min(kRound, n - r0);
-    constexpr int PER = kRound / kTopkThreads;   // wave w owns keys [512w, 512w + 512) of the round
-    uint32_t kv[PER];
-    bool keep[PER];
-    int cnt = 0;
+  for (int i0 = lo; i0 < hi; i0 += 4 * kWave) {
+    uint32_t kv[4];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int i = wave * (PER * kWave) + u * kWave + lane;
-      kv[u] = i < rn ? keys[r0 + i] : 0u;
-      keep[u] = i < rn && (int)(kv[u] >> kBinShift) >= tb;
-      cnt += __popcll(__ballot(keep[u]));
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kWave + lane;
+      kv[u] = i < hi ? keys[i] : 0u;
     }
-    if (lane == 0) scan[wave] = cnt;
-    __syncthreads();
-    int pos = written, round_total = 0;
 #pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) {
-      const int cw = scan[w];
-      if (w < wave) pos += cw;
-      round_total += cw;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const uint64_t m = __ballot(keep[u]);
-      if (keep[u]) {
-        const int p = pos + __popcll(m & lanemask_lt());
-        const int i = wave * (PER * kWave) + u * kWave + lane;
-        ws_ckey[cbase + p] = kv[u];
-        ws_cidx[cbase + p] = (int32_t)(start + r0 + i);
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kWave + lane;
+      const bool keep = i < hi && (int)(kv[u] >> kBinShift) >= tb;
+      const uint64_t m = __ballot(keep);
+      if (keep) {
+        const int p = written + __popcll(m & lanemask_lt());
+        ck[p] = kv[u];
+        ci[p] = (int32_t)(start + i);
       }
-      pos += __popcll(m);
+      written += __popcll(m);
     }
-    written += round_total;
   }
-  if (t == 0) ws_cnt[b * n_chunks + c] = written;
+  if (lane == 0) ws_cnt[list] = written;
 }
 
 // ------------------------------------------------------------- selection
 
 struct SelectLds {
-  uint32_t ckey[kCandCap];
+  alignas(16) uint32_t ckey[kCandCap];
   int32_t cidx[kCandCap];
   uint8_t chosen[kCandCap];      // tie keys taken
   uint32_t rhist[kFinalWaves * kRadixPad];
   uint32_t h2[kSubBins];         // next 8 bits of the threshold bin's keys
   uint32_t tkey[kTieCap];        // keys sharing the k-th key's 20-bit prefix
   int tpos[kTieCap];             // ... and their candidate positions
-  int pre[kMaxChunks + 1];
+  uint32_t bkey[kTbCap];         // the threshold bin's keys
+  int bpos[kTbCap];              // ... and their candidate positions
+  int pre[kMaxLists + 1];
   int misc[kMisc];
   int scan[kFinalWaves];
+  int hscan[kFinalWaves];
 };
 
 // Writes, in candidate order, the ids of the candidates whose key's top 20
@@ -492,11 +465,11 @@ __device__ int ordered_emit(const uint32_t* keys, const int32_t* idxs, const uin
 }
 
 // One workgroup per sequence: finds the threshold bin from the complete
-// histogram, gathers the chunks' candidates at or above it, resolves the
-// remaining 20 bits on full keys, writes the ids (ascending, -1 padded) and
+// histogram, gathers the candidates of the chunks' lists at or above it,
+// resolves the remaining 20 bits on full keys, writes the ids (ascending, -1 padded) and
 // clears the histogram for the next call.
 __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
-    const int32_t* __restrict__ n_entries, int64_t n_max, int k, int chunk, int n_chunks,
+    const int32_t* __restrict__ n_entries, int64_t n_max, int k, int list_cap, int n_lists,
     uint32_t* __restrict__ ws_hist, uint32_t* __restrict__ ws_ckey, int32_t* __restrict__ ws_cidx,
     const int32_t* __restrict__ ws_cnt, int32_t* __restrict__ ids) {
   __shared__ SelectLds L;
@@ -507,40 +480,75 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
   uint32_t* gh = ws_hist + b * kHistBins;
   const bool take_all = nv <= k;
   int32_t* out = ids + b * k;
-  if (nv == 0) {   // no entry was scored (the chunk counts may not even exist)
+  if (nv == 0) {   // no entry was scored (the list counts may not even exist)
     for (int i = t; i < k; i += kFinalThreads) out[i] = -1;
     return;
   }
 
-  // chunk counts (thread t owns chunks CPT*t ..) and the histogram, loaded together
-  constexpr int CPT = kMaxChunks / kFinalThreads;   // 4
-  const int32_t* cnt_b = ws_cnt + b * n_chunks;
+  // list counts (thread t owns lists CPT*t ..) and the histogram (thread t
+  // owns bins 4095 - 4t down to 4092 - 4t), loaded together; one pair of
+  // barriers serves the offsets of the lists and the threshold bin
+  constexpr int CPT = kMaxLists / kFinalThreads;   // 8
+  static_assert(kHistBins == 4 * kFinalThreads, "four histogram bins per thread");
+  const int32_t* cnt_b = ws_cnt + b * n_lists;
   int c[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     const int si = CPT * t + j;
-    c[j] = si < n_chunks ? cnt_b[si] : 0;
+    c[j] = si < n_lists ? cnt_b[si] : 0;
   }
-  uint32_t h[kHistBins / kFinalThreads];
-  load_hist16<kFinalThreads>(gh, h);
+  const int top = kHistBins - 1 - 4 * t;
+  const uint4 hv = *reinterpret_cast<const uint4*>(gh + top - 3);   // bins top-3 .. top
   for (int i = t; i < kSubBins; i += kFinalThreads) L.h2[i] = 0u;
-
-  // chunk offsets of the candidates
+  if (t == 0) L.misc[5] = 0;                        // threshold-bin list length
   int mine = 0;
 #pragma unroll
   for (int j = 0; j < CPT; ++j) mine += c[j];
-  int total;
-  int run = block_exclusive_scan<kFinalThreads>(mine, L.scan, total);
+  const int hs = (int)(hv.x + hv.y + hv.z + hv.w);
+  const int incl = wave_inclusive_scan(mine);
+  const int hincl = wave_inclusive_scan(hs);
+  if (lane == kWave - 1) {
+    L.scan[wave] = incl;
+    L.hscan[wave] = hincl;
+  }
+  __syncthreads();
+  int run = incl - mine, total = 0, hrun = hincl - hs;
+#pragma unroll
+  for (int w = 0; w < kFinalWaves; ++w) {
+    const int x = L.scan[w], y = L.hscan[w];
+    if (w < wave) {
+      run += x;
+      hrun += y;
+    }
+    total += x;
+  }
+  // the thread whose bins hold the k-th largest key records the bin, the keys
+  // above it and its count
+  if (!take_all && hrun < k && k <= hrun + hs) {
+    const int hb[4] = {(int)hv.w, (int)hv.z, (int)hv.y, (int)hv.x};   // from the top down
+    int r = hrun;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (r < k && k <= r + hb[i]) {
+        L.misc[0] = top - i;
+        L.misc[1] = r;
+        L.misc[2] = hb[i];
+      }
+      r += hb[i];
+    }
+  }
+  // list offsets of the candidates
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     const int si = CPT * t + j;
-    if (si < n_chunks) L.pre[si] = run;
+    if (si < n_lists) L.pre[si] = run;
     run += c[j];
   }
-  if (t == 0) L.pre[n_chunks] = total;
-  int tbin = 0, above = 0, tcount = 0;
-  if (!take_all) threshold_bin<kFinalThreads>(h, k, L.scan, L.misc, tbin, above, tcount);
+  if (t == 0) L.pre[n_lists] = total;
   __syncthreads();
+  const int tbin = take_all ? 0 : L.misc[0];
+  const int above = take_all ? 0 : L.misc[1];
+  const int tcount = take_all ? 0 : L.misc[2];
   // candidates at or above the threshold bin: every key there is one
   const int kept = take_all ? total : above + tcount;
 
@@ -548,7 +556,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
   if (kept <= kCandCap) {
     // Gather into LDS, in candidate order, the ones at or above the threshold
     // bin, counting the next 8 bits of the threshold bin's keys on the way.
-    // Each position's chunk comes from a search over the chunk offsets with
+    // Each position's list comes from a search over the list offsets with
     // the same trip count in every lane; the loads follow all the searches.
     constexpr int PER = 4;
     constexpr int ROUND = PER * kFinalThreads;
@@ -561,7 +569,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
         base[u] = 0;
         start[u] = 0;
       }
-      for (int n = n_chunks + 1; n > 1;) {
+      for (int n = n_lists + 1; n > 1;) {
         const int half = n >> 1;
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
@@ -577,7 +585,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
       int32_t ii[PER];
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
-        const int64_t off = (b * n_chunks + base[u]) * (int64_t)chunk + (jj[u] - start[u]);
+        const int64_t off = (b * n_lists + base[u]) * (int64_t)list_cap + (jj[u] - start[u]);
         kk[u] = ws_ckey[off];
         ii[u] = ws_cidx[off];
       }
@@ -600,6 +608,20 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
         if (w < wave) pos += x;
         round_total += x;
       }
+      // the threshold bin's keys also go to a list of their own (one slot
+      // reservation per wave)
+      uint64_t mb[PER];
+      int nb_w = 0;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        mb[u] = __ballot(!take_all && keep[u] && (int)(kk[u] >> kBinShift) == tbin);
+        nb_w += __popcll(mb[u]);
+      }
+      int slot = 0;
+      if (nb_w > 0) {
+        if (lane == 0) slot = atomicAdd(&L.misc[5], nb_w);
+        slot = __shfl(slot, 0);
+      }
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
         const uint64_t m = __ballot(keep[u]);
@@ -609,6 +631,12 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
           L.cidx[p] = ii[u];
         }
         pos += __popcll(m);
+        const int sl = slot + __popcll(mb[u] & lanemask_lt());
+        if (((mb[u] >> lane) & 1u) && sl < kTbCap) {
+          L.bkey[sl] = kk[u];
+          L.bpos[sl] = p;
+        }
+        slot += __popcll(mb[u]);
       }
       n_sel += round_total;
       __syncthreads();
@@ -618,31 +646,44 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
     if (take_all) {
       cnt = ordered_emit<kFinalThreads>(L.ckey, L.cidx, L.chosen, n_sel, true, 0u, L.scan, out, k);
     } else {
-      // the sub-bin holding the k-th largest key: sub-bins from the top down
+      // the sub-bin holding the k-th largest key, found by every wave alone:
+      // lane l holds sub-bins 255 - 4l .. 252 - 4l, scanned from the top down
       const int need = k - above;                  // keys still to take from the threshold bin
-      const int h2v = t < kSubBins ? (int)L.h2[kSubBins - 1 - t] : 0;
-      if (t == 0) L.misc[3] = 0;                   // tie counter
-      int sub_total;
-      const int above2 = block_exclusive_scan<kFinalThreads>(h2v, L.scan, sub_total);   // keys in higher sub-bins
-      if (above2 < need && need <= above2 + h2v) {
-        L.misc[0] = kSubBins - 1 - t;
-        L.misc[1] = need - above2;
-        L.misc[2] = h2v;
+      int hc[4], hs = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hc[j] = (int)L.h2[kSubBins - 1 - 4 * lane - j];
+        hs += hc[j];
       }
-      __syncthreads();
-      const uint32_t pstar = ((uint32_t)tbin << kSubBits) | (uint32_t)L.misc[0];   // 20-bit prefix
-      const int rem = L.misc[1];                   // keys to take among those with that prefix
-      const int m = L.misc[2];                     // keys with that prefix
-      if (m <= kTieCap) {
+      int run2 = wave_inclusive_scan(hs) - hs;     // keys in higher sub-bins
+      int sb = 0, rem = 0, m = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (run2 < need && need <= run2 + hc[j]) {
+          sb = kSubBins - 1 - 4 * lane - j;
+          rem = need - run2;
+          m = hc[j];
+        }
+        run2 += hc[j];
+      }
+      const int owner = __ffsll((unsigned long long)__ballot(m > 0 && rem > 0)) - 1;
+      sb = __shfl(sb, owner);
+      rem = __shfl(rem, owner);                    // keys to take among those sharing the prefix
+      m = __shfl(m, owner);                        // keys sharing the prefix
+      const uint32_t pstar = ((uint32_t)tbin << kSubBits) | (uint32_t)sb;   // 20-bit prefix
+      const int nb = L.misc[5];
+      if (m <= kTieCap && nb <= kTbCap) {
         // rank the keys sharing the prefix against each other (descending key,
         // then ascending entry, which candidate order gives)
-        for (int i = t; i < n_sel; i += kFinalThreads) {
-          const uint32_t key = L.ckey[i];
+        if (t == 0) L.misc[3] = 0;                 // tie counter (read after the barrier below)
+        __syncthreads();
+        for (int i = t; i < nb; i += kFinalThreads) {
+          const uint32_t key = L.bkey[i];
           if ((key >> kLowBits) == pstar) {
             const int slot = atomicAdd(&L.misc[3], 1);
             if (slot < kTieCap) {   // (there are exactly m of them)
               L.tkey[slot] = key;
-              L.tpos[slot] = i;
+              L.tpos[slot] = L.bpos[i];
             }
           }
         }
@@ -655,7 +696,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
             const uint32_t ks = L.tkey[s2];
             rank += (ks > key || (ks == key && L.tpos[s2] < pos)) ? 1 : 0;
           }
-          L.chosen[pos] = rank < rem ? 1 : 0;
+          if (pos < kCandCap) L.chosen[pos] = rank < rem ? 1 : 0;
         }
         __syncthreads();
         cnt = ordered_emit<kFinalThreads>(L.ckey, L.cidx, L.chosen, n_sel, false, pstar, L.scan, out, k);
@@ -668,14 +709,14 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
     }
   } else {
     // more keys at or above the threshold bin than LDS holds (heavily tied
-    // scores): compact the chunks' lists in place in global memory and select
+    // scores): compact the lists in place in global memory and select
     // there (reads never overtake writes: a list's destination offset is at
     // most its source offset)
-    uint32_t* ck = ws_ckey + b * n_chunks * (int64_t)chunk;
-    int32_t* ci = ws_cidx + b * n_chunks * (int64_t)chunk;
-    for (int s1 = 1; s1 < n_chunks; ++s1) {
+    uint32_t* ck = ws_ckey + b * n_lists * (int64_t)list_cap;
+    int32_t* ci = ws_cidx + b * n_lists * (int64_t)list_cap;
+    for (int s1 = 1; s1 < n_lists; ++s1) {
       const int cs = L.pre[s1 + 1] - L.pre[s1];
-      const int64_t from = (int64_t)s1 * chunk, to = L.pre[s1];
+      const int64_t from = (int64_t)s1 * list_cap, to = L.pre[s1];
       for (int j0 = 0; j0 < cs; j0 += kFinalThreads) {
         const int j = j0 + t;
         uint32_t kk = 0u;
@@ -723,7 +764,7 @@ bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, TopkPlan* p) {
   size_t off = 0;
   p->off_hist = off; off = align256(off + nb * kHistBins * 4);
   p->zero_bytes = off;
-  p->off_cnt = off; off = align256(off + nb * (size_t)p->n_chunks * 4);
+  p->off_cnt = off; off = align256(off + nb * (size_t)p->n_chunks * kTopkWaves * 4);
   p->off_ckey = off; off = align256(off + slots * 4);
   p->off_cidx = off; off = align256(off + slots * 4);
   p->bytes = off;
@@ -766,7 +807,8 @@ hipError_t launch_index_topk(const TopkPlan& p, const uint16_t* q_idx, bool fp4,
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_topk_final, dim3((unsigned)B), dim3(kFinalThreads), 0, stream, n_entries, n_max, k,
-                     (int)p.chunk, (int)p.n_chunks, reinterpret_cast<uint32_t*>(ws + p.off_hist),
+                     (int)(p.chunk / kTopkWaves), (int)(p.n_chunks * kTopkWaves),
+                     reinterpret_cast<uint32_t*>(ws + p.off_hist),
                      reinterpret_cast<uint32_t*>(ws + p.off_ckey), reinterpret_cast<int32_t*>(ws + p.off_cidx),
                      reinterpret_cast<const int32_t*>(ws + p.off_cnt), ids);
   return hipGetLastError();

@@ -16,11 +16,11 @@ hipError_t launch_compress(int kind, const uint16_t* S, const float* gate, int64
 
 // ---- index_topk.hip
 // Plan of the indexer: k_index_score scores `chunk` entries per workgroup and
-// writes the chunk's candidates, k_topk_final finishes one sequence per
-// workgroup. Workspace regions (byte offsets): the per-sequence histogram
-// comes first (it must be zero when a call starts and every call leaves it
-// zero), then the chunks' candidate counts and their candidate keys / entry
-// numbers (room for every entry).
+// writes the chunk's candidates as one list per wave, k_topk_final finishes
+// one sequence per workgroup. Workspace regions (byte offsets): the
+// per-sequence histogram comes first (it must be zero when a call starts and
+// every call leaves it zero), then the lists' candidate counts and their
+// candidate keys / entry numbers (room for every entry).
 struct TopkPlan {
   int64_t chunk, n_chunks;     // entries per scoring workgroup, workgroups per sequence
   size_t off_hist, off_cnt, off_ckey, off_cidx;

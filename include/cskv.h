@@ -114,8 +114,8 @@ cskv_status cskv_compress(int32_t kind, const void* S, const float* gate, int64_
  *             served another purpose. Every completed call leaves that region
  *             zero (whatever n_entries held), so calls with the same arguments
  *             can reuse the workspace as it is.
- * EUNSUPPORTED if a sequence would need more than 4096 chunks (n_max > 4096 *
- * chunk; with automatic chunking, n_max > 67108864).
+ * EUNSUPPORTED if a sequence would need more than 2048 chunks (n_max > 2048 *
+ * chunk; with automatic chunking, n_max > 33554432).
  */
 size_t cskv_index_topk_workspace(int64_t B, int64_t n_max, int32_t Di, int32_t k,
                                  int32_t key_dtype, int32_t chunk);

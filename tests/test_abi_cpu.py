@@ -40,7 +40,7 @@ def test_version_and_status_strings(lib):
 def test_topk_workspace_sizes(lib):
     # 32 x 32767 entries, k = 512: a 4096-bin histogram per sequence and room
     # for every entry as a candidate (key + entry number), padded to whole
-    # chunks, plus a candidate count per chunk
+    # chunks, plus a candidate count per chunk and wave
     B, N = 32, 32767
     ws = lib._lib_topk_ws(B, N, 128, 512, lib.BF16, 0)
     need = B * (4096 * 4 + 2 * N * 4)
@@ -52,10 +52,11 @@ def test_topk_workspace_sizes(lib):
     # rejected shapes report 0
     assert lib._lib_topk_ws(1, 100, 64, 8, lib.BF16, 0) == 0
     assert lib._lib_topk_ws(1, 100, 128, 4096, lib.BF16, 0) == 0
-    # a sequence may span at most 4096 scoring chunks
-    assert lib._lib_topk_ws(1, 4096 * 256, 128, 512, lib.BF16, 256) > 0
-    assert lib._lib_topk_ws(1, 4096 * 256 + 1, 128, 512, lib.BF16, 256) == 0
-    assert lib._lib_topk_ws(1, 4096 * 16384 + 1, 128, 512, lib.BF16, 0) == 0
+    # a sequence may span at most 2048 scoring chunks
+    assert lib._lib_topk_ws(1, 2048 * 256, 128, 512, lib.BF16, 256) > 0
+    assert lib._lib_topk_ws(1, 2048 * 256 + 1, 128, 512, lib.BF16, 256) == 0
+    assert lib._lib_topk_ws(1, 2048 * 16384, 128, 512, lib.BF16, 0) > 0
+    assert lib._lib_topk_ws(1, 2048 * 16384 + 1, 128, 512, lib.BF16, 0) == 0
 
 
 def test_attend_workspace_sizes(lib):

@@ -89,6 +89,27 @@ def test_topk_no_entries(cskv):
     assert ids.shape == (2, 16) and (ids == -1).all()
 
 
+def test_topk_tie_groups(cskv):
+    """Exact ties at the k-th score, spread over many chunks: a small group
+    (ranked pairwise) and a group larger than 256 (radix select)."""
+    B, N, Di = 2, 20000, 128
+    rng = np.random.default_rng(17)
+    q = np.zeros((B, Di), dtype=np.uint16)
+    q[:, 0] = F.f32_to_bf16(np.float32(1.0))
+    kk = np.zeros((B, N, Di), dtype=np.uint16)
+    val = lambda x: F.f32_to_bf16(np.float32(x))
+    kk[:, :, 0] = val(1.0)
+    top = rng.choice(N, 130, replace=False)
+    kk[0, top[:30], 0] = val(9.0)           # 30 above, then 100 tied at 5: take 20 of them
+    kk[0, top[30:], 0] = val(5.0)
+    many = rng.choice(N, 1000, replace=False)
+    kk[1, many[:10], 0] = val(9.0)          # 10 above, then 990 tied at 5: take 290 of them
+    kk[1, many[10:], 0] = val(5.0)
+    for k in (50, 300):
+        ids = cskv.index_topk(to_dev_bf16(q), to_dev_bf16(kk), k, chunk=512).cpu().numpy()
+        assert np.array_equal(ids, _oracle_ids(q, kk, k)), k
+
+
 def test_topk_all_equal_and_nan(cskv):
     B, N, Di, k = 2, 3000, 128, 300
     q = np.full((B, Di), F.f32_to_bf16(np.float32(1.0)), dtype=np.uint16)
