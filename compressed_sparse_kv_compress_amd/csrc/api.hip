@@ -99,7 +99,7 @@ static cskv_status topk_common(int64_t B, int64_t n_max, int32_t Di, int32_t k, 
         "index_topk: chunk=%d must be 0 or a multiple of 256 in [256, 16384]", chunk);
   CHECK(B <= 65535, CSKV_EUNSUPPORTED, "index_topk: B=%lld > 65535", (long long)B);
   CHECK(n_max <= 0x7FFFFFFF, CSKV_EUNSUPPORTED, "index_topk: n_max too large for int32 ids");
-  CHECK(cskv::plan_topk(B, n_max, k, chunk, plan), CSKV_EUNSUPPORTED,
+  CHECK(cskv::plan_topk(B, n_max, k, chunk, key_dtype == CSKV_FP4_E2M1, plan), CSKV_EUNSUPPORTED,
         "index_topk: no selection plan for n_max=%lld k=%d chunk=%d", (long long)n_max, k, chunk);
   return ok();
 }

@@ -744,15 +744,19 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, TopkPlan* p) {
+bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, bool fp4, TopkPlan* p) {
   (void)k;
   int64_t chunk = chunk_hint;
   if (chunk == 0) {
-    // about 1500 scoring workgroups over the batch, chunks of 512 .. 8192 entries
-    // (more when a sequence would need more chunks than the final select tracks)
-    const int64_t want = (B * n_max + 1535) / 1536;
+    // bf16 keys (256 B per entry): about 768 scoring workgroups over the batch,
+    // chunks of 512 .. 4096 entries; fp4 keys (72 B per entry): about 1536,
+    // chunks of 512 .. 8192 (measured best on the c4a workloads); more when a
+    // sequence would need more chunks than the final select tracks
+    const int64_t groups = fp4 ? 1536 : 768;
+    const int64_t cap = fp4 ? 8192 : 4096;
+    const int64_t want = (B * n_max + groups - 1) / groups;
     chunk = 512;
-    while (chunk < want && chunk < 8192) chunk *= 2;
+    while (chunk < want && chunk < cap) chunk *= 2;
     while ((n_max + chunk - 1) / chunk > kMaxChunks && chunk < 16384) chunk *= 2;
   }
   if (chunk < 256 || chunk > 16384 || chunk % 256 != 0) return false;

@@ -27,7 +27,7 @@ struct TopkPlan {
   size_t zero_bytes;           // leading bytes that must be zero between calls
   size_t bytes;                // workspace bytes
 };
-bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, TopkPlan* plan);
+bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, bool fp4, TopkPlan* plan);
 hipError_t launch_index_topk(const TopkPlan& plan, const uint16_t* q_idx, bool fp4,
                              const void* k_idx, const uint8_t* k_scale, const int32_t* n_entries,
                              int64_t B, int64_t n_max, int Di, int k, int32_t* ids,
