@@ -57,14 +57,11 @@ __device__ int block_exclusive_scan(int v, int* scratch, int& total) {
   const int incl = wave_inclusive_scan(v);
   if (lane == kWave - 1) scratch[wave] = incl;
   __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < (NT / kWave); ++w) {
-    const int s = scratch[w];
-    if (w < wave) before += s;
-    total += s;
-  }
+  // the waves' totals, scanned across the first NT / 64 lanes
+  const int x = lane < NT / kWave ? scratch[lane] : 0;
+  const int wincl = wave_inclusive_scan(x);
+  total = __shfl(wincl, NT / kWave - 1);
+  const int before = wave > 0 ? __shfl(wincl, wave - 1) : 0;
   __syncthreads();
   return before + incl - v;
 }
@@ -464,6 +461,16 @@ __device__ int ordered_emit(const uint32_t* keys, const int32_t* idxs, const uin
   return total < out_cap ? total : out_cap;
 }
 
+// Sum of per-wave counts cnt[0 .. wave) and of all kFinalWaves of them, by
+// a scan over the first kFinalWaves lanes (same result in every lane).
+__device__ __forceinline__ int waves_before(const int* cnt, int wave, int& all) {
+  const int lane = lane_id();
+  const int x = lane < kFinalWaves ? cnt[lane] : 0;
+  const int incl = wave_inclusive_scan(x);
+  all = __shfl(incl, kFinalWaves - 1);
+  return wave > 0 ? __shfl(incl, wave - 1) : 0;
+}
+
 // One workgroup per sequence: finds the threshold bin from the complete
 // histogram, gathers the candidates of the chunks' lists at or above it,
 // resolves the remaining 20 bits on full keys, writes the ids (ascending, -1 padded) and
@@ -512,16 +519,9 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
     L.hscan[wave] = hincl;
   }
   __syncthreads();
-  int run = incl - mine, total = 0, hrun = hincl - hs;
-#pragma unroll
-  for (int w = 0; w < kFinalWaves; ++w) {
-    const int x = L.scan[w], y = L.hscan[w];
-    if (w < wave) {
-      run += x;
-      hrun += y;
-    }
-    total += x;
-  }
+  int total, htotal;
+  int run = incl - mine + waves_before(L.scan, wave, total);
+  int hrun = hincl - hs + waves_before(L.hscan, wave, htotal);
   // the thread whose bins hold the k-th largest key records the bin, the keys
   // above it and its count
   if (!take_all && hrun < k && k <= hrun + hs) {
@@ -558,36 +558,33 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
     // bin, counting the next 8 bits of the threshold bin's keys on the way.
     // Each position's list comes from a search over the list offsets with
     // the same trip count in every lane; the loads follow all the searches.
+    // (offsets within the sequence's lists fit 32 bits: at most 2048 chunks
+    // of 16384 entries)
     constexpr int PER = 4;
     constexpr int ROUND = PER * kFinalThreads;
+    const uint32_t* ck_b = ws_ckey + (int64_t)b * n_lists * list_cap;
+    const int32_t* ci_b = ws_cidx + (int64_t)b * n_lists * list_cap;
     int n_sel = 0;
     for (int j0 = 0; j0 < total; j0 += ROUND) {
-      int jj[PER], base[PER], start[PER];
+      int jj[PER], base[PER];
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
         jj[u] = min(j0 + wave * (PER * kWave) + u * kWave + lane, total - 1);
         base[u] = 0;
-        start[u] = 0;
       }
       for (int n = n_lists + 1; n > 1;) {
         const int half = n >> 1;
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          const int v = L.pre[base[u] + half];
-          if (v <= jj[u]) {
-            base[u] += half;
-            start[u] = v;
-          }
-        }
+        for (int u = 0; u < PER; ++u) base[u] = L.pre[base[u] + half] <= jj[u] ? base[u] + half : base[u];
         n -= half;
       }
       uint32_t kk[PER];
       int32_t ii[PER];
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
-        const int64_t off = (b * n_lists + base[u]) * (int64_t)list_cap + (jj[u] - start[u]);
-        kk[u] = ws_ckey[off];
-        ii[u] = ws_cidx[off];
+        const uint32_t off = (uint32_t)base[u] * (uint32_t)list_cap + (uint32_t)(jj[u] - L.pre[base[u]]);
+        kk[u] = ck_b[off];
+        ii[u] = ci_b[off];
       }
       bool keep[PER];
       int cw = 0;
@@ -601,13 +598,8 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
       }
       if (lane == 0) L.scan[wave] = cw;
       __syncthreads();
-      int pos = n_sel, round_total = 0;
-#pragma unroll
-      for (int w = 0; w < kFinalWaves; ++w) {
-        const int x = L.scan[w];
-        if (w < wave) pos += x;
-        round_total += x;
-      }
+      int round_total;
+      int pos = n_sel + waves_before(L.scan, wave, round_total);
       // the threshold bin's keys also go to a list of their own (one slot
       // reservation per wave)
       uint64_t mb[PER];
@@ -677,11 +669,16 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
         // then ascending entry, which candidate order gives)
         if (t == 0) L.misc[3] = 0;                 // tie counter (read after the barrier below)
         __syncthreads();
-        for (int i = t; i < nb; i += kFinalThreads) {
-          const uint32_t key = L.bkey[i];
-          if ((key >> kLowBits) == pstar) {
-            const int slot = atomicAdd(&L.misc[3], 1);
-            if (slot < kTieCap) {   // (there are exactly m of them)
+        for (int i0 = 0; i0 < nb; i0 += kFinalThreads) {   // (one slot reservation per wave)
+          const int i = i0 + t;
+          const uint32_t key = i < nb ? L.bkey[i] : 0u;
+          const bool tie = i < nb && (key >> kLowBits) == pstar;
+          const uint64_t mt = __ballot(tie);
+          if (mt) {
+            int slot = 0;
+            if (lane == 0) slot = atomicAdd(&L.misc[3], __popcll(mt));
+            slot = __shfl(slot, 0) + __popcll(mt & lanemask_lt());
+            if (tie && slot < kTieCap) {   // (there are exactly m of them)
               L.tkey[slot] = key;
               L.tpos[slot] = L.bpos[i];
             }
