@@ -38,6 +38,7 @@ struct AttendPlan {
   int splits;            // key-row splits per sequence
   int64_t keys_per_split;
   size_t bytes;          // workspace bytes (partials), 0 when splits == 1
+  bool head_split;       // sparse reads may use the head-split kernel (no partials)
 };
 // Plans the key-slot splits of an attend call; sparse calls stage their entry
 // ids in LDS, which bounds a split's length. False if no plan exists.

@@ -184,3 +184,49 @@ def test_fp8_logits_far_from_zero(cskv):
                         window_scale=to_dev(wsc), softmax_scale=tau, rope_dims=R, q_pos=to_dev(pos),
                         splits=splits)
         assert row_rel_err(O.cpu().numpy(), ref) <= 6e-2
+
+
+@pytest.mark.parametrize("B,H,k,W,R", [
+    (64, 64, 512, 128, 64),   # the c4a layer shape, at a batch that takes the head-split kernel
+    (64, 64, 300, 40, 64),    # a ragged last tile and a short window
+    (256, 16, 100, 0, 0),     # one head group, no window, no rotation
+])
+def test_sparse_head_split_matches_oracle(cskv, B, H, k, W, R):
+    """Sparse bf16 reads with automatic splits at B x H/16 >= 256 run the
+    head-split kernel (no partials); some sequences end in -1 ids."""
+    D, N = 512, 2000
+    seed = 700 + B + H
+    Q = _bf16(seed, synth.T_Q, (B, H, D))
+    cache = _bf16(seed, synth.T_CACHE, (B, N, D))
+    win = _bf16(seed, synth.T_WIN, (B, W, D))
+    rng = np.random.default_rng(seed)
+    ids = np.stack([sorted_ids(rng, N, k, n_valid=k - (5 if b % 7 == 3 else 0)) for b in range(B)])
+    pos = np.array([1000 + 977 * b for b in range(B)], dtype=np.int64)
+    tau = 1 / np.sqrt(D)
+    ref = _oracle(F.bf16_to_f64(Q), F.bf16_to_f64(cache), ids, F.bf16_to_f64(win) if W else None, tau, R,
+                  10000.0, pos)
+    for splits in (0, 1):
+        O = cskv.attend(to_dev_bf16(Q), to_dev_bf16(cache), to_dev(ids), to_dev_bf16(win) if W else None,
+                        softmax_scale=tau, rope_dims=R, q_pos=to_dev(pos), splits=splits)
+        err = row_rel_err(O.cpu().numpy(), ref)
+        assert err <= 2e-2, (splits, err)
+
+
+def test_sparse_head_split_far_logits(cskv):
+    """The head-split kernel's second pass: heads against, along and across a
+    common row direction, so some heads' logits lie far below zero."""
+    B, H, D, N, k, W, R = 64, 64, 512, 1200, 256, 40, 64
+    seed = 64
+    Q = F.bf16_to_f64(_bf16(seed, synth.T_Q, (B, H, D)))
+    cache = 1.0 + 0.1 * F.bf16_to_f64(_bf16(seed, synth.T_CACHE, (B, N, D)))
+    win = 1.0 + 0.1 * F.bf16_to_f64(_bf16(seed, synth.T_WIN, (B, W, D)))
+    Q = np.array([-1.0, 1.0, 0.0])[np.arange(H) % 3][None, :, None] + 0.1 * Q
+    tau = 0.2
+    Qb, cb, wb = (F.f32_to_bf16(x.astype(np.float32)) for x in (Q, cache, win))
+    rng = np.random.default_rng(seed)
+    ids = np.stack([sorted_ids(rng, N, k) for _ in range(B)])
+    pos = np.array([77 + (1 << 14) * b for b in range(B)], dtype=np.int64)
+    ref = _oracle(F.bf16_to_f64(Qb), F.bf16_to_f64(cb), ids, F.bf16_to_f64(wb), tau, R, 10000.0, pos)
+    O = cskv.attend(to_dev_bf16(Qb), to_dev_bf16(cb), to_dev(ids), to_dev_bf16(wb), softmax_scale=tau,
+                    rope_dims=R, q_pos=to_dev(pos))
+    assert row_rel_err(O.cpu().numpy(), ref) <= 2e-2
