@@ -12,7 +12,9 @@ precision the encoded caches are defined in):
   formats' public definitions, and the fp8-row / fp4-group-of-16 encoders.
 * ``method``    - compression into c4a / c128a entries, indexer scores, exact
   top-k, shared-K/V softmax attention over gathered entries plus the window,
-  and the inverse rotary embedding of the output.
+  the inverse rotary embedding of the output, and the streaming decode step
+  that appends one state per sequence to a ring of the newest W states and
+  emits each entry when its window completes.
 * ``accounting`` - bytes per token and per sequence for the cache layouts whose
   sizes the pages print.
 

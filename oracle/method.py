@@ -182,3 +182,39 @@ def c4a_decode(Q, q_idx, k_idx, cache, window, k, tau, R, base, q_pos, n_entries
 def c128a_decode(Q, cache, window, tau, R, base, q_pos, n_entries=None):
     """A c128a layer for one sequence: dense attention over every entry."""
     return attend(Q, cache, None, window, tau, R, base, q_pos, n_entries)
+
+
+# ------------------------------------------------------- streaming decode
+#
+# [P1] cache-block paragraph: besides the compressed entries, each layer keeps
+# a constant-size compressor state and the sliding window; [P1] "c4a" / "c128a"
+# and [P2] Step 4: an entry exists once the last state of its window exists,
+# so a decoder appending one state per step completes a c4a entry every 4
+# steps and a c128a entry every 128. [P2] Step 6: the window is the newest W
+# states. Reading: one ring of the last W states and their gate logits per
+# sequence (token p in slot p mod W) is both the window and the compressor's
+# carry; it needs W >= 8 (c4a) or W >= 128 (c128a).
+
+def append(kind: str, ring: np.ndarray, ring_gate: np.ndarray, s_new: np.ndarray, g_new: float,
+           pos: int):
+    """Appends state s_new with gate logit g_new as token ``pos`` of one
+    sequence: stores it in ring slot pos mod W (ring [W, D], ring_gate [W],
+    both modified in place) and, when the token completes an entry, returns
+    (c, entry row) computed from the ring as the definition does from the
+    states; otherwise (None, None)."""
+    w, s = WINDOW[kind]
+    W = ring.shape[0]
+    assert W >= w and pos >= 0
+    ring[pos % W] = np.asarray(s_new, dtype=np.float64)
+    ring_gate[pos % W] = float(g_new)
+    first = pos + 1 - w                    # first state of the window ending at pos
+    if first < 0 or first % s != 0:
+        return None, None
+    slots = [(first + j) % W for j in range(w)]
+    wts = softmax(np.asarray(ring_gate, dtype=np.float64)[slots])
+    return first // s, wts @ np.asarray(ring, dtype=np.float64)[slots]
+
+
+def stream_counts(kind: str, pos: int, W: int) -> tuple[int, int]:
+    """(complete entries, window rows) of a sequence whose newest token is pos."""
+    return entry_count(kind, pos + 1), min(pos + 1, W)

@@ -452,3 +452,76 @@ def test_quantised_layout_halves_again():
     assert A.entry_bytes(M.C4A, quantised=True) == 588 and A.entry_bytes(M.C128A, quantised=True) == 516
     r = A.v4_sequence_bytes(1 << 20) / A.v4_sequence_bytes(1 << 20, quantised=True)
     assert abs(r - f["value"]) <= f["tol"]
+
+
+# ------------------------------------------------------- streaming decode
+
+def _stream(kind, S, g, W, p0=0):
+    """Appends states S[p0:] one per step; returns {entry: row} and the ring."""
+    ring, rg = np.zeros((W, S.shape[1])), np.zeros(W)
+    got = {}
+    for p in range(p0, S.shape[0]):
+        c, row = M.append(kind, ring, rg, S[p], g[p], p)
+        if c is not None:
+            assert c not in got
+            got[c] = row
+    return got, ring, rg
+
+
+@pytest.mark.parametrize("kind,W", [(M.C4A, 8), (M.C4A, 13), (M.C4A, 128), (M.C128A, 128), (M.C128A, 300)])
+def test_stream_appends_reproduce_the_worked_windows(kind, W):
+    # unit-vector states: every streamed entry must fold exactly the states of
+    # the pages' worked example (P2, Step 4), whatever the ring size
+    ex = GOLD["worked_examples"]["c4a_windows" if kind == M.C4A else "c128a_windows"]
+    T = ex["states"]
+    got, _, _ = _stream(kind, np.eye(T), np.zeros(T), W)
+    assert sorted(got) == list(range(len(ex["entries"])))
+    for c, members in enumerate(ex["entries"]):
+        members = members if kind == M.C4A else list(range(members[0], members[1] + 1))
+        assert np.nonzero(got[c])[0].tolist() == members
+        np.testing.assert_allclose(got[c][members], 1.0 / len(members), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("kind,W", [(M.C4A, 8), (M.C4A, 37), (M.C128A, 128), (M.C128A, 129)])
+def test_stream_entries_equal_batch_compress(kind, W):
+    T = 777
+    S, g = RNG.standard_normal((T, 5)), 3.0 * RNG.standard_normal(T)
+    got, _, _ = _stream(kind, S, g, W)
+    ref = M.compress(kind, S, g)
+    assert sorted(got) == list(range(ref.shape[0]))
+    for c in got:   # the same states and logits in the same order: identical values
+        assert np.array_equal(got[c], ref[c])
+
+
+@pytest.mark.parametrize("L,n4,n128", [(2048, 511, 16), (131072, 32767, 1024), (262144, 65535, 2048)])
+def test_stream_counts_at_the_workload_contexts(L, n4, n128):
+    # after the token at position L-1 the counts are the closed forms
+    assert M.stream_counts(M.C4A, L - 1, 128) == (n4, 128)
+    assert M.stream_counts(M.C128A, L - 1, 128) == (n128, 128)
+
+
+def test_stream_counts_brute_force():
+    for kind in (M.C4A, M.C128A):
+        done = 0
+        W = 128
+        ring, rg = np.zeros((W, 1)), np.zeros(W)
+        for p in range(600):
+            c, _ = M.append(kind, ring, rg, np.ones(1), 0.0, p)
+            done += c is not None
+            assert M.stream_counts(kind, p, W) == (done, min(p + 1, W))
+
+
+def test_ring_holds_the_newest_states_and_serves_as_the_window():
+    W, T, D = 16, 53, 6
+    S, g = RNG.standard_normal((T, D)), RNG.standard_normal(T)
+    _, ring, rg = _stream(M.C4A, S, g, W)
+    newest = list(range(T - W, T))
+    assert sorted(ring[p % W].tolist() for p in newest) == sorted(S[p].tolist() for p in newest)
+    assert all(rg[p % W] == g[p] for p in newest)
+    # attention is blind to the ring's slot order: the ring as stored gives the
+    # same output as the newest W states in token order (within rounding)
+    Q, cache = RNG.standard_normal((3, D)), RNG.standard_normal((9, D))
+    ids = np.array([0, 4, 7])
+    a = M.attend(Q, cache, ids, ring, 0.3, 2, 10000.0, T - 1)
+    b = M.attend(Q, cache, ids, S[T - W:], 0.3, 2, 10000.0, T - 1)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
