@@ -48,13 +48,15 @@ _lib_topk_ws = _sig("cskv_index_topk_workspace", _sz, _i64, _i64, _i32, _i32, _i
 _lib_topk = _sig("cskv_index_topk", _i32, _p, _i32, _p, _p, _p, _i64, _i64, _i32, _i32, _p, _i32, _p, _sz, _p)
 _lib_attend_ws = _sig("cskv_attend_workspace", _sz, _i64, _i32, _i32, _i64, _i32)
 _lib_attend = _sig("cskv_attend", _i32, _p, _i64, _i32, _i32, _i32, _p, _p, _i64, _p, _i32, _p,
-                   _i32, _p, _p, _i32, _i64, _i32, _f32, _p, _f32, _p, _i32, _p, _sz, _p)
+                   _i32, _p, _p, _i32, _i64, _p, _i32, _f32, _p, _f32, _p, _i32, _p, _sz, _p)
+_lib_append = _sig("cskv_append", _i32, _i32, _p, _p, _p, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _i64,
+                   _p, _p, _p)
 _lib_enc8 = _sig("cskv_encode_fp8_rows", _i32, _i32, _p, _i64, _i32, _p, _p, _p)
 _lib_dec8 = _sig("cskv_decode_fp8_rows", _i32, _p, _p, _i64, _i32, _p, _p)
 _lib_enc4 = _sig("cskv_encode_fp4_g16", _i32, _i32, _p, _i64, _i32, _p, _p, _p)
 _lib_dec4 = _sig("cskv_decode_fp4_g16", _i32, _p, _p, _i64, _i32, _p, _p)
 
-EXPORTS = ["cskv_status_string", "cskv_last_error", "cskv_version", "cskv_compress",
+EXPORTS = ["cskv_status_string", "cskv_last_error", "cskv_version", "cskv_compress", "cskv_append",
            "cskv_index_topk_workspace", "cskv_index_topk", "cskv_attend_workspace", "cskv_attend",
            "cskv_encode_fp8_rows", "cskv_decode_fp8_rows", "cskv_encode_fp4_g16", "cskv_decode_fp4_g16"]
 
@@ -148,6 +150,48 @@ def compress(kind, S: torch.Tensor, gate: torch.Tensor, cache: torch.Tensor,
     return 0 if T < w else (T - w) // s + 1
 
 
+def append(kind, s_new: torch.Tensor, g_new: torch.Tensor, pos: torch.Tensor, ring: torch.Tensor,
+           ring_gate: torch.Tensor, cache: torch.Tensor, cache_scale: torch.Tensor | None = None,
+           n_entries: torch.Tensor | None = None, n_window: torch.Tensor | None = None) -> None:
+    """Streaming decode: sequence b appends s_new[b] ([B, D] bf16, gate logit
+    g_new[b] fp32) as token pos[b] (int64 [B]; negative skips it) into its ring
+    ([B, W, D] bf16, ring_gate [B, W] fp32; token p in slot p mod W) and, when
+    the token completes an entry, writes that entry into cache (as compress()).
+    Optionally sets n_entries / n_window (int32 [B]) for index_topk / attend."""
+    kind = KINDS[kind]
+    _need_cuda(s_new, g_new, pos, ring, ring_gate, cache, cache_scale, n_entries, n_window)
+    _bf16_like(s_new, "s_new"); _bf16_like(ring, "ring")
+    for t, n in ((s_new, "s_new"), (g_new, "g_new"), (pos, "pos"), (ring, "ring"), (ring_gate, "ring_gate"),
+                 (cache, "cache")):
+        _dense(t, n)
+    B, D = s_new.shape
+    if g_new.dtype != torch.float32 or g_new.numel() != B:
+        raise ValueError("g_new must be fp32 [B]")
+    if pos.dtype != torch.int64 or pos.numel() != B:
+        raise ValueError("pos must be int64 [B]")
+    if ring.dim() != 3 or ring.shape[0] != B or ring.shape[2] != D:
+        raise ValueError("ring must be [B, W, D]")
+    W = ring.shape[1]
+    if ring_gate.dtype != torch.float32 or tuple(ring_gate.shape) != (B, W):
+        raise ValueError("ring_gate must be fp32 [B, W]")
+    if cache.dim() != 3 or cache.shape[0] != B or cache.shape[2] != D:
+        raise ValueError("cache must be [B, rows, D]")
+    if cache.dtype == torch.uint8 or cache.dtype == torch.float8_e4m3fn:
+        dt = FP8_E4M3
+        if cache_scale is None or cache_scale.dtype != torch.float32 or tuple(cache_scale.shape) != tuple(cache.shape[:2]):
+            raise ValueError("an fp8 cache needs cache_scale fp32 [B, rows]")
+        _dense(cache_scale, "cache_scale")
+    else:
+        _bf16_like(cache, "cache")
+        dt = BF16
+    for t, n in ((n_entries, "n_entries"), (n_window, "n_window")):
+        if t is not None and (t.dtype != torch.int32 or t.numel() != B or not t.is_contiguous()):
+            raise ValueError(f"{n} must be contiguous int32 [B]")
+    _check(_lib_append(kind, _ptr(s_new), _ptr(g_new), _ptr(pos), B, D, _ptr(ring), _ptr(ring_gate), W, dt,
+                       _ptr(cache), _ptr(cache_scale), cache.shape[1], _ptr(n_entries), _ptr(n_window),
+                       _stream(s_new.device)))
+
+
 # ------------------------------------------------------------------ index / top-k
 
 def index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, k: int, k_scale: torch.Tensor | None = None,
@@ -194,13 +238,16 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
            softmax_scale: float, rope_dims: int = 0, rope_base: float = 10000.0,
            q_pos: torch.Tensor | None = None, cache_scale: torch.Tensor | None = None,
            window_scale: torch.Tensor | None = None, n_entries: torch.Tensor | None = None,
-           out: torch.Tensor | None = None, splits: int = 0) -> torch.Tensor:
+           n_window: torch.Tensor | None = None, out: torch.Tensor | None = None,
+           splits: int = 0) -> torch.Tensor:
     """O [B, H, D] fp32: softmax attention of Q [B, H, D] (bf16) over the cache
     rows named by ids [B, k] (or all of the first n_entries rows when ids is
     None) followed by the window rows [B, W, D], then inverse RoPE on the last
     rope_dims channels at positions q_pos [B] int64. The window may be a view
-    whose last two dimensions are dense (e.g. the tail of a state span)."""
-    _need_cuda(Q, cache, ids, window, q_pos, cache_scale, window_scale, n_entries, out)
+    whose last two dimensions are dense (e.g. the tail of a state span).
+    n_window [B] int32 keeps only the first n_window[b] window rows (a ring
+    from append() that has not wrapped yet)."""
+    _need_cuda(Q, cache, ids, window, q_pos, cache_scale, window_scale, n_entries, n_window, out)
     _bf16_like(Q, "Q")
     _dense(Q, "Q"); _dense(cache, "cache")
     B, H, D = Q.shape
@@ -220,6 +267,9 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
         k = ids.shape[1]
     if n_entries is not None and (n_entries.dtype != torch.int32 or n_entries.numel() != B):
         raise ValueError("n_entries must be int32 [B]")
+    if n_window is not None and (n_window.dtype != torch.int32 or n_window.numel() != B
+                                 or not n_window.is_contiguous()):
+        raise ValueError("n_window must be contiguous int32 [B]")
     W, wstride, win_fp8 = 0, 0, False
     if window is not None and window.shape[1] > 0:
         if window.dim() != 3 or window.shape[0] != B or window.shape[2] != D:
@@ -249,7 +299,8 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
     ws = _workspace("attend", nbytes, Q.device)
     _check(_lib_attend(_ptr(Q), B, H, D, FP8_E4M3 if cache_fp8 else BF16, _ptr(cache), _ptr(cache_scale),
                        cache.shape[1], _ptr(ids), k, _ptr(n_entries), FP8_E4M3 if win_fp8 else BF16,
-                       _ptr(window), _ptr(window_scale), W, wstride, rope_dims, rope_base, _ptr(q_pos),
+                       _ptr(window), _ptr(window_scale), W, wstride, _ptr(n_window), rope_dims, rope_base,
+                       _ptr(q_pos),
                        softmax_scale, _ptr(out), splits, _ptr(ws), 0 if ws is None else ws.numel(),
                        _stream(Q.device)))
     return out

@@ -85,6 +85,37 @@ cskv_status cskv_compress(int32_t kind, const void* S, const float* gate, int64_
                     "compress launch");
 }
 
+// ------------------------------------------------------------------ append
+
+cskv_status cskv_append(int32_t kind, const void* s_new, const float* g_new, const int64_t* pos,
+                        int64_t B, int32_t D, void* ring, float* ring_gate, int32_t W,
+                        int32_t cache_dtype, void* cache, float* cache_scale, int64_t cache_rows,
+                        int32_t* n_entries, int32_t* n_window, void* stream) {
+  CHECK(kind == CSKV_C4A || kind == CSKV_C128A, CSKV_EINVAL, "append: unknown kind %d", kind);
+  CHECK(B >= 0 && cache_rows >= 0, CSKV_EINVAL, "append: negative size (B=%lld cache_rows=%lld)",
+        (long long)B, (long long)cache_rows);
+  CHECK(D == 128 || D == 512, CSKV_EUNSUPPORTED, "append: D=%d (supported: 128, 512)", D);
+  CHECK(cache_dtype == CSKV_BF16 || cache_dtype == CSKV_FP8_E4M3, CSKV_EUNSUPPORTED,
+        "append: cache dtype %d (supported: bf16, fp8)", cache_dtype);
+  const int32_t w = kind == CSKV_C4A ? 8 : 128;
+  CHECK(W >= w, CSKV_EINVAL, "append: W=%d must be >= %d, the states of one entry", W, w);
+  CHECK(cache_rows <= 0x7FFFFFFF, CSKV_EUNSUPPORTED, "append: cache_rows too large for int32 counts");
+  if (B == 0) return ok();
+  CHECK(s_new && g_new && pos && ring && ring_gate, CSKV_EINVAL, "append: null s_new, g_new, pos or ring");
+  CHECK(cache_rows == 0 || cache, CSKV_EINVAL, "append: null cache");
+  CHECK(cache_dtype != CSKV_FP8_E4M3 || cache_rows == 0 || cache_scale, CSKV_EINVAL,
+        "append: fp8 cache needs cache_scale");
+  CHECK(aligned(s_new, 16) && aligned(ring, 16) && (!cache || aligned(cache, 16)) && aligned(g_new, 4) &&
+            aligned(ring_gate, 4) && aligned(pos, 8),
+        CSKV_EINVAL, "append: s_new, ring and cache must be 16-byte aligned");
+  CHECK(B <= 0x7FFFFFFF, CSKV_EUNSUPPORTED, "append: B=%lld too large", (long long)B);
+  return hip_status(cskv::launch_append(kind, reinterpret_cast<const uint16_t*>(s_new), g_new, pos, B, D,
+                                        reinterpret_cast<uint16_t*>(ring), ring_gate, W,
+                                        cache_dtype == CSKV_FP8_E4M3, cache, cache_scale, cache_rows,
+                                        n_entries, n_window, reinterpret_cast<hipStream_t>(stream)),
+                    "append launch");
+}
+
 // ------------------------------------------------------------------ index / top-k
 
 static cskv_status topk_common(int64_t B, int64_t n_max, int32_t Di, int32_t k, int32_t key_dtype,
@@ -153,8 +184,9 @@ cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t 
                         const void* cache, const float* cache_scale, int64_t cache_rows,
                         const int32_t* ids, int32_t k, const int32_t* n_entries,
                         int32_t window_dtype, const void* window, const float* window_scale,
-                        int32_t W, int64_t window_batch_stride, int32_t rope_dims,
-                        float rope_base, const int64_t* q_pos, float softmax_scale, float* O,
+                        int32_t W, int64_t window_batch_stride, const int32_t* n_window,
+                        int32_t rope_dims, float rope_base, const int64_t* q_pos,
+                        float softmax_scale, float* O,
                         int32_t splits, void* workspace, size_t workspace_bytes, void* stream) {
   CHECK(B >= 0 && cache_rows >= 0 && W >= 0, CSKV_EINVAL, "attend: negative size");
   CHECK(H >= 1 && H <= 64, CSKV_EUNSUPPORTED, "attend: H=%d (supported: 1..64)", H);
@@ -208,6 +240,7 @@ cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t 
   a.window = window;
   a.window_scale = window_scale;
   a.W = W;
+  a.n_window = W > 0 ? n_window : nullptr;
   a.win_bstride = window_batch_stride;
   a.rope_dims = rope_dims;
   a.rope_base = rope_base;

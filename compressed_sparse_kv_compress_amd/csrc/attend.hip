@@ -116,6 +116,14 @@ __device__ __forceinline__ uint64_t lane_u64(uint64_t p, int lane) {
   return ((uint64_t)hi32 << 32) | lo32;
 }
 
+// Window rows of sequence b that are keys: the first n_window[b] (clamped to
+// [0, W]), or all W.
+__device__ __forceinline__ int64_t window_rows(const AttendArgs& a, int64_t b) {
+  if (!a.n_window) return a.W;
+  const int64_t n = a.n_window[b];
+  return n < 0 ? 0 : (n > a.W ? a.W : n);
+}
+
 // Kernel-uniform sources of key rows (held in scalar registers, so choosing
 // between cache and window selects values instead of loading an argument).
 struct RowSrc {
@@ -333,7 +341,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   } else {
     n_sel = a.k;
   }
-  const int64_t n_keys = n_sel + a.W;
+  const int64_t n_keys = n_sel + window_rows(a, b);
   const int64_t lo = (int64_t)s * keys_per_split;
   const int64_t hi = lo + keys_per_split < n_keys ? lo + keys_per_split : n_keys;
   const int n_tiles = hi > lo ? (int)((hi - lo + kTK - 1) / kTK) : 0;
@@ -667,7 +675,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend_hs(AttendArgs a, int 
   const int64_t b = (int64_t)(rest / n_hg) * 8 + (id & 7);
   if (b >= a.B) return;
   const int n_sel = a.k;
-  const int64_t n_keys = (int64_t)n_sel + a.W;
+  const int64_t n_keys = (int64_t)n_sel + window_rows(a, b);
   const int n_tiles = (int)((n_keys + kHsTK - 1) / kHsTK);
   const float tau_log2e = a.softmax_scale * kLog2e;
   const int h = 16 * hg + l16;                    // this lane's head

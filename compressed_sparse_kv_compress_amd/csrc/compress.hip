@@ -8,6 +8,14 @@
 //
 // Both kernels stream S once from HBM (a c4a state feeds two entries but is
 // loaded once per wave run) and fuse the output rounding / fp8 row encoding.
+//
+// The append kernels serve streaming decode ([P1] cache-block paragraph: a
+// constant-size compressor state per layer beside the entries and the
+// window): each sequence appends one state to a ring of its newest W states
+// (token p in slot p mod W), which is both the attention window and the
+// compressor's carry, and an entry is written when its window completes. They
+// fold an entry with the same routines as the span kernels, so a streamed
+// entry is bit-identical to the one cskv_compress writes for the same states.
 #include "kernels.h"
 
 namespace cskv {
@@ -72,6 +80,33 @@ __device__ __forceinline__ void store_entry(const float* acc, int lane, void* ca
 }
 
 // ---------------------------------------------------------------- c4a
+// One c4a entry from its 8 states (lo: states 0-3, hi: states 4-7) and their
+// gate logits: softmax weights in fp32, then one fma per state in order.
+template <int D>
+__device__ __forceinline__ void fold_c4a(const RowSlice<D>* lo, const RowSlice<D>* hi, const float* g,
+                                         float* acc) {
+  float m = g[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) m = fmaxf(m, g[j]);
+  float e[8], z = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { e[j] = expf(g[j] - m); z += e[j]; }
+#pragma unroll
+  for (int i = 0; i < RowSlice<D>::CPL; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float w = e[j] / z;
+#pragma unroll
+    for (int i = 0; i < RowSlice<D>::CPL; ++i) acc[i] = fmaf(w, lo[j].v[i], acc[i]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float w = e[4 + j] / z;
+#pragma unroll
+    for (int i = 0; i < RowSlice<D>::CPL; ++i) acc[i] = fmaf(w, hi[j].v[i], acc[i]);
+  }
+}
+
 // One wave owns a run of kC4aRun consecutive entries of one sequence. Entry c
 // reads stride blocks c and c+1 (4 states each); the wave keeps the previous
 // block in registers so every state of the run is loaded once.
@@ -103,31 +138,11 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress_c4a(
   for (int64_t c = c0; c < c1; ++c) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) load_row<D>(Sb + (4 * c + 4 + j) * D, lane, cur[j]);
-    // softmax of the window's 8 gate logits (fp32)
     float g[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) g[j] = gb[4 * c + j];
-    float m = g[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) m = fmaxf(m, g[j]);
-    float e[8], z = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) { e[j] = expf(g[j] - m); z += e[j]; }
     float acc[RowSlice<D>::CPL];
-#pragma unroll
-    for (int i = 0; i < RowSlice<D>::CPL; ++i) acc[i] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float w = e[j] / z;
-#pragma unroll
-      for (int i = 0; i < RowSlice<D>::CPL; ++i) acc[i] = fmaf(w, prev[j].v[i], acc[i]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float w = e[4 + j] / z;
-#pragma unroll
-      for (int i = 0; i < RowSlice<D>::CPL; ++i) acc[i] = fmaf(w, cur[j].v[i], acc[i]);
-    }
+    fold_c4a<D>(prev, cur, g, acc);
     store_entry<D, FP8>(acc, lane, cb + c * (int64_t)D * ESZ, FP8 ? sb + c : nullptr);
 #pragma unroll
     for (int j = 0; j < 4; ++j) prev[j] = cur[j];
@@ -135,38 +150,29 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress_c4a(
 }
 
 // ---------------------------------------------------------------- c128a
-// One workgroup per entry: wave w folds states 32w .. 32w+31 of the window,
-// then the four partial rows are added in wave order through LDS.
-template <int D, bool FP8>
-__global__ __launch_bounds__(kCompressThreads) void k_compress_c128a(
-    const uint16_t* __restrict__ S, const float* __restrict__ gate, int64_t T, int64_t n_entries,
-    int64_t first_entry, void* __restrict__ cache, float* __restrict__ cache_scale,
-    int64_t cache_rows) {
+// One c128a entry from its 128 states (row_at(j): state j's row, gate_at(j):
+// its logit), by the 4 waves of a workgroup: wave w folds states 32w .. 32w+31,
+// then the four partial rows are added in wave order through LDS. The entry
+// ends in wave 0's acc. Every thread of the workgroup must call it.
+template <int D, class RowAt, class GateAt>
+__device__ __forceinline__ void fold_c128a(RowAt row_at, GateAt gate_at, float (*part)[D], float* acc) {
   constexpr int CPL = D / kWave;
   constexpr int NW = kCompressThreads / kWave;
-  __shared__ float part[NW][D];
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
-  const int64_t b = blockIdx.y;
-  const int64_t c = blockIdx.x;
-  const uint16_t* Sw = S + (b * T + 128 * c) * D;
-  const float* gw = gate + b * T + 128 * c;
-
   // softmax over the 128 logits; every wave computes the same max and sum
-  const float g0 = gw[lane], g1 = gw[lane + 64];
+  const float g0 = gate_at(lane), g1 = gate_at(lane + 64);
   const float m = wave_max(fmaxf(g0, g1));
   const float z = wave_sum(expf(g0 - m) + expf(g1 - m));
-
-  float acc[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = 0.0f;
   RowSlice<D> r[8];
   for (int j0 = 0; j0 < 32; j0 += 8) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load_row<D>(Sw + (int64_t)(32 * wave + j0 + u) * D, lane, r[u]);
+    for (int u = 0; u < 8; ++u) load_row<D>(row_at(32 * wave + j0 + u), lane, r[u]);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float w = expf(gw[32 * wave + j0 + u] - m) / z;
+      const float w = expf(gate_at(32 * wave + j0 + u) - m) / z;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) acc[i] = fmaf(w, r[u].v[i], acc[i]);
     }
@@ -182,8 +188,138 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress_c128a(
     for (int w = 1; w < NW; ++w) s += part[w][lane * CPL + i];
     acc[i] = s;
   }
+}
+
+// One workgroup per entry.
+template <int D, bool FP8>
+__global__ __launch_bounds__(kCompressThreads) void k_compress_c128a(
+    const uint16_t* __restrict__ S, const float* __restrict__ gate, int64_t T, int64_t n_entries,
+    int64_t first_entry, void* __restrict__ cache, float* __restrict__ cache_scale,
+    int64_t cache_rows) {
+  constexpr int CPL = D / kWave;
+  constexpr int NW = kCompressThreads / kWave;
+  __shared__ float part[NW][D];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int64_t b = blockIdx.y;
+  const int64_t c = blockIdx.x;
+  const uint16_t* Sw = S + (b * T + 128 * c) * D;
+  const float* gw = gate + b * T + 128 * c;
+  float acc[CPL];
+  fold_c128a<D>([&](int j) { return Sw + (int64_t)j * D; }, [&](int j) { return gw[j]; }, part, acc);
+  if (wave != 0) return;
   constexpr int ESZ = FP8 ? 1 : 2;
   const int64_t row = b * cache_rows + first_entry + c;
+  store_entry<D, FP8>(acc, lane, reinterpret_cast<uint8_t*>(cache) + row * (int64_t)D * ESZ,
+                      FP8 ? cache_scale + row : nullptr);
+}
+
+// ---------------------------------------------------------------- append
+// Sequence b appends state s_new[b] (gate logit g_new[b]) as token p = pos[b]
+// (p < 0: the sequence is skipped). The state goes to ring slot p mod W; the
+// entry whose window ends at p (c4a: p % 4 == 3 and p >= 7; c128a: p % 128 ==
+// 127) is folded from the ring's older states plus the new one, read from the
+// input, so no thread reads what this launch writes. The counts are the
+// entries present in the cache and the window rows in the ring.
+
+// The new state into its ring slot: lane l copies channels CPL*l .. CPL*l+CPL-1.
+template <int D>
+__device__ __forceinline__ void ring_put(const uint16_t* snew, uint16_t* dst, int lane) {
+  constexpr int CPL = D / kWave;
+  if constexpr (CPL == 8) {
+    *reinterpret_cast<uint4*>(dst + lane * 8) = *reinterpret_cast<const uint4*>(snew + lane * 8);
+  } else {
+    *reinterpret_cast<uint32_t*>(dst + lane * 2) = *reinterpret_cast<const uint32_t*>(snew + lane * 2);
+  }
+}
+
+__device__ __forceinline__ void append_counts(int64_t n, int64_t p, int W, int64_t cache_rows, int64_t b,
+                                              int32_t* n_entries, int32_t* n_window) {
+  if (n_entries) n_entries[b] = (int32_t)(n < cache_rows ? n : cache_rows);
+  if (n_window) n_window[b] = (int32_t)(p + 1 < W ? p + 1 : W);
+}
+
+constexpr int kAppendC4aSeqs = kCompressThreads / kWave;   // c4a: one wave per sequence
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(kCompressThreads) void k_append_c4a(
+    const uint16_t* __restrict__ s_new, const float* __restrict__ g_new, const int64_t* __restrict__ pos,
+    int64_t B, uint16_t* __restrict__ ring, float* __restrict__ ring_gate, int W, void* __restrict__ cache,
+    float* __restrict__ cache_scale, int64_t cache_rows, int32_t* __restrict__ n_entries,
+    int32_t* __restrict__ n_window) {
+  const int lane = lane_id();
+  const int64_t b = (int64_t)blockIdx.x * kAppendC4aSeqs + threadIdx.x / kWave;
+  if (b >= B) return;
+  const int64_t p = pos[b];
+  if (p < 0) return;
+  const uint16_t* snew = s_new + b * D;
+  uint16_t* rb = ring + b * (int64_t)W * D;
+  float* gb = ring_gate + b * (int64_t)W;
+  const int64_t slot = p % W;
+  ring_put<D>(snew, rb + slot * D, lane);
+  if (lane == 0) {
+    gb[slot] = g_new[b];
+    append_counts(p >= 7 ? (p - 7) / 4 + 1 : 0, p, W, cache_rows, b, n_entries, n_window);
+  }
+  if (p < 7 || (p & 3) != 3) return;
+  const int64_t c = (p - 7) >> 2;
+  if (c >= cache_rows) return;
+  const int64_t s0 = (p - 7) % W;
+  RowSlice<D> r[8];
+  float g[8];
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const int64_t sl = s0 + j < W ? s0 + j : s0 + j - W;
+    load_row<D>(rb + sl * D, lane, r[j]);
+    g[j] = gb[sl];
+  }
+  load_row<D>(snew, lane, r[7]);
+  g[7] = g_new[b];
+  float acc[RowSlice<D>::CPL];
+  fold_c4a<D>(r, r + 4, g, acc);
+  constexpr int ESZ = FP8 ? 1 : 2;
+  const int64_t row = b * cache_rows + c;
+  store_entry<D, FP8>(acc, lane, reinterpret_cast<uint8_t*>(cache) + row * (int64_t)D * ESZ,
+                      FP8 ? cache_scale + row : nullptr);
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(kCompressThreads) void k_append_c128a(
+    const uint16_t* __restrict__ s_new, const float* __restrict__ g_new, const int64_t* __restrict__ pos,
+    uint16_t* __restrict__ ring, float* __restrict__ ring_gate, int W, void* __restrict__ cache,
+    float* __restrict__ cache_scale, int64_t cache_rows, int32_t* __restrict__ n_entries,
+    int32_t* __restrict__ n_window) {
+  constexpr int CPL = D / kWave;
+  constexpr int NW = kCompressThreads / kWave;
+  __shared__ float part[NW][D];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int64_t b = blockIdx.x;
+  const int64_t p = pos[b];   // (every exit below is uniform over the workgroup)
+  if (p < 0) return;
+  const uint16_t* snew = s_new + b * D;
+  uint16_t* rb = ring + b * (int64_t)W * D;
+  float* gb = ring_gate + b * (int64_t)W;
+  if (wave == 0) {
+    const int64_t slot = p % W;
+    ring_put<D>(snew, rb + slot * D, lane);
+    if (lane == 0) {
+      gb[slot] = g_new[b];
+      append_counts((p + 1) / 128, p, W, cache_rows, b, n_entries, n_window);
+    }
+  }
+  if ((p & 127) != 127) return;
+  const int64_t c = p >> 7;
+  if (c >= cache_rows) return;
+  const int64_t s0 = (p - 127) % W;
+  const float gn = g_new[b];
+  auto slot_of = [&](int j) { return s0 + j < W ? s0 + j : s0 + j - W; };
+  float acc[CPL];
+  fold_c128a<D>([&](int j) { return j == 127 ? snew : rb + slot_of(j) * D; },
+                [&](int j) { return j == 127 ? gn : gb[slot_of(j)]; }, part, acc);
+  if (wave != 0) return;
+  constexpr int ESZ = FP8 ? 1 : 2;
+  const int64_t row = b * cache_rows + c;
   store_entry<D, FP8>(acc, lane, reinterpret_cast<uint8_t*>(cache) + row * (int64_t)D * ESZ,
                       FP8 ? cache_scale + row : nullptr);
 }
@@ -205,6 +341,33 @@ static hipError_t launch_compress_t(int kind, const uint16_t* S, const float* ga
                        gate, T, n, first_entry, cache, cache_scale, cache_rows);
   }
   return hipGetLastError();
+}
+
+template <int D, bool FP8>
+static hipError_t launch_append_t(int kind, const uint16_t* s_new, const float* g_new, const int64_t* pos,
+                                  int64_t B, uint16_t* ring, float* ring_gate, int W, void* cache,
+                                  float* cache_scale, int64_t cache_rows, int32_t* n_entries,
+                                  int32_t* n_window, hipStream_t stream) {
+  if (kind == 0) {
+    dim3 grid((unsigned)((B + kAppendC4aSeqs - 1) / kAppendC4aSeqs));
+    hipLaunchKernelGGL((k_append_c4a<D, FP8>), grid, dim3(kCompressThreads), 0, stream, s_new, g_new, pos, B,
+                       ring, ring_gate, W, cache, cache_scale, cache_rows, n_entries, n_window);
+  } else {
+    hipLaunchKernelGGL((k_append_c128a<D, FP8>), dim3((unsigned)B), dim3(kCompressThreads), 0, stream, s_new,
+                       g_new, pos, ring, ring_gate, W, cache, cache_scale, cache_rows, n_entries, n_window);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_append(int kind, const uint16_t* s_new, const float* g_new, const int64_t* pos, int64_t B,
+                         int D, uint16_t* ring, float* ring_gate, int W, bool fp8, void* cache,
+                         float* cache_scale, int64_t cache_rows, int32_t* n_entries, int32_t* n_window,
+                         hipStream_t stream) {
+  if (D == 512)
+    return fp8 ? launch_append_t<512, true>(kind, s_new, g_new, pos, B, ring, ring_gate, W, cache, cache_scale, cache_rows, n_entries, n_window, stream)
+               : launch_append_t<512, false>(kind, s_new, g_new, pos, B, ring, ring_gate, W, cache, cache_scale, cache_rows, n_entries, n_window, stream);
+  return fp8 ? launch_append_t<128, true>(kind, s_new, g_new, pos, B, ring, ring_gate, W, cache, cache_scale, cache_rows, n_entries, n_window, stream)
+             : launch_append_t<128, false>(kind, s_new, g_new, pos, B, ring, ring_gate, W, cache, cache_scale, cache_rows, n_entries, n_window, stream);
 }
 
 hipError_t launch_compress(int kind, const uint16_t* S, const float* gate, int64_t B, int64_t T,

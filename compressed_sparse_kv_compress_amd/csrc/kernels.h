@@ -13,6 +13,10 @@ namespace cskv {
 hipError_t launch_compress(int kind, const uint16_t* S, const float* gate, int64_t B, int64_t T,
                            int D, int64_t n, int64_t first_entry, bool fp8, void* cache,
                            float* cache_scale, int64_t cache_rows, hipStream_t stream);
+hipError_t launch_append(int kind, const uint16_t* s_new, const float* g_new, const int64_t* pos, int64_t B,
+                         int D, uint16_t* ring, float* ring_gate, int W, bool fp8, void* cache,
+                         float* cache_scale, int64_t cache_rows, int32_t* n_entries, int32_t* n_window,
+                         hipStream_t stream);
 
 // ---- index_topk.hip
 // Plan of the indexer: k_index_score scores `chunk` entries per workgroup and
@@ -58,6 +62,7 @@ struct AttendArgs {
   const void* window;
   const float* window_scale;
   int W;
+  const int32_t* n_window;   // per-sequence window rows that are keys, or NULL for W
   int64_t win_bstride;
   int rope_dims;
   float rope_base;

@@ -85,6 +85,42 @@ cskv_status cskv_compress(int32_t kind, const void* S, const float* gate, int64_
                           float* cache_scale, int64_t cache_rows, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Streaming decode append ([P1] paragraph on cache block types: besides the
+ * compressed entries each layer keeps a constant-size compressor state and the
+ * sliding window; [P1] "c4a" / "c128a" and [P2] Step 4: an entry exists once
+ * its window of w states is complete, i.e. every 4 (C4A) or 128 (C128A)
+ * decode steps; [P2] Step 6: the window holds the newest states).
+ *
+ * Sequence b appends state s_new[b] with gate logit g_new[b] as its token
+ * pos[b] (absolute, 0-based; positions may differ between sequences; a
+ * negative position skips the sequence). The caller-owned ring keeps each
+ * sequence's newest W states and gate logits, token p in slot p mod W; it is
+ * both the compressor's carry and the attention window (pass it to cskv_attend
+ * as the window with n_window). The call stores the new state and logit in
+ * their slot and, when token pos[b] completes an entry (C4A: pos % 4 == 3 and
+ * pos >= 7, entry (pos-7)/4 from tokens pos-7 .. pos; C128A: pos % 128 == 127,
+ * entry pos/128 from tokens pos-127 .. pos), writes that entry to its cache
+ * row with exactly the arithmetic of cskv_compress (bit-identical to what
+ * cskv_compress writes from the same states). Entries at rows >= cache_rows
+ * are not written. The ring must already hold the entry's older states: append
+ * each token of a sequence once, in order.
+ *
+ *   s_new      [B, D] bf16;  g_new [B] fp32;  pos [B] int64 device array
+ *   ring       [B, W, D] bf16;  ring_gate [B, W] fp32;  W >= 8 (C4A), >= 128 (C128A)
+ *   cache      as cskv_compress (bf16, or fp8 codes + cache_scale)
+ *   n_entries  [B] int32 or NULL: set to the sequence's entries in the cache,
+ *              min(complete entries, cache_rows) (C4A: pos >= 7 ? (pos-7)/4+1
+ *              : 0; C128A: (pos+1)/128), for cskv_index_topk / cskv_attend
+ *   n_window   [B] int32 or NULL: set to min(pos+1, W), the ring rows that
+ *              hold states (the leading ones until the ring has wrapped)
+ * Sequences with a negative position keep their counts.
+ */
+cskv_status cskv_append(int32_t kind, const void* s_new, const float* g_new, const int64_t* pos,
+                        int64_t B, int32_t D, void* ring, float* ring_gate, int32_t W,
+                        int32_t cache_dtype, void* cache, float* cache_scale, int64_t cache_rows,
+                        int32_t* n_entries, int32_t* n_window, void* stream);
+
+/* ------------------------------------------------------------------------
  * Indexer scores and exact top-k ([P1] "c4a": top-k selection, default
  * k = 512; [P2] Step 5 "The query now reads a mixed memory map": a learned
  * indexer scores the compressed blocks and the query reads only the chosen
@@ -146,6 +182,9 @@ cskv_status cskv_index_topk(const void* q_idx, int32_t key_dtype, const void* k_
  *   window       rows at window + b*window_batch_stride*D (elements), W of them
  *                (W may be 0); window_dtype CSKV_BF16 or CSKV_FP8_E4M3 (then
  *                window_scale at window_scale + b*window_batch_stride)
+ *   n_window     [B] int32 device counts or NULL: only the first n_window[b]
+ *                window rows of sequence b (clamped to [0, W]) are keys; NULL
+ *                = all W (a ring from cskv_append that has not wrapped yet)
  *   rope_dims    even, <= D (0 = no rotation);  q_pos [B] int64 device positions
  *   O            [B, H, D] fp32
  *   splits       key-row splits per sequence: 0 = automatic, else >= 1 (sparse
@@ -159,8 +198,9 @@ cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t 
                         const void* cache, const float* cache_scale, int64_t cache_rows,
                         const int32_t* ids, int32_t k, const int32_t* n_entries,
                         int32_t window_dtype, const void* window, const float* window_scale,
-                        int32_t W, int64_t window_batch_stride, int32_t rope_dims,
-                        float rope_base, const int64_t* q_pos, float softmax_scale, float* O,
+                        int32_t W, int64_t window_batch_stride, const int32_t* n_window,
+                        int32_t rope_dims, float rope_base, const int64_t* q_pos,
+                        float softmax_scale, float* O,
                         int32_t splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------

@@ -80,6 +80,29 @@ def test_compress_validation(lib):
     assert lib._lib_compress(1, None, None, 0, 4096, 512, 0, lib.BF16, None, None, 32, None) == lib.OK
 
 
+def test_append_validation(lib):
+    p = ctypes.c_void_p(256)          # never dereferenced: every call below is rejected first
+    f = lib._lib_append
+
+    def call(**kw):
+        a = dict(kind=0, s=p, g=p, pos=p, B=2, D=512, ring=p, rg=p, W=128, cdt=lib.BF16, cache=p, cs=None,
+                 rows=64, ne=None, nw=None, stream=None)
+        a.update(kw)
+        return f(*a.values())
+
+    assert call(kind=3) == lib.EINVAL
+    assert call(D=384) == lib.EUNSUPPORTED
+    assert call(cdt=lib.FP4_E2M1) == lib.EUNSUPPORTED
+    assert call(W=7) == lib.EINVAL                          # a c4a entry needs 8 states
+    assert call(kind=1, W=127) == lib.EINVAL                # a c128a entry needs 128
+    assert b"W=127" in lib._lib_last_error()
+    assert call(pos=None) == lib.EINVAL
+    assert call(cdt=lib.FP8_E4M3) == lib.EINVAL             # fp8 cache without scales
+    assert call(ring=ctypes.c_void_p(264)) == lib.EINVAL    # misaligned
+    assert call(rows=-1) == lib.EINVAL
+    assert call(B=0, s=None, g=None, pos=None, ring=None, rg=None, cache=None) == lib.OK
+
+
 def test_topk_validation(lib):
     p = ctypes.c_void_p(256)
     f = lib._lib_topk
@@ -100,7 +123,7 @@ def test_attend_validation(lib):
 
     def call(**kw):
         a = dict(Q=p, B=1, H=64, D=512, cdt=lib.BF16, cache=p, cs=None, rows=10, ids=p, k=4, ne=None,
-                 wdt=lib.BF16, win=p, ws_=None, W=4, wst=4, R=64, base=10000.0, pos=p, tau=0.1, O=p,
+                 wdt=lib.BF16, win=p, ws_=None, W=4, wst=4, nw=None, R=64, base=10000.0, pos=p, tau=0.1, O=p,
                  splits=1, work=None, wsb=0, stream=None)
         a.update(kw)
         return f(*a.values())
