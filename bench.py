@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4a_128k_bf16",
-                    choices=["c4a_128k_bf16", "c128a_1m_bf16", "c4a_1m_fp8_fp4", "mixed61_256k_bf16", "tiny_c4a_2k"])
+                    choices=["c4a_128k_bf16", "c128a_1m_bf16", "c4a_1m_fp8_fp4", "mixed61_256k_bf16", "tiny_c4a_2k",
+                             "stream_c4a_128k_bf16"])
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -246,6 +247,12 @@ class Mixed61(Workload):
             if lay["kind"] == "c4a":
                 self.cskv.index_topk(lay["qidx"], lay["kidx"], c.k, ids=lay["ids"], chunk=self.args.chunk)
 
+    def step(self, i, dominant_only=False):
+        if dominant_only:
+            self.dominant_layers()
+        else:
+            self.step_layers()
+
     def bytes(self):
         c = self.cfg
         n4 = sum(1 for l in range(c.layers) if c.layer_kind(l) == "c4a")
@@ -264,6 +271,78 @@ class Mixed61(Workload):
                       n128 * 4 * c.H * c.D * (self.N128 + c.W))
 
 
+class StreamC4a(Workload):
+    """Streaming c4a decode of a ragged batch: every step appends one new state
+    per sequence (cskv_append: ring write, an entry every 4 tokens), then
+    index_topk over the per-sequence entry counts and attend over the selected
+    entries plus the ring as window. The state carries over from step to step,
+    so there is one input set; prefix caches, indexer keys and rings are drawn
+    directly (their contents do not change the work)."""
+
+    N_TOKENS = 8     # distinct new-state sets cycled through
+
+    def setup(self, n_sets):
+        torch, sd, s = self.torch, self.sd, self.synth
+        c = self.cfg
+        B, L, D, H, Di, W = c.B, c.L, c.D, c.H, c.Di, c.W
+        from synth.configs import c4a_entries
+        self.n_steps = self.args.warmup + self.args.steps
+        self.rows = c4a_entries(L + self.n_steps) + 1
+        log(f"setup: stream caches ({B} x {self.rows} entries)")
+        self.cache = sd.new((B, self.rows, D), s.KIND_NORMAL_BF16, self.key(0, s.T_CACHE), device=self.dev)
+        self.kidx = sd.new((B, self.rows, Di), s.KIND_INT_BF16, self.key(0, s.T_KIDX), device=self.dev,
+                           a=c.idx_range)
+        self.qidx = sd.new((B, Di), s.KIND_INT_BF16, self.key(0, s.T_QIDX), device=self.dev, a=c.idx_range)
+        self.Q = sd.new((B, H, D), s.KIND_NORMAL_BF16, self.key(0, s.T_Q), device=self.dev)
+        self.ring = sd.new((B, W, D), s.KIND_NORMAL_BF16, self.key(0, s.T_WIN), device=self.dev)
+        self.ring_gate = sd.new((B, W), s.KIND_NORMAL_F32, self.key(0, s.T_MISC), device=self.dev)
+        self.s_new = sd.new((self.N_TOKENS, B, D), s.KIND_NORMAL_BF16, self.key(0, s.T_S), device=self.dev)
+        self.g_new = sd.new((self.N_TOKENS, B), s.KIND_NORMAL_F32, self.key(0, s.T_GATE), device=self.dev)
+        # step t appends token L - lag_b + t of sequence b
+        lag = torch.tensor([c.stream_lag(b) for b in range(B)], dtype=torch.int64)
+        self.pos = (L - lag[None, :] + torch.arange(self.n_steps, dtype=torch.int64)[:, None]).to(self.dev)
+        self.n_entries = torch.zeros((B,), dtype=torch.int32, device=self.dev)
+        self.n_window = torch.zeros((B,), dtype=torch.int32, device=self.dev)
+        self.ids = torch.empty((B, c.k), dtype=torch.int32, device=self.dev)
+        self.O = torch.empty((B, H, D), dtype=torch.float32, device=self.dev)
+        self.sets = [None]
+        self.t = 0
+        torch.cuda.synchronize()
+
+    def step(self, i, dominant_only=False):
+        c, cskv = self.cfg, self.cskv
+        if dominant_only:
+            cskv.index_topk(self.qidx, self.kidx, c.k, n_entries=self.n_entries, ids=self.ids, chunk=self.args.chunk)
+            return
+        t = self.t
+        if t >= self.n_steps:
+            raise RuntimeError("stream workload: more steps than planned")
+        self.t += 1
+        j = t % self.N_TOKENS
+        cskv.append("c4a", self.s_new[j], self.g_new[j], self.pos[t], self.ring, self.ring_gate, self.cache,
+                    n_entries=self.n_entries, n_window=self.n_window)
+        cskv.index_topk(self.qidx, self.kidx, c.k, n_entries=self.n_entries, ids=self.ids, chunk=self.args.chunk)
+        cskv.attend(self.Q, self.cache, self.ids, self.ring, softmax_scale=c.tau, rope_dims=c.R,
+                    rope_base=c.rope_base, q_pos=self.pos[t], n_window=self.n_window, out=self.O,
+                    splits=self.args.splits)
+
+    def bytes(self):
+        c = self.cfg
+        from synth.configs import c4a_entries
+        # entries at the start of the timed steps (they grow by one per 4 steps)
+        n = sum(c4a_entries(c.L - c.stream_lag(b)) for b in range(c.B))
+        dom = n * c.Di * 2 + c.B * (c.Di * 2 + c.k * 4)
+        # append: new state read + ring write (+ gate), and a quarter of the
+        # 8-state folds and entry writes; attend: k + W rows, Q and O
+        app = c.B * (2 * c.D * 2 + 8 + (8 * c.D * 2 + c.D * 2) // 4)
+        att = c.B * ((c.k + c.W) * c.D * 2 + c.k * 4 + c.H * c.D * 6)
+        return dom, app + att
+
+    def flops(self):
+        c = self.cfg
+        return c.B * (2 * c.n_entries * c.Di + 4 * c.H * c.D * (c.k + c.W))
+
+
 # ------------------------------------------------------------------ CPU oracle baseline
 
 def cpu_baseline(cfg, seconds):
@@ -279,7 +358,7 @@ def cpu_baseline(cfg, seconds):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
-    kind = cfg.layer_kind(1) if cfg.kind == "mixed" else cfg.kind
+    kind = cfg.layer_kind(1) if cfg.kind in ("mixed", "stream") else cfg.kind
     from synth.configs import c128a_entries, c4a_entries
     N = c4a_entries(cfg.L) if kind == "c4a" else c128a_entries(cfg.L)
     n_seq = 2
@@ -291,7 +370,7 @@ def cpu_baseline(cfg, seconds):
         # only the rows a query can read are filled: every row for c128a, the
         # rows the oracle's own top-k picks for c4a (filled after selection)
         cache = np.zeros((N, cfg.D), dtype=np.float64)
-        st = {"Q": Q, "win": win, "cache": cache}
+        st = {"Q": Q, "win": win, "cache": cache, "ring": win.copy(), "ring_gate": np.zeros(cfg.W)}
         if kind == "c4a":
             st["qidx"] = F.bf16_to_f64(synth.int_bf16(key(synth.T_QIDX), b * cfg.Di, cfg.Di, cfg.idx_range))
             if cfg.key_dtype == "fp4":
@@ -312,6 +391,9 @@ def cpu_baseline(cfg, seconds):
         seqs.append(st)
 
     def one(st):
+        if cfg.kind == "stream":
+            # the step's append first (token L-1 completes an entry: the 8-state fold)
+            M.append("c4a", st["ring"], st["ring_gate"], st["win"][0], 0.0, cfg.L - 1)
         if kind == "c4a":
             keys = st["kidx"] if "kidx" in st else F.decode_fp4_g16(st["kidx_codes"], st["kidx_scales"])
             M.c4a_decode(st["Q"], st["qidx"], keys, st["cache"], st["win"], cfg.k, cfg.tau, cfg.R,
@@ -450,9 +532,10 @@ def main():
     import synth
     from synth import device as sd
 
-    cls = {"c4a": C4aLayer, "c128a": C128aLayer, "mixed": Mixed61}[cfg.kind]
+    cls = {"c4a": C4aLayer, "c128a": C128aLayer, "mixed": Mixed61, "stream": StreamC4a}[cfg.kind]
     wl = cls(cfg, args, torch, cskv, sd, synth)
-    n_sets = args.sets or (1 if cfg.kind == "mixed" else 4)
+    stateful = cfg.kind in ("mixed", "stream")   # steps that carry state: no input-set rotation, no graphs
+    n_sets = args.sets or (1 if stateful else 4)
     t_setup = time.perf_counter()
     wl.setup(n_sets)
     setup_s = time.perf_counter() - t_setup
@@ -467,8 +550,8 @@ def main():
     mixed = cfg.kind == "mixed"
     n4 = sum(1 for l in range(cfg.layers) if cfg.layer_kind(l) == "c4a") if mixed else 1
     for i in range(args.warmup):
-        if mixed:
-            wl.step_layers()
+        if stateful:
+            wl.step(i)
         else:
             st = wl.sets[i % n_sets]
             wl.dominant(st)
@@ -478,7 +561,7 @@ def main():
     # (the dominant call in a graph of its own, so that its duration is timed on
     # the launch stream) and replayed.
     graphs = None
-    if not mixed and args.graphs:
+    if not stateful and args.graphs:
         graphs = []
         for st in wl.sets:
             g_dom, g_rest = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
@@ -496,11 +579,8 @@ def main():
         f"({'eager launches' if graphs is None else 'HIP graph replays'})")
 
     def run_step(i, dominant_only=False):
-        if mixed:
-            if dominant_only:
-                wl.dominant_layers()
-            else:
-                wl.step_layers()
+        if stateful:
+            wl.step(i, dominant_only)
             return
         if graphs is not None:
             g_dom, g_rest = graphs[i % n_sets]
@@ -554,12 +634,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg.cache_dtype == "bf16" and cfg.key_dtype == "bf16" else "fp8+fp4 (bf16 MFMA, fp32 accumulate)",
-        "data": "synthetic (SplitMix64 streams; caches built by the library's compress kernel)" if not mixed
+        "data": "synthetic (SplitMix64 streams; caches built by the library's compress kernel)" if not stateful
                 else "synthetic (SplitMix64 streams; prefix caches drawn directly, new states compressed in the step)",
         "config": {"workload": cfg.name, "batch": cfg.B, "context": cfg.L, "heads": cfg.H, "D": cfg.D,
                    "rotary": cfg.R, "window": cfg.W, "top_k": cfg.k or None, "indexer_dim": cfg.Di or None,
                    "cache": cfg.cache_dtype, "indexer_keys": cfg.key_dtype if cfg.k else None,
                    "layers": cfg.layers, "input_sets_rotated": n_sets,
+                   **({"ragged_context": f"{cfg.L} - (0..127)", "append": "one state per sequence per step"}
+                      if cfg.kind == "stream" else {}),
                    "launch": "eager" if graphs is None else "hip_graph"},
         "roofline": {
             "bound": "hbm",

@@ -25,7 +25,7 @@ def c128a_entries(L: int) -> int:
 class Workload:
     name: str
     number: int
-    kind: str              # "c4a", "c128a" or "mixed"
+    kind: str              # "c4a", "c128a", "mixed" or "stream" (c4a, one token appended per step)
     B: int                 # sequences in the batch
     L: int                 # context length in tokens (the query is token L-1)
     D: int                 # shared-state width (keys and values are the same S rows)
@@ -55,7 +55,7 @@ class Workload:
 
     @property
     def n_entries(self) -> int:
-        if self.kind == "c4a":
+        if self.kind in ("c4a", "stream"):
             return c4a_entries(self.L)
         if self.kind == "c128a":
             return c128a_entries(self.L)
@@ -63,9 +63,16 @@ class Workload:
 
     def layer_kind(self, layer: int) -> str:
         """Mixed stack: c128a on even layers (31 of 61), c4a on odd layers (30)."""
+        if self.kind == "stream":
+            return "c4a"
         if self.kind != "mixed":
             return self.kind
         return "c128a" if layer % 2 == 0 else "c4a"
+
+    def stream_lag(self, b: int) -> int:
+        """Streaming workload: sequence b's context is L - stream_lag(b) tokens
+        when the timed steps start (a ragged batch: lags 0 .. 127)."""
+        return (37 * b) % 128
 
 
 TINY = Workload(
@@ -102,5 +109,13 @@ MIXED_61 = Workload(
                 "x 262144 tokens; each layer compresses 128 new tokens, then attends",
 )
 
-ALL = [TINY, C4A_128K, C128A_1M, C4A_1M_Q, MIXED_61]
+STREAM_C4A_128K = Workload(
+    name="stream_c4a_128k_bf16", number=6, kind="stream", B=32, L=131072, D=512, R=64, H=64, W=128,
+    Di=128, k=512, idx_range=8,
+    description="streaming c4a decode: 32 sequences at ragged contexts 131072 - (0..127) tokens; each step "
+                "appends one state per sequence to its 128-row ring (an entry every 4 steps), then "
+                "index_topk over the ragged entry counts and attend over the ring as window",
+)
+
+ALL = [TINY, C4A_128K, C128A_1M, C4A_1M_Q, MIXED_61, STREAM_C4A_128K]
 BY_NAME = {w.name: w for w in ALL}
