@@ -9,7 +9,8 @@ in float64 (the codec encoders take their rounding decisions in float32, the
 precision the encoded caches are defined in):
 
 * ``formats``   - bf16, E4M3 (OCP "E4M3FN") and E2M1 value tables from the
-  formats' public definitions, and the fp8-row / fp4-group-of-16 encoders.
+  formats' public definitions, the fp8-row / fp4-group-of-16 encoders, and the
+  mixed rows that keep the rotary channels in bf16 and the rest in fp8.
 * ``method``    - compression into c4a / c128a entries, indexer scores, exact
   top-k, shared-K/V softmax attention over gathered entries plus the window,
   the inverse rotary embedding of the output, and the streaming decode step

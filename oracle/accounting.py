@@ -13,6 +13,8 @@ Layouts (widths D = 512 shared-state channels, Di = 128 indexer channels):
 * bf16: c4a entry = (D + Di) * 2 bytes; c128a entry = D * 2 bytes.
 * quantised: c4a entry = D fp8 codes + 4-byte row scale + Di/2 fp4 bytes +
   Di/16 E4M3 group scales; c128a entry = D fp8 codes + 4-byte row scale.
+* mixed ([P1] mixed-precision bullet): the R rotary channels in bf16, the other
+  D - R in fp8 with a 4-byte row scale.
 """
 from __future__ import annotations
 
@@ -48,3 +50,8 @@ def v4_sequence_bytes(tokens: int, n_c4a: int = 30, n_c128a: int = 31, D: int = 
     total = n_c4a * layer_bytes(C4A, tokens, D, Di, quantised) + n_c128a * layer_bytes(C128A, tokens, D, Di, quantised)
     row = (D + 4) if quantised else 2 * D
     return total + (n_c4a + n_c128a) * window * row
+
+
+def mixed_attention_row_bytes(D: int = 512, R: int = 64) -> int:
+    """An attention row with bf16 rotary channels and fp8 for the rest."""
+    return (D - R) + 2 * R + 4

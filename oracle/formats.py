@@ -118,6 +118,28 @@ def decode_fp8_rows(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
 
 # --------------------------------------------------------------------- E2M1
 
+def encode_mixed_rows(x: np.ndarray, R: int):
+    """[P1] mixed-precision bullet and quantisation paragraph: the rotary
+    channels (the last R) stay bf16, the other channels are fp8 with one scale
+    per row (token), as encode_fp8_rows over those channels alone.
+    Returns (codes uint8 [..., D-R], rotary bf16 bits uint16 [..., R], scale fp32 [...])."""
+    x = np.asarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    codes, scale = encode_fp8_rows(x[..., : D - R])
+    return codes, f32_to_bf16(x[..., D - R:]), scale
+
+
+def decode_mixed_rows(codes: np.ndarray, rope_bits: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Rows back to float64: fp8 part value(code) * scale, then the bf16 rotary part."""
+    return np.concatenate([decode_fp8_rows(codes, scale), bf16_to_f64(rope_bits)], axis=-1)
+
+
+def mixed_row_bytes(codes: np.ndarray, rope_bits: np.ndarray) -> np.ndarray:
+    """The stored row: the D-R codes, then the R bf16 channels little-endian."""
+    rb = np.ascontiguousarray(rope_bits, dtype="<u2").view(np.uint8)
+    return np.concatenate([np.asarray(codes, dtype=np.uint8), rb.reshape(rope_bits.shape[:-1] + (-1,))], axis=-1)
+
+
 def _e2m1_value(code: int) -> float:
     s = (code >> 3) & 1
     e = (code >> 1) & 0x3

@@ -525,3 +525,40 @@ def test_ring_holds_the_newest_states_and_serves_as_the_window():
     a = M.attend(Q, cache, ids, ring, 0.3, 2, 10000.0, T - 1)
     b = M.attend(Q, cache, ids, S[T - W:], 0.3, 2, 10000.0, T - 1)
     np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------- mixed-precision rows
+
+def test_mixed_rows_keep_rotary_channels_in_bf16():
+    D, R = 512, 64
+    x = (RNG.standard_normal((6, D)) * 3.0).astype(np.float32)
+    x[2, D - R:] *= 1e4                   # huge rotary values do not move the fp8 scale
+    codes, rope, scale = F.encode_mixed_rows(x, R)
+    assert codes.shape == (6, D - R) and rope.shape == (6, R)
+    # rotary part: bf16 round-to-nearest-even, as torch rounds
+    ref_rope = torch.from_numpy(x[:, D - R:]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(rope, ref_rope)
+    # the rest: E4M3 codes with a row scale over those channels only (torch's float8 rounding)
+    s_ref = np.abs(x[:, : D - R]).max(axis=1) / np.float32(448.0)
+    np.testing.assert_array_equal(scale, s_ref.astype(np.float32))
+    q = torch.from_numpy((x[:, : D - R] / scale[:, None]).astype(np.float32)).to(torch.float8_e4m3fn)
+    assert np.array_equal(codes, q.view(torch.uint8).numpy())
+    dec = F.decode_mixed_rows(codes, rope, scale)
+    np.testing.assert_array_equal(dec[:, D - R:], F.bf16_to_f64(rope))
+    # relative error bound of E4M3 (3 mantissa bits) against the row's largest value
+    err = np.abs(dec[:, : D - R] - x[:, : D - R]).max(axis=1) / np.abs(x[:, : D - R]).max(axis=1)
+    assert np.all(err <= 2.0 ** -4 + 1e-7)
+
+
+def test_mixed_row_layout_and_size():
+    codes = np.arange(448, dtype=np.uint8).reshape(1, 448)
+    rope = np.arange(64, dtype=np.uint16).reshape(1, 64) + 0x3F00
+    row = F.mixed_row_bytes(codes, rope)
+    assert row.shape == (1, 576)
+    assert np.array_equal(row[0, :448], codes[0])
+    assert row[0, 448] == 0x00 and row[0, 449] == 0x3F and row[0, 575] == 0x3F and row[0, 574] == 63
+    # [P1] mixed-precision bullet: bf16 rotary + fp8 rest cuts the attention
+    # cache by nearly half again (580 of 1,024 bytes per bf16 row)
+    assert A.mixed_attention_row_bytes() == 580
+    ratio = A.mixed_attention_row_bytes() / (512 * 2)
+    assert 0.5 < ratio < 0.6
