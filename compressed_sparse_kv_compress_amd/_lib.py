@@ -22,7 +22,8 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
-BF16, F32, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
+BF16, F32, FP8_E4M3, FP4_E2M1, FP8_ROPE64 = 0, 1, 2, 3, 4
+MIX_ROPE = 64   # rotary channels a mixed (FP8_ROPE64) cache row keeps in bf16
 C4A, C128A = 0, 1
 KINDS = {"c4a": C4A, "c128a": C128A, C4A: C4A, C128A: C128A}
 
@@ -122,6 +123,30 @@ def _workspace(purpose: str, nbytes: int, device, layout=None) -> torch.Tensor |
 
 # ------------------------------------------------------------------ compress
 
+def _cache_format(cache: torch.Tensor, cache_scale: torch.Tensor | None, B: int, D: int) -> int:
+    """The cache's row format from its dtype and width: bf16 [B, rows, D];
+    fp8 codes uint8 [B, rows, D]; or mixed rows uint8 [B, rows, D + 64] (the
+    D - 64 fp8 codes, then the 64 rotary channels as bf16). Both fp8 forms need
+    cache_scale fp32 [B, rows]."""
+    if cache.dim() != 3 or cache.shape[0] != B:
+        raise ValueError("cache must be [B, rows, D] (or [B, rows, D + 64] uint8 for mixed rows)")
+    if cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        if cache.shape[2] == D:
+            fmt = FP8_E4M3
+        elif cache.shape[2] == D + MIX_ROPE and cache.dtype == torch.uint8:
+            fmt = FP8_ROPE64
+        else:
+            raise ValueError(f"an fp8 cache must be [B, rows, {D}] (codes) or [B, rows, {D + MIX_ROPE}] (mixed rows)")
+        if cache_scale is None or cache_scale.dtype != torch.float32 or tuple(cache_scale.shape) != tuple(cache.shape[:2]):
+            raise ValueError("an fp8 cache needs cache_scale fp32 [B, rows]")
+        _dense(cache_scale, "cache_scale")
+        return fmt
+    if cache.shape[2] != D:
+        raise ValueError("cache must be [B, rows, D]")
+    _bf16_like(cache, "cache")
+    return BF16
+
+
 def compress(kind, S: torch.Tensor, gate: torch.Tensor, cache: torch.Tensor,
              cache_scale: torch.Tensor | None = None, first_entry: int = 0) -> int:
     """Writes the complete entries of the span S [B, T, D] (gate [B, T] fp32)
@@ -134,16 +159,7 @@ def compress(kind, S: torch.Tensor, gate: torch.Tensor, cache: torch.Tensor,
     B, T, D = S.shape
     if gate.dtype != torch.float32 or tuple(gate.shape) != (B, T):
         raise ValueError("gate must be fp32 [B, T]")
-    if cache.dim() != 3 or cache.shape[0] != B or cache.shape[2] != D:
-        raise ValueError("cache must be [B, rows, D]")
-    if cache.dtype == torch.uint8 or cache.dtype == torch.float8_e4m3fn:
-        dt = FP8_E4M3
-        if cache_scale is None or cache_scale.dtype != torch.float32 or tuple(cache_scale.shape) != tuple(cache.shape[:2]):
-            raise ValueError("an fp8 cache needs cache_scale fp32 [B, rows]")
-        _dense(cache_scale, "cache_scale")
-    else:
-        _bf16_like(cache, "cache")
-        dt = BF16
+    dt = _cache_format(cache, cache_scale, B, D)
     _check(_lib_compress(kind, _ptr(S), _ptr(gate), B, T, D, first_entry, dt, _ptr(cache),
                          _ptr(cache_scale), cache.shape[1], _stream(S.device)))
     w, s = (8, 4) if kind == C4A else (128, 128)
@@ -174,16 +190,7 @@ def append(kind, s_new: torch.Tensor, g_new: torch.Tensor, pos: torch.Tensor, ri
     W = ring.shape[1]
     if ring_gate.dtype != torch.float32 or tuple(ring_gate.shape) != (B, W):
         raise ValueError("ring_gate must be fp32 [B, W]")
-    if cache.dim() != 3 or cache.shape[0] != B or cache.shape[2] != D:
-        raise ValueError("cache must be [B, rows, D]")
-    if cache.dtype == torch.uint8 or cache.dtype == torch.float8_e4m3fn:
-        dt = FP8_E4M3
-        if cache_scale is None or cache_scale.dtype != torch.float32 or tuple(cache_scale.shape) != tuple(cache.shape[:2]):
-            raise ValueError("an fp8 cache needs cache_scale fp32 [B, rows]")
-        _dense(cache_scale, "cache_scale")
-    else:
-        _bf16_like(cache, "cache")
-        dt = BF16
+    dt = _cache_format(cache, cache_scale, B, D)
     for t, n in ((n_entries, "n_entries"), (n_window, "n_window")):
         if t is not None and (t.dtype != torch.int32 or t.numel() != B or not t.is_contiguous()):
             raise ValueError(f"{n} must be contiguous int32 [B]")
@@ -251,15 +258,7 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
     _bf16_like(Q, "Q")
     _dense(Q, "Q"); _dense(cache, "cache")
     B, H, D = Q.shape
-    if cache.dim() != 3 or cache.shape[0] != B or cache.shape[2] != D:
-        raise ValueError("cache must be [B, rows, D]")
-    cache_fp8 = cache.dtype in (torch.uint8, torch.float8_e4m3fn)
-    if cache_fp8:
-        if cache_scale is None or cache_scale.dtype != torch.float32 or tuple(cache_scale.shape) != tuple(cache.shape[:2]):
-            raise ValueError("an fp8 cache needs cache_scale fp32 [B, rows]")
-        _dense(cache_scale, "cache_scale")
-    else:
-        _bf16_like(cache, "cache")
+    cache_dt = _cache_format(cache, cache_scale, B, D)
     k = 0
     if ids is not None:
         if ids.dtype != torch.int32 or ids.dim() != 2 or ids.shape[0] != B or not ids.is_contiguous():
@@ -297,7 +296,7 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
     max_keys = (k if ids is not None else cache.shape[1]) + W
     nbytes = _lib_attend_ws(B, H, D, max_keys, splits)
     ws = _workspace("attend", nbytes, Q.device)
-    _check(_lib_attend(_ptr(Q), B, H, D, FP8_E4M3 if cache_fp8 else BF16, _ptr(cache), _ptr(cache_scale),
+    _check(_lib_attend(_ptr(Q), B, H, D, cache_dt, _ptr(cache), _ptr(cache_scale),
                        cache.shape[1], _ptr(ids), k, _ptr(n_entries), FP8_E4M3 if win_fp8 else BF16,
                        _ptr(window), _ptr(window_scale), W, wstride, _ptr(n_window), rope_dims, rope_base,
                        _ptr(q_pos),

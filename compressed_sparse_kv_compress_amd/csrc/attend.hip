@@ -73,12 +73,14 @@ static __device__ float g_empty_scale = 0.0f;
 // Swizzle of a tile row's 16-byte chunks.
 __device__ __forceinline__ int chunk_swz(int row) { return (row >> 3) & 3; }
 
-template <int D, bool CFP8, bool WFP8>
+// CF: cache row format (kFmtBf16, kFmtFp8 or kFmtMix); WFP8: fp8 window rows.
+template <int D, int CF, bool WFP8>
 struct AttCfg {
-  static constexpr bool kDma = D == 512 && !CFP8 && !WFP8;      // bf16 rows by DMA
-  static constexpr bool kDmaFp8 = D == 512 && CFP8 && WFP8;     // fp8 rows by DMA + widening pass
-  static constexpr bool kReg = !kDma && !kDmaFp8;               // register-staged fill
-  static constexpr bool kScaled = CFP8 || WFP8;                 // rows carry a value scale
+  static constexpr bool kDma = D == 512 && CF == kFmtBf16 && !WFP8;   // bf16 rows by DMA
+  static constexpr bool kDmaFp8 = D == 512 && CF == kFmtFp8 && WFP8;  // fp8 rows by DMA + widening pass
+  static constexpr bool kReg = !kDma && !kDmaFp8;                     // register-staged fill
+  // rows carry a value scale (mixed rows are widened with theirs applied)
+  static constexpr bool kScaled = CF == kFmtFp8 || WFP8;
   static constexpr int KROW = D + 16;                           // bf16 per tile row
   static constexpr int kTileElems = kTK * KROW;                 // bf16 per tile
   // fp8 staging tile: the rows' codes, then their 32 scales (one DMA target per slot)
@@ -134,11 +136,11 @@ struct RowSrc {
   int64_t cache_rows;
 };
 
-template <int D, bool CFP8, bool WFP8>
+template <int D, int CF, bool WFP8>
 __device__ __forceinline__ RowSrc row_src(const AttendArgs& a, int64_t b) {
   RowSrc r;
-  r.cache = reinterpret_cast<const uint8_t*>(a.cache) + b * a.cache_rows * D * (CFP8 ? 1 : 2);
-  r.cache_scale = CFP8 ? a.cache_scale + b * a.cache_rows : nullptr;
+  r.cache = reinterpret_cast<const uint8_t*>(a.cache) + b * a.cache_rows * row_bytes<D, CF>();
+  r.cache_scale = CF != kFmtBf16 ? a.cache_scale + b * a.cache_rows : nullptr;
   r.window = reinterpret_cast<const uint8_t*>(a.window) + b * a.win_bstride * D * (WFP8 ? 1 : 2);
   r.window_scale = WFP8 ? a.window_scale + b * a.win_bstride : nullptr;
   r.cache_rows = a.cache_rows;
@@ -147,7 +149,7 @@ __device__ __forceinline__ RowSrc row_src(const AttendArgs& a, int64_t b) {
 
 // The row a slot reads: pointer (nullptr for an empty slot) and fp8 scale
 // pointer (nullptr for bf16). Sparse ids come from the split's LDS copy.
-template <int D, bool CFP8, bool WFP8>
+template <int D, int CF, bool WFP8>
 __device__ __forceinline__ void slot_source(const RowSrc& rs, int64_t slot, int64_t lo, int64_t n_sel,
                                             int64_t n_keys, bool dense, const int32_t* ids_l,
                                             const uint8_t*& ptr, const float*& scale) {
@@ -159,8 +161,7 @@ __device__ __forceinline__ void slot_source(const RowSrc& rs, int64_t slot, int6
   if (in_cache && (id < 0 || id >= rs.cache_rows)) return;
   const uint8_t* base = in_cache ? rs.cache : rs.window;
   const float* sbase = in_cache ? rs.cache_scale : rs.window_scale;
-  const bool fp8 = in_cache ? CFP8 : WFP8;
-  ptr = base + id * D * (fp8 ? 1 : 2);
+  ptr = base + id * (in_cache ? row_bytes<D, CF>() : (WFP8 ? D : 2 * D));
   scale = sbase ? sbase + id : nullptr;
 }
 
@@ -169,12 +170,12 @@ __device__ __forceinline__ void slot_source(const RowSrc& rs, int64_t slot, int6
 // (DMA and register paths), `stage` the fp8 staging buffer; per slot, `pb` is
 // the logit bias (0, or -inf for an empty slot) and `vs` the row's value scale
 // (fp8 rows: the row scale; bf16 rows: 1; empty slots: 0).
-template <int D, bool CFP8, bool WFP8>
+template <int D, int CF, bool WFP8>
 __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, int64_t lo,
                                            int64_t n_sel, int64_t n_keys, bool dense, const int32_t* ids_l,
                                            uint16_t* tile, uint8_t* stage, float* pb, float* vs, int wave,
                                            int lane) {
-  using C = AttCfg<D, CFP8, WFP8>;
+  using C = AttCfg<D, CF, WFP8>;
   if constexpr (C::kReg) {
     // thread (kb, cb): rows 8kb .. 8kb+7, logical chunk cb (8 channels)
     const int t = threadIdx.x, kb = t >> 6, cb = t & 63;
@@ -185,13 +186,22 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
     for (int i = 0; i < 8; ++i) {
       const uint8_t* p;
       const float* sp;
-      slot_source<D, CFP8, WFP8>(rsrc, tile0 + 8 * kb + i, lo, n_sel, n_keys, dense, ids_l, p, sp);
+      slot_source<D, CF, WFP8>(rsrc, tile0 + 8 * kb + i, lo, n_sel, n_keys, dense, ids_l, p, sp);
+      // a cache row of the mixed format: codes widened with the row scale applied,
+      // the rotary channels copied (value scale 1)
+      const bool mix = CF == kFmtMix && tile0 + 8 * kb + i < n_sel;
       r[i] = make_uint4(0, 0, 0, 0);
-      sc[i] = p ? (sp ? *sp : 1.0f) : 0.0f;
+      sc[i] = p ? (sp && !mix ? *sp : 1.0f) : 0.0f;
       bias[i] = p ? 0.0f : -INFINITY;
       if (p && active_c) {
-        if (sp) r[i] = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(p + cb * 8));
-        else r[i] = *reinterpret_cast<const uint4*>(p + cb * 16);
+        if (mix) {
+          if (cb * 8 < D - kMixRope) r[i] = fp8x8_to_bf16x8_scaled(*reinterpret_cast<const uint2*>(p + cb * 8), *sp);
+          else r[i] = *reinterpret_cast<const uint4*>(p + (D - kMixRope) + 2 * (cb * 8 - (D - kMixRope)));
+        } else if (sp) {
+          r[i] = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(p + cb * 8));
+        } else {
+          r[i] = *reinterpret_cast<const uint4*>(p + cb * 16);
+        }
       }
     }
     if (active_c) {
@@ -246,7 +256,7 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
     }
     const uint8_t* p = nullptr;
     const float* sp = nullptr;
-    if (lane < 8) slot_source<D, CFP8, WFP8>(rsrc, tile0 + 8 * wave + lane, lo, n_sel, n_keys, dense, ids_l, p, sp);
+    if (lane < 8) slot_source<D, CF, WFP8>(rsrc, tile0 + 8 * wave + lane, lo, n_sel, n_keys, dense, ids_l, p, sp);
     const uint64_t src_l = reinterpret_cast<uint64_t>(p ? p : g_zero_row);
     if (lane < 8) pb[8 * wave + lane] = p ? 0.0f : -INFINITY;
     if constexpr (C::kDma) {
@@ -301,10 +311,10 @@ __device__ __forceinline__ void widen_tile(const uint8_t* stage, uint16_t* tile)
   }
 }
 
-template <int D, bool CFP8, bool WFP8>
+template <int D, int CF, bool WFP8>
 __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int splits, int64_t keys_per_split,
                                                           uint16_t* __restrict__ ws_acc, float* __restrict__ ws_ml) {
-  using C = AttCfg<D, CFP8, WFP8>;
+  using C = AttCfg<D, CF, WFP8>;
   constexpr int KS = D / 32;          // k-steps of QK^T
   constexpr int CTW = D / 64;         // 16-channel tiles of O^T per wave (a quarter of D)
   constexpr int KROW = C::KROW;
@@ -392,7 +402,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   // P^T B operand of head tile ht: lane (l16, g) reads row 16 ht + l16, slots 8g .. 8g+7
   const int p_off = l16 * kTK + 8 * g;
 
-  const RowSrc rsrc = row_src<D, CFP8, WFP8>(a, b);
+  const RowSrc rsrc = row_src<D, CF, WFP8>(a, b);
 
   // ring slot S: bf16 tile, staging tile, slot scales
   auto tile_of = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
@@ -414,7 +424,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
     else return S == 0 ? vs0 : (S == 1 ? vs1 : (S == 2 ? vs2 : vs3));
   };
   auto issue = [&](auto sc, int i) __attribute__((always_inline)) {
-    issue_tile<D, CFP8, WFP8>(rsrc, lo + (int64_t)i * kTK, lo, n_sel, n_keys, dense, ids_l, tile_of(sc),
+    issue_tile<D, CF, WFP8>(rsrc, lo + (int64_t)i * kTK, lo, n_sel, n_keys, dense, ids_l, tile_of(sc),
                               stage_of(sc), pb_of(sc), vs_of(sc), wave, lane);
   };
   // Softmax state of head h: probabilities are exp2(logit - m_ref) with m_ref
@@ -1000,10 +1010,10 @@ bool plan_attend(int64_t B, int H, int D, int64_t max_keys, bool sparse, int spl
   return true;
 }
 
-template <int D, bool CFP8, bool WFP8>
+template <int D, int CF, bool WFP8>
 static hipError_t launch_attend_t(const AttendPlan& p, const AttendArgs& a, void* workspace,
                                   hipStream_t stream) {
-  auto kern = k_attend<D, CFP8, WFP8>;
+  auto kern = k_attend<D, CF, WFP8>;
   uint16_t* ws_acc = reinterpret_cast<uint16_t*>(workspace);
   float* ws_ml = p.splits > 1 ? reinterpret_cast<float*>(ws_acc + (size_t)a.B * p.splits * kHMax * D) : nullptr;
   dim3 grid((unsigned)p.splits, (unsigned)a.B);
@@ -1018,7 +1028,7 @@ static hipError_t launch_attend_t(const AttendPlan& p, const AttendArgs& a, void
 
 hipError_t launch_attend(const AttendPlan& p, const AttendArgs& a, void* workspace,
                          hipStream_t stream) {
-  if (p.head_split && a.ids && a.D == 512 && !a.cache_fp8 && !a.win_fp8 && a.H % 16 == 0 &&
+  if (p.head_split && a.ids && a.D == 512 && !a.cache_fp8 && !a.cache_mix && !a.win_fp8 && a.H % 16 == 0 &&
       a.k <= kMaxSplitIds) {
     const int n_hg = a.H / 16;
     const unsigned n_wg = (unsigned)(8 * ((a.B + 7) / 8) * n_hg);
@@ -1026,15 +1036,17 @@ hipError_t launch_attend(const AttendPlan& p, const AttendArgs& a, void* workspa
     return hipGetLastError();
   }
   if (a.D == 512) {
-    if (a.cache_fp8) return a.win_fp8 ? launch_attend_t<512, true, true>(p, a, workspace, stream)
-                                      : launch_attend_t<512, true, false>(p, a, workspace, stream);
-    return a.win_fp8 ? launch_attend_t<512, false, true>(p, a, workspace, stream)
-                     : launch_attend_t<512, false, false>(p, a, workspace, stream);
+    if (a.cache_mix) return a.win_fp8 ? launch_attend_t<512, kFmtMix, true>(p, a, workspace, stream)
+                                      : launch_attend_t<512, kFmtMix, false>(p, a, workspace, stream);
+    if (a.cache_fp8) return a.win_fp8 ? launch_attend_t<512, kFmtFp8, true>(p, a, workspace, stream)
+                                      : launch_attend_t<512, kFmtFp8, false>(p, a, workspace, stream);
+    return a.win_fp8 ? launch_attend_t<512, kFmtBf16, true>(p, a, workspace, stream)
+                     : launch_attend_t<512, kFmtBf16, false>(p, a, workspace, stream);
   }
-  if (a.cache_fp8) return a.win_fp8 ? launch_attend_t<128, true, true>(p, a, workspace, stream)
-                                    : launch_attend_t<128, true, false>(p, a, workspace, stream);
-  return a.win_fp8 ? launch_attend_t<128, false, true>(p, a, workspace, stream)
-                   : launch_attend_t<128, false, false>(p, a, workspace, stream);
+  if (a.cache_fp8) return a.win_fp8 ? launch_attend_t<128, kFmtFp8, true>(p, a, workspace, stream)
+                                    : launch_attend_t<128, kFmtFp8, false>(p, a, workspace, stream);
+  return a.win_fp8 ? launch_attend_t<128, kFmtBf16, true>(p, a, workspace, stream)
+                   : launch_attend_t<128, kFmtBf16, false>(p, a, workspace, stream);
 }
 
 }  // namespace cskv

@@ -41,13 +41,41 @@ __device__ __forceinline__ void load_row(const uint16_t* row, int lane, RowSlice
   }
 }
 
-// Writes one finished entry row held as CPL fp32 values per lane: bf16 (RNE)
-// or fp8 codes + one fp32 row scale (amax / 448 over the whole row).
-template <int D, bool FP8>
+// Writes one finished entry row held as CPL fp32 values per lane: bf16 (RNE);
+// or fp8 codes + one fp32 row scale (amax / 448 over the whole row); or a
+// mixed row: the channels below D-64 as fp8 codes with a row scale over them
+// alone, then the 64 rotary channels as bf16 (RNE).
+template <int D, int FMT>
 __device__ __forceinline__ void store_entry(const float* acc, int lane, void* cache_row,
                                             float* scale_slot) {
   constexpr int CPL = D / kWave;
-  if constexpr (!FP8) {
+  if constexpr (FMT == kFmtMix) {
+    static_assert(D == 512, "mixed rows: D = 512");
+    const bool rope = lane * CPL >= D - kMixRope;          // lanes 56 .. 63
+    float amax = 0.0f;
+    if (!rope) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) amax = fmaxf(amax, fabsf(acc[i]));
+    }
+    amax = wave_max(amax);
+    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    uint8_t* row = reinterpret_cast<uint8_t*>(cache_row);
+    if (!rope) {
+      uint32_t c[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) c[i] = f32_to_e4m3(acc[i] / scale);
+      uint2 q;
+      q.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      q.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+      *reinterpret_cast<uint2*>(row + lane * CPL) = q;
+    } else {
+      uint4 q;
+      q.x = pack_bf16x2(acc[0], acc[1]); q.y = pack_bf16x2(acc[2], acc[3]);
+      q.z = pack_bf16x2(acc[4], acc[5]); q.w = pack_bf16x2(acc[6], acc[7]);
+      *reinterpret_cast<uint4*>(row + (D - kMixRope) + 2 * (lane * CPL - (D - kMixRope))) = q;
+    }
+    if (lane == 0) *scale_slot = scale;
+  } else if constexpr (FMT == kFmtBf16) {
     uint16_t* out = reinterpret_cast<uint16_t*>(cache_row) + lane * CPL;
     if constexpr (CPL == 8) {
       uint4 q;
@@ -57,7 +85,7 @@ __device__ __forceinline__ void store_entry(const float* acc, int lane, void* ca
     } else {
       *reinterpret_cast<uint32_t*>(out) = pack_bf16x2(acc[0], acc[1]);
     }
-  } else {
+  } else {   // fp8
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) amax = fmaxf(amax, fabsf(acc[i]));
@@ -113,7 +141,7 @@ __device__ __forceinline__ void fold_c4a(const RowSlice<D>* lo, const RowSlice<D
 constexpr int kC4aRun = 16;
 constexpr int kCompressThreads = 256;
 
-template <int D, bool FP8>
+template <int D, int FMT>
 __global__ __launch_bounds__(kCompressThreads) void k_compress_c4a(
     const uint16_t* __restrict__ S, const float* __restrict__ gate, int64_t T, int64_t n_entries,
     int64_t first_entry, void* __restrict__ cache, float* __restrict__ cache_scale,
@@ -127,9 +155,9 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress_c4a(
 
   const uint16_t* Sb = S + b * T * D;
   const float* gb = gate + b * T;
-  constexpr int ESZ = FP8 ? 1 : 2;
-  uint8_t* cb = reinterpret_cast<uint8_t*>(cache) + (b * cache_rows + first_entry) * (int64_t)D * ESZ;
-  float* sb = FP8 ? cache_scale + b * cache_rows + first_entry : nullptr;
+  constexpr int RB = row_bytes<D, FMT>();
+  uint8_t* cb = reinterpret_cast<uint8_t*>(cache) + (b * cache_rows + first_entry) * (int64_t)RB;
+  float* sb = FMT != kFmtBf16 ? cache_scale + b * cache_rows + first_entry : nullptr;
 
   RowSlice<D> prev[4], cur[4];
 #pragma unroll
@@ -143,7 +171,7 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress_c4a(
     for (int j = 0; j < 8; ++j) g[j] = gb[4 * c + j];
     float acc[RowSlice<D>::CPL];
     fold_c4a<D>(prev, cur, g, acc);
-    store_entry<D, FP8>(acc, lane, cb + c * (int64_t)D * ESZ, FP8 ? sb + c : nullptr);
+    store_entry<D, FMT>(acc, lane, cb + c * (int64_t)RB, FMT != kFmtBf16 ? sb + c : nullptr);
 #pragma unroll
     for (int j = 0; j < 4; ++j) prev[j] = cur[j];
   }
@@ -191,7 +219,7 @@ __device__ __forceinline__ void fold_c128a(RowAt row_at, GateAt gate_at, float (
 }
 
 // One workgroup per entry.
-template <int D, bool FP8>
+template <int D, int FMT>
 __global__ __launch_bounds__(kCompressThreads) void k_compress_c128a(
     const uint16_t* __restrict__ S, const float* __restrict__ gate, int64_t T, int64_t n_entries,
     int64_t first_entry, void* __restrict__ cache, float* __restrict__ cache_scale,
@@ -208,10 +236,9 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress_c128a(
   float acc[CPL];
   fold_c128a<D>([&](int j) { return Sw + (int64_t)j * D; }, [&](int j) { return gw[j]; }, part, acc);
   if (wave != 0) return;
-  constexpr int ESZ = FP8 ? 1 : 2;
   const int64_t row = b * cache_rows + first_entry + c;
-  store_entry<D, FP8>(acc, lane, reinterpret_cast<uint8_t*>(cache) + row * (int64_t)D * ESZ,
-                      FP8 ? cache_scale + row : nullptr);
+  store_entry<D, FMT>(acc, lane, reinterpret_cast<uint8_t*>(cache) + row * (int64_t)row_bytes<D, FMT>(),
+                      FMT != kFmtBf16 ? cache_scale + row : nullptr);
 }
 
 // ---------------------------------------------------------------- append
@@ -241,7 +268,7 @@ __device__ __forceinline__ void append_counts(int64_t n, int64_t p, int W, int64
 
 constexpr int kAppendC4aSeqs = kCompressThreads / kWave;   // c4a: one wave per sequence
 
-template <int D, bool FP8>
+template <int D, int FMT>
 __global__ __launch_bounds__(kCompressThreads) void k_append_c4a(
     const uint16_t* __restrict__ s_new, const float* __restrict__ g_new, const int64_t* __restrict__ pos,
     int64_t B, uint16_t* __restrict__ ring, float* __restrict__ ring_gate, int W, void* __restrict__ cache,
@@ -277,13 +304,12 @@ __global__ __launch_bounds__(kCompressThreads) void k_append_c4a(
   g[7] = g_new[b];
   float acc[RowSlice<D>::CPL];
   fold_c4a<D>(r, r + 4, g, acc);
-  constexpr int ESZ = FP8 ? 1 : 2;
   const int64_t row = b * cache_rows + c;
-  store_entry<D, FP8>(acc, lane, reinterpret_cast<uint8_t*>(cache) + row * (int64_t)D * ESZ,
-                      FP8 ? cache_scale + row : nullptr);
+  store_entry<D, FMT>(acc, lane, reinterpret_cast<uint8_t*>(cache) + row * (int64_t)row_bytes<D, FMT>(),
+                      FMT != kFmtBf16 ? cache_scale + row : nullptr);
 }
 
-template <int D, bool FP8>
+template <int D, int FMT>
 __global__ __launch_bounds__(kCompressThreads) void k_append_c128a(
     const uint16_t* __restrict__ s_new, const float* __restrict__ g_new, const int64_t* __restrict__ pos,
     uint16_t* __restrict__ ring, float* __restrict__ ring_gate, int W, void* __restrict__ cache,
@@ -318,66 +344,65 @@ __global__ __launch_bounds__(kCompressThreads) void k_append_c128a(
   fold_c128a<D>([&](int j) { return j == 127 ? snew : rb + slot_of(j) * D; },
                 [&](int j) { return j == 127 ? gn : gb[slot_of(j)]; }, part, acc);
   if (wave != 0) return;
-  constexpr int ESZ = FP8 ? 1 : 2;
   const int64_t row = b * cache_rows + c;
-  store_entry<D, FP8>(acc, lane, reinterpret_cast<uint8_t*>(cache) + row * (int64_t)D * ESZ,
-                      FP8 ? cache_scale + row : nullptr);
+  store_entry<D, FMT>(acc, lane, reinterpret_cast<uint8_t*>(cache) + row * (int64_t)row_bytes<D, FMT>(),
+                      FMT != kFmtBf16 ? cache_scale + row : nullptr);
 }
 
 // ---------------------------------------------------------------- launch
 
-template <int D, bool FP8>
+template <int D, int FMT>
 static hipError_t launch_compress_t(int kind, const uint16_t* S, const float* gate, int64_t B,
                                     int64_t T, int64_t n, int64_t first_entry, void* cache,
                                     float* cache_scale, int64_t cache_rows, hipStream_t stream) {
   if (kind == 0) {
     const int64_t per_block = (int64_t)kC4aRun * (kCompressThreads / kWave);
     dim3 grid((unsigned)((n + per_block - 1) / per_block), (unsigned)B);
-    hipLaunchKernelGGL((k_compress_c4a<D, FP8>), grid, dim3(kCompressThreads), 0, stream, S, gate,
+    hipLaunchKernelGGL((k_compress_c4a<D, FMT>), grid, dim3(kCompressThreads), 0, stream, S, gate,
                        T, n, first_entry, cache, cache_scale, cache_rows);
   } else {
     dim3 grid((unsigned)n, (unsigned)B);
-    hipLaunchKernelGGL((k_compress_c128a<D, FP8>), grid, dim3(kCompressThreads), 0, stream, S,
+    hipLaunchKernelGGL((k_compress_c128a<D, FMT>), grid, dim3(kCompressThreads), 0, stream, S,
                        gate, T, n, first_entry, cache, cache_scale, cache_rows);
   }
   return hipGetLastError();
 }
 
-template <int D, bool FP8>
+template <int D, int FMT>
 static hipError_t launch_append_t(int kind, const uint16_t* s_new, const float* g_new, const int64_t* pos,
                                   int64_t B, uint16_t* ring, float* ring_gate, int W, void* cache,
                                   float* cache_scale, int64_t cache_rows, int32_t* n_entries,
                                   int32_t* n_window, hipStream_t stream) {
   if (kind == 0) {
     dim3 grid((unsigned)((B + kAppendC4aSeqs - 1) / kAppendC4aSeqs));
-    hipLaunchKernelGGL((k_append_c4a<D, FP8>), grid, dim3(kCompressThreads), 0, stream, s_new, g_new, pos, B,
+    hipLaunchKernelGGL((k_append_c4a<D, FMT>), grid, dim3(kCompressThreads), 0, stream, s_new, g_new, pos, B,
                        ring, ring_gate, W, cache, cache_scale, cache_rows, n_entries, n_window);
   } else {
-    hipLaunchKernelGGL((k_append_c128a<D, FP8>), dim3((unsigned)B), dim3(kCompressThreads), 0, stream, s_new,
+    hipLaunchKernelGGL((k_append_c128a<D, FMT>), dim3((unsigned)B), dim3(kCompressThreads), 0, stream, s_new,
                        g_new, pos, ring, ring_gate, W, cache, cache_scale, cache_rows, n_entries, n_window);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_append(int kind, const uint16_t* s_new, const float* g_new, const int64_t* pos, int64_t B,
-                         int D, uint16_t* ring, float* ring_gate, int W, bool fp8, void* cache,
+                         int D, uint16_t* ring, float* ring_gate, int W, int fmt, void* cache,
                          float* cache_scale, int64_t cache_rows, int32_t* n_entries, int32_t* n_window,
                          hipStream_t stream) {
-  if (D == 512)
-    return fp8 ? launch_append_t<512, true>(kind, s_new, g_new, pos, B, ring, ring_gate, W, cache, cache_scale, cache_rows, n_entries, n_window, stream)
-               : launch_append_t<512, false>(kind, s_new, g_new, pos, B, ring, ring_gate, W, cache, cache_scale, cache_rows, n_entries, n_window, stream);
-  return fp8 ? launch_append_t<128, true>(kind, s_new, g_new, pos, B, ring, ring_gate, W, cache, cache_scale, cache_rows, n_entries, n_window, stream)
-             : launch_append_t<128, false>(kind, s_new, g_new, pos, B, ring, ring_gate, W, cache, cache_scale, cache_rows, n_entries, n_window, stream);
+#define CSKV_APPEND(DD, FF) launch_append_t<DD, FF>(kind, s_new, g_new, pos, B, ring, ring_gate, W, cache, \
+                                                   cache_scale, cache_rows, n_entries, n_window, stream)
+  if (D == 512) return fmt == kFmtMix ? CSKV_APPEND(512, kFmtMix) : (fmt == kFmtFp8 ? CSKV_APPEND(512, kFmtFp8) : CSKV_APPEND(512, kFmtBf16));
+  return fmt == kFmtFp8 ? CSKV_APPEND(128, kFmtFp8) : CSKV_APPEND(128, kFmtBf16);
+#undef CSKV_APPEND
 }
 
 hipError_t launch_compress(int kind, const uint16_t* S, const float* gate, int64_t B, int64_t T,
-                           int D, int64_t n, int64_t first_entry, bool fp8, void* cache,
+                           int D, int64_t n, int64_t first_entry, int fmt, void* cache,
                            float* cache_scale, int64_t cache_rows, hipStream_t stream) {
-  if (D == 512)
-    return fp8 ? launch_compress_t<512, true>(kind, S, gate, B, T, n, first_entry, cache, cache_scale, cache_rows, stream)
-               : launch_compress_t<512, false>(kind, S, gate, B, T, n, first_entry, cache, cache_scale, cache_rows, stream);
-  return fp8 ? launch_compress_t<128, true>(kind, S, gate, B, T, n, first_entry, cache, cache_scale, cache_rows, stream)
-             : launch_compress_t<128, false>(kind, S, gate, B, T, n, first_entry, cache, cache_scale, cache_rows, stream);
+#define CSKV_COMPRESS(DD, FF) launch_compress_t<DD, FF>(kind, S, gate, B, T, n, first_entry, cache, cache_scale, \
+                                                       cache_rows, stream)
+  if (D == 512) return fmt == kFmtMix ? CSKV_COMPRESS(512, kFmtMix) : (fmt == kFmtFp8 ? CSKV_COMPRESS(512, kFmtFp8) : CSKV_COMPRESS(512, kFmtBf16));
+  return fmt == kFmtFp8 ? CSKV_COMPRESS(128, kFmtFp8) : CSKV_COMPRESS(128, kFmtBf16);
+#undef CSKV_COMPRESS
 }
 
 }  // namespace cskv

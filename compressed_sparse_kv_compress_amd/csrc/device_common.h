@@ -117,6 +117,27 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 c) {
                     fp8x2_to_bf16x2<true>(c.y));
 }
 
+// Cache row formats shared by the compressor and the attention kernels.
+constexpr int kFmtBf16 = 0;   // D bf16 channels
+constexpr int kFmtFp8 = 1;    // D E4M3 codes + one fp32 scale per row (separate array)
+constexpr int kFmtMix = 2;    // D-64 E4M3 codes, then the 64 rotary channels in bf16; fp32 row scale of the codes
+constexpr int kMixRope = 64;  // rotary channels a mixed row keeps in bf16
+template <int D, int FMT>
+constexpr int row_bytes() { return FMT == kFmtBf16 ? 2 * D : (FMT == kFmtFp8 ? D : D - kMixRope + 2 * kMixRope); }
+
+// 8 E4M3 codes times the row scale, rounded to bf16 (mixed rows enter the
+// tile already scaled, so their value scale is 1).
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8_scaled(uint2 c, float s) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = e4m3_to_f32((c.x >> (8 * i)) & 0xFFu) * s;
+    v[4 + i] = e4m3_to_f32((c.y >> (8 * i)) & 0xFFu) * s;
+  }
+  return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7]));
+}
+
 // ---------------------------------------------------------------- streaming loads
 // Data read exactly once (indexer keys, cache rows) is loaded non-temporally so
 // that it does not displace reusable lines from the caches.

@@ -11,10 +11,10 @@ namespace cskv {
 
 // ---- compress.hip
 hipError_t launch_compress(int kind, const uint16_t* S, const float* gate, int64_t B, int64_t T,
-                           int D, int64_t n, int64_t first_entry, bool fp8, void* cache,
+                           int D, int64_t n, int64_t first_entry, int fmt, void* cache,
                            float* cache_scale, int64_t cache_rows, hipStream_t stream);
 hipError_t launch_append(int kind, const uint16_t* s_new, const float* g_new, const int64_t* pos, int64_t B,
-                         int D, uint16_t* ring, float* ring_gate, int W, bool fp8, void* cache,
+                         int D, uint16_t* ring, float* ring_gate, int W, int fmt, void* cache,
                          float* cache_scale, int64_t cache_rows, int32_t* n_entries, int32_t* n_window,
                          hipStream_t stream);
 
@@ -52,6 +52,7 @@ struct AttendArgs {
   int64_t B;
   int H, D;
   bool cache_fp8;
+  bool cache_mix;            // mixed rows (kFmtMix); cache_fp8 is false then
   const void* cache;
   const float* cache_scale;
   int64_t cache_rows;

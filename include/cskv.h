@@ -47,6 +47,11 @@ typedef int32_t cskv_status;
 #define CSKV_FP8_E4M3  2  /* 1 byte per channel (OCP E4M3, max 448) + one fp32 scale per row */
 #define CSKV_FP4_E2M1  3  /* 2 channels per byte (channel 2j in the low nibble) + one E4M3
                              scale byte per 16 channels */
+#define CSKV_FP8_ROPE64 4 /* mixed attention-cache row ([P1] mixed-precision bullet and
+                             quantisation paragraph: bf16 kept for the rotary channels, fp8 for
+                             the rest): D-64 E4M3 codes, then the last 64 channels as bf16, i.e.
+                             D+64 bytes per row (576 for D = 512), plus one fp32 scale per row
+                             for the codes (max |x| over the D-64 channels / 448); D = 512 only */
 
 /* Compression kinds ([P1] paragraphs "c4a" and "c128a"; [P2] Step 4). */
 #define CSKV_C4A    0  /* an entry folds 8 consecutive states; entries start every 4 states */
@@ -74,7 +79,8 @@ int32_t cskv_version(void);
  *   gate      [B, T] fp32      one gate logit per state
  *   D         128 or 512
  *   cache     [B, cache_rows, D] bf16, or fp8 codes [B, cache_rows, D] plus
- *             cache_scale [B, cache_rows] fp32 (cache_dtype CSKV_FP8_E4M3)
+ *             cache_scale [B, cache_rows] fp32 (cache_dtype CSKV_FP8_E4M3), or mixed
+ *             rows [B, cache_rows, D+64] bytes plus cache_scale (CSKV_FP8_ROPE64)
  *
  * Writes rows first_entry .. first_entry+n-1 of every sequence's cache, where
  * n = floor((T-w)/s)+1 complete windows (n = 0 when T < w: nothing is written).
@@ -175,7 +181,8 @@ cskv_status cskv_index_topk(const void* q_idx, int32_t key_dtype, const void* k_
  * fp64). A sequence with no key rows gets O = 0.
  *
  *   Q            [B, H, D] bf16;  1 <= H <= 64;  D 128 or 512
- *   cache        [B, cache_rows, D] bf16, or fp8 codes + cache_scale [B, cache_rows] fp32
+ *   cache        [B, cache_rows, D] bf16, or fp8 codes + cache_scale [B, cache_rows] fp32,
+ *                or mixed rows (CSKV_FP8_ROPE64, D = 512) + cache_scale
  *   ids          [B, k] int32 entry ids (ids < 0 or >= cache_rows are skipped),
  *                or NULL for dense attention over entries 0 .. n_entries[b]-1
  *   n_entries    dense mode only: [B] int32 device counts, or NULL for cache_rows
