@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4a_128k_bf16",
                     choices=["c4a_128k_bf16", "c128a_1m_bf16", "c4a_1m_fp8_fp4", "mixed61_256k_bf16", "tiny_c4a_2k",
-                             "stream_c4a_128k_bf16"])
+                             "stream_c4a_128k_bf16", "c128a_1m_mixed"])
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -154,17 +154,23 @@ class C128aLayer(Workload):
         self.sets = []
         for i in range(n_sets):
             log(f"setup: c128a input set {i + 1}/{n_sets}")
-            cache = torch.empty((B, N, D), dtype=torch.bfloat16, device=self.dev)
+            mixed = c.cache_dtype == "mixed"   # 448 fp8 codes + 64 bf16 rotary channels per row
+            if mixed:
+                cache = torch.empty((B, N, D + cskv.MIX_ROPE), dtype=torch.uint8, device=self.dev)
+                cscale = torch.empty((B, N), dtype=torch.float32, device=self.dev)
+            else:
+                cache = torch.empty((B, N, D), dtype=torch.bfloat16, device=self.dev)
+                cscale = None
             win = torch.empty((B, W, D), dtype=torch.bfloat16, device=self.dev)
             for b in range(B):
                 S = torch.empty((1, L, D), dtype=torch.bfloat16, device=self.dev)
                 g = torch.empty((1, L), dtype=torch.float32, device=self.dev)
                 sd.fill(S, s.KIND_NORMAL_BF16, self.key(i, s.T_S), offset=b * L * D)
                 sd.fill(g, s.KIND_NORMAL_F32, self.key(i, s.T_GATE), offset=b * L)
-                cskv.compress("c128a", S, g, cache[b:b + 1])
+                cskv.compress("c128a", S, g, cache[b:b + 1], None if cscale is None else cscale[b:b + 1])
                 win[b].copy_(S[0, L - W:])
                 del S, g
-            self.sets.append(dict(cache=cache, win=win,
+            self.sets.append(dict(cache=cache, cscale=cscale, win=win,
                                   Q=sd.new((B, H, D), s.KIND_NORMAL_BF16, self.key(i, s.T_Q), device=self.dev),
                                   O=torch.empty((B, H, D), dtype=torch.float32, device=self.dev),
                                   pos=torch.full((B,), c.q_pos, dtype=torch.int64, device=self.dev)))
@@ -172,15 +178,16 @@ class C128aLayer(Workload):
 
     def dominant(self, st):
         c = self.cfg
-        self.cskv.attend(st["Q"], st["cache"], None, st["win"], softmax_scale=c.tau, rope_dims=c.R,
-                         rope_base=c.rope_base, q_pos=st["pos"], out=st["O"], splits=self.args.splits)
+        self.cskv.attend(st["Q"], st["cache"], None, st["win"], cache_scale=st["cscale"], softmax_scale=c.tau,
+                         rope_dims=c.R, rope_base=c.rope_base, q_pos=st["pos"], out=st["O"], splits=self.args.splits)
 
     def rest(self, st):
         pass
 
     def bytes(self):
         c = self.cfg
-        return c.B * ((c.n_entries + c.W) * c.D * 2 + c.H * c.D * 2 + c.H * c.D * 4), 0
+        row = (c.D - 64) + 2 * 64 + 4 if c.cache_dtype == "mixed" else c.D * 2
+        return c.B * (c.n_entries * row + c.W * c.D * 2 + c.H * c.D * 2 + c.H * c.D * 4), 0
 
     def flops(self):
         c = self.cfg
@@ -633,7 +640,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.cache_dtype == "bf16" and cfg.key_dtype == "bf16" else "fp8+fp4 (bf16 MFMA, fp32 accumulate)",
+        "dtype": ("bf16" if cfg.cache_dtype == "bf16" and cfg.key_dtype == "bf16" else
+                  "fp8 + bf16 rotary (bf16 MFMA, fp32 accumulate)" if cfg.cache_dtype == "mixed" else
+                  "fp8+fp4 (bf16 MFMA, fp32 accumulate)"),
         "data": "synthetic (SplitMix64 streams; caches built by the library's compress kernel)" if not stateful
                 else "synthetic (SplitMix64 streams; prefix caches drawn directly, new states compressed in the step)",
         "config": {"workload": cfg.name, "batch": cfg.B, "context": cfg.L, "heads": cfg.H, "D": cfg.D,

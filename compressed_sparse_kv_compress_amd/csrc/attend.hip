@@ -78,14 +78,18 @@ template <int D, int CF, bool WFP8>
 struct AttCfg {
   static constexpr bool kDma = D == 512 && CF == kFmtBf16 && !WFP8;   // bf16 rows by DMA
   static constexpr bool kDmaFp8 = D == 512 && CF == kFmtFp8 && WFP8;  // fp8 rows by DMA + widening pass
-  static constexpr bool kReg = !kDma && !kDmaFp8;                     // register-staged fill
+  // mixed cache rows by DMA into their tile rows as raw bytes + an in-place
+  // widening pass; bf16 window rows by DMA as in the bf16 path
+  static constexpr bool kDmaMix = D == 512 && CF == kFmtMix && !WFP8;
+  static constexpr bool kReg = !kDma && !kDmaFp8 && !kDmaMix;         // register-staged fill
   // rows carry a value scale (mixed rows are widened with theirs applied)
   static constexpr bool kScaled = CF == kFmtFp8 || WFP8;
   static constexpr int KROW = D + 16;                           // bf16 per tile row
   static constexpr int kTileElems = kTK * KROW;                 // bf16 per tile
   // fp8 staging tile: the rows' codes, then their 32 scales (one DMA target per slot)
   static constexpr int kStageBytes = kDmaFp8 ? kTK * D + kTK * 4 : 16;
-  static constexpr int kOpsPerTile = kDma ? 8 : (kDmaFp8 ? 5 : 0);   // DMA instructions per wave
+  // DMA instructions per wave and tile: 8 rows (+ their scales for fp8 / mixed rows)
+  static constexpr int kOpsPerTile = kDma ? 8 : (kDmaFp8 ? 5 : (kDmaMix ? 9 : 0));
 };
 
 // vmcnt(n) with the other counters left alone (n <= 63).
@@ -259,6 +263,32 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
     if (lane < 8) slot_source<D, CF, WFP8>(rsrc, tile0 + 8 * wave + lane, lo, n_sel, n_keys, dense, ids_l, p, sp);
     const uint64_t src_l = reinterpret_cast<uint64_t>(p ? p : g_zero_row);
     if (lane < 8) pb[8 * wave + lane] = p ? 0.0f : -INFINITY;
+    if constexpr (C::kDmaMix) {
+      // row scale of each mixed row (0 for window and empty rows: no widening),
+      // the wave's 8 of them in the 32 pad bytes of its first row (the tile
+      // buffers stay the only DMA targets besides the first dummy one)
+      const bool mix_l = lane < 8 && p && tile0 + 8 * wave + lane < n_sel;
+      if (lane < 8) {
+        const float* s = mix_l ? sp : &g_empty_scale;
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)s,
+                                         (__attribute__((address_space(3))) void*)(tile + 8 * wave * C::KROW + D),
+                                         4, 0, 0);
+      }
+      const uint64_t mix_m = __ballot(mix_l);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 8 * wave + i;
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(lane_u64(src_l, i));
+        // mixed row: its 576 raw bytes land at chunk positions 0..35 (lanes 36..63
+        // read the zero row); bf16 row: swizzled chunks as in the bf16 path
+        const uint8_t* a = ((mix_m >> i) & 1) ? (lane < kMixRowChunks ? src + 16 * lane : g_zero_row + 16 * lane)
+                                              : src + 16 * (lane ^ chunk_swz(row));
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)a,
+                                         (__attribute__((address_space(3))) void*)(tile + row * C::KROW), 16, 0,
+                                         kCachePolicyStream);
+      }
+      return;
+    }
     if constexpr (C::kDma) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -308,6 +338,55 @@ __device__ __forceinline__ void widen_tile(const uint8_t* stage, uint16_t* tile)
     const int ch0 = 8 * part + 2 * j;          // logical chunks ch0, ch0 + 1
     *reinterpret_cast<uint4*>(row + 8 * (ch0 ^ swz)) = fp8x8_to_bf16x8(make_uint2(c[j].x, c[j].y));
     *reinterpret_cast<uint4*>(row + 8 * ((ch0 + 1) ^ swz)) = fp8x8_to_bf16x8(make_uint2(c[j].z, c[j].w));
+  }
+}
+
+// A 16-byte LDS store the compiler does not see as one: it would otherwise
+// wait for every LDS DMA in flight first (it cannot tell the DMA targets from
+// this address). Used only for stores into a tile whose DMA has landed; the
+// next lds_barrier() waits for the store (lgkmcnt(0)).
+__device__ __forceinline__ void lds_store_b128_unordered(void* p, uint4 v) {
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  const uint32_t addr = (uint32_t)reinterpret_cast<uintptr_t>(p);   // LDS offset
+  const u32x4v d = {v.x, v.y, v.z, v.w};
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(d) : "memory");
+}
+
+// Widens the mixed rows of a tile in place (rows whose scale is 0 are bf16
+// already; the scales of rows 8w .. 8w+7 sit in the pad of row 8w): thread t
+// takes row t/8; part p < 7 turns the 64 codes at raw
+// bytes 64p .. 64p+63 into channels 64p .. 64p+63 times the row scale, part 7
+// moves the 64 rotary channels (raw bytes 448 .. 575) to channels 448 .. 511,
+// all in the swizzled chunk layout. The 8 threads of a row are lanes of one
+// wave: their LDS reads are issued before any of their writes.
+template <int D>
+__device__ __forceinline__ void widen_mix_tile(uint16_t* tile) {
+  using C = AttCfg<D, kFmtMix, false>;
+  const int t = threadIdx.x;
+  const int r = t >> 3, part = t & 7;
+  const float sc = reinterpret_cast<const float*>(tile + (r & ~7) * C::KROW + D)[r & 7];
+  uint16_t* row = tile + r * C::KROW;
+  const int swz = chunk_swz(r);
+  // 128 bytes from raw byte 64 part (codes; the upper half unused) or from the
+  // rotary channels' raw bytes, read whatever the row holds
+  const uint4* src = reinterpret_cast<const uint4*>(row + (part < 7 ? 32 * part : (D - kMixRope) / 2));
+  uint4 c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j] = src[j];
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the row's reads are done before its writes
+  if (sc > 0.0f) {
+    if (part < 7) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ch0 = 8 * part + 2 * j;          // logical chunks ch0, ch0 + 1
+        lds_store_b128_unordered(row + 8 * (ch0 ^ swz), fp8x8_to_bf16x8_scaled(make_uint2(c[j].x, c[j].y), sc));
+        lds_store_b128_unordered(row + 8 * ((ch0 + 1) ^ swz), fp8x8_to_bf16x8_scaled(make_uint2(c[j].z, c[j].w), sc));
+      }
+    } else {
+      // rotary channels 448 + 8j .. +7: logical chunk 56 + j
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lds_store_b128_unordered(row + 8 * ((56 + j) ^ swz), c[j]);
+    }
   }
 }
 
@@ -525,6 +604,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
     wait_tile<C::kOpsPerTile>(min(kNStage - 2, n_tiles - 1 - i));
     lds_barrier();   // tile i visible to all waves; ring slot S-1 free again
     if (i + kNStage - 1 < n_tiles) issue(std::integral_constant<int, (S + kNStage - 1) % kNStage>{}, i + kNStage - 1);
+    if constexpr (C::kDmaMix) {
+      widen_mix_tile<D>(tile_of(sc));
+      lds_barrier();
+    }
     if constexpr (C::kDmaFp8) {
       widen_tile<D>(stage_of(sc), tile_of(sc));
       lds_barrier();

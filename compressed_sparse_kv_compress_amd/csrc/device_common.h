@@ -122,20 +122,17 @@ constexpr int kFmtBf16 = 0;   // D bf16 channels
 constexpr int kFmtFp8 = 1;    // D E4M3 codes + one fp32 scale per row (separate array)
 constexpr int kFmtMix = 2;    // D-64 E4M3 codes, then the 64 rotary channels in bf16; fp32 row scale of the codes
 constexpr int kMixRope = 64;  // rotary channels a mixed row keeps in bf16
+constexpr int kMixRowChunks = (512 - kMixRope + 2 * kMixRope) / 16;   // 16-byte chunks of a D = 512 mixed row
 template <int D, int FMT>
 constexpr int row_bytes() { return FMT == kFmtBf16 ? 2 * D : (FMT == kFmtFp8 ? D : D - kMixRope + 2 * kMixRope); }
 
 // 8 E4M3 codes times the row scale, rounded to bf16 (mixed rows enter the
-// tile already scaled, so their value scale is 1).
+// tile already scaled, so their value scale is 1): exact bf16 of each code by
+// the hardware converter, then one fp32 multiply and one rounding.
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8_scaled(uint2 c, float s) {
-  float v[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[i] = e4m3_to_f32((c.x >> (8 * i)) & 0xFFu) * s;
-    v[4 + i] = e4m3_to_f32((c.y >> (8 * i)) & 0xFFu) * s;
-  }
-  return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                    pack_bf16x2(v[6], v[7]));
+  const uint4 v = fp8x8_to_bf16x8(c);
+  return make_uint4(pack_bf16x2(bf16_lo(v.x) * s, bf16_hi(v.x) * s), pack_bf16x2(bf16_lo(v.y) * s, bf16_hi(v.y) * s),
+                    pack_bf16x2(bf16_lo(v.z) * s, bf16_hi(v.z) * s), pack_bf16x2(bf16_lo(v.w) * s, bf16_hi(v.w) * s));
 }
 
 // ---------------------------------------------------------------- streaming loads

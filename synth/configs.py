@@ -35,7 +35,7 @@ class Workload:
     Di: int = 0            # indexer key width (c4a)
     k: int = 0             # top-k (c4a)
     idx_range: int = 0     # indexer values are integers in [-idx_range, idx_range]
-    cache_dtype: str = "bf16"   # "bf16" or "fp8"
+    cache_dtype: str = "bf16"   # "bf16", "fp8", or "mixed" (fp8 codes + bf16 rotary channels)
     key_dtype: str = "bf16"     # indexer keys: "bf16" or "fp4"
     rope_base: float = 10000.0
     layers: int = 1
@@ -117,5 +117,12 @@ STREAM_C4A_128K = Workload(
                 "index_topk over the ragged entry counts and attend over the ring as window",
 )
 
-ALL = [TINY, C4A_128K, C128A_1M, C4A_1M_Q, MIXED_61, STREAM_C4A_128K]
+C128A_1M_MIXED = Workload(
+    name="c128a_1m_mixed", number=7, kind="c128a", B=16, L=1 << 20, D=512, R=64, H=64, W=128,
+    cache_dtype="mixed",
+    description="one c128a layer as c128a_1m_bf16, with the mixed-precision attention cache: 448 fp8 "
+                "channels (per-token scale) + the 64 rotary channels in bf16, 580 B per entry; bf16 window",
+)
+
+ALL = [TINY, C4A_128K, C128A_1M, C4A_1M_Q, MIXED_61, STREAM_C4A_128K, C128A_1M_MIXED]
 BY_NAME = {w.name: w for w in ALL}
