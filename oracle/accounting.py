@@ -15,6 +15,8 @@ Layouts (widths D = 512 shared-state channels, Di = 128 indexer channels):
   Di/16 E4M3 group scales; c128a entry = D fp8 codes + 4-byte row scale.
 * mixed ([P1] mixed-precision bullet): the R rotary channels in bf16, the other
   D - R in fp8 with a 4-byte row scale.
+* fp4 main rows ([P3] "Three mechanisms", third): D/2 E2M1 code bytes plus one
+  E4M3 scale byte per 16 channels.
 """
 from __future__ import annotations
 
@@ -55,3 +57,8 @@ def v4_sequence_bytes(tokens: int, n_c4a: int = 30, n_c128a: int = 31, D: int = 
 def mixed_attention_row_bytes(D: int = 512, R: int = 64) -> int:
     """An attention row with bf16 rotary channels and fp8 for the rest."""
     return (D - R) + 2 * R + 4
+
+
+def fp4_attention_row_bytes(D: int = 512) -> int:
+    """An attention row of E2M1 codes with one E4M3 scale byte per 16 channels."""
+    return D // 2 + D // 16

@@ -140,6 +140,19 @@ def mixed_row_bytes(codes: np.ndarray, rope_bits: np.ndarray) -> np.ndarray:
     return np.concatenate([np.asarray(codes, dtype=np.uint8), rb.reshape(rope_bits.shape[:-1] + (-1,))], axis=-1)
 
 
+def fp4_row_bytes(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """An fp4 attention-cache row as stored ([P3] "Three mechanisms", third: E2M1
+    values with one E4M3 scale per 16 channels, applied to the main KV): the D/2
+    packed code bytes, then the D/16 scale bytes."""
+    return np.concatenate([np.asarray(packed, dtype=np.uint8), np.asarray(scales, dtype=np.uint8)], axis=-1)
+
+
+def decode_fp4_rows(rows: np.ndarray, D: int) -> np.ndarray:
+    """Stored fp4 rows [..., D/2 + D/16] back to float64 [..., D]."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    return decode_fp4_g16(rows[..., : D // 2], rows[..., D // 2: D // 2 + D // 16])
+
+
 def _e2m1_value(code: int) -> float:
     s = (code >> 3) & 1
     e = (code >> 1) & 0x3

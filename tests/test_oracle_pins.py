@@ -562,3 +562,19 @@ def test_mixed_row_layout_and_size():
     assert A.mixed_attention_row_bytes() == 580
     ratio = A.mixed_attention_row_bytes() / (512 * 2)
     assert 0.5 < ratio < 0.6
+
+
+def test_fp4_attention_rows_layout_and_size():
+    x = (RNG.standard_normal((3, 512)) * 2.0).astype(np.float32)
+    packed, sc = F.encode_fp4_g16(x)
+    rows = F.fp4_row_bytes(packed, sc)
+    assert rows.shape == (3, 288)
+    assert np.array_equal(rows[:, :256], packed) and np.array_equal(rows[:, 256:], sc)
+    np.testing.assert_array_equal(F.decode_fp4_rows(rows, 512), F.decode_fp4_g16(packed, sc))
+    # [P3]: 4 bits per value plus an 8-bit scale per 16 values = 4.5 bits per channel,
+    # half of the mixed fp8 row's 9 bits per channel
+    assert A.fp4_attention_row_bytes() * 8 / 512 == 4.5
+    assert A.fp4_attention_row_bytes() * 2 == 576
+    # every decoded value is an E2M1 value times its group's E4M3 scale: exact in bf16
+    dec = F.decode_fp4_rows(rows, 512)
+    assert np.array_equal(F.bf16_to_f64(F.f32_to_bf16(dec.astype(np.float32))), dec)
