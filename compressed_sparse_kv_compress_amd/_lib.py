@@ -125,11 +125,14 @@ def _workspace(purpose: str, nbytes: int, device, layout=None) -> torch.Tensor |
 
 def _cache_format(cache: torch.Tensor, cache_scale: torch.Tensor | None, B: int, D: int) -> int:
     """The cache's row format from its dtype and width: bf16 [B, rows, D];
-    fp8 codes uint8 [B, rows, D]; or mixed rows uint8 [B, rows, D + 64] (the
-    D - 64 fp8 codes, then the 64 rotary channels as bf16). Both fp8 forms need
-    cache_scale fp32 [B, rows]."""
+    fp8 codes uint8 [B, rows, D]; mixed rows uint8 [B, rows, D + 64] (the
+    D - 64 fp8 codes, then the 64 rotary channels as bf16); or fp4 rows uint8
+    [B, rows, D/2 + D/16] (E2M1 codes, then one E4M3 scale byte per 16
+    channels). Both fp8 forms need cache_scale fp32 [B, rows]."""
     if cache.dim() != 3 or cache.shape[0] != B:
-        raise ValueError("cache must be [B, rows, D] (or [B, rows, D + 64] uint8 for mixed rows)")
+        raise ValueError("cache must be [B, rows, D] (or uint8 rows of a quantised format)")
+    if cache.dtype == torch.uint8 and cache.shape[2] == D // 2 + D // 16:
+        return FP4_E2M1
     if cache.dtype in (torch.uint8, torch.float8_e4m3fn):
         if cache.shape[2] == D:
             fmt = FP8_E4M3

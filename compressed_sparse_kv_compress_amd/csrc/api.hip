@@ -32,9 +32,20 @@ cskv_status hip_status(hipError_t e, const char* what) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int row_format(int32_t cache_dtype) {
-  return cache_dtype == CSKV_FP8_ROPE64 ? cskv::kFmtMix
-                                        : (cache_dtype == CSKV_FP8_E4M3 ? cskv::kFmtFp8 : cskv::kFmtBf16);
+  switch (cache_dtype) {
+    case CSKV_FP8_ROPE64: return cskv::kFmtMix;
+    case CSKV_FP8_E4M3: return cskv::kFmtFp8;
+    case CSKV_FP4_E2M1: return cskv::kFmtFp4;
+    default: return cskv::kFmtBf16;
+  }
 }
+
+// Cache formats: bf16, fp8 rows, mixed rows and fp4 rows (the last two D = 512).
+bool cache_format_ok(int32_t dt) {
+  return dt == CSKV_BF16 || dt == CSKV_FP8_E4M3 || dt == CSKV_FP8_ROPE64 || dt == CSKV_FP4_E2M1;
+}
+// Formats with a separate fp32 scale per row.
+bool needs_row_scale(int32_t dt) { return dt == CSKV_FP8_E4M3 || dt == CSKV_FP8_ROPE64; }
 
 #define CHECK(cond, status, ...) \
   do {                           \
@@ -69,10 +80,10 @@ cskv_status cskv_compress(int32_t kind, const void* S, const float* gate, int64_
         "compress: negative size (B=%lld T=%lld first_entry=%lld cache_rows=%lld)", (long long)B,
         (long long)T, (long long)first_entry, (long long)cache_rows);
   CHECK(D == 128 || D == 512, CSKV_EUNSUPPORTED, "compress: D=%d (supported: 128, 512)", D);
-  CHECK(cache_dtype == CSKV_BF16 || cache_dtype == CSKV_FP8_E4M3 || cache_dtype == CSKV_FP8_ROPE64,
-        CSKV_EUNSUPPORTED, "compress: cache dtype %d (supported: bf16, fp8, fp8 + bf16 rotary)", cache_dtype);
-  CHECK(cache_dtype != CSKV_FP8_ROPE64 || D == 512, CSKV_EUNSUPPORTED,
-        "compress: fp8 + bf16 rotary rows need D = 512");
+  CHECK(cache_format_ok(cache_dtype), CSKV_EUNSUPPORTED,
+        "compress: cache dtype %d (supported: bf16, fp8, fp8 + bf16 rotary, fp4)", cache_dtype);
+  CHECK((cache_dtype != CSKV_FP8_ROPE64 && cache_dtype != CSKV_FP4_E2M1) || D == 512, CSKV_EUNSUPPORTED,
+        "compress: fp8 + bf16 rotary and fp4 rows need D = 512");
   const int64_t w = kind == CSKV_C4A ? 8 : 128, s = kind == CSKV_C4A ? 4 : 128;
   const int64_t n = T < w ? 0 : (T - w) / s + 1;
   CHECK(first_entry + n <= cache_rows, CSKV_EINVAL,
@@ -80,7 +91,7 @@ cskv_status cskv_compress(int32_t kind, const void* S, const float* gate, int64_
         (long long)(first_entry + n - 1), (long long)cache_rows);
   if (B == 0 || n == 0) return ok();
   CHECK(S && gate && cache, CSKV_EINVAL, "compress: null S, gate or cache");
-  CHECK(cache_dtype == CSKV_BF16 || cache_scale, CSKV_EINVAL, "compress: fp8 cache needs cache_scale");
+  CHECK(!needs_row_scale(cache_dtype) || cache_scale, CSKV_EINVAL, "compress: fp8 cache needs cache_scale");
   CHECK(aligned(S, 16) && aligned(cache, 16) && aligned(gate, 4), CSKV_EINVAL,
         "compress: S and cache must be 16-byte aligned");
   CHECK(B <= 65535, CSKV_EUNSUPPORTED, "compress: B=%lld > 65535", (long long)B);
@@ -102,17 +113,17 @@ cskv_status cskv_append(int32_t kind, const void* s_new, const float* g_new, con
   CHECK(B >= 0 && cache_rows >= 0, CSKV_EINVAL, "append: negative size (B=%lld cache_rows=%lld)",
         (long long)B, (long long)cache_rows);
   CHECK(D == 128 || D == 512, CSKV_EUNSUPPORTED, "append: D=%d (supported: 128, 512)", D);
-  CHECK(cache_dtype == CSKV_BF16 || cache_dtype == CSKV_FP8_E4M3 || cache_dtype == CSKV_FP8_ROPE64,
-        CSKV_EUNSUPPORTED, "append: cache dtype %d (supported: bf16, fp8, fp8 + bf16 rotary)", cache_dtype);
-  CHECK(cache_dtype != CSKV_FP8_ROPE64 || D == 512, CSKV_EUNSUPPORTED,
-        "append: fp8 + bf16 rotary rows need D = 512");
+  CHECK(cache_format_ok(cache_dtype), CSKV_EUNSUPPORTED,
+        "append: cache dtype %d (supported: bf16, fp8, fp8 + bf16 rotary, fp4)", cache_dtype);
+  CHECK((cache_dtype != CSKV_FP8_ROPE64 && cache_dtype != CSKV_FP4_E2M1) || D == 512, CSKV_EUNSUPPORTED,
+        "append: fp8 + bf16 rotary and fp4 rows need D = 512");
   const int32_t w = kind == CSKV_C4A ? 8 : 128;
   CHECK(W >= w, CSKV_EINVAL, "append: W=%d must be >= %d, the states of one entry", W, w);
   CHECK(cache_rows <= 0x7FFFFFFF, CSKV_EUNSUPPORTED, "append: cache_rows too large for int32 counts");
   if (B == 0) return ok();
   CHECK(s_new && g_new && pos && ring && ring_gate, CSKV_EINVAL, "append: null s_new, g_new, pos or ring");
   CHECK(cache_rows == 0 || cache, CSKV_EINVAL, "append: null cache");
-  CHECK(cache_dtype == CSKV_BF16 || cache_rows == 0 || cache_scale, CSKV_EINVAL,
+  CHECK(!needs_row_scale(cache_dtype) || cache_rows == 0 || cache_scale, CSKV_EINVAL,
         "append: fp8 cache needs cache_scale");
   CHECK(aligned(s_new, 16) && aligned(ring, 16) && (!cache || aligned(cache, 16)) && aligned(g_new, 4) &&
             aligned(ring_gate, 4) && aligned(pos, 8),
@@ -200,10 +211,10 @@ cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t 
   CHECK(B >= 0 && cache_rows >= 0 && W >= 0, CSKV_EINVAL, "attend: negative size");
   CHECK(H >= 1 && H <= 64, CSKV_EUNSUPPORTED, "attend: H=%d (supported: 1..64)", H);
   CHECK(D == 128 || D == 512, CSKV_EUNSUPPORTED, "attend: D=%d (supported: 128, 512)", D);
-  CHECK(cache_dtype == CSKV_BF16 || cache_dtype == CSKV_FP8_E4M3 || cache_dtype == CSKV_FP8_ROPE64,
-        CSKV_EUNSUPPORTED, "attend: cache dtype %d (supported: bf16, fp8, fp8 + bf16 rotary)", cache_dtype);
-  CHECK(cache_dtype != CSKV_FP8_ROPE64 || D == 512, CSKV_EUNSUPPORTED,
-        "attend: fp8 + bf16 rotary rows need D = 512");
+  CHECK(cache_format_ok(cache_dtype), CSKV_EUNSUPPORTED,
+        "attend: cache dtype %d (supported: bf16, fp8, fp8 + bf16 rotary, fp4)", cache_dtype);
+  CHECK((cache_dtype != CSKV_FP8_ROPE64 && cache_dtype != CSKV_FP4_E2M1) || D == 512, CSKV_EUNSUPPORTED,
+        "attend: fp8 + bf16 rotary and fp4 rows need D = 512");
   CHECK(window_dtype == CSKV_BF16 || window_dtype == CSKV_FP8_E4M3, CSKV_EUNSUPPORTED,
         "attend: window dtype %d (supported: bf16, fp8)", window_dtype);
   CHECK(ids == nullptr || k >= 0, CSKV_EINVAL, "attend: k=%d must be >= 0", k);
@@ -219,7 +230,7 @@ cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t 
   CHECK(rope_dims == 0 || q_pos, CSKV_EINVAL, "attend: rope_dims > 0 needs q_pos");
   const int64_t n_sel_max = ids ? (int64_t)k : cache_rows;
   CHECK(n_sel_max == 0 || cache, CSKV_EINVAL, "attend: null cache");
-  CHECK(cache_dtype == CSKV_BF16 || n_sel_max == 0 || cache_scale, CSKV_EINVAL,
+  CHECK(!needs_row_scale(cache_dtype) || n_sel_max == 0 || cache_scale, CSKV_EINVAL,
         "attend: fp8 cache needs cache_scale");
   CHECK(W == 0 || window, CSKV_EINVAL, "attend: null window");
   CHECK(window_dtype != CSKV_FP8_E4M3 || W == 0 || window_scale, CSKV_EINVAL,
@@ -242,6 +253,7 @@ cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t 
   a.D = D;
   a.cache_fp8 = cache_dtype == CSKV_FP8_E4M3;
   a.cache_mix = cache_dtype == CSKV_FP8_ROPE64;
+  a.cache_fp4 = cache_dtype == CSKV_FP4_E2M1;
   a.cache = cache;
   a.cache_scale = cache_scale;
   a.cache_rows = cache_rows;

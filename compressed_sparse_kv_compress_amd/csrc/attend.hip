@@ -69,6 +69,7 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 // their addresses are PC-relative constants rather than loads).
 static __device__ __attribute__((aligned(16))) uint8_t g_zero_row[1024];
 static __device__ float g_empty_scale = 0.0f;
+static __device__ float g_one_scale = 1.0f;
 
 // Swizzle of a tile row's 16-byte chunks.
 __device__ __forceinline__ int chunk_swz(int row) { return (row >> 3) & 3; }
@@ -81,7 +82,10 @@ struct AttCfg {
   // mixed cache rows by DMA into their tile rows as raw bytes + an in-place
   // widening pass; bf16 window rows by DMA as in the bf16 path
   static constexpr bool kDmaMix = D == 512 && CF == kFmtMix && !WFP8;
-  static constexpr bool kReg = !kDma && !kDmaFp8 && !kDmaMix;         // register-staged fill
+  static constexpr bool kDmaFp4 = D == 512 && CF == kFmtFp4 && !WFP8;  // fp4 rows: likewise
+  static constexpr bool kDmaRaw = kDmaMix || kDmaFp4;                 // raw rows widened in place
+  static constexpr int kRawChunks = kDmaMix ? kMixRowChunks : kFp4RowChunks;
+  static constexpr bool kReg = !kDma && !kDmaFp8 && !kDmaRaw;         // register-staged fill
   // rows carry a value scale (mixed rows are widened with theirs applied)
   static constexpr bool kScaled = CF == kFmtFp8 || WFP8;
   static constexpr int KROW = D + 16;                           // bf16 per tile row
@@ -89,7 +93,7 @@ struct AttCfg {
   // fp8 staging tile: the rows' codes, then their 32 scales (one DMA target per slot)
   static constexpr int kStageBytes = kDmaFp8 ? kTK * D + kTK * 4 : 16;
   // DMA instructions per wave and tile: 8 rows (+ their scales for fp8 / mixed rows)
-  static constexpr int kOpsPerTile = kDma ? 8 : (kDmaFp8 ? 5 : (kDmaMix ? 9 : 0));
+  static constexpr int kOpsPerTile = kDma ? 8 : (kDmaFp8 ? 5 : (kDmaRaw ? 9 : 0));
 };
 
 // vmcnt(n) with the other counters left alone (n <= 63).
@@ -144,7 +148,7 @@ template <int D, int CF, bool WFP8>
 __device__ __forceinline__ RowSrc row_src(const AttendArgs& a, int64_t b) {
   RowSrc r;
   r.cache = reinterpret_cast<const uint8_t*>(a.cache) + b * a.cache_rows * row_bytes<D, CF>();
-  r.cache_scale = CF != kFmtBf16 ? a.cache_scale + b * a.cache_rows : nullptr;
+  r.cache_scale = CF == kFmtFp8 || CF == kFmtMix ? a.cache_scale + b * a.cache_rows : nullptr;
   r.window = reinterpret_cast<const uint8_t*>(a.window) + b * a.win_bstride * D * (WFP8 ? 1 : 2);
   r.window_scale = WFP8 ? a.window_scale + b * a.win_bstride : nullptr;
   r.cache_rows = a.cache_rows;
@@ -194,11 +198,14 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
       // a cache row of the mixed format: codes widened with the row scale applied,
       // the rotary channels copied (value scale 1)
       const bool mix = CF == kFmtMix && tile0 + 8 * kb + i < n_sel;
+      const bool f4 = CF == kFmtFp4 && tile0 + 8 * kb + i < n_sel;   // fp4 cache row: exact widening
       r[i] = make_uint4(0, 0, 0, 0);
       sc[i] = p ? (sp && !mix ? *sp : 1.0f) : 0.0f;
       bias[i] = p ? 0.0f : -INFINITY;
       if (p && active_c) {
-        if (mix) {
+        if (f4) {
+          r[i] = fp4x8_to_bf16x8_scaled(*reinterpret_cast<const uint32_t*>(p + cb * 4), e4m3_to_f32(p[D / 2 + cb / 2]));
+        } else if (mix) {
           if (cb * 8 < D - kMixRope) r[i] = fp8x8_to_bf16x8_scaled(*reinterpret_cast<const uint2*>(p + cb * 8), *sp);
           else r[i] = *reinterpret_cast<const uint4*>(p + (D - kMixRope) + 2 * (cb * 8 - (D - kMixRope)));
         } else if (sp) {
@@ -263,13 +270,14 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
     if (lane < 8) slot_source<D, CF, WFP8>(rsrc, tile0 + 8 * wave + lane, lo, n_sel, n_keys, dense, ids_l, p, sp);
     const uint64_t src_l = reinterpret_cast<uint64_t>(p ? p : g_zero_row);
     if (lane < 8) pb[8 * wave + lane] = p ? 0.0f : -INFINITY;
-    if constexpr (C::kDmaMix) {
-      // row scale of each mixed row (0 for window and empty rows: no widening),
-      // the wave's 8 of them in the 32 pad bytes of its first row (the tile
-      // buffers stay the only DMA targets besides the first dummy one)
+    if constexpr (C::kDmaRaw) {
+      // per row a scale that marks raw rows for the widening pass (mixed rows:
+      // their row scale; fp4 rows: 1; window and empty rows: 0), the wave's 8
+      // of them in the 32 pad bytes of its first row (the tile buffers stay the
+      // only DMA targets besides the first dummy one)
       const bool mix_l = lane < 8 && p && tile0 + 8 * wave + lane < n_sel;
       if (lane < 8) {
-        const float* s = mix_l ? sp : &g_empty_scale;
+        const float* s = mix_l ? (C::kDmaMix ? sp : &g_one_scale) : &g_empty_scale;
         __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)s,
                                          (__attribute__((address_space(3))) void*)(tile + 8 * wave * C::KROW + D),
                                          4, 0, 0);
@@ -279,9 +287,10 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
       for (int i = 0; i < 8; ++i) {
         const int row = 8 * wave + i;
         const uint8_t* src = reinterpret_cast<const uint8_t*>(lane_u64(src_l, i));
-        // mixed row: its 576 raw bytes land at chunk positions 0..35 (lanes 36..63
-        // read the zero row); bf16 row: swizzled chunks as in the bf16 path
-        const uint8_t* a = ((mix_m >> i) & 1) ? (lane < kMixRowChunks ? src + 16 * lane : g_zero_row + 16 * lane)
+        // raw row: its bytes land at chunk positions 0 .. kRawChunks-1 (the
+        // other lanes read the zero row); bf16 row: swizzled chunks as in the
+        // bf16 path
+        const uint8_t* a = ((mix_m >> i) & 1) ? (lane < C::kRawChunks ? src + 16 * lane : g_zero_row + 16 * lane)
                                               : src + 16 * (lane ^ chunk_swz(row));
         __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)a,
                                          (__attribute__((address_space(3))) void*)(tile + row * C::KROW), 16, 0,
@@ -386,6 +395,37 @@ __device__ __forceinline__ void widen_mix_tile(uint16_t* tile) {
       // rotary channels 448 + 8j .. +7: logical chunk 56 + j
 #pragma unroll
       for (int j = 0; j < 8; ++j) lds_store_b128_unordered(row + 8 * ((56 + j) ^ swz), c[j]);
+    }
+  }
+}
+
+// Widens the fp4 rows of a tile in place (flag 0: bf16 already; flags of rows
+// 8w .. 8w+7 in the pad of row 8w): thread t takes row t/8, part p turns the
+// 32 code bytes at raw byte 32p and their 4 group scales (raw bytes 256 + 4p
+// ..) into channels 64p .. 64p+63, exactly, in the swizzled chunk layout. The
+// 8 threads of a row are lanes of one wave: their reads precede their writes.
+template <int D>
+__device__ __forceinline__ void widen_fp4_tile(uint16_t* tile) {
+  using C = AttCfg<D, kFmtFp4, false>;
+  const int t = threadIdx.x;
+  const int r = t >> 3, part = t & 7;
+  const float flag = reinterpret_cast<const float*>(tile + (r & ~7) * C::KROW + D)[r & 7];
+  uint16_t* row = tile + r * C::KROW;
+  const int swz = chunk_swz(r);
+  const uint4 c0 = reinterpret_cast<const uint4*>(row + 16 * part)[0];
+  const uint4 c1 = reinterpret_cast<const uint4*>(row + 16 * part)[1];
+  const uint32_t sw = reinterpret_cast<const uint32_t*>(row + D / 4)[part];
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the row's reads are done before its writes
+  if (flag > 0.0f) {
+    const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {            // group 4p + j: channels 64p + 16j .. +15
+      const float s = e4m3_to_f32((sw >> (8 * j)) & 0xFFu);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ch = 8 * part + 2 * j + h;   // logical chunk
+        lds_store_b128_unordered(row + 8 * (ch ^ swz), fp4x8_to_bf16x8_scaled(w[2 * j + h], s));
+      }
     }
   }
 }
@@ -606,6 +646,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
     if (i + kNStage - 1 < n_tiles) issue(std::integral_constant<int, (S + kNStage - 1) % kNStage>{}, i + kNStage - 1);
     if constexpr (C::kDmaMix) {
       widen_mix_tile<D>(tile_of(sc));
+      lds_barrier();
+    }
+    if constexpr (C::kDmaFp4) {
+      widen_fp4_tile<D>(tile_of(sc));
       lds_barrier();
     }
     if constexpr (C::kDmaFp8) {
@@ -1111,7 +1155,8 @@ static hipError_t launch_attend_t(const AttendPlan& p, const AttendArgs& a, void
 
 hipError_t launch_attend(const AttendPlan& p, const AttendArgs& a, void* workspace,
                          hipStream_t stream) {
-  if (p.head_split && a.ids && a.D == 512 && !a.cache_fp8 && !a.cache_mix && !a.win_fp8 && a.H % 16 == 0 &&
+  if (p.head_split && a.ids && a.D == 512 && !a.cache_fp8 && !a.cache_mix && !a.cache_fp4 && !a.win_fp8 &&
+      a.H % 16 == 0 &&
       a.k <= kMaxSplitIds) {
     const int n_hg = a.H / 16;
     const unsigned n_wg = (unsigned)(8 * ((a.B + 7) / 8) * n_hg);
@@ -1121,6 +1166,8 @@ hipError_t launch_attend(const AttendPlan& p, const AttendArgs& a, void* workspa
   if (a.D == 512) {
     if (a.cache_mix) return a.win_fp8 ? launch_attend_t<512, kFmtMix, true>(p, a, workspace, stream)
                                       : launch_attend_t<512, kFmtMix, false>(p, a, workspace, stream);
+    if (a.cache_fp4) return a.win_fp8 ? launch_attend_t<512, kFmtFp4, true>(p, a, workspace, stream)
+                                      : launch_attend_t<512, kFmtFp4, false>(p, a, workspace, stream);
     if (a.cache_fp8) return a.win_fp8 ? launch_attend_t<512, kFmtFp8, true>(p, a, workspace, stream)
                                       : launch_attend_t<512, kFmtFp8, false>(p, a, workspace, stream);
     return a.win_fp8 ? launch_attend_t<512, kFmtBf16, true>(p, a, workspace, stream)

@@ -44,12 +44,30 @@ __device__ __forceinline__ void load_row(const uint16_t* row, int lane, RowSlice
 // Writes one finished entry row held as CPL fp32 values per lane: bf16 (RNE);
 // or fp8 codes + one fp32 row scale (amax / 448 over the whole row); or a
 // mixed row: the channels below D-64 as fp8 codes with a row scale over them
-// alone, then the 64 rotary channels as bf16 (RNE).
+// alone, then the 64 rotary channels as bf16 (RNE); or an fp4 row: E2M1 codes
+// with one E4M3 scale per 16 channels, encoded exactly as cskv_encode_fp4_g16
+// does (a group is the 16 channels of a lane pair).
 template <int D, int FMT>
 __device__ __forceinline__ void store_entry(const float* acc, int lane, void* cache_row,
                                             float* scale_slot) {
   constexpr int CPL = D / kWave;
-  if constexpr (FMT == kFmtMix) {
+  if constexpr (FMT == kFmtFp4) {
+    static_assert(D == 512, "fp4 rows: D = 512");
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) amax = fmaxf(amax, fabsf(acc[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));          // the group's other 8 channels
+    uint32_t sc = f32_to_e4m3(amax / 6.0f);
+    if (e4m3_to_f32(sc) == 0.0f && amax > 0.0f) sc = 0x01u;
+    const float sv = e4m3_to_f32(sc);
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) w |= (sv == 0.0f ? 0u : f32_to_e2m1(acc[i] / sv)) << (4 * i);
+    uint8_t* row = reinterpret_cast<uint8_t*>(cache_row);
+    *reinterpret_cast<uint32_t*>(row + lane * (CPL / 2)) = w;
+    if ((lane & 1) == 0) row[D / 2 + lane / 2] = (uint8_t)sc;
+    (void)scale_slot;
+  } else if constexpr (FMT == kFmtMix) {
     static_assert(D == 512, "mixed rows: D = 512");
     const bool rope = lane * CPL >= D - kMixRope;          // lanes 56 .. 63
     float amax = 0.0f;
@@ -157,7 +175,7 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress_c4a(
   const float* gb = gate + b * T;
   constexpr int RB = row_bytes<D, FMT>();
   uint8_t* cb = reinterpret_cast<uint8_t*>(cache) + (b * cache_rows + first_entry) * (int64_t)RB;
-  float* sb = FMT != kFmtBf16 ? cache_scale + b * cache_rows + first_entry : nullptr;
+  float* sb = FMT == kFmtFp8 || FMT == kFmtMix ? cache_scale + b * cache_rows + first_entry : nullptr;
 
   RowSlice<D> prev[4], cur[4];
 #pragma unroll
@@ -171,7 +189,7 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress_c4a(
     for (int j = 0; j < 8; ++j) g[j] = gb[4 * c + j];
     float acc[RowSlice<D>::CPL];
     fold_c4a<D>(prev, cur, g, acc);
-    store_entry<D, FMT>(acc, lane, cb + c * (int64_t)RB, FMT != kFmtBf16 ? sb + c : nullptr);
+    store_entry<D, FMT>(acc, lane, cb + c * (int64_t)RB, sb ? sb + c : nullptr);
 #pragma unroll
     for (int j = 0; j < 4; ++j) prev[j] = cur[j];
   }
@@ -238,7 +256,7 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress_c128a(
   if (wave != 0) return;
   const int64_t row = b * cache_rows + first_entry + c;
   store_entry<D, FMT>(acc, lane, reinterpret_cast<uint8_t*>(cache) + row * (int64_t)row_bytes<D, FMT>(),
-                      FMT != kFmtBf16 ? cache_scale + row : nullptr);
+                      FMT == kFmtFp8 || FMT == kFmtMix ? cache_scale + row : nullptr);
 }
 
 // ---------------------------------------------------------------- append
@@ -306,7 +324,7 @@ __global__ __launch_bounds__(kCompressThreads) void k_append_c4a(
   fold_c4a<D>(r, r + 4, g, acc);
   const int64_t row = b * cache_rows + c;
   store_entry<D, FMT>(acc, lane, reinterpret_cast<uint8_t*>(cache) + row * (int64_t)row_bytes<D, FMT>(),
-                      FMT != kFmtBf16 ? cache_scale + row : nullptr);
+                      FMT == kFmtFp8 || FMT == kFmtMix ? cache_scale + row : nullptr);
 }
 
 template <int D, int FMT>
@@ -346,7 +364,7 @@ __global__ __launch_bounds__(kCompressThreads) void k_append_c128a(
   if (wave != 0) return;
   const int64_t row = b * cache_rows + c;
   store_entry<D, FMT>(acc, lane, reinterpret_cast<uint8_t*>(cache) + row * (int64_t)row_bytes<D, FMT>(),
-                      FMT != kFmtBf16 ? cache_scale + row : nullptr);
+                      FMT == kFmtFp8 || FMT == kFmtMix ? cache_scale + row : nullptr);
 }
 
 // ---------------------------------------------------------------- launch
@@ -390,7 +408,10 @@ hipError_t launch_append(int kind, const uint16_t* s_new, const float* g_new, co
                          hipStream_t stream) {
 #define CSKV_APPEND(DD, FF) launch_append_t<DD, FF>(kind, s_new, g_new, pos, B, ring, ring_gate, W, cache, \
                                                    cache_scale, cache_rows, n_entries, n_window, stream)
-  if (D == 512) return fmt == kFmtMix ? CSKV_APPEND(512, kFmtMix) : (fmt == kFmtFp8 ? CSKV_APPEND(512, kFmtFp8) : CSKV_APPEND(512, kFmtBf16));
+  if (D == 512) {
+    if (fmt == kFmtFp4) return CSKV_APPEND(512, kFmtFp4);
+    return fmt == kFmtMix ? CSKV_APPEND(512, kFmtMix) : (fmt == kFmtFp8 ? CSKV_APPEND(512, kFmtFp8) : CSKV_APPEND(512, kFmtBf16));
+  }
   return fmt == kFmtFp8 ? CSKV_APPEND(128, kFmtFp8) : CSKV_APPEND(128, kFmtBf16);
 #undef CSKV_APPEND
 }
@@ -400,7 +421,10 @@ hipError_t launch_compress(int kind, const uint16_t* S, const float* gate, int64
                            float* cache_scale, int64_t cache_rows, hipStream_t stream) {
 #define CSKV_COMPRESS(DD, FF) launch_compress_t<DD, FF>(kind, S, gate, B, T, n, first_entry, cache, cache_scale, \
                                                        cache_rows, stream)
-  if (D == 512) return fmt == kFmtMix ? CSKV_COMPRESS(512, kFmtMix) : (fmt == kFmtFp8 ? CSKV_COMPRESS(512, kFmtFp8) : CSKV_COMPRESS(512, kFmtBf16));
+  if (D == 512) {
+    if (fmt == kFmtFp4) return CSKV_COMPRESS(512, kFmtFp4);
+    return fmt == kFmtMix ? CSKV_COMPRESS(512, kFmtMix) : (fmt == kFmtFp8 ? CSKV_COMPRESS(512, kFmtFp8) : CSKV_COMPRESS(512, kFmtBf16));
+  }
   return fmt == kFmtFp8 ? CSKV_COMPRESS(128, kFmtFp8) : CSKV_COMPRESS(128, kFmtBf16);
 #undef CSKV_COMPRESS
 }

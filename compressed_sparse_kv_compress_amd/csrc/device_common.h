@@ -121,10 +121,25 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 c) {
 constexpr int kFmtBf16 = 0;   // D bf16 channels
 constexpr int kFmtFp8 = 1;    // D E4M3 codes + one fp32 scale per row (separate array)
 constexpr int kFmtMix = 2;    // D-64 E4M3 codes, then the 64 rotary channels in bf16; fp32 row scale of the codes
+constexpr int kFmtFp4 = 3;    // D/2 bytes of E2M1 codes (channel 2j in the low nibble), then D/16 E4M3 group scales
 constexpr int kMixRope = 64;  // rotary channels a mixed row keeps in bf16
 constexpr int kMixRowChunks = (512 - kMixRope + 2 * kMixRope) / 16;   // 16-byte chunks of a D = 512 mixed row
 template <int D, int FMT>
-constexpr int row_bytes() { return FMT == kFmtBf16 ? 2 * D : (FMT == kFmtFp8 ? D : D - kMixRope + 2 * kMixRope); }
+constexpr int row_bytes() {
+  return FMT == kFmtBf16 ? 2 * D : (FMT == kFmtFp8 ? D : (FMT == kFmtMix ? D - kMixRope + 2 * kMixRope : D / 2 + D / 16));
+}
+constexpr int kFp4RowChunks = (512 / 2 + 512 / 16) / 16;   // 16-byte chunks of a D = 512 fp4 row
+
+// 8 E2M1 codes (one 32-bit word, channel 2j in the low nibble of byte j) times
+// their group's E4M3 scale value, as 8 bf16 (exact: at most 5 significant bits).
+__device__ __forceinline__ uint4 fp4x8_to_bf16x8_scaled(uint32_t w, float s) {
+  const uint32_t b0 = __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<0>(w));
+  const uint32_t b1 = __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<1>(w));
+  const uint32_t b2 = __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<2>(w));
+  const uint32_t b3 = __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<3>(w));
+  return make_uint4(pack_bf16x2(bf16_lo(b0) * s, bf16_hi(b0) * s), pack_bf16x2(bf16_lo(b1) * s, bf16_hi(b1) * s),
+                    pack_bf16x2(bf16_lo(b2) * s, bf16_hi(b2) * s), pack_bf16x2(bf16_lo(b3) * s, bf16_hi(b3) * s));
+}
 
 // 8 E4M3 codes times the row scale, rounded to bf16 (mixed rows enter the
 // tile already scaled, so their value scale is 1): exact bf16 of each code by

@@ -53,6 +53,7 @@ struct AttendArgs {
   int H, D;
   bool cache_fp8;
   bool cache_mix;            // mixed rows (kFmtMix); cache_fp8 is false then
+  bool cache_fp4;            // fp4 rows (kFmtFp4), group scales inside the row
   const void* cache;
   const float* cache_scale;
   int64_t cache_rows;

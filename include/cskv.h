@@ -80,7 +80,10 @@ int32_t cskv_version(void);
  *   D         128 or 512
  *   cache     [B, cache_rows, D] bf16, or fp8 codes [B, cache_rows, D] plus
  *             cache_scale [B, cache_rows] fp32 (cache_dtype CSKV_FP8_E4M3), or mixed
- *             rows [B, cache_rows, D+64] bytes plus cache_scale (CSKV_FP8_ROPE64)
+ *             rows [B, cache_rows, D+64] bytes plus cache_scale (CSKV_FP8_ROPE64), or fp4
+ *             rows [B, cache_rows, D/2 + D/16] bytes (CSKV_FP4_E2M1, D = 512: the
+ *             packed E2M1 codes, then one E4M3 scale byte per 16 channels, encoded as
+ *             cskv_encode_fp4_g16 does; [P3] "Three mechanisms", third; no cache_scale)
  *
  * Writes rows first_entry .. first_entry+n-1 of every sequence's cache, where
  * n = floor((T-w)/s)+1 complete windows (n = 0 when T < w: nothing is written).
@@ -182,7 +185,8 @@ cskv_status cskv_index_topk(const void* q_idx, int32_t key_dtype, const void* k_
  *
  *   Q            [B, H, D] bf16;  1 <= H <= 64;  D 128 or 512
  *   cache        [B, cache_rows, D] bf16, or fp8 codes + cache_scale [B, cache_rows] fp32,
- *                or mixed rows (CSKV_FP8_ROPE64, D = 512) + cache_scale
+ *                or mixed rows (CSKV_FP8_ROPE64, D = 512) + cache_scale, or fp4 rows
+ *                (CSKV_FP4_E2M1, D = 512, layout as in cskv_compress)
  *   ids          [B, k] int32 entry ids (ids < 0 or >= cache_rows are skipped),
  *                or NULL for dense attention over entries 0 .. n_entries[b]-1
  *   n_entries    dense mode only: [B] int32 device counts, or NULL for cache_rows

@@ -92,7 +92,9 @@ def test_append_validation(lib):
 
     assert call(kind=3) == lib.EINVAL
     assert call(D=384) == lib.EUNSUPPORTED
-    assert call(cdt=lib.FP4_E2M1) == lib.EUNSUPPORTED
+    assert call(cdt=9) == lib.EUNSUPPORTED
+    assert call(cdt=lib.FP4_E2M1, D=128) == lib.EUNSUPPORTED      # fp4 rows: D = 512 only
+    assert call(cdt=lib.FP8_ROPE64, D=128) == lib.EUNSUPPORTED    # mixed rows: D = 512 only
     assert call(W=7) == lib.EINVAL                          # a c4a entry needs 8 states
     assert call(kind=1, W=127) == lib.EINVAL                # a c128a entry needs 128
     assert b"W=127" in lib._lib_last_error()
@@ -135,6 +137,8 @@ def test_attend_validation(lib):
     assert call(R=1024) == lib.EINVAL
     assert call(wst=3) == lib.EINVAL
     assert call(cdt=lib.FP8_E4M3) == lib.EINVAL            # fp8 cache without scales
+    assert call(cdt=lib.FP8_ROPE64) == lib.EINVAL          # mixed rows without scales
+    assert call(cdt=lib.FP4_E2M1, D=128) == lib.EUNSUPPORTED
     assert call(wdt=lib.FP8_E4M3) == lib.EINVAL
     assert call(pos=None) == lib.EINVAL
     assert call(Q=ctypes.c_void_p(8)) == lib.EINVAL        # misaligned

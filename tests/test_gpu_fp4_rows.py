@@ -1,0 +1,94 @@
+"""fp4 attention-cache rows (E2M1 codes, one E4M3 scale byte per 16 channels,
+288 B per 512-channel row) through the C ABI: compress and the streaming
+append write them, attend widens them exactly; against the oracle's group
+codec and attention on the same bytes."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats as F
+from oracle import method as M
+from tests.helpers import row_rel_err, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+D, RB = 512, 288
+
+
+@pytest.fixture(scope="module")
+def cskv():
+    import compressed_sparse_kv_compress_amd as m
+    return m
+
+
+def _states(seed, B, T):
+    S = synth.normal_bf16(synth.stream_key(seed, synth.T_S), 0, B * T * D).reshape(B, T, D)
+    g = (synth.normal_f32(synth.stream_key(seed, synth.T_GATE), 0, B * T) * np.float32(2.0)).reshape(B, T)
+    return S, g
+
+
+@pytest.mark.parametrize("kind,T", [("c4a", 1030), ("c128a", 640)])
+def test_compress_fp4_rows(cskv, kind, T):
+    B = 2
+    S, g = _states(70 + T, B, T)
+    n = M.entry_count(kind, T)
+    rows = torch.zeros((B, n, RB), dtype=torch.uint8, device="cuda")
+    assert cskv.compress(kind, to_dev_bf16(S), to_dev(g), rows) == n
+    got = rows.cpu().numpy()
+    flips = scale_flips = 0
+    for b in range(B):
+        ref = M.compress(kind, F.bf16_to_f64(S[b]), g[b].astype(np.float64))
+        # the group codec on the oracle's entries: the same codes and scales
+        # except where the two fp32 sums round differently next to a boundary
+        rp, rs = F.encode_fp4_g16(ref.astype(np.float32))
+        flips += int(np.sum(F.unpack_fp4(got[b, :, :256]) != F.unpack_fp4(rp)))
+        scale_flips += int(np.sum(got[b, :, 256:] != rs))
+        # and the decoded rows are within the 4-bit codec's own error of the entries
+        dec = F.decode_fp4_rows(got[b], D)
+        assert row_rel_err(dec, ref) <= 0.35
+        assert np.array_equal(dec, F.decode_fp4_rows(F.fp4_row_bytes(rp, rs), D)) or flips > 0
+    assert flips <= 0.01 * B * n * D and scale_flips <= 0.01 * B * n * (D // 16)
+
+
+def test_append_fp4_rows_equal_compress(cskv):
+    B, T, W = 2, 90, 128
+    S, g = _states(75, B, T)
+    n = M.entry_count("c4a", T)
+    rows = torch.zeros((B, n, RB), dtype=torch.uint8, device="cuda")
+    ring = torch.zeros((B, W, D), dtype=torch.bfloat16, device="cuda")
+    rg = torch.zeros((B, W), dtype=torch.float32, device="cuda")
+    Sd, gd = to_dev_bf16(S), to_dev(g)
+    for p in range(T):
+        cskv.append("c4a", Sd[:, p].contiguous(), gd[:, p].contiguous(),
+                    torch.full((B,), p, dtype=torch.int64, device="cuda"), ring, rg, rows)
+    ref = torch.zeros_like(rows)
+    cskv.compress("c4a", Sd, gd, ref)
+    assert torch.equal(rows, ref)
+
+
+@pytest.mark.parametrize("sparse,win_fp8", [(True, False), (False, False), (True, True)])
+def test_attend_fp4_rows_matches_oracle(cskv, sparse, win_fp8):
+    B, H, N, W, k, R = 3, 64, 700, 128, 96, 64
+    rng = np.random.default_rng(15 + sparse + 2 * win_fp8)
+    x = synth.normal_f32(synth.stream_key(71, synth.T_CACHE), 0, B * N * D).reshape(B, N, D) * np.float32(1.5)
+    packed, sc = F.encode_fp4_g16(x)
+    rows = F.fp4_row_bytes(packed, sc)                           # [B, N, 288]
+    Q = synth.normal_bf16(synth.stream_key(72, synth.T_Q), 0, B * H * D).reshape(B, H, D)
+    win = synth.normal_bf16(synth.stream_key(73, synth.T_WIN), 0, B * W * D).reshape(B, W, D)
+    pos = rng.integers(10_000, 1 << 20, size=B).astype(np.int64)
+    tau = 1.0 / np.sqrt(D)
+    ids = np.stack([np.sort(rng.choice(N, size=k, replace=False)).astype(np.int32) for _ in range(B)]) if sparse else None
+    n_ent = np.array([N, 123, 0], dtype=np.int32)
+    if win_fp8:
+        wc, ws = F.encode_fp8_rows(F.bf16_to_f64(win).astype(np.float32))
+        win_dev, wsc_dev, win_ref = to_dev(wc), to_dev(ws), F.decode_fp8_rows(wc, ws)
+    else:
+        win_dev, wsc_dev, win_ref = to_dev_bf16(win), None, F.bf16_to_f64(win)
+    O = cskv.attend(to_dev_bf16(Q), to_dev(rows), None if ids is None else to_dev(ids), win_dev,
+                    window_scale=wsc_dev, softmax_scale=float(tau), rope_dims=R, q_pos=to_dev(pos),
+                    n_entries=None if sparse else to_dev(n_ent)).cpu().numpy()
+    dec = F.decode_fp4_rows(rows, D)
+    for b in range(B):
+        ref = M.attend(F.bf16_to_f64(Q[b]), dec[b], None if ids is None else ids[b], win_ref[b], tau, R, 10000.0,
+                       int(pos[b]), n_entries=None if sparse else int(n_ent[b]))
+        assert row_rel_err(O[b], ref) <= 2e-2
