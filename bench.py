@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4a_128k_bf16",
                     choices=["c4a_128k_bf16", "c128a_1m_bf16", "c4a_1m_fp8_fp4", "mixed61_256k_bf16", "tiny_c4a_2k",
-                             "stream_c4a_128k_bf16", "c128a_1m_mixed"])
+                             "stream_c4a_128k_bf16", "c128a_1m_mixed", "c128a_1m_fp4"])
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -158,6 +158,9 @@ class C128aLayer(Workload):
             if mixed:
                 cache = torch.empty((B, N, D + cskv.MIX_ROPE), dtype=torch.uint8, device=self.dev)
                 cscale = torch.empty((B, N), dtype=torch.float32, device=self.dev)
+            elif c.cache_dtype == "fp4":        # E2M1 codes + one E4M3 scale byte per 16 channels
+                cache = torch.empty((B, N, D // 2 + D // 16), dtype=torch.uint8, device=self.dev)
+                cscale = None
             else:
                 cache = torch.empty((B, N, D), dtype=torch.bfloat16, device=self.dev)
                 cscale = None
@@ -186,7 +189,7 @@ class C128aLayer(Workload):
 
     def bytes(self):
         c = self.cfg
-        row = (c.D - 64) + 2 * 64 + 4 if c.cache_dtype == "mixed" else c.D * 2
+        row = {"mixed": (c.D - 64) + 2 * 64 + 4, "fp4": c.D // 2 + c.D // 16}.get(c.cache_dtype, c.D * 2)
         return c.B * (c.n_entries * row + c.W * c.D * 2 + c.H * c.D * 2 + c.H * c.D * 4), 0
 
     def flops(self):
@@ -642,6 +645,7 @@ def main():
         "vs_baseline": None,
         "dtype": ("bf16" if cfg.cache_dtype == "bf16" and cfg.key_dtype == "bf16" else
                   "fp8 + bf16 rotary (bf16 MFMA, fp32 accumulate)" if cfg.cache_dtype == "mixed" else
+                  "fp4 E2M1 + E4M3/16 (bf16 MFMA, fp32 accumulate)" if cfg.cache_dtype == "fp4" else
                   "fp8+fp4 (bf16 MFMA, fp32 accumulate)"),
         "data": "synthetic (SplitMix64 streams; caches built by the library's compress kernel)" if not stateful
                 else "synthetic (SplitMix64 streams; prefix caches drawn directly, new states compressed in the step)",

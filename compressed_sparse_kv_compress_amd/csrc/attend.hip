@@ -265,6 +265,31 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
         return;
       }
     }
+    if constexpr (C::kDmaRaw) {
+      // dense rows that all come from the cache: contiguous raw rows, scalar
+      // row addresses, the lanes past a row's bytes read the zero row
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      const int64_t row0 = tile0 + 8 * wv;
+      if (dense && row0 + 8 <= n_sel) {
+        if (lane < 8) {
+          pb[8 * wv + lane] = 0.0f;
+          const float* s = C::kDmaMix ? rsrc.cache_scale + row0 + lane : &g_one_scale;
+          __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)s,
+                                           (__attribute__((address_space(3))) void*)(tile + 8 * wv * C::KROW + D),
+                                           4, 0, 0);
+        }
+        constexpr int RBY = row_bytes<D, CF>();
+        const uint8_t* src = lane < C::kRawChunks ? rsrc.cache + row0 * RBY + 16 * lane : g_zero_row + 16 * lane;
+        const int step = lane < C::kRawChunks ? RBY : 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + i * step),
+                                           (__attribute__((address_space(3))) void*)(tile + (8 * wv + i) * C::KROW),
+                                           16, 0, kCachePolicyStream);
+        }
+        return;
+      }
+    }
     const uint8_t* p = nullptr;
     const float* sp = nullptr;
     if (lane < 8) slot_source<D, CF, WFP8>(rsrc, tile0 + 8 * wave + lane, lo, n_sel, n_keys, dense, ids_l, p, sp);

@@ -35,7 +35,7 @@ class Workload:
     Di: int = 0            # indexer key width (c4a)
     k: int = 0             # top-k (c4a)
     idx_range: int = 0     # indexer values are integers in [-idx_range, idx_range]
-    cache_dtype: str = "bf16"   # "bf16", "fp8", or "mixed" (fp8 codes + bf16 rotary channels)
+    cache_dtype: str = "bf16"   # "bf16", "fp8", "mixed" (fp8 codes + bf16 rotary channels) or "fp4"
     key_dtype: str = "bf16"     # indexer keys: "bf16" or "fp4"
     rope_base: float = 10000.0
     layers: int = 1
@@ -124,5 +124,12 @@ C128A_1M_MIXED = Workload(
                 "channels (per-token scale) + the 64 rotary channels in bf16, 580 B per entry; bf16 window",
 )
 
-ALL = [TINY, C4A_128K, C128A_1M, C4A_1M_Q, MIXED_61, STREAM_C4A_128K, C128A_1M_MIXED]
+C128A_1M_FP4 = Workload(
+    name="c128a_1m_fp4", number=8, kind="c128a", B=16, L=1 << 20, D=512, R=64, H=64, W=128,
+    cache_dtype="fp4",
+    description="one c128a layer as c128a_1m_bf16, with an fp4 attention cache: E2M1 codes and one E4M3 "
+                "scale per 16 channels, 288 B per entry; bf16 window",
+)
+
+ALL = [TINY, C4A_128K, C128A_1M, C4A_1M_Q, MIXED_61, STREAM_C4A_128K, C128A_1M_MIXED, C128A_1M_FP4]
 BY_NAME = {w.name: w for w in ALL}
