@@ -92,3 +92,33 @@ def test_attend_fp4_rows_matches_oracle(cskv, sparse, win_fp8):
         ref = M.attend(F.bf16_to_f64(Q[b]), dec[b], None if ids is None else ids[b], win_ref[b], tau, R, 10000.0,
                        int(pos[b]), n_entries=None if sparse else int(n_ent[b]))
         assert row_rel_err(O[b], ref) <= 2e-2
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "mixed"])
+def test_attend_raw_rows_skip_invalid_ids(cskv, fmt):
+    """-1 padding and ids past the cache read the zero row with a zero flag and
+    stay out of the softmax (top-k pads with -1 when a sequence is short)."""
+    B, H, N, W, k, R = 2, 64, 300, 16, 80, 64
+    rng = np.random.default_rng(21)
+    x = synth.normal_f32(synth.stream_key(81, synth.T_CACHE), 0, B * N * D).reshape(B, N, D)
+    if fmt == "fp4":
+        packed, sc = F.encode_fp4_g16(x)
+        rows, cscale, dec = F.fp4_row_bytes(packed, sc), None, F.decode_fp4_g16(packed, sc)
+    else:
+        codes, rope, scale = F.encode_mixed_rows(x, R)
+        rows, cscale, dec = F.mixed_row_bytes(codes, rope), to_dev(scale), F.decode_mixed_rows(codes, rope, scale)
+    ids = np.full((B, k), -1, dtype=np.int32)
+    ids[0, :50] = np.sort(rng.choice(N, size=50, replace=False))
+    ids[1, :k] = np.sort(rng.choice(N, size=k, replace=False))
+    ids[1, 7] = N + 5                      # out of range: skipped
+    ids[1, 40] = 1 << 30
+    Q = synth.normal_bf16(synth.stream_key(82, synth.T_Q), 0, B * H * D).reshape(B, H, D)
+    win = synth.normal_bf16(synth.stream_key(83, synth.T_WIN), 0, B * W * D).reshape(B, W, D)
+    pos = np.array([5000, 77], dtype=np.int64)
+    tau = 1.0 / np.sqrt(D)
+    O = cskv.attend(to_dev_bf16(Q), to_dev(rows), to_dev(ids), to_dev_bf16(win), cache_scale=cscale,
+                    softmax_scale=float(tau), rope_dims=R, q_pos=to_dev(pos)).cpu().numpy()
+    for b in range(B):
+        valid = ids[b][(ids[b] >= 0) & (ids[b] < N)]
+        ref = M.attend(F.bf16_to_f64(Q[b]), dec[b], valid, F.bf16_to_f64(win[b]), tau, R, 10000.0, int(pos[b]))
+        assert row_rel_err(O[b], ref) <= 2e-2
