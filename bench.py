@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4a_128k_bf16",
                     choices=["c4a_128k_bf16", "c128a_1m_bf16", "c4a_1m_fp8_fp4", "mixed61_256k_bf16", "tiny_c4a_2k",
-                             "stream_c4a_128k_bf16", "c128a_1m_mixed", "c128a_1m_fp4"])
+                             "stream_c4a_128k_bf16", "c128a_1m_mixed", "c128a_1m_fp4", "mixed61_256k_reuse"])
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -221,11 +221,13 @@ class Mixed61(Workload):
             lay["O"] = torch.empty((B, H, D), dtype=torch.float32, device=self.dev)
             if kind == "c4a":
                 lay["cache"] = sd.new((B, self.N4, D), s.KIND_NORMAL_BF16, self.key(i, s.T_CACHE, layer), device=self.dev)
-                lay["kidx"] = sd.new((B, self.N4, Di), s.KIND_INT_BF16, self.key(i, s.T_KIDX, layer), device=self.dev,
-                                     a=c.idx_range)
-                lay["qidx"] = sd.new((B, Di), s.KIND_INT_BF16, self.key(i, s.T_QIDX, layer), device=self.dev,
-                                     a=c.idx_range)
-                lay["ids"] = torch.empty((B, c.k), dtype=torch.int32, device=self.dev)
+                lay["reuse"] = c.reuses(layer)
+                if lay["reuse"] is None:   # a layer that reuses ids has no indexer of its own
+                    lay["kidx"] = sd.new((B, self.N4, Di), s.KIND_INT_BF16, self.key(i, s.T_KIDX, layer),
+                                         device=self.dev, a=c.idx_range)
+                    lay["qidx"] = sd.new((B, Di), s.KIND_INT_BF16, self.key(i, s.T_QIDX, layer), device=self.dev,
+                                         a=c.idx_range)
+                    lay["ids"] = torch.empty((B, c.k), dtype=torch.int32, device=self.dev)
                 lay["first"] = (L - 132) // 4
                 lay["win"] = lay["span"][:, 4:, :]
             else:
@@ -243,8 +245,11 @@ class Mixed61(Workload):
         for lay in self.layers:
             cskv.compress(lay["kind"], lay["span"], lay["gate"], lay["cache"], first_entry=lay["first"])
             if lay["kind"] == "c4a":
-                cskv.index_topk(lay["qidx"], lay["kidx"], c.k, ids=lay["ids"], chunk=self.args.chunk)
-                ids = lay["ids"]
+                if lay["reuse"] is None:
+                    cskv.index_topk(lay["qidx"], lay["kidx"], c.k, ids=lay["ids"], chunk=self.args.chunk)
+                    ids = lay["ids"]
+                else:
+                    ids = self.layers[lay["reuse"]]["ids"]   # computed earlier in this step
             else:
                 ids = None
             cskv.attend(lay["Q"], lay["cache"], ids, lay["win"], softmax_scale=c.tau, rope_dims=c.R,
@@ -254,7 +259,7 @@ class Mixed61(Workload):
         # the index calls of the c4a layers alone (the dominant call's timing pass)
         c = self.cfg
         for lay in self.layers:
-            if lay["kind"] == "c4a":
+            if lay["kind"] == "c4a" and lay["reuse"] is None:
                 self.cskv.index_topk(lay["qidx"], lay["kidx"], c.k, ids=lay["ids"], chunk=self.args.chunk)
 
     def step(self, i, dominant_only=False):
@@ -263,11 +268,16 @@ class Mixed61(Workload):
         else:
             self.step_layers()
 
+    def n_dominant(self):
+        """Index calls per step (c4a layers that do not reuse another's ids)."""
+        c = self.cfg
+        return sum(1 for l in range(c.layers) if c.layer_kind(l) == "c4a" and c.reuses(l) is None)
+
     def bytes(self):
         c = self.cfg
         n4 = sum(1 for l in range(c.layers) if c.layer_kind(l) == "c4a")
         n128 = c.layers - n4
-        dom = n4 * c.B * (self.N4 * c.Di * 2 + c.Di * 2 + c.k * 4)
+        dom = self.n_dominant() * c.B * (self.N4 * c.Di * 2 + c.Di * 2 + c.k * 4)
         qo = c.H * c.D * 6
         c4_rest = c.B * (132 * c.D * 2 + 132 * 4 + 32 * c.D * 2 + (c.k + c.W) * c.D * 2 + c.k * 4 + qo)
         c128 = c.B * (128 * c.D * 2 + 128 * 4 + c.D * 2 + (self.N128 + c.W) * c.D * 2 + qo)
@@ -277,7 +287,7 @@ class Mixed61(Workload):
         c = self.cfg
         n4 = sum(1 for l in range(c.layers) if c.layer_kind(l) == "c4a")
         n128 = c.layers - n4
-        return c.B * (n4 * (2 * self.N4 * c.Di + 4 * c.H * c.D * (c.k + c.W)) +
+        return c.B * (self.n_dominant() * 2 * self.N4 * c.Di + n4 * 4 * c.H * c.D * (c.k + c.W) +
                       n128 * 4 * c.H * c.D * (self.N128 + c.W))
 
 
@@ -558,7 +568,7 @@ def main():
         del a, b
 
     mixed = cfg.kind == "mixed"
-    n4 = sum(1 for l in range(cfg.layers) if cfg.layer_kind(l) == "c4a") if mixed else 1
+    n4 = wl.n_dominant() if mixed else 1
     for i in range(args.warmup):
         if stateful:
             wl.step(i)

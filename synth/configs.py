@@ -39,6 +39,7 @@ class Workload:
     key_dtype: str = "bf16"     # indexer keys: "bf16" or "fp4"
     rope_base: float = 10000.0
     layers: int = 1
+    reuse_ids: bool = False     # mixed stack: every second c4a layer reuses the ids of the one before
     description: str = ""
 
     @property
@@ -68,6 +69,13 @@ class Workload:
         if self.kind != "mixed":
             return self.kind
         return "c128a" if layer % 2 == 0 else "c4a"
+
+    def reuses(self, layer: int):
+        """Mixed stack with id reuse: the c4a layer whose ids this layer takes
+        (c4a layers 3, 7, 11, ... take those of layers 1, 5, 9, ...), or None."""
+        if not self.reuse_ids or self.layer_kind(layer) != "c4a" or layer % 4 != 3:
+            return None
+        return layer - 2
 
     def stream_lag(self, b: int) -> int:
         """Streaming workload: sequence b's context is L - stream_lag(b) tokens
@@ -109,6 +117,13 @@ MIXED_61 = Workload(
                 "x 262144 tokens; each layer compresses 128 new tokens, then attends",
 )
 
+MIXED_61_REUSE = Workload(
+    name="mixed61_256k_reuse", number=9, kind="mixed", B=64, L=262144, D=512, R=64, H=64, W=128,
+    Di=128, k=512, idx_range=8, layers=61, reuse_ids=True,
+    description="the 61-layer step with top-k ids reused across c4a layers: 15 of the 30 c4a layers "
+                "skip their indexer and attend over the previous c4a layer's selection",
+)
+
 STREAM_C4A_128K = Workload(
     name="stream_c4a_128k_bf16", number=6, kind="stream", B=32, L=131072, D=512, R=64, H=64, W=128,
     Di=128, k=512, idx_range=8,
@@ -131,5 +146,5 @@ C128A_1M_FP4 = Workload(
                 "scale per 16 channels, 288 B per entry; bf16 window",
 )
 
-ALL = [TINY, C4A_128K, C128A_1M, C4A_1M_Q, MIXED_61, STREAM_C4A_128K, C128A_1M_MIXED, C128A_1M_FP4]
+ALL = [TINY, C4A_128K, C128A_1M, C4A_1M_Q, MIXED_61, STREAM_C4A_128K, C128A_1M_MIXED, C128A_1M_FP4, MIXED_61_REUSE]
 BY_NAME = {w.name: w for w in ALL}

@@ -62,10 +62,14 @@ def _check_layer(wl, layer, b, full_cache_rows=None):
     O_gpu = lay["O"][b].cpu().numpy()
     if kind == "c4a":
         Di = c.Di
-        q = F.bf16_to_f64(synth.int_bf16(key(synth.T_QIDX), b * Di, Di, c.idx_range))
-        kk = F.bf16_to_f64(synth.int_bf16(key(synth.T_KIDX), b * N * Di, N * Di, c.idx_range).reshape(N, Di))
+        # a layer that reuses ids attends over the selection of the layer it names
+        src = lay.get("reuse")
+        src = layer if src is None else src
+        ikey = lambda tensor: wl.key(0, tensor, src)  # noqa: E731
+        q = F.bf16_to_f64(synth.int_bf16(ikey(synth.T_QIDX), b * Di, Di, c.idx_range))
+        kk = F.bf16_to_f64(synth.int_bf16(ikey(synth.T_KIDX), b * N * Di, N * Di, c.idx_range).reshape(N, Di))
         ids = M.topk_ids(M.index_scores(q, kk), c.k)
-        assert np.array_equal(lay["ids"][b].cpu().numpy(), ids), (layer, b)
+        assert np.array_equal(wl.layers[src]["ids"][b].cpu().numpy(), ids), (layer, b)
         # only the selected rows are needed: drawn rows, or rows the span rewrote
         cache = np.zeros((N, D))
         drawn = [r for r in ids if r < first or r >= first + new.shape[0]]
@@ -99,4 +103,16 @@ def test_mixed_step_full_size_first_layers(cskv):
     wl = _run(cfg, cskv)
     for layer in (0, 1):
         for b in (0, cfg.B - 1):
+            _check_layer(wl, layer, b)
+
+
+def test_mixed_step_reusing_ids(cskv):
+    """Eight layers with id reuse: c4a layers 3 and 7 skip their indexer and
+    attend over the selections of layers 1 and 5."""
+    cfg = dataclasses.replace(configs.MIXED_61_REUSE, name="mixed_reuse_small", number=51, B=2, L=8192, layers=8)
+    wl = _run(cfg, cskv)
+    assert [l for l in range(cfg.layers) if cfg.reuses(l) is not None] == [3, 7]
+    assert wl.n_dominant() == 2
+    for layer in range(cfg.layers):
+        for b in range(cfg.B):
             _check_layer(wl, layer, b)
