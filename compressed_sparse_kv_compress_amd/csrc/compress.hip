@@ -153,23 +153,25 @@ __device__ __forceinline__ void fold_c4a(const RowSlice<D>* lo, const RowSlice<D
   }
 }
 
-// One wave owns a run of kC4aRun consecutive entries of one sequence. Entry c
+// One wave owns a run of `run` consecutive entries of one sequence. Entry c
 // reads stride blocks c and c+1 (4 states each); the wave keeps the previous
-// block in registers so every state of the run is loaded once.
-constexpr int kC4aRun = 16;
+// block in registers so every state of the run is loaded once. Long spans use
+// runs of 16; short decode-time spans shorter ones, down to one entry per wave,
+// so that there are enough waves in flight (the entries do not depend on it).
+constexpr int kC4aRunMax = 16;
 constexpr int kCompressThreads = 256;
 
 template <int D, int FMT>
 __global__ __launch_bounds__(kCompressThreads) void k_compress_c4a(
     const uint16_t* __restrict__ S, const float* __restrict__ gate, int64_t T, int64_t n_entries,
     int64_t first_entry, void* __restrict__ cache, float* __restrict__ cache_scale,
-    int64_t cache_rows) {
+    int64_t cache_rows, int run) {
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int64_t b = blockIdx.y;
-  const int64_t c0 = ((int64_t)blockIdx.x * (kCompressThreads / kWave) + wave) * kC4aRun;
+  const int64_t c0 = ((int64_t)blockIdx.x * (kCompressThreads / kWave) + wave) * run;
   if (c0 >= n_entries) return;
-  const int64_t c1 = c0 + kC4aRun < n_entries ? c0 + kC4aRun : n_entries;
+  const int64_t c1 = c0 + run < n_entries ? c0 + run : n_entries;
 
   const uint16_t* Sb = S + b * T * D;
   const float* gb = gate + b * T;
@@ -374,10 +376,13 @@ static hipError_t launch_compress_t(int kind, const uint16_t* S, const float* ga
                                     int64_t T, int64_t n, int64_t first_entry, void* cache,
                                     float* cache_scale, int64_t cache_rows, hipStream_t stream) {
   if (kind == 0) {
-    const int64_t per_block = (int64_t)kC4aRun * (kCompressThreads / kWave);
+    // about 4096 waves over the batch, or runs of kC4aRunMax when there are more
+    int run = kC4aRunMax;
+    while (run > 1 && B * ((n + run - 1) / run) < 4096) run /= 2;
+    const int64_t per_block = (int64_t)run * (kCompressThreads / kWave);
     dim3 grid((unsigned)((n + per_block - 1) / per_block), (unsigned)B);
     hipLaunchKernelGGL((k_compress_c4a<D, FMT>), grid, dim3(kCompressThreads), 0, stream, S, gate,
-                       T, n, first_entry, cache, cache_scale, cache_rows);
+                       T, n, first_entry, cache, cache_scale, cache_rows, run);
   } else {
     dim3 grid((unsigned)n, (unsigned)B);
     hipLaunchKernelGGL((k_compress_c128a<D, FMT>), grid, dim3(kCompressThreads), 0, stream, S,
