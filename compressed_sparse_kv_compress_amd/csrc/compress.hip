@@ -208,21 +208,42 @@ __device__ __forceinline__ void fold_c128a(RowAt row_at, GateAt gate_at, float (
   constexpr int NW = kCompressThreads / kWave;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
+  // 4 batches of 8 states, the next batch's rows and logits loaded while the
+  // current one is folded; the first batch is loaded with the logits
+  RowSlice<D> r[8], nx[8];
+  float gr[8], gn[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    load_row<D>(row_at(32 * wave + u), lane, r[u]);
+    gr[u] = gate_at(32 * wave + u);
+  }
   // softmax over the 128 logits; every wave computes the same max and sum
   const float g0 = gate_at(lane), g1 = gate_at(lane + 64);
   const float m = wave_max(fmaxf(g0, g1));
   const float z = wave_sum(expf(g0 - m) + expf(g1 - m));
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = 0.0f;
-  RowSlice<D> r[8];
-  for (int j0 = 0; j0 < 32; j0 += 8) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load_row<D>(row_at(32 * wave + j0 + u), lane, r[u]);
+  for (int j0 = 0; j0 < 32; j0 += 8) {
+    if (j0 + 8 < 32) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        load_row<D>(row_at(32 * wave + j0 + 8 + u), lane, nx[u]);
+        gn[u] = gate_at(32 * wave + j0 + 8 + u);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float w = expf(gate_at(32 * wave + j0 + u) - m) / z;
+      const float w = expf(gr[u] - m) / z;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) acc[i] = fmaf(w, r[u].v[i], acc[i]);
+    }
+    if (j0 + 8 < 32) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        r[u] = nx[u];
+        gr[u] = gn[u];
+      }
     }
   }
 #pragma unroll
