@@ -667,16 +667,12 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
     constexpr int S = decltype(sc)::value;
     if (i >= n_tiles) return;
     wait_tile<C::kOpsPerTile>(min(kNStage - 2, n_tiles - 1 - i));
+    // raw rows: wave w widens rows 8w .. 8w+7, the ones its own DMA brought
+    // (landed by its own wait), before the barrier that shows the tile to all
+    if constexpr (C::kDmaMix) widen_mix_tile<D>(tile_of(sc));
+    if constexpr (C::kDmaFp4) widen_fp4_tile<D>(tile_of(sc));
     lds_barrier();   // tile i visible to all waves; ring slot S-1 free again
     if (i + kNStage - 1 < n_tiles) issue(std::integral_constant<int, (S + kNStage - 1) % kNStage>{}, i + kNStage - 1);
-    if constexpr (C::kDmaMix) {
-      widen_mix_tile<D>(tile_of(sc));
-      lds_barrier();
-    }
-    if constexpr (C::kDmaFp4) {
-      widen_fp4_tile<D>(tile_of(sc));
-      lds_barrier();
-    }
     if constexpr (C::kDmaFp8) {
       widen_tile<D>(stage_of(sc), tile_of(sc));
       lds_barrier();
