@@ -116,13 +116,19 @@ cskv_status cskv_compress(int32_t kind, const void* S, const float* gate, int64_
  *
  *   s_new      [B, D] bf16;  g_new [B] fp32;  pos [B] int64 device array
  *   ring       [B, W, D] bf16;  ring_gate [B, W] fp32;  W >= 8 (C4A), >= 128 (C128A)
- *   cache      as cskv_compress (bf16, or fp8 codes + cache_scale)
+ *   cache      any cache format of cskv_compress (bf16; fp8 rows or mixed rows with
+ *              cache_scale; fp4 rows), cache_rows rows per sequence
  *   n_entries  [B] int32 or NULL: set to the sequence's entries in the cache,
  *              min(complete entries, cache_rows) (C4A: pos >= 7 ? (pos-7)/4+1
  *              : 0; C128A: (pos+1)/128), for cskv_index_topk / cskv_attend
  *   n_window   [B] int32 or NULL: set to min(pos+1, W), the ring rows that
  *              hold states (the leading ones until the ring has wrapped)
  * Sequences with a negative position keep their counts.
+ * EINVAL for W below the entry's w, a null or misaligned pointer (s_new, ring
+ * and cache 16-byte aligned) or a missing cache_scale; EUNSUPPORTED for D not
+ * in {128, 512}, mixed or fp4 rows with D != 512, or an unknown cache format.
+ * Positions are device data: the host cannot check them, so a position whose
+ * older states were never appended folds whatever the ring holds.
  */
 cskv_status cskv_append(int32_t kind, const void* s_new, const float* g_new, const int64_t* pos,
                         int64_t B, int32_t D, void* ring, float* ring_gate, int32_t W,
