@@ -683,6 +683,23 @@ def main():
         "tflops_per_s": round(wl.flops() / (ms_step * 1e-3) / 1e12, 2),
         "setup_s": round(setup_s, 1),
     }
+    # what a plain read stream reaches on this machine: torch's max over 1 GiB viewed
+    # as int64 (a reduction that only reads), after the timed steps, median of 5
+    probe = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
+    probe.amax()
+    times = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        probe.amax()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del probe
+    probe_gbs = (1 << 30) / (sorted(times)[2] * 1e-3) / 1e9
+    out["hbm_probe"] = {"read_gbs": round(probe_gbs, 1),
+                        "kind": "torch amax over 1 GiB of int64 (read-only stream), median of 5"}
+    out["roofline"]["frac_of_probe"] = round(achieved / probe_gbs, 4)
     log(f"timed: {ms_step:.4f} ms/step")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
