@@ -386,73 +386,107 @@ __device__ __forceinline__ void lds_store_b128_unordered(void* p, uint4 v) {
   asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(d) : "memory");
 }
 
-// Widens the mixed rows of a tile in place (rows whose scale is 0 are bf16
-// already; the scales of rows 8w .. 8w+7 sit in the pad of row 8w): thread t
-// takes row t/8; part p < 7 turns the 64 codes at raw
-// bytes 64p .. 64p+63 into channels 64p .. 64p+63 times the row scale, part 7
-// moves the 64 rotary channels (raw bytes 448 .. 575) to channels 448 .. 511,
-// all in the swizzled chunk layout. The 8 threads of a row are lanes of one
-// wave: their LDS reads are issued before any of their writes.
+// Raw rows (mixed or fp4) are widened in place in two phases: a read phase
+// that takes one thread's share of the tile's raw bytes into registers, then
+// eight write slices. Thread t takes row t/8 (rows 8w .. 8w+7 are the ones
+// wave w's own DMA brought, so the wave's own tile wait covers them), and
+// writes 8 of the row's 64 output chunks (16 bytes, 8 channels each, in the
+// swizzled chunk layout). A row's reads are all issued before any of its
+// writes, by the lanes of one wave, and LDS runs one wave's accesses in
+// order; the stores' memory clobber keeps the compiler from moving a read
+// past them. Rows whose scale (mixed) or flag (fp4) is 0 are bf16 already;
+// the values of rows 8w .. 8w+7 sit in the pad of row 8w. A thread with
+// nothing to write (such a row, or no next tile) stores into its row's pad
+// instead, which nothing reads after the read phase: the stores need no
+// branch.
+//
+// Mixed rows: part p = t % 8 turns codes 8c .. 8c+7 (raw bytes 8c ..) of
+// chunks c = p + 8s, s < 7, into channels 8c .. 8c+7 times the row scale, and
+// moves rotary chunk 56 + p (raw bytes 448 + 16p ..) to its place: every part
+// does the same work.
+struct MixRaw {
+  uint2 code[7];
+  uint4 rope;
+  float sc;
+};
+
 template <int D>
-__device__ __forceinline__ void widen_mix_tile(uint16_t* tile) {
+__device__ __forceinline__ void raw_read(const uint16_t* tile, MixRaw& m) {
   using C = AttCfg<D, kFmtMix, false>;
-  const int t = threadIdx.x;
-  const int r = t >> 3, part = t & 7;
-  const float sc = reinterpret_cast<const float*>(tile + (r & ~7) * C::KROW + D)[r & 7];
-  uint16_t* row = tile + r * C::KROW;
-  const int swz = chunk_swz(r);
-  // 128 bytes from raw byte 64 part (codes; the upper half unused) or from the
-  // rotary channels' raw bytes, read whatever the row holds
-  const uint4* src = reinterpret_cast<const uint4*>(row + (part < 7 ? 32 * part : (D - kMixRope) / 2));
-  uint4 c[8];
+  const int t = threadIdx.x, r = t >> 3, p = t & 7;
+  const uint16_t* row = tile + r * C::KROW;
+  m.sc = reinterpret_cast<const float*>(tile + (r & ~7) * C::KROW + D)[r & 7];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) c[j] = src[j];
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the row's reads are done before its writes
-  if (sc > 0.0f) {
-    if (part < 7) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ch0 = 8 * part + 2 * j;          // logical chunks ch0, ch0 + 1
-        lds_store_b128_unordered(row + 8 * (ch0 ^ swz), fp8x8_to_bf16x8_scaled(make_uint2(c[j].x, c[j].y), sc));
-        lds_store_b128_unordered(row + 8 * ((ch0 + 1) ^ swz), fp8x8_to_bf16x8_scaled(make_uint2(c[j].z, c[j].w), sc));
-      }
-    } else {
-      // rotary channels 448 + 8j .. +7: logical chunk 56 + j
-#pragma unroll
-      for (int j = 0; j < 8; ++j) lds_store_b128_unordered(row + 8 * ((56 + j) ^ swz), c[j]);
-    }
-  }
+  for (int s = 0; s < 7; ++s) m.code[s] = reinterpret_cast<const uint2*>(row)[p + 8 * s];
+  m.rope = reinterpret_cast<const uint4*>(row + (D - kMixRope) / 2)[p];
 }
 
-// Widens the fp4 rows of a tile in place (flag 0: bf16 already; flags of rows
-// 8w .. 8w+7 in the pad of row 8w): thread t takes row t/8, part p turns the
-// 32 code bytes at raw byte 32p and their 4 group scales (raw bytes 256 + 4p
-// ..) into channels 64p .. 64p+63, exactly, in the swizzled chunk layout. The
-// 8 threads of a row are lanes of one wave: their reads precede their writes.
 template <int D>
-__device__ __forceinline__ void widen_fp4_tile(uint16_t* tile) {
-  using C = AttCfg<D, kFmtFp4, false>;
-  const int t = threadIdx.x;
-  const int r = t >> 3, part = t & 7;
-  const float flag = reinterpret_cast<const float*>(tile + (r & ~7) * C::KROW + D)[r & 7];
+__device__ __forceinline__ void raw_write(uint16_t* tile, const MixRaw& m, int s, bool on) {
+  using C = AttCfg<D, kFmtMix, false>;
+  static_assert(D - kMixRope == 7 * 64, "mixed rows: 7 code chunks per part");
+  const int t = threadIdx.x, r = t >> 3, p = t & 7;
   uint16_t* row = tile + r * C::KROW;
-  const int swz = chunk_swz(r);
-  const uint4 c0 = reinterpret_cast<const uint4*>(row + 16 * part)[0];
-  const uint4 c1 = reinterpret_cast<const uint4*>(row + 16 * part)[1];
-  const uint32_t sw = reinterpret_cast<const uint32_t*>(row + D / 4)[part];
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the row's reads are done before its writes
-  if (flag > 0.0f) {
-    const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const int chunk = (s < 7 ? p + 8 * s : 56 + p) ^ chunk_swz(r);
+  const uint4 v = s < 7 ? fp8x8_to_bf16x8_scaled(m.code[s], m.sc) : m.rope;
+  lds_store_b128_unordered(row + (on && m.sc > 0.0f ? 8 * chunk : D), v);
+}
+
+// fp4 rows: part p takes chunks c = p + 8s: the code word at raw byte 4c
+// (channels 8c .. 8c+7) times the scale of group c/2 (raw byte 256 + c/2),
+// exactly. The strided chunks keep the word reads and the widened stores of a
+// wave's 64 lanes on distinct LDS banks.
+struct Fp4Raw {
+  uint32_t code[8];
+  uint4 sc0, sc1;   // the row's 32 group scales
+  float flag;
+};
+
+template <int D>
+__device__ __forceinline__ void raw_read(const uint16_t* tile, Fp4Raw& m) {
+  using C = AttCfg<D, kFmtFp4, false>;
+  static_assert(D == 512, "fp4 rows: 8 chunks per part");
+  const int t = threadIdx.x, r = t >> 3, p = t & 7;
+  const uint16_t* row = tile + r * C::KROW;
+  m.flag = reinterpret_cast<const float*>(tile + (r & ~7) * C::KROW + D)[r & 7];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {            // group 4p + j: channels 64p + 16j .. +15
-      const float s = e4m3_to_f32((sw >> (8 * j)) & 0xFFu);
+  for (int s = 0; s < 8; ++s) m.code[s] = reinterpret_cast<const uint32_t*>(row)[p + 8 * s];
+  m.sc0 = reinterpret_cast<const uint4*>(row + D / 4)[0];
+  m.sc1 = reinterpret_cast<const uint4*>(row + D / 4)[1];
+}
+
+template <int D>
+__device__ __forceinline__ void raw_write(uint16_t* tile, const Fp4Raw& m, int s, bool on) {
+  using C = AttCfg<D, kFmtFp4, false>;
+  const int t = threadIdx.x, r = t >> 3, p = t & 7;
+  uint16_t* row = tile + r * C::KROW;
+  const uint32_t sw[8] = {m.sc0.x, m.sc0.y, m.sc0.z, m.sc0.w, m.sc1.x, m.sc1.y, m.sc1.z, m.sc1.w};
+  // group 4s + p/2: byte p/2 of scale word s, exactly, through the hardware
+  // E4M3 converter
+  const uint32_t code = (sw[s] >> (8 * (p >> 1))) & 0xFFu;
+  const float gs = __uint_as_float(fp8x2_to_bf16x2<false>(code) << 16);
+  const uint4 v = fp4x8_to_bf16x8_scaled(m.code[s], gs);
+  lds_store_b128_unordered(row + (on && m.flag > 0.0f ? 8 * ((p + 8 * s) ^ chunk_swz(r)) : D), v);
+}
+
+// The register share of a raw tile for row format CF (an empty type for others).
+struct NoRaw {};
+template <int D>
+__device__ __forceinline__ void raw_read(const uint16_t*, NoRaw&) {}
+template <int D>
+__device__ __forceinline__ void raw_write(uint16_t*, const NoRaw&, int, bool) {}
+template <int CF> struct RawOf { using type = NoRaw; };
+template <> struct RawOf<kFmtMix> { using type = MixRaw; };
+template <> struct RawOf<kFmtFp4> { using type = Fp4Raw; };
+
+// The whole widening of a tile's rows, waiting for the reads before the writes.
+template <int D, typename R>
+__device__ __forceinline__ void widen_raw_tile(uint16_t* tile) {
+  R m;
+  raw_read<D>(tile, m);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int ch = 8 * part + 2 * j + h;   // logical chunk
-        lds_store_b128_unordered(row + 8 * (ch ^ swz), fp4x8_to_bf16x8_scaled(w[2 * j + h], s));
-      }
-    }
-  }
+  for (int s = 0; s < 8; ++s) raw_write<D>(tile, m, s, true);
 }
 
 template <int D, int CF, bool WFP8>
@@ -635,9 +669,15 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
     *reinterpret_cast<uint4*>(p_l + 16 * wave * kTK + p_off) = pw;
   };
 
+  // raw rows: this thread's share of the next tile, read before this tile's
+  // PV products and written back widened between them
+  typename RawOf<CF>::type raw;
+
   // O^T[this wave's channels x 64 heads] += K^T P^T on a ready tile whose
-  // probabilities are in p_l
-  auto pv = [&](const uint16_t* kt) __attribute__((always_inline)) {
+  // probabilities are in p_l; with WIDEN, write slice j of the next raw tile
+  // (held in `raw`, at nt) after the products of channel tile j if `on`
+  auto pv = [&](const uint16_t* kt, auto widen, uint16_t* nt, bool on) __attribute__((always_inline)) {
+    constexpr bool WIDEN = decltype(widen)::value;
     bf16x8_t pb[4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) pb[ht] = *reinterpret_cast<const bf16x8_t*>(p_l + 16 * ht * kTK + p_off);
@@ -658,6 +698,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
       const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, kk);
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) acc[j][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, pb[ht], acc[j][ht], 0, 0, 0);
+      if constexpr (WIDEN) {
+        static_assert(CTW == 8, "one widening slice per channel tile");
+        raw_write<D>(nt, raw, j, on);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -666,20 +710,33 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   auto step = [&](auto sc, int i) __attribute__((always_inline)) {
     constexpr int S = decltype(sc)::value;
     if (i >= n_tiles) return;
+    // (raw rows: tile i was waited for and widened in the previous step)
     wait_tile<C::kOpsPerTile>(min(kNStage - 2, n_tiles - 1 - i));
-    // raw rows: wave w widens rows 8w .. 8w+7, the ones its own DMA brought
-    // (landed by its own wait), before the barrier that shows the tile to all
-    if constexpr (C::kDmaMix) widen_mix_tile<D>(tile_of(sc));
-    if constexpr (C::kDmaFp4) widen_fp4_tile<D>(tile_of(sc));
     lds_barrier();   // tile i visible to all waves; ring slot S-1 free again
     if (i + kNStage - 1 < n_tiles) issue(std::integral_constant<int, (S + kNStage - 1) % kNStage>{}, i + kNStage - 1);
     if constexpr (C::kDmaFp8) {
       widen_tile<D>(stage_of(sc), tile_of(sc));
       lds_barrier();
     }
+    // raw rows: wave w widens rows 8w .. 8w+7 of tile i+1, the ones its own
+    // DMA brought (tiles i+2, i+3 may still be in flight behind it): it reads
+    // them before this tile's QK^T and writes them back under its PV
+    // products; the next step's barrier shows them. One PV body either way
+    // (the last tile reads its successor's slot and writes nothing), so the
+    // accumulators keep their registers.
+    constexpr int SN = (S + 1) % kNStage;
+    const bool nxt = i + 1 < n_tiles;
+    if constexpr (C::kDmaRaw) {
+      if (nxt) wait_tile<C::kOpsPerTile>(min(kNStage - 2, n_tiles - 2 - i));
+      raw_read<D>(tile_of(std::integral_constant<int, SN>{}), raw);
+    }
     if (wave_on) qk_softmax(tile_of(sc), pb_of(sc), vs_of(sc));
     lds_barrier();   // probabilities of all heads visible
-    pv(tile_of(sc));
+    if constexpr (C::kDmaRaw) {
+      pv(tile_of(sc), std::true_type{}, tile_of(std::integral_constant<int, SN>{}), nxt);
+    } else {
+      pv(tile_of(sc), std::false_type{}, nullptr, false);
+    }
   };
 
   // At most two passes over the split: the second only when some head's true
@@ -700,6 +757,14 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
     if (n_tiles > 0) issue(std::integral_constant<int, 0>{}, 0);
     if (n_tiles > 1) issue(std::integral_constant<int, 1>{}, 1);
     if (n_tiles > 2) issue(std::integral_constant<int, 2>{}, 2);
+    if constexpr (C::kDmaRaw) {
+      // raw rows: the first tile is widened here, later ones under the
+      // previous tile's PV products
+      if (n_tiles > 0) {
+        wait_tile<C::kOpsPerTile>(min(kNStage - 2, n_tiles - 1));
+        widen_raw_tile<D, typename RawOf<CF>::type>(tile0);
+      }
+    }
     if (pass == 0 && splits == 1 && t < a.rope_dims / 2) {
       // the rotary table of a single split, while the first tiles are in flight
       const double theta = pow((double)a.rope_base, -2.0 * (double)t / (double)a.rope_dims);
