@@ -267,7 +267,9 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
     }
     if constexpr (C::kDmaRaw) {
       // dense rows that all come from the cache: contiguous raw rows, scalar
-      // row addresses, the lanes past a row's bytes read the zero row
+      // row addresses; only the lanes of a row's bytes move data (the other
+      // chunks are written by the widening), and every DMA has active lanes,
+      // so each still counts once in the wave's vmcnt
       const int wv = __builtin_amdgcn_readfirstlane(wave);
       const int64_t row0 = tile0 + 8 * wv;
       if (dense && row0 + 8 <= n_sel) {
@@ -279,13 +281,14 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
                                            4, 0, 0);
         }
         constexpr int RBY = row_bytes<D, CF>();
-        const uint8_t* src = lane < C::kRawChunks ? rsrc.cache + row0 * RBY + 16 * lane : g_zero_row + 16 * lane;
-        const int step = lane < C::kRawChunks ? RBY : 0;
+        const uint8_t* src = rsrc.cache + row0 * RBY + 16 * lane;
+        if (lane < C::kRawChunks) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + i * step),
-                                           (__attribute__((address_space(3))) void*)(tile + (8 * wv + i) * C::KROW),
-                                           16, 0, kCachePolicyStream);
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + i * RBY),
+                                             (__attribute__((address_space(3))) void*)(tile + (8 * wv + i) * C::KROW),
+                                             16, 0, kCachePolicyStream);
+          }
         }
         return;
       }
@@ -312,14 +315,16 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
       for (int i = 0; i < 8; ++i) {
         const int row = 8 * wave + i;
         const uint8_t* src = reinterpret_cast<const uint8_t*>(lane_u64(src_l, i));
-        // raw row: its bytes land at chunk positions 0 .. kRawChunks-1 (the
-        // other lanes read the zero row); bf16 row: swizzled chunks as in the
-        // bf16 path
-        const uint8_t* a = ((mix_m >> i) & 1) ? (lane < C::kRawChunks ? src + 16 * lane : g_zero_row + 16 * lane)
-                                              : src + 16 * (lane ^ chunk_swz(row));
-        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)a,
-                                         (__attribute__((address_space(3))) void*)(tile + row * C::KROW), 16, 0,
-                                         kCachePolicyStream);
+        // raw row: its bytes land at chunk positions 0 .. kRawChunks-1, moved
+        // by those lanes only (the widening writes the other chunks); bf16 row:
+        // swizzled chunks as in the bf16 path. Every DMA has active lanes.
+        const bool raw_row = (mix_m >> i) & 1;
+        const uint8_t* a = raw_row ? src + 16 * lane : src + 16 * (lane ^ chunk_swz(row));
+        if (!raw_row || lane < C::kRawChunks) {
+          __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)a,
+                                           (__attribute__((address_space(3))) void*)(tile + row * C::KROW), 16, 0,
+                                           kCachePolicyStream);
+        }
       }
       return;
     }
