@@ -1116,6 +1116,17 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
       cs_l[1][t] = (float)sin(ang);
     }
   }
+  // thread (grp, hh0) folds the (reference maximum, sum) pairs of head hh0
+  // over splits grp, grp + 4, ..; the first kMlU of them are loaded at once,
+  // ahead of the partials, and kept for the weights
+  const int hh0 = t & 63, grp = t >> 6;
+  constexpr int kMlU = 4;
+  float2 mlr[kMlU];
+#pragma unroll
+  for (int u = 0; u < kMlU; ++u) {
+    const int sp = grp + 4 * u;
+    mlr[u] = ml[(int64_t)(sp < splits ? sp : 0) * kHMax + hh0];
+  }
   // the first 16 splits' blocks are loaded before the weights are known
   constexpr int U = 16;
   const int ht = t >> 6, lane = t & 63;
@@ -1126,18 +1137,21 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
   uint2 v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) v[u] = src[(int64_t)(u < splits ? u : splits - 1) * pstride];
-  const int hh0 = t & 63, grp = t >> 6;
   {
     float M = -INFINITY, L = 0.0f;
-    for (int sp = grp; sp < splits; sp += 4) {
-      const float2 v = ml[(int64_t)sp * kHMax + hh0];
+    auto fold = [&](float2 v) {
       if (v.x > M) {
         L = (M == -INFINITY ? 0.0f : L * exp2f(M - v.x)) + v.y;
         M = v.x;
       } else {
         L += v.y * exp2f(v.x - M);
       }
+    };
+#pragma unroll
+    for (int u = 0; u < kMlU; ++u) {
+      if (grp + 4 * u < splits) fold(mlr[u]);
     }
+    for (int sp = grp + 4 * kMlU; sp < splits; sp += 4) fold(ml[(int64_t)sp * kHMax + hh0]);
     mq_l[grp][hh0] = M;
     lq_l[grp][hh0] = L;
   }
@@ -1153,10 +1167,13 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
       if (mg != -INFINITY) L += lq_l[gg][hh0] * exp2f(mg - M);
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    for (int sp = grp; sp < splits; sp += 4) {
-      const float2 v = ml[(int64_t)sp * kHMax + hh0];
-      w_l[sp * kHMax + hh0] = v.x == -INFINITY ? 0.0f : exp2f(v.x - M) * v.y * inv;
+    auto weight = [&](float2 v) { return v.x == -INFINITY ? 0.0f : exp2f(v.x - M) * v.y * inv; };
+#pragma unroll
+    for (int u = 0; u < kMlU; ++u) {
+      const int sp = grp + 4 * u;
+      if (sp < splits) w_l[sp * kHMax + hh0] = weight(mlr[u]);
     }
+    for (int sp = grp + 4 * kMlU; sp < splits; sp += 4) w_l[sp * kHMax + hh0] = weight(ml[(int64_t)sp * kHMax + hh0]);
   }
   __syncthreads();
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
