@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--repeats", type=int, default=10,
+                    help="repeats of the K timed steps after the main measurement, for the spread of the step time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--chunk", type=int, default=0, help="index_topk chunk override")
@@ -306,7 +308,8 @@ class StreamC4a(Workload):
         c = self.cfg
         B, L, D, H, Di, W = c.B, c.L, c.D, c.H, c.Di, c.W
         from synth.configs import c4a_entries
-        self.n_steps = self.args.warmup + self.args.steps
+        # warmup, the timed steps, then their repeats for the spread of the step time
+        self.n_steps = self.args.warmup + self.args.steps * (1 + self.args.repeats)
         self.rows = c4a_entries(L + self.n_steps) + 1
         log(f"setup: stream caches ({B} x {self.rows} entries)")
         self.cache = sd.new((B, self.rows, D), s.KIND_NORMAL_BF16, self.key(0, s.T_CACHE), device=self.dev)
@@ -421,17 +424,41 @@ def cpu_baseline(cfg, seconds):
         else:
             M.c128a_decode(st["Q"], st["cache"], st["win"], cfg.tau, cfg.R, cfg.rope_base, cfg.q_pos)
 
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        one(seqs[done % n_seq])
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": done / el, "unit": "decode tokens/s per layer", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} single-sequence {kind} layer decodes ({n_seq} distinct sequences of the "
-                      f"{cfg.name} workload, inputs generated before timing) in {el:.1f} s"}
+    def timed(limit):
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            one(seqs[done % n_seq])
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= limit:
+                return done, el
+
+    done, el = timed(seconds)
+    out = {"value": done / el, "unit": "decode tokens/s per layer", "cores": int(cores), "kind": "oracle",
+           "sample": f"{done} single-sequence {kind} layer decodes ({n_seq} distinct sequences of the "
+                     f"{cfg.name} workload, inputs generated before timing) in {el:.1f} s",
+           "nproc": os.cpu_count(), "cpu_model": _cpu_model()}
+    # a per-core rate: the same sample with the BLAS pool held to one thread
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            d1, e1 = timed(max(seconds / 4, 1.0))
+        out["one_thread"] = {"value": d1 / e1, "sample": f"{d1} decodes in {e1:.1f} s"}
+    except Exception as e:   # no thread control: report without it
+        out["one_thread"] = {"value": None, "sample": f"not measured ({type(e).__name__})"}
+    return out
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # ------------------------------------------------------------------ HBM traffic from counters
@@ -634,6 +661,17 @@ def main():
     torch.cuda.synchronize()
     dom_ms = start.elapsed_time(end) / (args.steps * n4)
 
+    # spread of the step time: the K timed steps repeated, each repeat between
+    # two events as above (a stateful workload continues its stream)
+    rep_ms = []
+    for r in range(args.repeats):
+        start.record()
+        for i in range(args.steps):
+            run_step(args.steps * (1 + r) + i if stateful else i)
+        end.record()
+        torch.cuda.synchronize()
+        rep_ms.append(start.elapsed_time(end) / args.steps)
+
     dom_bytes, rest_bytes = wl.bytes()
     dom_bytes_launch = dom_bytes / n4
     achieved = dom_bytes_launch / (dom_ms * 1e-3) / 1e9
@@ -683,6 +721,15 @@ def main():
         "tflops_per_s": round(wl.flops() / (ms_step * 1e-3) / 1e12, 2),
         "setup_s": round(setup_s, 1),
     }
+    if rep_ms:
+        import numpy as np
+        out["step_ms_spread"] = {
+            "repeats": len(rep_ms),
+            "median": round(float(np.percentile(rep_ms, 50)), 5),
+            "p10": round(float(np.percentile(rep_ms, 10)), 5),
+            "p90": round(float(np.percentile(rep_ms, 90)), 5),
+            "of": f"ms per step of each repeat of the {args.steps} timed steps, after the timed region",
+        }
     # what a plain read stream reaches on this machine: torch's max over 1 GiB viewed
     # as int64 (a reduction that only reads), after the timed steps, median of 5
     probe = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
@@ -707,6 +754,8 @@ def main():
         if mixed:
             # the oracle sample is one c4a layer; a 61-layer step costs about 61 of them
             out["cpu_baseline"]["value"] /= cfg.layers
+            if out["cpu_baseline"]["one_thread"]["value"]:
+                out["cpu_baseline"]["one_thread"]["value"] /= cfg.layers
             out["cpu_baseline"]["unit"] = "decode tokens/s per 61-layer step (sampled c4a layer rate / 61)"
     print(json.dumps(out), flush=True)
 
