@@ -55,7 +55,7 @@ def v4_sequence_bytes(tokens: int, n_c4a: int = 30, n_c128a: int = 31, D: int = 
 
 
 def mixed_attention_row_bytes(D: int = 512, R: int = 64) -> int:
-    """An attention row with bf16 rotary channels and fp8 for the rest."""
+    """An attention row: the rotary channels in bf16, every other channel an fp8 code."""
     return (D - R) + 2 * R + 4
 
 
