@@ -192,7 +192,9 @@ cskv_status cskv_index_topk(const void* q_idx, int32_t key_dtype, const void* k_
  *   Q            [B, H, D] bf16;  1 <= H <= 64;  D 128 or 512
  *   cache        [B, cache_rows, D] bf16, or fp8 codes + cache_scale [B, cache_rows] fp32,
  *                or mixed rows (CSKV_FP8_ROPE64, D = 512) + cache_scale, or fp4 rows
- *                (CSKV_FP4_E2M1, D = 512, layout as in cskv_compress)
+ *                (CSKV_FP4_E2M1, D = 512, layout as in cskv_compress); the scale of a
+ *                mixed row must be positive and finite, as cskv_compress writes it (an
+ *                all-zero row gets 1): a row read with another scale has undefined values
  *   ids          [B, k] int32 entry ids (ids < 0 or >= cache_rows are skipped),
  *                or NULL for dense attention over entries 0 .. n_entries[b]-1
  *   n_entries    dense mode only: [B] int32 device counts, or NULL for cache_rows
