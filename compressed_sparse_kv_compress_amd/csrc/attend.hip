@@ -1092,7 +1092,9 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend_hs(AttendArgs a, int 
 // block of all splits at once and sums them weighted.
 constexpr int kMergeMaxSplits = 256;
 
-template <int D>
+// U: partial blocks a thread loads at once (4, 8 or 16: the smallest that
+// holds every split when there are at most 16, so that no load repeats another)
+template <int D, int U>
 __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
                                                       const uint16_t* __restrict__ ws_acc,
                                                       const float* __restrict__ ws_ml) {
@@ -1117,18 +1119,18 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
     }
   }
   // thread (grp, hh0) folds the (reference maximum, sum) pairs of head hh0
-  // over splits grp, grp + 4, ..; the first kMlU of them are loaded at once,
-  // ahead of the partials, and kept for the weights
+  // over splits grp, grp + 4, ..; the first kMlU of them (every split when
+  // there are at most U) are loaded at once, ahead of the partials, and kept
+  // for the weights
   const int hh0 = t & 63, grp = t >> 6;
-  constexpr int kMlU = 4;
+  constexpr int kMlU = U / 4;
   float2 mlr[kMlU];
 #pragma unroll
   for (int u = 0; u < kMlU; ++u) {
     const int sp = grp + 4 * u;
     mlr[u] = ml[(int64_t)(sp < splits ? sp : 0) * kHMax + hh0];
   }
-  // the first 16 splits' blocks are loaded before the weights are known
-  constexpr int U = 16;
+  // the first U splits' blocks are loaded before the weights are known
   const int ht = t >> 6, lane = t & 63;
   const int hh = 16 * ht + (lane & 15);
   const int w = q / CTW, j = q % CTW;
@@ -1256,8 +1258,14 @@ static hipError_t launch_attend_t(const AttendPlan& p, const AttendArgs& a, void
                      p.keys_per_split, ws_acc, ws_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((k_attend_merge<D>), dim3((unsigned)(D / 16), (unsigned)a.B), dim3(256),
-                     (size_t)p.splits * kHMax * sizeof(float), stream, a, p.splits, ws_acc, ws_ml);
+  const dim3 mgrid((unsigned)(D / 16), (unsigned)a.B);
+  const size_t mlds = (size_t)p.splits * kHMax * sizeof(float);
+  if (p.splits <= 4)
+    hipLaunchKernelGGL((k_attend_merge<D, 4>), mgrid, dim3(256), mlds, stream, a, p.splits, ws_acc, ws_ml);
+  else if (p.splits <= 8)
+    hipLaunchKernelGGL((k_attend_merge<D, 8>), mgrid, dim3(256), mlds, stream, a, p.splits, ws_acc, ws_ml);
+  else
+    hipLaunchKernelGGL((k_attend_merge<D, 16>), mgrid, dim3(256), mlds, stream, a, p.splits, ws_acc, ws_ml);
   return hipGetLastError();
 }
 
