@@ -282,6 +282,30 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress_c128a(
                       FMT == kFmtFp8 || FMT == kFmtMix ? cache_scale + row : nullptr);
 }
 
+// bf16 rows when entries are fewer than compute units: workgroup (c, b, q)
+// folds channels 128q .. 128q+127 of entry c. Every channel's fold (weights,
+// order of the sums) is the whole-row kernel's, so the rows are bit-identical.
+template <int D>
+__global__ __launch_bounds__(kCompressThreads) void k_compress_c128a_slice(
+    const uint16_t* __restrict__ S, const float* __restrict__ gate, int64_t T, int64_t first_entry,
+    uint16_t* __restrict__ cache, int64_t cache_rows) {
+  constexpr int DS = 128;
+  constexpr int NW = kCompressThreads / kWave;
+  __shared__ float part[NW][DS];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int64_t b = blockIdx.y;
+  const int64_t c = blockIdx.x;
+  const int q = blockIdx.z;
+  const uint16_t* Sw = S + (b * T + 128 * c) * D + DS * q;
+  const float* gw = gate + b * T + 128 * c;
+  float acc[DS / kWave];
+  fold_c128a<DS>([&](int j) { return Sw + (int64_t)j * D; }, [&](int j) { return gw[j]; }, part, acc);
+  if (wave != 0) return;
+  const int64_t row = b * cache_rows + first_entry + c;
+  store_entry<DS, kFmtBf16>(acc, lane, cache + row * D + DS * q, nullptr);
+}
+
 // ---------------------------------------------------------------- append
 // Sequence b appends state s_new[b] (gate logit g_new[b]) as token p = pos[b]
 // (p < 0: the sequence is skipped). The state goes to ring slot p mod W; the
@@ -405,6 +429,15 @@ static hipError_t launch_compress_t(int kind, const uint16_t* S, const float* ga
     hipLaunchKernelGGL((k_compress_c4a<D, FMT>), grid, dim3(kCompressThreads), 0, stream, S, gate,
                        T, n, first_entry, cache, cache_scale, cache_rows, run);
   } else {
+    if constexpr (FMT == kFmtBf16 && D == 512) {
+      if (n * B < 256) {
+        // fewer entries than compute units: four channel slices per entry
+        dim3 grid((unsigned)n, (unsigned)B, D / 128);
+        hipLaunchKernelGGL((k_compress_c128a_slice<D>), grid, dim3(kCompressThreads), 0, stream, S, gate, T,
+                           first_entry, reinterpret_cast<uint16_t*>(cache), cache_rows);
+        return hipGetLastError();
+      }
+    }
     dim3 grid((unsigned)n, (unsigned)B);
     hipLaunchKernelGGL((k_compress_c128a<D, FMT>), grid, dim3(kCompressThreads), 0, stream, S,
                        gate, T, n, first_entry, cache, cache_scale, cache_rows);

@@ -7,7 +7,7 @@ import torch
 import synth
 from oracle import formats as F
 from oracle import method as M
-from tests.helpers import bf16_f64, row_rel_err, to_dev, to_dev_bf16
+from tests.helpers import bf16_bits, bf16_f64, row_rel_err, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -112,3 +112,18 @@ def test_compress_deterministic(cskv):
         cskv.compress("c4a", to_dev_bf16(S), to_dev(g), cache)
         outs.append(cache.view(torch.int16).cpu().numpy())
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_c128a_channel_slices_match_whole_rows(cskv):
+    """bf16 c128a rows of a launch with fewer entries than compute units are
+    folded in four channel slices; they equal, bit for bit, the rows of a
+    launch large enough for whole-row workgroups, and the oracle's entries."""
+    D, T = 512, 128 * 300
+    S, g = _inputs(77, 1, T, D)
+    whole = torch.zeros((1, 300, D), dtype=torch.bfloat16, device="cuda")
+    cskv.compress("c128a", to_dev_bf16(S), to_dev(g), whole)            # 300 workgroups
+    part = torch.zeros((1, 100, D), dtype=torch.bfloat16, device="cuda")
+    cskv.compress("c128a", to_dev_bf16(S[:, : 128 * 100].copy()), to_dev(g[:, : 128 * 100].copy()), part)
+    assert np.array_equal(bf16_bits(part), bf16_bits(whole)[:, :100])
+    ref = M.compress("c128a", F.bf16_to_f64(S[0, : 128 * 100]), g[0, : 128 * 100].astype(np.float64))
+    assert row_rel_err(bf16_f64(part)[0], ref) <= 4e-3
