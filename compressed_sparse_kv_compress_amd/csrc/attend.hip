@@ -16,6 +16,8 @@
 //     instruction per row, no registers); fp8 rows go by DMA into a staging
 //     ring and one cooperative pass widens the codes to bf16 exactly, and the
 //     row scales travel by DMA too (folded into logits and probabilities);
+//     mixed and fp4 rows land raw in their tile rows and are widened in place,
+//     tile i+1 under tile i's PV products (see raw_read / raw_write);
 //     other shapes go through registers. Empty slots (an id out of range, or
 //     past the last key) load a zero row, so every wave issues the same number
 //     of DMA instructions per tile and the wait for a tile is an exact count of
