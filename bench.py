@@ -23,6 +23,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -38,12 +40,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4a_128k_bf16",
+    ap.add_argument("--workload", default=None,
                     choices=["c4a_128k_bf16", "c128a_1m_bf16", "c4a_1m_fp8_fp4", "mixed61_256k_bf16", "tiny_c4a_2k",
                              "stream_c4a_128k_bf16", "c128a_1m_mixed", "c128a_1m_fp4", "mixed61_256k_reuse"])
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0 = automatic)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="without --workload: measure the headline workload only, not the 1M and 61-layer ones")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
+                    help="parallel oracle time per workload (the one-thread rate takes a quarter of it more)")
     ap.add_argument("--repeats", type=int, default=10,
                     help="repeats of the K timed steps after the main measurement, for the spread of the step time")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -60,6 +65,16 @@ def parse():
 
 
 # ------------------------------------------------------------------ workloads
+
+def _host(t):
+    """A device tensor's bytes on the host: bf16 as uint16 bit patterns."""
+    if t is None:
+        return None
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy()
+
 
 class Workload:
     """Device inputs for one or more sets, a step function and byte accounting."""
@@ -145,6 +160,27 @@ class C4aLayer(Workload):
         return c.B * (2 * c.n_entries * c.Di + 4 * c.H * c.D * (c.k + c.W))
 
 
+    def cpu_groups(self):
+        c, st = self.cfg, self.sets[0]
+        fp8, fp4 = c.cache_dtype == "fp8", c.key_dtype == "fp4"
+        h = {"Q": _host(st["Q"]), "qidx": _host(st["qidx"]), "cache": _host(st["cache"]), "win": _host(st["win"]),
+             "cache_fmt": "fp8" if fp8 else "bf16", "win_fmt": "fp8" if fp8 else "bf16",
+             "cscale": _host(st["cscale"]), "wscale": _host(st["wscale"]),
+             "key_fmt": "fp4" if fp4 else "bf16", "k": c.k, "D": c.D, "tau": c.tau, "R": c.R,
+             "base": c.rope_base, "pos": c.q_pos}
+        if fp4:
+            h["kcodes"], h["kscale"] = _host(st["kidx"]), _host(st["kscale"])
+        else:
+            h["kidx"] = _host(st["kidx"])
+        _CPU.clear()
+        _CPU["main"] = h
+        return [("c4a", [("c4a", b) for b in range(c.B)], 1)]
+
+    def cpu_inputs_note(self):
+        return (f"input set 0 as the GPU consumed it (indexer keys, {self.cfg.cache_dtype} cache built by the "
+                f"library's compress, window, Q), all {self.cfg.B} sequences")
+
+
 class C128aLayer(Workload):
     """One c128a layer: dense attend over every entry plus the window."""
 
@@ -197,6 +233,20 @@ class C128aLayer(Workload):
     def flops(self):
         c = self.cfg
         return c.B * 4 * c.H * c.D * (c.n_entries + c.W)
+
+
+    def cpu_groups(self):
+        c, st = self.cfg, self.sets[0]
+        h = {"Q": _host(st["Q"]), "cache": _host(st["cache"]), "win": _host(st["win"]), "cscale": _host(st["cscale"]),
+             "cache_fmt": c.cache_dtype, "win_fmt": "bf16", "N": c.n_entries, "D": c.D, "tau": c.tau, "R": c.R,
+             "base": c.rope_base, "pos": c.q_pos}
+        _CPU.clear()
+        _CPU["main"] = h
+        return [("c128a", [("c128a", b) for b in range(c.B)], 1)]
+
+    def cpu_inputs_note(self):
+        return (f"input set 0 as the GPU consumed it ({self.cfg.cache_dtype} cache built by the library's compress, "
+                f"window, Q), all {self.cfg.B} sequences")
 
 
 class Mixed61(Workload):
@@ -293,6 +343,36 @@ class Mixed61(Workload):
                       n128 * 4 * c.H * c.D * (self.N128 + c.W))
 
 
+    SAMPLE_LAYERS = (0, 1, 59, 60)
+
+    def cpu_groups(self):
+        c = self.cfg
+        _CPU.clear()
+        g128, g4 = [], []
+        for layer in self.SAMPLE_LAYERS:
+            lay = self.layers[layer]
+            h = {"Q": _host(lay["Q"]), "span": _host(lay["span"]), "gate": _host(lay["gate"]),
+                 "cache": _host(lay["cache"]), "first": lay["first"], "D": c.D, "k": c.k, "tau": c.tau, "R": c.R,
+                 "base": c.rope_base, "pos": c.q_pos, "key_fmt": "bf16"}
+            key = f"L{layer}"
+            if lay["kind"] == "c4a":
+                if lay.get("reuse") is None:
+                    h["kidx"], h["qidx"] = _host(lay["kidx"]), _host(lay["qidx"])
+                else:   # a layer that reuses another's ids attends over them
+                    h["kidx"], h["ids"] = None, _host(self.layers[lay["reuse"]]["ids"])
+                g4 += [("m4", b, key) for b in range(c.B)]
+            else:
+                g128 += [("m128", b, key) for b in range(c.B)]
+            _CPU[key] = h
+        n4 = sum(1 for l in range(c.layers) if c.layer_kind(l) == "c4a")
+        return [("c128a layers 0, 60", g128, (c.layers - n4) / 2), ("c4a layers 1, 59", g4, n4 / 2)]
+
+    def cpu_inputs_note(self):
+        return (f"layers {', '.join(map(str, self.SAMPLE_LAYERS))} of the stack after the timed steps (spans, "
+                f"gates, caches, indexer keys, Q as the GPU consumed them), all {self.cfg.B} sequences; the "
+                f"step time scales the c128a sample by 31/2 and the c4a sample by 30/2")
+
+
 class StreamC4a(Workload):
     """Streaming c4a decode of a ragged batch: every step appends one new state
     per sequence (cskv_append: ring write, an entry every 4 tokens), then
@@ -366,87 +446,180 @@ class StreamC4a(Workload):
         return c.B * (2 * c.n_entries * c.Di + 4 * c.H * c.D * (c.k + c.W))
 
 
-# ------------------------------------------------------------------ CPU oracle baseline
+    def cpu_groups(self):
+        c = self.cfg
+        h = {"Q": _host(self.Q), "qidx": _host(self.qidx), "kidx": _host(self.kidx), "cache": _host(self.cache),
+             "win": _host(self.ring), "n_entries": _host(self.n_entries), "cache_fmt": "bf16", "win_fmt": "bf16",
+             "key_fmt": "bf16", "k": c.k, "D": c.D, "tau": c.tau, "R": c.R, "base": c.rope_base, "pos": c.q_pos}
+        _CPU.clear()
+        _CPU["main"] = h
+        return [("c4a", [("c4a", b) for b in range(c.B)], 1)]
 
-def cpu_baseline(cfg, seconds):
-    """The oracle, as it is, on a bounded sample of the same workload: a few
-    sequences of one layer (inputs regenerated on the host, outside the timed
-    region), run repeatedly for about `seconds`. Returns a dict for the JSON."""
-    import numpy as np
-    import synth
+    def cpu_inputs_note(self):
+        return ("the stream's state after the timed steps (ragged entry counts, keys, cache, ring as window), all "
+                f"{self.cfg.B} sequences; the append's ring write and occasional 8-state fold are not timed")
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+#
+# The oracle as it stands, on the input bytes the GPU step consumed (input set
+# 0, copied from the device after the GPU timing), run over the sequences in
+# parallel on the host cores: a pool of worker processes forked after the
+# inputs are on the host, each worker with one BLAS thread. A task is one
+# sequence's decode step through one layer; it starts from the raw cache and
+# key bytes (bf16 bits, fp8 / fp4 codes), so the oracle's own decoding of its
+# inputs is part of the timed work. The one-thread rate is the same tasks run
+# one after the other in the parent with its BLAS pool held to one thread.
+
+_CPU = {}    # the host inputs of the workload being timed (inherited by the forked workers)
+
+
+def _rows_f64(st, b, rows):
+    """Decoded cache rows `rows` of sequence b (oracle decoders)."""
+    from oracle import formats as F
+    c = st["cache"][b]
+    if st["cache_fmt"] == "fp8":
+        return F.decode_fp8_rows(c[rows], st["cscale"][b][rows])
+    if st["cache_fmt"] == "mixed":
+        D = st["D"]
+        raw = c[rows]
+        codes = raw[:, :D - 64]
+        rope = np.ascontiguousarray(raw[:, D - 64:]).view(np.uint16)
+        return F.decode_mixed_rows(codes, rope, st["cscale"][b][rows])
+    if st["cache_fmt"] == "fp4":
+        return F.decode_fp4_rows(c[rows], st["D"])
+    return F.bf16_to_f64(c[rows])
+
+
+def _window_f64(st, b):
+    from oracle import formats as F
+    if st["win_fmt"] == "fp8":
+        return F.decode_fp8_rows(st["win"][b], st["wscale"][b])
+    return F.bf16_to_f64(st["win"][b])
+
+
+def _c4a_ids(st, b):
     from oracle import formats as F
     from oracle import method as M
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    kind = cfg.layer_kind(1) if cfg.kind in ("mixed", "stream") else cfg.kind
-    from synth.configs import c128a_entries, c4a_entries
-    N = c4a_entries(cfg.L) if kind == "c4a" else c128a_entries(cfg.L)
-    n_seq = 2
-    seqs = []
-    for b in range(n_seq):
-        key = lambda t: synth.stream_key(cfg.seed, t, 1)  # noqa: E731
-        Q = F.bf16_to_f64(synth.normal_bf16(key(synth.T_Q), b * cfg.H * cfg.D, cfg.H * cfg.D).reshape(cfg.H, cfg.D))
-        win = F.bf16_to_f64(synth.normal_bf16(key(synth.T_WIN), b * cfg.W * cfg.D, cfg.W * cfg.D).reshape(cfg.W, cfg.D))
-        # only the rows a query can read are filled: every row for c128a, the
-        # rows the oracle's own top-k picks for c4a (filled after selection)
-        cache = np.zeros((N, cfg.D), dtype=np.float64)
-        st = {"Q": Q, "win": win, "cache": cache, "ring": win.copy(), "ring_gate": np.zeros(cfg.W)}
-        if kind == "c4a":
-            st["qidx"] = F.bf16_to_f64(synth.int_bf16(key(synth.T_QIDX), b * cfg.Di, cfg.Di, cfg.idx_range))
-            if cfg.key_dtype == "fp4":
-                codes = synth.random_bytes(key(synth.T_KIDX), b * N * cfg.Di // 2, N * cfg.Di // 2).reshape(N, cfg.Di // 2)
-                sc = synth.pow2_e4m3(key(synth.T_KIDX_SCALE), b * N * cfg.Di // 16, N * cfg.Di // 16, -2, 2
-                                     ).reshape(N, cfg.Di // 16)
-                st["kidx_codes"], st["kidx_scales"] = codes, sc
-            else:
-                st["kidx"] = F.bf16_to_f64(synth.int_bf16(key(synth.T_KIDX), b * N * cfg.Di, N * cfg.Di,
-                                                          cfg.idx_range).reshape(N, cfg.Di))
-            ids = M.topk_ids(M.index_scores(st["qidx"], st["kidx"] if "kidx" in st else
-                                            F.decode_fp4_g16(st["kidx_codes"], st["kidx_scales"])), cfg.k)
-            rows = ids[ids >= 0]
-        else:
-            rows = np.arange(N)
-        cache[rows] = F.bf16_to_f64(synth.normal_bf16(key(synth.T_CACHE), 0, rows.size * cfg.D)
-                                    .reshape(rows.size, cfg.D))
-        seqs.append(st)
+    q = F.bf16_to_f64(st["qidx"][b])
+    if st["key_fmt"] == "fp4":
+        keys = F.decode_fp4_g16(st["kcodes"][b], st["kscale"][b])
+    else:
+        keys = F.bf16_to_f64(st["kidx"][b])
+    nv = None if st.get("n_entries") is None else int(st["n_entries"][b])
+    return M.topk_ids(M.index_scores(q, keys), st["k"], nv)
 
-    def one(st):
-        if cfg.kind == "stream":
-            # the step's append first (token L-1 completes an entry: the 8-state fold)
-            M.append("c4a", st["ring"], st["ring_gate"], st["win"][0], 0.0, cfg.L - 1)
-        if kind == "c4a":
-            keys = st["kidx"] if "kidx" in st else F.decode_fp4_g16(st["kidx_codes"], st["kidx_scales"])
-            M.c4a_decode(st["Q"], st["qidx"], keys, st["cache"], st["win"], cfg.k, cfg.tau, cfg.R,
-                         cfg.rope_base, cfg.q_pos)
-        else:
-            M.c128a_decode(st["Q"], st["cache"], st["win"], cfg.tau, cfg.R, cfg.rope_base, cfg.q_pos)
 
-    def timed(limit):
-        done = 0
-        t0 = time.perf_counter()
-        while True:
-            one(seqs[done % n_seq])
-            done += 1
-            el = time.perf_counter() - t0
-            if el >= limit:
-                return done, el
+def _cpu_task(task):
+    """One sequence's decode step through one layer, from raw input bytes."""
+    from oracle import formats as F
+    from oracle import method as M
+    kind, b = task[0], task[1]
+    st = _CPU[task[2]] if len(task) > 2 else _CPU["main"]
+    Q = F.bf16_to_f64(st["Q"][b])
+    if kind == "c4a":
+        ids = _c4a_ids(st, b)
+        rows = _rows_f64(st, b, ids[ids >= 0])
+        O = M.attend(Q, rows, None, _window_f64(st, b), st["tau"], st["R"], st["base"], st["pos"])
+    elif kind == "c128a":
+        O = M.attend(Q, _rows_f64(st, b, np.arange(st["N"])), None, _window_f64(st, b), st["tau"], st["R"],
+                     st["base"], st["pos"])
+    elif kind == "m4":
+        # a c4a layer of the stack: 32 new entries from the 132-state span
+        # (4 carried + 128 new), top-k over the keys, attention over the
+        # selected rows and the 128 new states
+        span = F.bf16_to_f64(st["span"][b])
+        new = M.compress(M.C4A, span, st["gate"][b].astype(np.float64))
+        ids = _c4a_ids(st, b) if st.get("kidx") is not None else st["ids"][b]
+        sel = ids[ids >= 0]
+        first = st["first"]
+        fresh = (sel >= first) & (sel < first + new.shape[0])
+        rows = np.empty((sel.size, st["D"]))
+        rows[~fresh] = F.bf16_to_f64(st["cache"][b][sel[~fresh]])
+        rows[fresh] = new[sel[fresh] - first]
+        O = M.attend(Q, rows, None, span[4:], st["tau"], st["R"], st["base"], st["pos"])
+    elif kind == "m128":
+        # a c128a layer of the stack: one new entry from the 128 new states,
+        # dense attention over every entry and the new states
+        span = F.bf16_to_f64(st["span"][b])
+        new = M.compress(M.C128A, span, st["gate"][b].astype(np.float64))
+        first = st["first"]
+        cache = np.concatenate([F.bf16_to_f64(st["cache"][b][:first]), new], axis=0)
+        O = M.attend(Q, cache, None, span, st["tau"], st["R"], st["base"], st["pos"])
+    else:
+        raise ValueError(kind)
+    return float(O[0, 0])
 
-    done, el = timed(seconds)
-    out = {"value": done / el, "unit": "decode tokens/s per layer", "cores": int(cores), "kind": "oracle",
-           "sample": f"{done} single-sequence {kind} layer decodes ({n_seq} distinct sequences of the "
-                     f"{cfg.name} workload, inputs generated before timing) in {el:.1f} s",
-           "nproc": os.cpu_count(), "cpu_model": _cpu_model()}
-    # a per-core rate: the same sample with the BLAS pool held to one thread
+
+def _pool_init():
     try:
         from threadpoolctl import threadpool_limits
-        with threadpool_limits(limits=1):
-            d1, e1 = timed(max(seconds / 4, 1.0))
-        out["one_thread"] = {"value": d1 / e1, "sample": f"{d1} decodes in {e1:.1f} s"}
-    except Exception as e:   # no thread control: report without it
-        out["one_thread"] = {"value": None, "sample": f"not measured ({type(e).__name__})"}
+        threadpool_limits(limits=1)
+    except Exception:
+        pass
+
+
+def _run_pool(tasks, procs):
+    import multiprocessing as mp
+    ctx = mp.get_context("fork")
+    with ctx.Pool(procs, initializer=_pool_init) as pool:
+        pool.map(_cpu_task, tasks[:procs], chunksize=1)         # workers up and warm
+        t0 = time.perf_counter()
+        pool.map(_cpu_task, tasks, chunksize=1)
+        return time.perf_counter() - t0
+
+
+def _one_thread_rate(tasks, seconds):
+    try:
+        from threadpoolctl import threadpool_limits
+        lim = threadpool_limits(limits=1)
+    except Exception:
+        lim = None
+    done, t0 = 0, time.perf_counter()
+    while True:
+        _cpu_task(tasks[done % len(tasks)])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    if lim is not None:
+        lim.restore_original_limits()
+    return done / el, done, el
+
+
+def cpu_baseline(wl, cfg, seconds):
+    """The oracle's decode rate on the host cores, for the JSON line: `value`
+    in the workload's unit (decode tokens/s per layer, or per 61-layer step),
+    with the one-thread rate beside it."""
+    procs = max(1, min(15, os.cpu_count() or 1))
+    groups = wl.cpu_groups()        # [(name, tasks, layers_per_step)], inputs in _CPU
+    out = {"unit": None, "cores": procs, "kind": "oracle", "nproc": os.cpu_count(), "cpu_model": _cpu_model()}
+    rates, rates1, parts = {}, {}, []
+    for name, tasks, per_step in groups:
+        r1, d1, e1 = _one_thread_rate(tasks, max(1.0, seconds / (4 * len(groups))))
+        # enough tasks for about `seconds` of parallel work, whole batches
+        est = r1 * procs * seconds / len(groups)
+        reps = max(1, int(est // len(tasks)))
+        wall = _run_pool(tasks * reps, procs)
+        rates[name] = len(tasks) * reps / wall
+        rates1[name] = r1
+        parts.append(f"{name}: {len(tasks) * reps} tasks ({reps} x {len(tasks)}) in {wall:.1f} s on {procs} "
+                     f"processes; one thread {d1} tasks in {e1:.1f} s")
+    if len(groups) == 1:
+        out["value"] = rates[groups[0][0]]
+        out["one_thread"] = {"value": rates1[groups[0][0]]}
+        out["unit"] = "decode tokens/s per layer"
+    else:
+        # a 61-layer step per sequence costs the sampled layers' times scaled
+        # to 31 c128a and 30 c4a layers
+        t = sum(per / rates[n] for n, _, per in groups)
+        t1 = sum(per / rates1[n] for n, _, per in groups)
+        out["value"] = 1.0 / t
+        out["one_thread"] = {"value": 1.0 / t1}
+        out["unit"] = "decode tokens/s per 61-layer step"
+        out["layer_rates"] = {n: rates[n] for n, _, _ in groups}
+    out["parallel_over_one_thread"] = out["value"] / out["one_thread"]["value"]
+    out["sample"] = "; ".join(parts) + f". Inputs: {wl.cpu_inputs_note()}"
     return out
 
 
@@ -474,7 +647,7 @@ COPY_BYTES = 1 << 30
 
 
 def dominant_kernels(kind):
-    return ("k_index_score", "k_topk_final") if kind != "c128a" else ("k_attend", "k_attend_merge")
+    return ("k_index_topk",) if kind != "c128a" else ("k_attend", "k_attend_merge")
 
 
 def kernel_source_digest():
@@ -561,18 +734,20 @@ def recorded_traffic(workload):
 
 # ------------------------------------------------------------------ main
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by "
-              "sequence with no communication, so N GPUs run N independent copies)", file=sys.stderr)
-        sys.exit(2)
-    from synth import configs
-    cfg = configs.BY_NAME[args.workload]
-    if args.summarize_traffic:
-        summarize_traffic(cfg, *args.summarize_traffic)
-        return
+# the default run: the headline workload, then these, each measured the same way
+EXTRA_WORKLOADS = ("c128a_1m_bf16", "c4a_1m_fp8_fp4", "mixed61_256k_bf16")
 
+
+def _roofline(bytes_per_launch, ms, kernel, traffic):
+    achieved = bytes_per_launch / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(bytes_per_launch), "avg_launch_ms": round(ms, 5)}
+
+
+def measure(cfg, args, with_cpu):
+    """Times one workload (its own inputs, set up and freed here) and returns
+    its part of the JSON line."""
     import torch
 
     import compressed_sparse_kv_compress_amd as cskv
@@ -583,6 +758,7 @@ def main():
     wl = cls(cfg, args, torch, cskv, sd, synth)
     stateful = cfg.kind in ("mixed", "stream")   # steps that carry state: no input-set rotation, no graphs
     n_sets = args.sets or (1 if stateful else 4)
+    log(f"{cfg.name}: setup ({n_sets} input set{'s' if n_sets > 1 else ''})")
     t_setup = time.perf_counter()
     wl.setup(n_sets)
     setup_s = time.perf_counter() - t_setup
@@ -622,12 +798,12 @@ def main():
             g_dom.replay()
             g_rest.replay()
         torch.cuda.synchronize()
-    log(f"setup {setup_s:.1f} s, warmup done; timing {args.steps} steps "
+    log(f"{cfg.name}: setup {setup_s:.1f} s, warmup done; timing {args.steps} steps "
         f"({'eager launches' if graphs is None else 'HIP graph replays'})")
 
-    def run_step(i, dominant_only=False):
+    def run_step(i, part="all"):
         if stateful:
-            wl.step(i, dominant_only)
+            wl.step(i, part == "dominant")
             return
         if graphs is not None:
             g_dom, g_rest = graphs[i % n_sets]
@@ -635,68 +811,47 @@ def main():
         else:
             st = wl.sets[i % n_sets]
             dom, rest = (lambda: wl.dominant(st)), (lambda: wl.rest(st))
-        dom()
-        if not dominant_only:
+        if part in ("all", "dominant"):
+            dom()
+        if part in ("all", "rest"):
             rest()
+
+    def timed(part, first=0):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(args.steps):
+            run_step(first + i, part)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
 
     # the timed region: K steps bracketed by two events only (an event record
     # between kernels costs the stream several microseconds)
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        run_step(i)
-    end.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
-    # the dominant call's duration: the dominant calls of K more steps issued
-    # back to back (same input-set rotation), bracketed by two events on the
-    # stream the kernels are launched on, so that no event record sits between
-    # its kernels and the next call's
-    start.record()
-    for i in range(args.steps):
-        run_step(i, dominant_only=True)
-    end.record()
-    torch.cuda.synchronize()
-    dom_ms = start.elapsed_time(end) / (args.steps * n4)
-
+    ms_step = timed("all")
+    # each call's duration: the calls of K more steps issued back to back
+    # (same input-set rotation), bracketed by two events on the stream the
+    # kernels are launched on
+    dom_ms = timed("dominant") / n4
+    rest_ms = timed("rest") if cfg.kind == "c4a" else None
     # spread of the step time: the K timed steps repeated, each repeat between
     # two events as above (a stateful workload continues its stream)
-    rep_ms = []
-    for r in range(args.repeats):
-        start.record()
-        for i in range(args.steps):
-            run_step(args.steps * (1 + r) + i if stateful else i)
-        end.record()
-        torch.cuda.synchronize()
-        rep_ms.append(start.elapsed_time(end) / args.steps)
+    rep_ms = [timed("all", args.steps * (1 + r) if stateful else 0) for r in range(args.repeats)]
 
     dom_bytes, rest_bytes = wl.bytes()
-    dom_bytes_launch = dom_bytes / n4
-    achieved = dom_bytes_launch / (dom_ms * 1e-3) / 1e9
     tokens = cfg.B / (ms_step * 1e-3)
-    if mixed:
-        metric = "decode tokens/s per 61-layer step"
-    else:
-        metric = "decode tokens/s per layer"
+    dom_kernel = ("index_topk (k_index_topk: scores, candidate lists, selection)" if cfg.kind != "c128a"
+                  else "attend (k_attend + k_attend_merge)")
     out = {
-        "metric": metric,
+        "metric": "decode tokens/s per 61-layer step" if mixed else "decode tokens/s per layer",
         "value": round(tokens, 1),
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": ("bf16" if cfg.cache_dtype == "bf16" and cfg.key_dtype == "bf16" else
                   "fp8 + bf16 rotary (bf16 MFMA, fp32 accumulate)" if cfg.cache_dtype == "mixed" else
                   "fp4 E2M1 + E4M3/16 (bf16 MFMA, fp32 accumulate)" if cfg.cache_dtype == "fp4" else
                   "fp8+fp4 (bf16 MFMA, fp32 accumulate)"),
-        "data": "synthetic (SplitMix64 streams; caches built by the library's compress kernel)" if not stateful
-                else "synthetic (SplitMix64 streams; prefix caches drawn directly, new states compressed in the step)",
         "config": {"workload": cfg.name, "batch": cfg.B, "context": cfg.L, "heads": cfg.H, "D": cfg.D,
                    "rotary": cfg.R, "window": cfg.W, "top_k": cfg.k or None, "indexer_dim": cfg.Di or None,
                    "cache": cfg.cache_dtype, "indexer_keys": cfg.key_dtype if cfg.k else None,
@@ -704,25 +859,16 @@ def main():
                    **({"ragged_context": f"{cfg.L} - (0..127)", "append": "one state per sequence per step"}
                       if cfg.kind == "stream" else {}),
                    "launch": "eager" if graphs is None else "hip_graph"},
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "index_topk (k_index_score + k_topk_final)" if (cfg.kind != "c128a") else
-                      "attend (k_attend + k_attend_merge)",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic(cfg.name),
-            "algorithmic_bytes_per_launch": int(dom_bytes_launch),
-            "avg_launch_ms": round(dom_ms, 5),
-        },
+        "roofline": _roofline(dom_bytes / n4, dom_ms, dom_kernel, recorded_traffic(cfg.name)),
         "step_bandwidth_gbs": round((dom_bytes + rest_bytes) / (ms_step * 1e-3) / 1e9, 1),
+        "step_frac": round((dom_bytes + rest_bytes) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": int(dom_bytes + rest_bytes),
         "tflops_per_s": round(wl.flops() / (ms_step * 1e-3) / 1e12, 2),
         "setup_s": round(setup_s, 1),
     }
+    if rest_ms is not None:
+        out["roofline_attend"] = _roofline(rest_bytes, rest_ms, "attend (sparse: k_attend + k_attend_merge)", None)
     if rep_ms:
-        import numpy as np
         out["step_ms_spread"] = {
             "repeats": len(rep_ms),
             "median": round(float(np.percentile(rep_ms, 50)), 5),
@@ -730,8 +876,21 @@ def main():
             "p90": round(float(np.percentile(rep_ms, 90)), 5),
             "of": f"ms per step of each repeat of the {args.steps} timed steps, after the timed region",
         }
-    # what a plain read stream reaches on this machine: torch's max over 1 GiB viewed
-    # as int64 (a reduction that only reads), after the timed steps, median of 5
+    log(f"{cfg.name}: {ms_step * 1e3:.1f} us/step, dominant call {dom_ms * 1e3:.1f} us")
+    if with_cpu:
+        log(f"{cfg.name}: cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(wl, cfg, args.cpu_seconds)
+        _CPU.clear()
+    del wl, graphs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def hbm_probe():
+    """What a plain read stream reaches on this machine: torch's max over 1 GiB
+    viewed as int64 (a reduction that only reads), median of 5."""
+    import torch
     probe = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
     probe.amax()
     times = []
@@ -743,20 +902,43 @@ def main():
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
     del probe
-    probe_gbs = (1 << 30) / (sorted(times)[2] * 1e-3) / 1e9
+    return (1 << 30) / (sorted(times)[2] * 1e-3) / 1e9
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by "
+              "sequence with no communication, so N GPUs run N independent copies)", file=sys.stderr)
+        sys.exit(2)
+    from synth import configs
+    name = args.workload or "c4a_128k_bf16"
+    cfg = configs.BY_NAME[name]
+    if args.summarize_traffic:
+        summarize_traffic(cfg, *args.summarize_traffic)
+        return
+    with_cpu = not args.no_cpu_baseline
+    head = measure(cfg, args, with_cpu)
+    extras = {}
+    if args.workload is None and not args.no_extra:
+        for w in EXTRA_WORKLOADS:
+            extras[w] = measure(configs.BY_NAME[w], args, with_cpu)
+    probe_gbs = hbm_probe()
+    out = {
+        "metric": head["metric"], "value": head["value"], "unit": head["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"],
+        "data": "synthetic (SplitMix64 streams; caches built by the library's compress kernel)"
+                if cfg.kind not in ("mixed", "stream") else
+                "synthetic (SplitMix64 streams; prefix caches drawn directly, new states compressed in the step)",
+    }
+    out.update({k: v for k, v in head.items() if k not in out})
+    for part in [out] + list(extras.values()):
+        part["roofline"]["frac_of_probe"] = round(part["roofline"]["achieved"] / probe_gbs, 4)
     out["hbm_probe"] = {"read_gbs": round(probe_gbs, 1),
                         "kind": "torch amax over 1 GiB of int64 (read-only stream), median of 5"}
-    out["roofline"]["frac_of_probe"] = round(achieved / probe_gbs, 4)
-    log(f"timed: {ms_step:.4f} ms/step")
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) ...")
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
-        if mixed:
-            # the oracle sample is one c4a layer; a 61-layer step costs about 61 of them
-            out["cpu_baseline"]["value"] /= cfg.layers
-            if out["cpu_baseline"]["one_thread"]["value"]:
-                out["cpu_baseline"]["one_thread"]["value"] /= cfg.layers
-            out["cpu_baseline"]["unit"] = "decode tokens/s per 61-layer step (sampled c4a layer rate / 61)"
+    if extras:
+        out["workloads"] = extras
     print(json.dumps(out), flush=True)
 
 

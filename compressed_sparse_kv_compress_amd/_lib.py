@@ -102,23 +102,41 @@ def _dense(t, name):
 
 
 _workspaces: dict = {}
+_retired: list = []
 
 
 def _workspace(purpose: str, nbytes: int, device, layout=None) -> torch.Tensor | None:
-    """A scratch buffer per (purpose, device), grown on demand. Calls on one
-    device are ordered on its current stream, so calls of one purpose can share
-    it. ``layout`` names the argument set a stateful workspace was last used
-    with: the buffer is zero-filled (a fill kernel) whenever it changes."""
+    """A scratch buffer for one (purpose, device, current stream, layout).
+
+    Calls on one stream are ordered, so they can share a buffer; calls on two
+    streams never do. ``layout`` names the argument set of a workspace that
+    carries state between calls (index_topk: histograms and counters that
+    every call leaves zero): each layout gets a buffer of its own, zero-filled
+    once when it is made, so a call with other arguments never sees or leaves
+    another layout's state. A stateless buffer (layout None) grows on demand.
+    No buffer is ever freed while the process runs (a grown one is retired,
+    not dropped), so a HIP graph captured with a buffer's address can be
+    replayed after later eager calls of any shape."""
     if nbytes == 0:
         return None
-    key = (purpose, torch.device(device).index)
-    buf, last = _workspaces.get(key, (None, None))
+    dev = torch.device(device)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    key = (purpose, dev.index, stream, layout)
+    buf = _workspaces.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
-    elif layout is not None and layout != last:
-        buf.zero_()
-    _workspaces[key] = (buf, layout)
+        if buf is not None:
+            _retired.append(buf)
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _workspaces[key] = buf
     return buf
+
+
+def _caller_workspace(ws: torch.Tensor, nbytes: int, name: str) -> torch.Tensor:
+    if not ws.is_cuda or ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.numel() < nbytes:
+        raise ValueError(f"{name} must be a contiguous uint8 GPU tensor of at least {nbytes} bytes")
+    if ws.data_ptr() % 256:
+        raise ValueError(f"{name} must be 256-byte aligned")
+    return ws
 
 
 # ------------------------------------------------------------------ compress
@@ -206,10 +224,13 @@ def append(kind, s_new: torch.Tensor, g_new: torch.Tensor, pos: torch.Tensor, ri
 
 def index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, k: int, k_scale: torch.Tensor | None = None,
                n_entries: torch.Tensor | None = None, ids: torch.Tensor | None = None,
-               chunk: int = 0) -> torch.Tensor:
+               chunk: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """ids [B, k] int32 of the best k entries per sequence (ascending, -1 padded).
     Keys are bf16 [B, N, Di], or fp4 packed uint8 [B, N, Di/2] with k_scale
-    uint8 [B, N, Di/16]."""
+    uint8 [B, N, Di/16]. ``workspace`` (uint8, at least
+    index_topk_workspace_bytes() bytes, zero-filled before its first use) is
+    the caller's own; otherwise the binding keeps one per stream and argument
+    set."""
     _need_cuda(q_idx, k_idx, k_scale, n_entries, ids)
     _bf16_like(q_idx, "q_idx")
     _dense(q_idx, "q_idx"); _dense(k_idx, "k_idx")
@@ -236,7 +257,10 @@ def index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, k: int, k_scale: torch.
     elif ids.dtype != torch.int32 or tuple(ids.shape) != (B, k) or not ids.is_contiguous():
         raise ValueError("ids must be contiguous int32 [B, k]")
     nbytes = _lib_topk_ws(B, N, Di, k, key_dtype, chunk)   # 0 also when the call will reject
-    ws = _workspace("index_topk", nbytes, q_idx.device, layout=(B, N, Di, k, key_dtype, chunk))
+    if workspace is not None:
+        ws = _caller_workspace(workspace, nbytes, "workspace")
+    else:
+        ws = _workspace("index_topk", nbytes, q_idx.device, layout=(B, N, Di, k, key_dtype, chunk))
     _check(_lib_topk(_ptr(q_idx), key_dtype, _ptr(k_idx), _ptr(k_scale), _ptr(n_entries), B, N, Di, k,
                      _ptr(ids), chunk, _ptr(ws), 0 if ws is None else ws.numel(), _stream(q_idx.device)))
     return ids
@@ -249,7 +273,7 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
            q_pos: torch.Tensor | None = None, cache_scale: torch.Tensor | None = None,
            window_scale: torch.Tensor | None = None, n_entries: torch.Tensor | None = None,
            n_window: torch.Tensor | None = None, out: torch.Tensor | None = None,
-           splits: int = 0) -> torch.Tensor:
+           splits: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """O [B, H, D] fp32: softmax attention of Q [B, H, D] (bf16) over the cache
     rows named by ids [B, k] (or all of the first n_entries rows when ids is
     None) followed by the window rows [B, W, D], then inverse RoPE on the last
@@ -298,7 +322,10 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
         raise ValueError("out must be contiguous fp32 [B, H, D]")
     max_keys = (k if ids is not None else cache.shape[1]) + W
     nbytes = _lib_attend_ws(B, H, D, max_keys, splits)
-    ws = _workspace("attend", nbytes, Q.device)
+    if workspace is not None:
+        ws = _caller_workspace(workspace, nbytes, "workspace")
+    else:
+        ws = _workspace("attend", nbytes, Q.device)
     _check(_lib_attend(_ptr(Q), B, H, D, cache_dt, _ptr(cache), _ptr(cache_scale),
                        cache.shape[1], _ptr(ids), k, _ptr(n_entries), FP8_E4M3 if win_fp8 else BF16,
                        _ptr(window), _ptr(window_scale), W, wstride, _ptr(n_window), rope_dims, rope_base,

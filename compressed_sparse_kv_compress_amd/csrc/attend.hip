@@ -1142,8 +1142,12 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
 #pragma unroll
   for (int u = 0; u < U; ++u) v[u] = src[(int64_t)(u < splits ? u : splits - 1) * pstride];
   {
+    // A split that saw no key (ragged counts, -1 ids, an empty range) has sum
+    // 0 and a reference maximum that says nothing about the logits: it takes
+    // no part in M, L or the weights.
     float M = -INFINITY, L = 0.0f;
     auto fold = [&](float2 v) {
+      if (!(v.y > 0.0f)) return;
       if (v.x > M) {
         L = (M == -INFINITY ? 0.0f : L * exp2f(M - v.x)) + v.y;
         M = v.x;
@@ -1171,7 +1175,7 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
       if (mg != -INFINITY) L += lq_l[gg][hh0] * exp2f(mg - M);
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    auto weight = [&](float2 v) { return v.x == -INFINITY ? 0.0f : exp2f(v.x - M) * v.y * inv; };
+    auto weight = [&](float2 v) { return v.y > 0.0f ? exp2f(v.x - M) * v.y * inv : 0.0f; };
 #pragma unroll
     for (int u = 0; u < kMlU; ++u) {
       const int sp = grp + 4 * u;

@@ -4,49 +4,71 @@
 // compressed entries per query (default k = 512). [P2] Step 5: a learned
 // indexer scores every compressed block; the query reads only the chosen ones.
 //
-// Two kernels:
-//   k_index_score  (grid: chunks x sequences) streams the indexer keys once
-//     from HBM with 16-byte coalesced loads (bf16, or fp4 codes + E4M3 group
-//     scales dequantised in registers), computes each entry's score as a GEMV
-//     against the query's indexer vector and turns it into an order-preserving
-//     32-bit key, kept in LDS. It adds the chunk's histogram of the top 12 key
-//     bits into a per-sequence histogram with returning atomics. The counts
-//     returned (plus the chunk's own) never exceed the final ones, so the bin
-//     they place the k-th largest key in is at or below the true one. Each
-//     wave keeps the entries of its quarter of the chunk in that bin or above
-//     as candidates (key and entry number, in entry order) in a list of its
-//     own: together a superset of the chunk's share of the top k.
-//   k_topk_final   (grid: sequences, 1024 threads) finds the true threshold
-//     bin from the complete histogram and gathers into LDS the candidates at
-//     or above it, counting the next 8 key bits of the threshold bin's keys on
-//     the way. That fixes the 20-bit prefix of the k-th largest key; the few
-//     keys sharing it are ranked against each other (a radix select on the
-//     last 12 bits when there are many). It writes the ids in ascending entry
-//     order (ties go to the lower entry) and clears the histogram for the next
-//     call.
+// One launch, k_index_topk (grid: chunks x sequences, 256 threads):
+//   Scoring. Each workgroup streams one chunk of a sequence's indexer keys
+//     once from HBM with 16-byte non-temporal loads (bf16, or fp4 codes +
+//     E4M3 group scales dequantised in registers), computes each entry's
+//     score as a GEMV against the query's indexer vector and turns it into an
+//     order-preserving 32-bit key, kept in LDS. It adds the chunk's histogram
+//     of the top 12 key bits into the sequence's histogram with returning
+//     atomics. The counts returned (plus the chunk's own) never exceed the
+//     final ones, so the bin they place the k-th largest key in is at or below
+//     the true one. The chunk's entries in that bin or above are written, in
+//     entry order, to the chunk's candidate list: a superset of the chunk's
+//     share of the top k.
+//   Arrival. The lists and counts are stored with agent-scope atomics; once
+//     every wave's stores have completed, one thread counts the chunk in on the
+//     sequence's arrival counter. The workgroup that counts last knows every
+//     chunk of its sequence is done; it reads their results with agent-scope
+//     atomic loads and finishes the selection while the other sequences are
+//     still being scored.
+//   Selection. From the complete histogram it finds the true threshold bin,
+//     gathers into LDS the candidates at or above it (counting the next 8 key
+//     bits of the threshold bin's keys on the way), which fixes the 20-bit
+//     prefix of the k-th largest key; the few keys sharing it are ranked
+//     against each other (a radix select on the last 12 bits when there are
+//     many). It writes the ids in ascending entry order (ties go to the lower
+//     entry) and clears the histogram and the counter for the next call.
 // The selection is exact: every entry of a bin above the threshold bin is in
 // the top k, and the threshold bin is resolved on full keys.
 #include "kernels.h"
 
 namespace cskv {
 
-constexpr int kTopkThreads = 256;            // scoring workgroups
-constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kFinalThreads = 1024;          // selection workgroups (one per sequence)
-constexpr int kFinalWaves = kFinalThreads / kWave;
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;   // per-sequence histogram of the top key bits
 constexpr int kBinShift = 32 - kHistBits;
 constexpr int kRadixPad = 257;              // per-wave radix histograms, bank-shifted
-constexpr int kCandCap = 8192;              // candidates the final select holds in LDS
-constexpr int kMaxChunks = 2048;            // scoring chunks per sequence
-constexpr int kMaxLists = kMaxChunks * kTopkWaves;   // candidate lists per sequence (one per chunk and wave)
-constexpr int kMisc = 4 + 2 * kFinalWaves;   // block_emit keeps two counts per wave after 4 words
+constexpr int kMaxChunks = 2048;            // scoring chunks (candidate lists) per sequence
 constexpr int kSubBits = 8;                 // key bits below the threshold bin counted while gathering
 constexpr int kSubBins = 1 << kSubBits;
 constexpr int kLowBits = kBinShift - kSubBits;   // 12 bits below the 20-bit prefix
 constexpr int kTieCap = 256;                // keys sharing the k-th key's 20-bit prefix ranked pairwise
-constexpr int kTbCap = 2048;                // threshold-bin keys the final select lists apart
+constexpr int kTbCap = 1024;                // threshold-bin keys the selection lists apart
+constexpr int kMisc = 40;                   // block_emit keeps two counts per wave after 4 words
+// Workgroup size (scoring and selection). With 1024 threads and about one
+// workgroup per compute unit every CU streams keys with 16 waves, and the
+// selection that ends each sequence runs with 16 waves too (measured on the
+// c4a 128K / 1M workloads: 59 / 48 us per call against 67 / 62 us with 256
+// threads and three times the workgroups).
+constexpr int kTopkThreads = 1024;
+// candidate positions per thread and gather round of the selection
+template <int NT>
+constexpr int gather_per() { return NT >= 1024 ? 4 : 16; }
+
+// Data that one workgroup hands to another within the launch (candidate
+// lists, their counts, the histogram read back by the selection) is written
+// and read with relaxed agent-scope atomics: gfx950 performs them at the
+// device's coherence point, so no workgroup needs an agent-scope fence (which
+// writes back and invalidates the whole L2 and costs far more than the data).
+template <typename T>
+__device__ __forceinline__ void put_shared(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T get_shared(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // ------------------------------------------------------------- block helpers
 
@@ -201,11 +223,11 @@ __device__ __forceinline__ void put_key(uint32_t* keys, uint32_t* hist, int e, f
 
 // Entry groups [g_begin, g_end) of a chunk of n entries, a group being the
 // 64/LPE consecutive entries one wave-wide load covers; g_end - g_begin is a
-// multiple of 4 waves x 8 unrolled groups, or g_end is the chunk's last group.
+// multiple of NW waves x 8 unrolled groups, or g_end is the chunk's last group.
 //
 // bf16 keys: LPE = DI/8 lanes read one 16-byte slice each of an entry; one
 // wave-wide load covers 64/LPE consecutive entries (1 KiB contiguous).
-template <int DI>
+template <int DI, int NW>
 __device__ void score_chunk_bf16(const uint16_t* q, const uint16_t* keys_g, int n, int g_begin, int g_end,
                                  uint32_t* keys, uint32_t* hist) {
   constexpr int LPE = DI / 8;
@@ -217,11 +239,11 @@ __device__ void score_chunk_bf16(const uint16_t* q, const uint16_t* keys_g, int 
   const bf16x2_t q0 = __builtin_bit_cast(bf16x2_t, qv.x), q1 = __builtin_bit_cast(bf16x2_t, qv.y);
   const bf16x2_t q2 = __builtin_bit_cast(bf16x2_t, qv.z), q3 = __builtin_bit_cast(bf16x2_t, qv.w);
   const uint4* kp = reinterpret_cast<const uint4*>(keys_g);
-  for (int g0 = g_begin + wave; g0 < g_end; g0 += kTopkWaves * U) {
+  for (int g0 = g_begin + wave; g0 < g_end; g0 += NW * U) {
     uint4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = (g0 + kTopkWaves * u) * EPL + sub;
+      const int e = (g0 + NW * u) * EPL + sub;
       v[u] = e < n ? load_stream(kp + (int64_t)e * LPE + cg) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
@@ -232,7 +254,7 @@ __device__ void score_chunk_bf16(const uint16_t* q, const uint16_t* keys_g, int 
       p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v[u].w), q3, p, false);
       if constexpr (LPE == 16) p = sum_row16(p);
       else if constexpr (LPE == 4) p = sum_quad(p);
-      const int e = (g0 + kTopkWaves * u) * EPL + sub;
+      const int e = (g0 + NW * u) * EPL + sub;
       if (cg == 0 && e < n) put_key(keys, hist, e, p);
     }
   }
@@ -241,7 +263,7 @@ __device__ void score_chunk_bf16(const uint16_t* q, const uint16_t* keys_g, int 
 // fp4 keys: each lane reads 16 code bytes (32 channels = two 16-channel groups)
 // and the two matching E4M3 group scales; LPE = DI/32 lanes per entry. The
 // E2M1 codes are widened to bf16 exactly by the gfx950 converter.
-template <int DI>
+template <int DI, int NW>
 __device__ void score_chunk_fp4(const uint16_t* q, const uint8_t* codes_g, const uint8_t* scales_g,
                                 int n, int g_begin, int g_end, uint32_t* keys, uint32_t* hist) {
   constexpr int LPE = DI / 32;
@@ -263,12 +285,12 @@ __device__ void score_chunk_fp4(const uint16_t* q, const uint8_t* codes_g, const
   }
   const uint4* cp = reinterpret_cast<const uint4*>(codes_g);
   const uint16_t* sp = reinterpret_cast<const uint16_t*>(scales_g);
-  for (int g0 = g_begin + wave; g0 < g_end; g0 += kTopkWaves * U) {
+  for (int g0 = g_begin + wave; g0 < g_end; g0 += NW * U) {
     uint4 v[U];
     uint32_t s[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = (g0 + kTopkWaves * u) * EPL + sub;
+      const int e = (g0 + NW * u) * EPL + sub;
       v[u] = e < n ? load_stream(cp + (int64_t)e * LPE + part) : make_uint4(0, 0, 0, 0);
       s[u] = e < n ? load_stream(sp + (int64_t)e * LPE + part) : 0u;
     }
@@ -293,13 +315,12 @@ __device__ void score_chunk_fp4(const uint16_t* q, const uint8_t* codes_g, const
       g1s = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<3>(v[u].w), qp[15], g1s, false);
       float p = fmaf(g1s, e4m3_to_f32(s[u] >> 8), g0s * e4m3_to_f32(s[u] & 0xFFu));
       if constexpr (LPE == 4) p = sum_quad(p);
-      const int e = (g0 + kTopkWaves * u) * EPL + sub;
+      const int e = (g0 + NW * u) * EPL + sub;
       if (part == 0 && e < n) put_key(keys, hist, e, p);
     }
   }
 }
 
-constexpr int kBinsPerThread = kHistBins / kTopkThreads;
 
 // The bin of the k-th largest key under the counts hist[0 .. 4096) in LDS, or
 // 0 when they hold fewer than k keys, found by one wave alone: lane l sums the
@@ -333,106 +354,50 @@ __device__ int wave_threshold_bin(const uint32_t* hist, int k, int& above, int& 
   return top - F;
 }
 
-template <int DI, bool FP4>
-__global__ __launch_bounds__(kTopkThreads) void k_index_score(
-    const uint16_t* __restrict__ q_idx, const void* __restrict__ k_idx,
-    const uint8_t* __restrict__ k_scale, const int32_t* __restrict__ n_entries, int64_t n_max,
-    int chunk, int n_chunks, int k, uint32_t* __restrict__ ws_hist, uint32_t* __restrict__ ws_ckey,
-    int32_t* __restrict__ ws_cidx, int32_t* __restrict__ ws_cnt) {
-  extern __shared__ __align__(16) uint32_t lds[];
-  uint32_t* hist = lds;
-  uint32_t* keys = lds + kHistBins;
-  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
-  const int64_t b = blockIdx.y;
-  const int c = blockIdx.x;
-  const int64_t list = ((int64_t)b * n_chunks + c) * kTopkWaves + wave;   // this wave's candidate list
-  int64_t nv = n_entries ? (int64_t)n_entries[b] : n_max;
-  nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
-  const int64_t start = (int64_t)c * chunk;
-  const int64_t rem = nv - start;
-  if (rem <= 0) {
-    if (lane == 0) ws_cnt[list] = 0;
-    return;
-  }
-  const int n = rem > chunk ? chunk : (int)rem;
-
-  for (int i = t; i < kHistBins; i += kTopkThreads) hist[i] = 0u;
-  __syncthreads();
-  const uint16_t* q = q_idx + b * DI;
-  constexpr int EPL = FP4 ? kWave / (DI / 32) : kWave / (DI / 8);   // entries per wave-wide load
-  const int n_groups = (n + EPL - 1) / EPL;
-  if constexpr (FP4) {
-    const uint8_t* codes = reinterpret_cast<const uint8_t*>(k_idx) + (b * n_max + start) * (DI / 2);
-    const uint8_t* scales = k_scale + (b * n_max + start) * (DI / 16);
-    score_chunk_fp4<DI>(q, codes, scales, n, 0, n_groups, keys, hist);
-  } else {
-    const uint16_t* kk = reinterpret_cast<const uint16_t*>(k_idx) + (b * n_max + start) * DI;
-    score_chunk_bf16<DI>(q, kk, n, 0, n_groups, keys, hist);
-  }
-  __syncthreads();
-
-  // Add the chunk histogram into the sequence's. A bin's returned count plus
-  // the chunk's own is at most its final count; untouched bins count 0.
-  uint32_t* gh = ws_hist + b * kHistBins;
-  uint32_t now[kBinsPerThread];
-#pragma unroll
-  for (int u = 0; u < kBinsPerThread; ++u) {
-    const uint32_t h = hist[t + u * kTopkThreads];
-    now[u] = h ? atomicAdd(&gh[t + u * kTopkThreads], h) + h : 0u;
-  }
-#pragma unroll
-  for (int u = 0; u < kBinsPerThread; ++u) hist[t + u * kTopkThreads] = now[u];
-  __syncthreads();
-  int tb_above, tb_count;
-  const int tb = wave_threshold_bin(hist, k, tb_above, tb_count);   // at or below the final threshold bin
-
-  // Wave w keeps the entries of its quarter of the chunk at or above that bin,
-  // in entry order, in its own list.
-  const int quarter = chunk / kTopkWaves;
-  const int lo = wave * quarter, hi = min(lo + quarter, n);
-  uint32_t* ck = ws_ckey + list * quarter;
-  int32_t* ci = ws_cidx + list * quarter;
-  int written = 0;
-  for (int i0 = lo; i0 < hi; i0 += 4 * kWave) {
-    uint32_t kv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * kWave + lane;
-      kv[u] = i < hi ? keys[i] : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * kWave + lane;
-      const bool keep = i < hi && (int)(kv[u] >> kBinShift) >= tb;
-      const uint64_t m = __ballot(keep);
-      if (keep) {
-        const int p = written + __popcll(m & lanemask_lt());
-        ck[p] = kv[u];
-        ci[p] = (int32_t)(start + i);
-      }
-      written += __popcll(m);
-    }
-  }
-  if (lane == 0) ws_cnt[list] = written;
-}
-
 // ------------------------------------------------------------- selection
 
-struct SelectLds {
-  alignas(16) uint32_t ckey[kCandCap];
-  int32_t cidx[kCandCap];
-  uint8_t chosen[kCandCap];      // tie keys taken
-  uint32_t rhist[kFinalWaves * kRadixPad];
-  uint32_t h2[kSubBins];         // next 8 bits of the threshold bin's keys
-  uint32_t tkey[kTieCap];        // keys sharing the k-th key's 20-bit prefix
-  int tpos[kTieCap];             // ... and their candidate positions
-  uint32_t bkey[kTbCap];         // the threshold bin's keys
-  int bpos[kTbCap];              // ... and their candidate positions
-  int pre[kMaxLists + 1];
-  int misc[kMisc];
-  int scan[kFinalWaves];
-  int hscan[kFinalWaves];
+// Word offsets of the selection's arrays in the workgroup's dynamic LDS (the
+// scoring arrays are dead by then). `cap` candidates at or above the
+// threshold bin are gathered; `n_lists` candidate lists are offset.
+struct SelectView {
+  uint32_t* ckey;     // candidate keys, in entry order
+  int32_t* cidx;      // ... and their entries
+  uint32_t* rhist;    // one radix histogram of kRadixPad words per wave
+  uint32_t* h2;       // next 8 bits of the threshold bin's keys
+  uint32_t* tkey;     // keys sharing the k-th key's 20-bit prefix
+  int* tpos;          // ... and their candidate positions
+  uint32_t* bkey;     // the threshold bin's keys
+  int* bpos;          // ... and their candidate positions
+  int* misc;
+  int* scan;
+  int* hscan;
+  int* pre;           // list offsets (n_lists + 1)
+  uint8_t* chosen;    // tie keys taken
 };
+
+__host__ __device__ inline size_t select_lds_words(int cap, int tbcap, int n_lists, int nw) {
+  return 2 * (size_t)cap + (size_t)nw * kRadixPad + kSubBins + 2 * kTieCap + 2 * (size_t)tbcap + kMisc +
+         2 * (size_t)nw + (size_t)n_lists + 1 + ((size_t)cap + 3) / 4;
+}
+
+__device__ inline SelectView select_view(uint32_t* lds, int cap, int tbcap, int n_lists, int nw) {
+  SelectView v;
+  uint32_t* p = lds;
+  v.ckey = p; p += cap;
+  v.cidx = reinterpret_cast<int32_t*>(p); p += cap;
+  v.rhist = p; p += nw * kRadixPad;
+  v.h2 = p; p += kSubBins;
+  v.tkey = p; p += kTieCap;
+  v.tpos = reinterpret_cast<int*>(p); p += kTieCap;
+  v.bkey = p; p += tbcap;
+  v.bpos = reinterpret_cast<int*>(p); p += tbcap;
+  v.misc = reinterpret_cast<int*>(p); p += kMisc;
+  v.scan = reinterpret_cast<int*>(p); p += nw;
+  v.hscan = reinterpret_cast<int*>(p); p += nw;
+  v.pre = reinterpret_cast<int*>(p); p += n_lists + 1;
+  v.chosen = reinterpret_cast<uint8_t*>(p);
+  return v;
+}
 
 // Writes, in candidate order, the ids of the candidates whose key's top 20
 // bits exceed `pstar`, or equal it with `chosen` set (every candidate when
@@ -461,57 +426,226 @@ __device__ int ordered_emit(const uint32_t* keys, const int32_t* idxs, const uin
   return total < out_cap ? total : out_cap;
 }
 
-// Sum of per-wave counts cnt[0 .. wave) and of all kFinalWaves of them, by
-// a scan over the first kFinalWaves lanes (same result in every lane).
+// Sum of per-wave counts cnt[0 .. wave) and of all NW of them, by a scan over
+// the first NW lanes (same result in every lane).
+template <int NW>
 __device__ __forceinline__ int waves_before(const int* cnt, int wave, int& all) {
   const int lane = lane_id();
-  const int x = lane < kFinalWaves ? cnt[lane] : 0;
+  const int x = lane < NW ? cnt[lane] : 0;
   const int incl = wave_inclusive_scan(x);
-  all = __shfl(incl, kFinalWaves - 1);
+  all = __shfl(incl, NW - 1);
   return wave > 0 ? __shfl(incl, wave - 1) : 0;
 }
 
-// One workgroup per sequence: finds the threshold bin from the complete
-// histogram, gathers the candidates of the chunks' lists at or above it,
-// resolves the remaining 20 bits on full keys, writes the ids (ascending, -1 padded) and
-// clears the histogram for the next call.
-__global__ __launch_bounds__(kFinalThreads) void k_topk_final(
-    const int32_t* __restrict__ n_entries, int64_t n_max, int k, int list_cap, int n_lists,
-    uint32_t* __restrict__ ws_hist, uint32_t* __restrict__ ws_ckey, int32_t* __restrict__ ws_cidx,
-    const int32_t* __restrict__ ws_cnt, int32_t* __restrict__ ids) {
-  __shared__ SelectLds L;
+// The common case of the selection, with the candidates kept in registers.
+// After the list counts and the histogram (one round trip, done by the
+// caller into L.pre and misc), thread t loads the PER consecutive candidate
+// positions t*PER .. (one search over the list offsets finds the list of the
+// first, later ones walk forward): threads in order hold the candidates in
+// entry order. The threshold bin's keys are listed in LDS to find the 20-bit
+// prefix of the k-th largest key and to rank the keys that share it (by key,
+// then entry); one block scan over the per-thread selected counts then places
+// every id. Returns false, before writing any id, when there are more
+// candidates than PER * NT or the threshold bin or its ties exceed what LDS
+// lists; the general path then runs. On success `cnt` is the number of ids
+// written.
+template <int NT>
+__device__ __forceinline__ bool select_registers(bool take_all, int k, int total, int tbin, int above,
+                                                 int n_lists, int list_cap, int tbcap,
+                                                 const uint32_t* __restrict__ ck_b, const int32_t* __restrict__ ci_b,
+                                                 int32_t* __restrict__ out, const SelectView& L, int& cnt) {
+  constexpr int PER = gather_per<NT>();
+  const int t = threadIdx.x, lane = t % kWave;
+  if (total > PER * NT) return false;
+  const int p0 = t * PER;
+  uint32_t kk[PER];
+  int32_t ii[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    kk[u] = 0u;
+    ii[u] = 0;
+  }
+  if (p0 < total) {
+    int lst = 0;   // the largest list whose offset is <= p0
+    for (int n = n_lists + 1; n > 1;) {
+      const int half = n >> 1;
+      lst = L.pre[lst + half] <= p0 ? lst + half : lst;
+      n -= half;
+    }
+    int cur = L.pre[lst], next = L.pre[lst + 1];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int pp = p0 + u;
+      if (pp < total) {
+        while (pp >= next) {   // (ends: pre[n_lists] = total > pp)
+          ++lst;
+          cur = next;
+          next = L.pre[lst + 1];
+        }
+        const int64_t off = (int64_t)lst * list_cap + (pp - cur);
+        kk[u] = get_shared(ck_b + off);
+        ii[u] = get_shared(ci_b + off);
+      }
+    }
+  }
+  // classify: above the threshold bin (taken), in it (listed apart), below
+  uint32_t gtm = 0u, tbm = 0u;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const bool valid = p0 + u < total;
+    const int bin = (int)(kk[u] >> kBinShift);
+    const bool gt = valid && (take_all || bin > tbin);
+    const bool tb = valid && !take_all && bin == tbin;
+    gtm |= (gt ? 1u : 0u) << u;
+    tbm |= (tb ? 1u : 0u) << u;
+    if (tb) atomicAdd(&L.h2[(kk[u] >> kLowBits) & (kSubBins - 1)], 1u);
+  }
+  // the threshold bin's keys, listed apart: one slot reservation per wave
+  const int ntb = __popc(tbm);
+  const int wincl = wave_inclusive_scan(ntb);
+  int slot = 0;
+  if (lane == kWave - 1 && wincl > 0) slot = atomicAdd(&L.misc[5], wincl);
+  slot = __shfl(slot, kWave - 1) + wincl - ntb;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    if ((tbm >> u) & 1u) {
+      if (slot < tbcap) {
+        L.bkey[slot] = kk[u];
+        L.bpos[slot] = ii[u];
+      }
+      ++slot;
+    }
+  }
+  __syncthreads();
+
+  uint32_t pstar = 0u;
+  int rem = 0, m = 0;
+  if (!take_all) {
+    const int nb = L.misc[5];
+    if (nb > tbcap) return false;
+    // the sub-bin of the k-th largest key, found by every wave alone: lane l
+    // holds sub-bins 255 - 4l .. 252 - 4l, scanned from the top down
+    const int need = k - above;
+    int hc[4], hsub = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hc[j] = (int)L.h2[kSubBins - 1 - 4 * lane - j];
+      hsub += hc[j];
+    }
+    int run2 = wave_inclusive_scan(hsub) - hsub;
+    int sb = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (run2 < need && need <= run2 + hc[j]) {
+        sb = kSubBins - 1 - 4 * lane - j;
+        rem = need - run2;
+        m = hc[j];
+      }
+      run2 += hc[j];
+    }
+    const int owner = __ffsll((unsigned long long)__ballot(m > 0 && rem > 0)) - 1;
+    sb = __shfl(sb, owner);
+    rem = __shfl(rem, owner);   // keys to take among those sharing the prefix
+    m = __shfl(m, owner);       // keys sharing the prefix
+    if (m > kTieCap) return false;
+    pstar = ((uint32_t)tbin << kSubBits) | (uint32_t)sb;
+    // the keys sharing the prefix, with their entries
+    for (int i0 = 0; i0 < nb; i0 += NT) {
+      const int i = i0 + t;
+      const uint32_t key = i < nb ? L.bkey[i] : 0u;
+      const bool tie = i < nb && (key >> kLowBits) == pstar;
+      const uint64_t mt = __ballot(tie);
+      if (mt) {
+        int s2 = 0;
+        if (lane == 0) s2 = atomicAdd(&L.misc[3], __popcll(mt));
+        s2 = __shfl(s2, 0) + __popcll(mt & lanemask_lt());
+        if (tie && s2 < kTieCap) {
+          L.tkey[s2] = key;
+          L.tpos[s2] = L.bpos[i];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // selected: above the threshold bin, or in it with a higher 20-bit prefix,
+  // or sharing the prefix and ranked among the first rem (key, then entry)
+  uint32_t selm = gtm;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    if ((tbm >> u) & 1u) {
+      const uint32_t pfx = kk[u] >> kLowBits;
+      bool take = pfx > pstar;
+      if (pfx == pstar) {
+        int rank = 0;
+        for (int s2 = 0; s2 < m; ++s2) {
+          const uint32_t ks = L.tkey[s2];
+          rank += (ks > kk[u] || (ks == kk[u] && L.tpos[s2] < ii[u])) ? 1 : 0;
+        }
+        take = rank < rem;
+      }
+      selm |= (take ? 1u : 0u) << u;
+    }
+  }
+  int n_out;
+  int pos = block_exclusive_scan<NT>(__popc(selm), L.scan, n_out);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    if ((selm >> u) & 1u) {
+      if (pos < k) out[pos] = ii[u];
+      ++pos;
+    }
+  }
+  cnt = n_out < k ? n_out : k;
+  return true;
+}
+
+// The selection of sequence b by the workgroup that scored its last chunk:
+// finds the threshold bin from the complete histogram, gathers the
+// candidates of the chunks' lists at or above it, resolves the remaining 20
+// bits on full keys, writes the ids (ascending, -1 padded), then clears the
+// histogram and the arrival counter for the next call.
+template <int NT>
+__device__ __forceinline__ void select_sequence(int64_t nv, int k, int n_lists, int list_cap, int cap, int tbcap,
+                                                uint32_t* __restrict__ gh, uint32_t* __restrict__ arrive,
+                                                uint32_t* __restrict__ ck_b, int32_t* __restrict__ ci_b,
+                                                const int32_t* __restrict__ cnt_b, int32_t* __restrict__ out,
+                                                uint32_t* lds) {
+  constexpr int NW = NT / kWave;
+  constexpr int LPT = kMaxChunks / NT;        // lists per thread
+  constexpr int BPT = kHistBins / NT;         // histogram bins per thread
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
-  const int64_t b = blockIdx.x;
-  int64_t nv = n_entries ? (int64_t)n_entries[b] : n_max;
-  nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
-  uint32_t* gh = ws_hist + b * kHistBins;
+  const SelectView L = select_view(lds, cap, tbcap, n_lists, NW);
   const bool take_all = nv <= k;
-  int32_t* out = ids + b * k;
-  if (nv == 0) {   // no entry was scored (the list counts may not even exist)
-    for (int i = t; i < k; i += kFinalThreads) out[i] = -1;
+  if (nv == 0) {   // no entry was scored: no histogram counts to clear
+    for (int i = t; i < k; i += NT) out[i] = -1;
+    if (t == 0) *arrive = 0u;
     return;
   }
 
-  // list counts (thread t owns lists CPT*t ..) and the histogram (thread t
-  // owns bins 4095 - 4t down to 4092 - 4t), loaded together; one pair of
-  // barriers serves the offsets of the lists and the threshold bin
-  constexpr int CPT = kMaxLists / kFinalThreads;   // 8
-  static_assert(kHistBins == 4 * kFinalThreads, "four histogram bins per thread");
-  const int32_t* cnt_b = ws_cnt + b * n_lists;
-  int c[CPT];
+  // list counts (thread t owns lists LPT * t ..) and the histogram (thread t
+  // owns bins 4095 - BPT t down to 4096 - BPT (t + 1)), loaded together; one
+  // pair of barriers serves the offsets of the lists and the threshold bin
+  int c[LPT];
 #pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    const int si = CPT * t + j;
-    c[j] = si < n_lists ? cnt_b[si] : 0;
+  for (int j = 0; j < LPT; ++j) {
+    const int si = LPT * t + j;
+    c[j] = si < n_lists ? get_shared(cnt_b + si) : 0;
   }
-  const int top = kHistBins - 1 - 4 * t;
-  const uint4 hv = *reinterpret_cast<const uint4*>(gh + top - 3);   // bins top-3 .. top
-  for (int i = t; i < kSubBins; i += kFinalThreads) L.h2[i] = 0u;
-  if (t == 0) L.misc[5] = 0;                        // threshold-bin list length
-  int mine = 0;
+  const int top = kHistBins - 1 - BPT * t;
+  int hb[BPT];   // hb[j]: bin top - j
 #pragma unroll
-  for (int j = 0; j < CPT; ++j) mine += c[j];
-  const int hs = (int)(hv.x + hv.y + hv.z + hv.w);
+  for (int j = 0; j < BPT; ++j) hb[j] = (int)get_shared(gh + top - j);
+  for (int i = t; i < kSubBins; i += NT) L.h2[i] = 0u;
+  if (t == 0) {
+    L.misc[3] = 0;                                  // tie list length (register path)
+    L.misc[5] = 0;                                  // threshold-bin list length
+  }
+  int mine = 0, hs = 0;
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) mine += c[j];
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) hs += hb[j];
   const int incl = wave_inclusive_scan(mine);
   const int hincl = wave_inclusive_scan(hs);
   if (lane == kWave - 1) {
@@ -520,15 +654,14 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
   }
   __syncthreads();
   int total, htotal;
-  int run = incl - mine + waves_before(L.scan, wave, total);
-  int hrun = hincl - hs + waves_before(L.hscan, wave, htotal);
+  int run = incl - mine + waves_before<NW>(L.scan, wave, total);
+  const int hrun = hincl - hs + waves_before<NW>(L.hscan, wave, htotal);
   // the thread whose bins hold the k-th largest key records the bin, the keys
   // above it and its count
   if (!take_all && hrun < k && k <= hrun + hs) {
-    const int hb[4] = {(int)hv.w, (int)hv.z, (int)hv.y, (int)hv.x};   // from the top down
     int r = hrun;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < BPT; ++i) {
       if (r < k && k <= r + hb[i]) {
         L.misc[0] = top - i;
         L.misc[1] = r;
@@ -539,8 +672,8 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
   }
   // list offsets of the candidates
 #pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    const int si = CPT * t + j;
+  for (int j = 0; j < LPT; ++j) {
+    const int si = LPT * t + j;
     if (si < n_lists) L.pre[si] = run;
     run += c[j];
   }
@@ -553,101 +686,108 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
   const int kept = take_all ? total : above + tcount;
 
   int cnt = 0;
-  if (kept <= kCandCap) {
+  if (select_registers<NT>(take_all, k, total, tbin, above, n_lists, list_cap, tbcap, ck_b, ci_b, out, L, cnt)) {
+    // done
+  } else if (kept <= cap) {
+    // the general path reuses the LDS the register path may have filled
+    __syncthreads();
+    for (int i = t; i < kSubBins; i += NT) L.h2[i] = 0u;
+    if (t == 0) L.misc[5] = 0;
+    __syncthreads();
     // Gather into LDS, in candidate order, the ones at or above the threshold
     // bin, counting the next 8 bits of the threshold bin's keys on the way.
-    // Each position's list comes from a search over the list offsets with
-    // the same trip count in every lane; the loads follow all the searches.
-    // (offsets within the sequence's lists fit 32 bits: at most 2048 chunks
-    // of 16384 entries)
-    constexpr int PER = 4;
-    constexpr int ROUND = PER * kFinalThreads;
-    const uint32_t* ck_b = ws_ckey + (int64_t)b * n_lists * list_cap;
-    const int32_t* ci_b = ws_cidx + (int64_t)b * n_lists * list_cap;
+    // Thread t takes PER consecutive positions per round: one search over the
+    // list offsets finds the list of the first, later ones walk forward, and
+    // every load is issued before any is used. A block scan of the per-thread
+    // counts places the kept ones. (Offsets within the sequence's lists fit
+    // 32 bits: at most 2048 chunks of 16384 entries.)
+    constexpr int PER = gather_per<NT>();
+    constexpr int ROUND = PER * NT;
     int n_sel = 0;
     for (int j0 = 0; j0 < total; j0 += ROUND) {
-      int jj[PER], base[PER];
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        jj[u] = min(j0 + wave * (PER * kWave) + u * kWave + lane, total - 1);
-        base[u] = 0;
-      }
-      for (int n = n_lists + 1; n > 1;) {
-        const int half = n >> 1;
-#pragma unroll
-        for (int u = 0; u < PER; ++u) base[u] = L.pre[base[u] + half] <= jj[u] ? base[u] + half : base[u];
-        n -= half;
-      }
+      const int p0 = j0 + t * PER;
       uint32_t kk[PER];
       int32_t ii[PER];
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
-        const uint32_t off = (uint32_t)base[u] * (uint32_t)list_cap + (uint32_t)(jj[u] - L.pre[base[u]]);
-        kk[u] = ck_b[off];
-        ii[u] = ci_b[off];
+        kk[u] = 0u;
+        ii[u] = 0;
       }
-      bool keep[PER];
-      int cw = 0;
+      if (p0 < total) {
+        int lst = 0;   // the largest list whose offset is <= p0
+        for (int n = n_lists + 1; n > 1;) {
+          const int half = n >> 1;
+          lst = L.pre[lst + half] <= p0 ? lst + half : lst;
+          n -= half;
+        }
+        int cur = L.pre[lst], next = L.pre[lst + 1];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          const int pp = p0 + u;
+          if (pp < total) {
+            while (pp >= next) {   // (ends: pre[n_lists] = total > pp)
+              ++lst;
+              cur = next;
+              next = L.pre[lst + 1];
+            }
+            const uint32_t off = 4u * ((uint32_t)lst * (uint32_t)list_cap + (uint32_t)(pp - cur));
+            kk[u] = get_shared(reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(ck_b) + off));
+            ii[u] = get_shared(reinterpret_cast<const int32_t*>(reinterpret_cast<const uint8_t*>(ci_b) + off));
+          }
+        }
+      }
+      uint32_t keepm = 0u, tbm = 0u;   // bit u: position p0 + u is kept / in the threshold bin
+      int nk = 0;
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
-        const bool valid = j0 + wave * (PER * kWave) + u * kWave + lane < total;
+        const bool valid = p0 + u < total;
         const int bin = (int)(kk[u] >> kBinShift);
-        keep[u] = valid && (take_all || bin >= tbin);
-        cw += __popcll(__ballot(keep[u]));
-        if (!take_all && valid && bin == tbin) atomicAdd(&L.h2[(kk[u] >> kLowBits) & (kSubBins - 1)], 1u);
+        const bool keep = valid && (take_all || bin >= tbin);
+        const bool tb = !take_all && valid && bin == tbin;
+        keepm |= (keep ? 1u : 0u) << u;
+        tbm |= (tb ? 1u : 0u) << u;
+        nk += keep ? 1 : 0;
+        if (tb) atomicAdd(&L.h2[(kk[u] >> kLowBits) & (kSubBins - 1)], 1u);
       }
-      if (lane == 0) L.scan[wave] = cw;
-      __syncthreads();
       int round_total;
-      int pos = n_sel + waves_before(L.scan, wave, round_total);
-      // the threshold bin's keys also go to a list of their own (one slot
-      // reservation per wave)
-      uint64_t mb[PER];
-      int nb_w = 0;
+      int pos = n_sel + block_exclusive_scan<NT>(nk, L.scan, round_total);
+      const int ntb = __popc(tbm);
+      int slot = ntb ? atomicAdd(&L.misc[5], ntb) : 0;   // the threshold bin's keys, listed apart
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
-        mb[u] = __ballot(!take_all && keep[u] && (int)(kk[u] >> kBinShift) == tbin);
-        nb_w += __popcll(mb[u]);
-      }
-      int slot = 0;
-      if (nb_w > 0) {
-        if (lane == 0) slot = atomicAdd(&L.misc[5], nb_w);
-        slot = __shfl(slot, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const uint64_t m = __ballot(keep[u]);
-        const int p = pos + __popcll(m & lanemask_lt());
-        if (keep[u] && p < kCandCap) {   // (p < kept always holds for a zeroed workspace)
-          L.ckey[p] = kk[u];
-          L.cidx[p] = ii[u];
+        if ((keepm >> u) & 1u) {
+          if (pos < cap) {   // (pos < kept always holds for a zeroed workspace)
+            L.ckey[pos] = kk[u];
+            L.cidx[pos] = ii[u];
+          }
+          if ((tbm >> u) & 1u) {
+            if (slot < tbcap) {
+              L.bkey[slot] = kk[u];
+              L.bpos[slot] = pos;
+            }
+            ++slot;
+          }
+          ++pos;
         }
-        pos += __popcll(m);
-        const int sl = slot + __popcll(mb[u] & lanemask_lt());
-        if (((mb[u] >> lane) & 1u) && sl < kTbCap) {
-          L.bkey[sl] = kk[u];
-          L.bpos[sl] = p;
-        }
-        slot += __popcll(mb[u]);
       }
       n_sel += round_total;
       __syncthreads();
     }
-    n_sel = min(n_sel, kCandCap);
+    n_sel = min(n_sel, cap);
 
     if (take_all) {
-      cnt = ordered_emit<kFinalThreads>(L.ckey, L.cidx, L.chosen, n_sel, true, 0u, L.scan, out, k);
+      cnt = ordered_emit<NT>(L.ckey, L.cidx, L.chosen, n_sel, true, 0u, L.scan, out, k);
     } else {
       // the sub-bin holding the k-th largest key, found by every wave alone:
       // lane l holds sub-bins 255 - 4l .. 252 - 4l, scanned from the top down
       const int need = k - above;                  // keys still to take from the threshold bin
-      int hc[4], hs = 0;
+      int hc[4], hsub = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         hc[j] = (int)L.h2[kSubBins - 1 - 4 * lane - j];
-        hs += hc[j];
+        hsub += hc[j];
       }
-      int run2 = wave_inclusive_scan(hs) - hs;     // keys in higher sub-bins
+      int run2 = wave_inclusive_scan(hsub) - hsub;   // keys in higher sub-bins
       int sb = 0, rem = 0, m = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -664,23 +804,23 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
       m = __shfl(m, owner);                        // keys sharing the prefix
       const uint32_t pstar = ((uint32_t)tbin << kSubBits) | (uint32_t)sb;   // 20-bit prefix
       const int nb = L.misc[5];
-      if (m <= kTieCap && nb <= kTbCap) {
+      if (m <= kTieCap && nb <= tbcap) {
         // rank the keys sharing the prefix against each other (descending key,
         // then ascending entry, which candidate order gives)
         if (t == 0) L.misc[3] = 0;                 // tie counter (read after the barrier below)
         __syncthreads();
-        for (int i0 = 0; i0 < nb; i0 += kFinalThreads) {   // (one slot reservation per wave)
+        for (int i0 = 0; i0 < nb; i0 += NT) {      // (one slot reservation per wave)
           const int i = i0 + t;
           const uint32_t key = i < nb ? L.bkey[i] : 0u;
           const bool tie = i < nb && (key >> kLowBits) == pstar;
           const uint64_t mt = __ballot(tie);
           if (mt) {
-            int slot = 0;
-            if (lane == 0) slot = atomicAdd(&L.misc[3], __popcll(mt));
-            slot = __shfl(slot, 0) + __popcll(mt & lanemask_lt());
-            if (tie && slot < kTieCap) {   // (there are exactly m of them)
-              L.tkey[slot] = key;
-              L.tpos[slot] = L.bpos[i];
+            int slot2 = 0;
+            if (lane == 0) slot2 = atomicAdd(&L.misc[3], __popcll(mt));
+            slot2 = __shfl(slot2, 0) + __popcll(mt & lanemask_lt());
+            if (tie && slot2 < kTieCap) {   // (there are exactly m of them)
+              L.tkey[slot2] = key;
+              L.tpos[slot2] = L.bpos[i];
             }
           }
         }
@@ -693,34 +833,33 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
             const uint32_t ks = L.tkey[s2];
             rank += (ks > key || (ks == key && L.tpos[s2] < pos)) ? 1 : 0;
           }
-          if (pos < kCandCap) L.chosen[pos] = rank < rem ? 1 : 0;
+          if (pos < cap) L.chosen[pos] = rank < rem ? 1 : 0;
         }
         __syncthreads();
-        cnt = ordered_emit<kFinalThreads>(L.ckey, L.cidx, L.chosen, n_sel, false, pstar, L.scan, out, k);
+        cnt = ordered_emit<NT>(L.ckey, L.cidx, L.chosen, n_sel, false, pstar, L.scan, out, k);
       } else {
         uint32_t T;
         int need_eq;
-        radix_select<kFinalThreads>(L.ckey, n_sel, rem, pstar << kLowBits, kLowBits, L.rhist, L.misc, T, need_eq);
-        cnt = block_emit<kFinalThreads>(L.ckey, n_sel, false, T, need_eq, L.misc, out, k, L.cidx, 0);
+        radix_select<NT>(L.ckey, n_sel, rem, pstar << kLowBits, kLowBits, L.rhist, L.misc, T, need_eq);
+        cnt = block_emit<NT>(L.ckey, n_sel, false, T, need_eq, L.misc, out, k, L.cidx, 0);
       }
     }
   } else {
     // more keys at or above the threshold bin than LDS holds (heavily tied
     // scores): compact the lists in place in global memory and select
     // there (reads never overtake writes: a list's destination offset is at
-    // most its source offset)
-    uint32_t* ck = ws_ckey + b * n_lists * (int64_t)list_cap;
-    int32_t* ci = ws_cidx + b * n_lists * (int64_t)list_cap;
+    // most its source offset; the lists of other workgroups are read through
+    // to the coherence point, the compacted copy is this workgroup's own)
     for (int s1 = 1; s1 < n_lists; ++s1) {
       const int cs = L.pre[s1 + 1] - L.pre[s1];
       const int64_t from = (int64_t)s1 * list_cap, to = L.pre[s1];
-      for (int j0 = 0; j0 < cs; j0 += kFinalThreads) {
+      for (int j0 = 0; j0 < cs; j0 += NT) {
         const int j = j0 + t;
         uint32_t kk = 0u;
         int32_t ii = 0;
-        if (j < cs) { kk = ck[from + j]; ii = ci[from + j]; }
+        if (j < cs) { kk = get_shared(ck_b + from + j); ii = get_shared(ci_b + from + j); }
         __syncthreads();
-        if (j < cs) { ck[to + j] = kk; ci[to + j] = ii; }
+        if (j < cs) { ck_b[to + j] = kk; ci_b[to + j] = ii; }
         __syncthreads();
       }
     }
@@ -728,13 +867,137 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
     __syncthreads();
     uint32_t T;
     int need_eq;
-    radix_select<kFinalThreads>(ck, total, k - above, (uint32_t)tbin << kBinShift, kBinShift, L.rhist, L.misc, T, need_eq);
-    cnt = block_emit<kFinalThreads>(ck, total, false, T, need_eq, L.misc, out, k, ci, 0);
+    radix_select<NT>(ck_b, total, k - above, (uint32_t)tbin << kBinShift, kBinShift, L.rhist, L.misc, T, need_eq);
+    cnt = block_emit<NT>(ck_b, total, false, T, need_eq, L.misc, out, k, ci_b, 0);
   }
-  for (int i = cnt + t; i < k; i += kFinalThreads) out[i] = -1;
+  for (int i = cnt + t; i < k; i += NT) out[i] = -1;
 
-  // leave the histogram clear for the next call
-  for (int i = t; i < kHistBins; i += kFinalThreads) gh[i] = 0u;
+  // leave the histogram and the arrival counter clear for the next call
+  for (int i = t; i < kHistBins; i += NT) gh[i] = 0u;
+  if (t == 0) *arrive = 0u;
+}
+
+// ------------------------------------------------------------- the launch
+
+template <int DI, bool FP4, int NT>
+__global__ __launch_bounds__(NT) void k_index_topk(
+    const uint16_t* __restrict__ q_idx, const void* __restrict__ k_idx,
+    const uint8_t* __restrict__ k_scale, const int32_t* __restrict__ n_entries, int64_t n_max,
+    int chunk, int n_chunks, int k, int cand_cap, int tb_cap, uint32_t* __restrict__ ws_hist,
+    uint32_t* __restrict__ ws_arrive, uint32_t* __restrict__ ws_ckey, int32_t* __restrict__ ws_cidx,
+    int32_t* __restrict__ ws_cnt, int32_t* __restrict__ ids) {
+  constexpr int NW = NT / kWave;
+  constexpr int BPT = kHistBins / NT;
+  extern __shared__ __align__(16) uint32_t lds[];
+  __shared__ int wcnt_l[NW];
+  __shared__ int last_l;
+  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  const int64_t b = blockIdx.y;
+  const int c = blockIdx.x;
+  int64_t nv = n_entries ? (int64_t)n_entries[b] : n_max;
+  nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
+  const int64_t start = (int64_t)c * chunk;
+  const int64_t rem = nv - start;
+  uint32_t* ck = ws_ckey + ((int64_t)b * n_chunks + c) * chunk;   // this chunk's candidate list
+  int32_t* ci = ws_cidx + ((int64_t)b * n_chunks + c) * chunk;
+  uint32_t* gh = ws_hist + b * kHistBins;
+
+  if (rem > 0) {
+    const int n = rem > chunk ? chunk : (int)rem;
+    uint32_t* hist = lds;
+    uint32_t* keys = lds + kHistBins;
+    for (int i = t; i < kHistBins; i += NT) hist[i] = 0u;
+    __syncthreads();
+    const uint16_t* q = q_idx + b * DI;
+    constexpr int EPL = FP4 ? kWave / (DI / 32) : kWave / (DI / 8);   // entries per wave-wide load
+    const int n_groups = (n + EPL - 1) / EPL;
+    if constexpr (FP4) {
+      const uint8_t* codes = reinterpret_cast<const uint8_t*>(k_idx) + (b * n_max + start) * (DI / 2);
+      const uint8_t* scales = k_scale + (b * n_max + start) * (DI / 16);
+      score_chunk_fp4<DI, NW>(q, codes, scales, n, 0, n_groups, keys, hist);
+    } else {
+      const uint16_t* kk = reinterpret_cast<const uint16_t*>(k_idx) + (b * n_max + start) * DI;
+      score_chunk_bf16<DI, NW>(q, kk, n, 0, n_groups, keys, hist);
+    }
+    __syncthreads();
+
+    // Add the chunk histogram into the sequence's. A bin's returned count plus
+    // the chunk's own is at most its final count; untouched bins count 0.
+    uint32_t now[BPT];
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      const uint32_t h = hist[t + u * NT];
+      now[u] = h ? atomicAdd(&gh[t + u * NT], h) + h : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) hist[t + u * NT] = now[u];
+    __syncthreads();
+    int tb_above, tb_count;
+    const int tb = wave_threshold_bin(hist, k, tb_above, tb_count);   // at or below the final threshold bin
+
+    // The chunk's entries at or above that bin go to its list in entry order:
+    // wave w counts those of its share of the chunk, then writes them after
+    // the lower shares' ones.
+    const int share = chunk / NW;
+    const int lo = wave * share, hi = min(lo + share, n);
+    auto kept = [&](int i, uint32_t& kv) __attribute__((always_inline)) {
+      kv = i < hi ? keys[i] : 0u;
+      return i < hi && (int)(kv >> kBinShift) >= tb;
+    };
+    int mine = 0;
+    for (int i0 = lo; i0 < hi; i0 += 4 * kWave) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        uint32_t kv;
+        mine += __popcll(__ballot(kept(i0 + u * kWave + lane, kv)));
+      }
+    }
+    if (lane == 0) wcnt_l[wave] = mine;
+    __syncthreads();
+    int written = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      written += w < wave ? wcnt_l[w] : 0;
+      total += wcnt_l[w];
+    }
+    for (int i0 = lo; i0 < hi; i0 += 4 * kWave) {
+      uint32_t kv[4];
+      bool keep[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) keep[u] = kept(i0 + u * kWave + lane, kv[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint64_t m = __ballot(keep[u]);
+        if (keep[u]) {
+          const int p = written + __popcll(m & lanemask_lt());
+          put_shared(ck + p, kv[u]);
+          put_shared(ci + p, (int32_t)(start + i0 + u * kWave + lane));
+        }
+        written += __popcll(m);
+      }
+    }
+    if (t == 0) put_shared(ws_cnt + b * n_chunks + c, total);
+  } else if (t == 0) {
+    put_shared(ws_cnt + b * n_chunks + c, 0);
+  }
+
+  // Arrival: every wave waits until its list stores and histogram atomics
+  // have completed at the coherence point, then the chunk counts in; the
+  // workgroup that counts the sequence's last chunk reads every chunk's
+  // results through to that point and runs the selection.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (t == 0) {
+    const uint32_t before = __hip_atomic_fetch_add(ws_arrive + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_l = before == (uint32_t)(n_chunks - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!last_l) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  select_sequence<NT>(nv, k, n_chunks, chunk, cand_cap, tb_cap, gh, ws_arrive + b,
+                      ws_ckey + (int64_t)b * n_chunks * chunk, ws_cidx + (int64_t)b * n_chunks * chunk,
+                      ws_cnt + b * n_chunks, ids + b * k, lds);
 }
 
 // ------------------------------------------------------------- planning / launch
@@ -742,53 +1005,76 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, bool fp4, TopkPlan* p) {
-  (void)k;
+  // Workgroups of 1024 threads, about one per compute unit: every CU streams
+  // with 16 waves, and the selection that ends each sequence runs with 16.
+  p->threads = kTopkThreads;
   int64_t chunk = chunk_hint;
   if (chunk == 0) {
-    // bf16 keys (256 B per entry): about 768 scoring workgroups over the batch,
-    // chunks of 512 .. 4096 entries; fp4 keys (72 B per entry): about 1536,
-    // chunks of 512 .. 8192 (measured best on the c4a workloads); more when a
-    // sequence would need more chunks than the final select tracks
-    const int64_t groups = fp4 ? 1536 : 768;
-    const int64_t cap = fp4 ? 8192 : 4096;
+    // about 256 scoring workgroups over the batch, chunks of 1024 .. 16384
+    // entries; more when a sequence would need more chunks than the
+    // selection tracks
+    const int64_t groups = 256;
     const int64_t want = (B * n_max + groups - 1) / groups;
-    chunk = 512;
-    while (chunk < want && chunk < cap) chunk *= 2;
+    chunk = 1024;
+    while (chunk < want && chunk < 16384) chunk *= 2;
     while ((n_max + chunk - 1) / chunk > kMaxChunks && chunk < 16384) chunk *= 2;
   }
   if (chunk < 256 || chunk > 16384 || chunk % 256 != 0) return false;
+  // (a chunk smaller than one round of the 1024-thread score loop leaves
+  // waves idle but stays correct)
   p->chunk = chunk;
   p->n_chunks = n_max <= 0 ? 1 : (n_max + chunk - 1) / chunk;
   if (p->n_chunks > kMaxChunks) return false;
+  // candidates the selection gathers into LDS: the k keys at or above the
+  // threshold bin plus that bin's other keys (a few hundred on the c4a
+  // workloads); more go through the global-memory path
+  p->cand_cap = k <= 1024 ? 2048 : 4096;
+  p->tb_cap = kTbCap;
+  const size_t score_words = (size_t)kHistBins + (size_t)chunk;
+  const size_t select_words = select_lds_words(p->cand_cap, p->tb_cap, (int)p->n_chunks, p->threads / kWave);
+  p->lds_bytes = 4 * (score_words > select_words ? score_words : select_words);
   const size_t nb = (size_t)B;
   const size_t slots = nb * (size_t)p->n_chunks * (size_t)chunk;
   size_t off = 0;
   p->off_hist = off; off = align256(off + nb * kHistBins * 4);
+  p->off_arrive = off; off = align256(off + nb * 4);
   p->zero_bytes = off;
-  p->off_cnt = off; off = align256(off + nb * (size_t)p->n_chunks * kTopkWaves * 4);
+  p->off_cnt = off; off = align256(off + nb * (size_t)p->n_chunks * 4);
   p->off_ckey = off; off = align256(off + slots * 4);
   p->off_cidx = off; off = align256(off + slots * 4);
   p->bytes = off;
   return true;
 }
 
-template <int DI, bool FP4>
-static hipError_t launch_score(const TopkPlan& p, const uint16_t* q_idx, const void* k_idx,
-                               const uint8_t* k_scale, const int32_t* n_entries, int64_t B,
-                               int64_t n_max, int k, uint8_t* ws, hipStream_t stream) {
-  const size_t shmem = (size_t)kHistBins * 4 + (size_t)p.chunk * 4;
-  auto kern = k_index_score<DI, FP4>;
-  if (shmem > 65536) {
+template <int DI, bool FP4, int NT>
+static hipError_t launch_t(const TopkPlan& p, const uint16_t* q_idx, const void* k_idx,
+                           const uint8_t* k_scale, const int32_t* n_entries, int64_t B, int64_t n_max,
+                           int k, int32_t* ids, uint8_t* ws, hipStream_t stream) {
+  auto kern = k_index_topk<DI, FP4, NT>;
+  if (p.lds_bytes > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
     if (e != hipSuccess) return e;
   }
   dim3 grid((unsigned)p.n_chunks, (unsigned)B);
-  hipLaunchKernelGGL(kern, grid, dim3(kTopkThreads), shmem, stream, q_idx, k_idx, k_scale, n_entries,
-                     n_max, (int)p.chunk, (int)p.n_chunks, k, reinterpret_cast<uint32_t*>(ws + p.off_hist),
+  hipLaunchKernelGGL(kern, grid, dim3(NT), p.lds_bytes, stream, q_idx, k_idx, k_scale, n_entries,
+                     n_max, (int)p.chunk, (int)p.n_chunks, k, p.cand_cap, p.tb_cap,
+                     reinterpret_cast<uint32_t*>(ws + p.off_hist), reinterpret_cast<uint32_t*>(ws + p.off_arrive),
                      reinterpret_cast<uint32_t*>(ws + p.off_ckey), reinterpret_cast<int32_t*>(ws + p.off_cidx),
-                     reinterpret_cast<int32_t*>(ws + p.off_cnt));
+                     reinterpret_cast<int32_t*>(ws + p.off_cnt), ids);
   return hipGetLastError();
+}
+
+template <int NT>
+static hipError_t launch_nt(const TopkPlan& p, const uint16_t* q_idx, bool fp4, const void* k_idx,
+                            const uint8_t* k_scale, const int32_t* n_entries, int64_t B, int64_t n_max,
+                            int Di, int k, int32_t* ids, uint8_t* ws, hipStream_t stream) {
+  if (fp4) {
+    return Di == 128 ? launch_t<128, true, NT>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream)
+                     : launch_t<32, true, NT>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream);
+  }
+  return Di == 128 ? launch_t<128, false, NT>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream)
+                   : launch_t<32, false, NT>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream);
 }
 
 hipError_t launch_index_topk(const TopkPlan& p, const uint16_t* q_idx, bool fp4, const void* k_idx,
@@ -796,23 +1082,7 @@ hipError_t launch_index_topk(const TopkPlan& p, const uint16_t* q_idx, bool fp4,
                              int64_t n_max, int Di, int k, int32_t* ids, void* workspace,
                              hipStream_t stream) {
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  hipError_t e = hipSuccess;
-  if (n_max > 0) {
-    if (fp4) {
-      e = Di == 128 ? launch_score<128, true>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ws, stream)
-                    : launch_score<32, true>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ws, stream);
-    } else {
-      e = Di == 128 ? launch_score<128, false>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ws, stream)
-                    : launch_score<32, false>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ws, stream);
-    }
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(k_topk_final, dim3((unsigned)B), dim3(kFinalThreads), 0, stream, n_entries, n_max, k,
-                     (int)(p.chunk / kTopkWaves), (int)(p.n_chunks * kTopkWaves),
-                     reinterpret_cast<uint32_t*>(ws + p.off_hist),
-                     reinterpret_cast<uint32_t*>(ws + p.off_ckey), reinterpret_cast<int32_t*>(ws + p.off_cidx),
-                     reinterpret_cast<const int32_t*>(ws + p.off_cnt), ids);
-  return hipGetLastError();
+  return launch_nt<kTopkThreads>(p, q_idx, fp4, k_idx, k_scale, n_entries, B, n_max, Di, k, ids, ws, stream);
 }
 
 }  // namespace cskv

@@ -19,15 +19,19 @@ hipError_t launch_append(int kind, const uint16_t* s_new, const float* g_new, co
                          hipStream_t stream);
 
 // ---- index_topk.hip
-// Plan of the indexer: k_index_score scores `chunk` entries per workgroup and
-// writes the chunk's candidates as one list per wave, k_topk_final finishes
-// one sequence per workgroup. Workspace regions (byte offsets): the
-// per-sequence histogram comes first (it must be zero when a call starts and
-// every call leaves it zero), then the lists' candidate counts and their
-// candidate keys / entry numbers (room for every entry).
+// Plan of the indexer: k_index_topk scores `chunk` entries per workgroup and
+// writes the chunk's candidates as one list; the workgroup that scores a
+// sequence's last chunk runs its selection. Workspace regions (byte offsets):
+// the per-sequence histograms and arrival counters come first (they must be
+// zero when a call starts and every call leaves them zero), then the lists'
+// candidate counts and their candidate keys / entry numbers (room for every
+// entry).
 struct TopkPlan {
   int64_t chunk, n_chunks;     // entries per scoring workgroup, workgroups per sequence
-  size_t off_hist, off_cnt, off_ckey, off_cidx;
+  int threads;                 // workgroup size
+  int cand_cap, tb_cap;        // selection: candidates gathered in LDS, threshold-bin keys listed
+  size_t lds_bytes;            // dynamic LDS per workgroup
+  size_t off_hist, off_arrive, off_cnt, off_ckey, off_cidx;
   size_t zero_bytes;           // leading bytes that must be zero between calls
   size_t bytes;                // workspace bytes
 };

@@ -159,12 +159,15 @@ cskv_status cskv_append(int32_t kind, const void* s_new, const float* g_new, con
  *   chunk     entries scored per workgroup: 0 = automatic, else a multiple
  *             of 256 in [256, 16384]
  *   workspace cskv_index_topk_workspace() bytes. Its leading region holds
- *             per-sequence histograms that must be zero when a call starts:
- *             zero-fill the workspace before the first call, and again before a
- *             call with different B, n_max, k or chunk or after the buffer
- *             served another purpose. Every completed call leaves that region
- *             zero (whatever n_entries held), so calls with the same arguments
- *             can reuse the workspace as it is.
+ *             per-sequence histograms and chunk arrival counters that must be
+ *             zero when a call starts: zero-fill the workspace before the first
+ *             call, and again before a call with different B, n_max, k or chunk
+ *             or after the buffer served another purpose. Every completed call
+ *             leaves that region zero (whatever n_entries held), so calls with
+ *             the same arguments can reuse the workspace as it is. The call is
+ *             one kernel launch: the workgroup that scores a sequence's last
+ *             chunk also selects that sequence's ids. Two calls in flight at
+ *             once on one workspace (two streams) corrupt each other.
  * EUNSUPPORTED if a sequence would need more than 2048 chunks (n_max > 2048 *
  * chunk; with automatic chunking, n_max > 33554432).
  */

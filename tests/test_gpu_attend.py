@@ -230,3 +230,35 @@ def test_sparse_head_split_far_logits(cskv):
     O = cskv.attend(to_dev_bf16(Qb), to_dev_bf16(cb), to_dev(ids), to_dev_bf16(wb), softmax_scale=tau,
                     rope_dims=R, q_pos=to_dev(pos))
     assert row_rel_err(O.cpu().numpy(), ref) <= 2e-2
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_far_negative_logits_with_empty_splits(cskv, sparse):
+    """Every logit far below zero (about -148 in log2 units) while some splits
+    hold no key at all: ragged n_entries (dense) or mostly -1 ids (sparse).
+    An empty split's (reference maximum, sum) pair must not enter the merge,
+    or its reference of 0 would underflow every real split's weight."""
+    B, H, D, N, k, W, R = 2, 64, 512, 1200, 256, 40, 64
+    seed = 65
+    Q = F.bf16_to_f64(_bf16(seed, synth.T_Q, (B, H, D)))
+    cache = 1.0 + 0.1 * F.bf16_to_f64(_bf16(seed, synth.T_CACHE, (B, N, D)))
+    win = 1.0 + 0.1 * F.bf16_to_f64(_bf16(seed, synth.T_WIN, (B, W, D)))
+    Q = -1.0 + 0.1 * Q
+    tau = 0.2
+    Qb, cb, wb = (F.f32_to_bf16(x.astype(np.float32)) for x in (Q, cache, win))
+    rng = np.random.default_rng(seed)
+    pos = np.array([77, 1 << 19], dtype=np.int64)
+    if sparse:
+        ids = np.stack([sorted_ids(rng, N, k), sorted_ids(rng, N, k, n_valid=30)])
+        nv = None
+    else:
+        ids = None
+        nv = np.array([N, 30], dtype=np.int32)
+    ref = _oracle(F.bf16_to_f64(Qb), F.bf16_to_f64(cb), ids, F.bf16_to_f64(wb), tau, R, 10000.0, pos, nv)
+    assert np.all(np.abs(ref).max(axis=-1) > 0.5)
+    for splits in (0, 4, 40):
+        O = cskv.attend(to_dev_bf16(Qb), to_dev_bf16(cb), None if ids is None else to_dev(ids), to_dev_bf16(wb),
+                        softmax_scale=tau, rope_dims=R, q_pos=to_dev(pos),
+                        n_entries=None if nv is None else to_dev(nv), splits=splits)
+        err = row_rel_err(O.cpu().numpy(), ref)
+        assert err <= 2e-2, (splits, err)
