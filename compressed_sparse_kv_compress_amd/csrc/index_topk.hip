@@ -52,6 +52,9 @@ constexpr int kMisc = 40;                   // block_emit keeps two counts per w
 // c4a 128K / 1M workloads: 59 / 48 us per call against 67 / 62 us with 256
 // threads and three times the workgroups).
 constexpr int kTopkThreads = 1024;
+// Scoring workgroups when the selection runs as a launch of its own.
+constexpr int kTopkScoreThreads = 256;
+constexpr bool kTopkFused = true;
 // candidate positions per thread and gather round of the selection
 template <int NT>
 constexpr int gather_per() { return NT >= 1024 ? 4 : 16; }
@@ -68,6 +71,14 @@ __device__ __forceinline__ void put_shared(T* p, T v) {
 template <typename T>
 __device__ __forceinline__ T get_shared(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A selection in a launch of its own reads what the scoring launch wrote with
+// plain loads (the launch boundary orders them); inside the scoring launch it
+// reads through to the coherence point.
+template <bool COH, typename T>
+__device__ __forceinline__ T ld(const T* p) {
+  if constexpr (COH) return get_shared(p);
+  else return *p;
 }
 
 // ------------------------------------------------------------- block helpers
@@ -449,7 +460,7 @@ __device__ __forceinline__ int waves_before(const int* cnt, int wave, int& all) 
 // candidates than PER * NT or the threshold bin or its ties exceed what LDS
 // lists; the general path then runs. On success `cnt` is the number of ids
 // written.
-template <int NT>
+template <int NT, bool COH>
 __device__ __forceinline__ bool select_registers(bool take_all, int k, int total, int tbin, int above,
                                                  int n_lists, int list_cap, int tbcap,
                                                  const uint32_t* __restrict__ ck_b, const int32_t* __restrict__ ci_b,
@@ -483,8 +494,8 @@ __device__ __forceinline__ bool select_registers(bool take_all, int k, int total
           next = L.pre[lst + 1];
         }
         const int64_t off = (int64_t)lst * list_cap + (pp - cur);
-        kk[u] = get_shared(ck_b + off);
-        ii[u] = get_shared(ci_b + off);
+        kk[u] = ld<COH>(ck_b + off);
+        ii[u] = ld<COH>(ci_b + off);
       }
     }
   }
@@ -605,7 +616,7 @@ __device__ __forceinline__ bool select_registers(bool take_all, int k, int total
 // candidates of the chunks' lists at or above it, resolves the remaining 20
 // bits on full keys, writes the ids (ascending, -1 padded), then clears the
 // histogram and the arrival counter for the next call.
-template <int NT>
+template <int NT, bool COH>
 __device__ __forceinline__ void select_sequence(int64_t nv, int k, int n_lists, int list_cap, int cap, int tbcap,
                                                 uint32_t* __restrict__ gh, uint32_t* __restrict__ arrive,
                                                 uint32_t* __restrict__ ck_b, int32_t* __restrict__ ci_b,
@@ -630,12 +641,12 @@ __device__ __forceinline__ void select_sequence(int64_t nv, int k, int n_lists, 
 #pragma unroll
   for (int j = 0; j < LPT; ++j) {
     const int si = LPT * t + j;
-    c[j] = si < n_lists ? get_shared(cnt_b + si) : 0;
+    c[j] = si < n_lists ? ld<COH>(cnt_b + si) : 0;
   }
   const int top = kHistBins - 1 - BPT * t;
   int hb[BPT];   // hb[j]: bin top - j
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) hb[j] = (int)get_shared(gh + top - j);
+  for (int j = 0; j < BPT; ++j) hb[j] = (int)ld<COH>(gh + top - j);
   for (int i = t; i < kSubBins; i += NT) L.h2[i] = 0u;
   if (t == 0) {
     L.misc[3] = 0;                                  // tie list length (register path)
@@ -686,7 +697,7 @@ __device__ __forceinline__ void select_sequence(int64_t nv, int k, int n_lists, 
   const int kept = take_all ? total : above + tcount;
 
   int cnt = 0;
-  if (select_registers<NT>(take_all, k, total, tbin, above, n_lists, list_cap, tbcap, ck_b, ci_b, out, L, cnt)) {
+  if (select_registers<NT, COH>(take_all, k, total, tbin, above, n_lists, list_cap, tbcap, ck_b, ci_b, out, L, cnt)) {
     // done
   } else if (kept <= cap) {
     // the general path reuses the LDS the register path may have filled
@@ -857,7 +868,7 @@ __device__ __forceinline__ void select_sequence(int64_t nv, int k, int n_lists, 
         const int j = j0 + t;
         uint32_t kk = 0u;
         int32_t ii = 0;
-        if (j < cs) { kk = get_shared(ck_b + from + j); ii = get_shared(ci_b + from + j); }
+        if (j < cs) { kk = ld<COH>(ck_b + from + j); ii = ld<COH>(ci_b + from + j); }
         __syncthreads();
         if (j < cs) { ck_b[to + j] = kk; ci_b[to + j] = ii; }
         __syncthreads();
@@ -879,7 +890,7 @@ __device__ __forceinline__ void select_sequence(int64_t nv, int k, int n_lists, 
 
 // ------------------------------------------------------------- the launch
 
-template <int DI, bool FP4, int NT>
+template <int DI, bool FP4, int NT, bool FUSED>
 __global__ __launch_bounds__(NT) void k_index_topk(
     const uint16_t* __restrict__ q_idx, const void* __restrict__ k_idx,
     const uint8_t* __restrict__ k_scale, const int32_t* __restrict__ n_entries, int64_t n_max,
@@ -970,8 +981,13 @@ __global__ __launch_bounds__(NT) void k_index_topk(
         const uint64_t m = __ballot(keep[u]);
         if (keep[u]) {
           const int p = written + __popcll(m & lanemask_lt());
-          put_shared(ck + p, kv[u]);
-          put_shared(ci + p, (int32_t)(start + i0 + u * kWave + lane));
+          if constexpr (FUSED) {
+            put_shared(ck + p, kv[u]);
+            put_shared(ci + p, (int32_t)(start + i0 + u * kWave + lane));
+          } else {
+            ck[p] = kv[u];
+            ci[p] = (int32_t)(start + i0 + u * kWave + lane);
+          }
         }
         written += __popcll(m);
       }
@@ -980,6 +996,7 @@ __global__ __launch_bounds__(NT) void k_index_topk(
   } else if (t == 0) {
     put_shared(ws_cnt + b * n_chunks + c, 0);
   }
+  if constexpr (!FUSED) return;   // the selection runs in a launch of its own
 
   // Arrival: every wave waits until its list stores and histogram atomics
   // have completed at the coherence point, then the chunk counts in; the
@@ -995,9 +1012,26 @@ __global__ __launch_bounds__(NT) void k_index_topk(
   __syncthreads();
   if (!last_l) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  select_sequence<NT>(nv, k, n_chunks, chunk, cand_cap, tb_cap, gh, ws_arrive + b,
+  select_sequence<NT, true>(nv, k, n_chunks, chunk, cand_cap, tb_cap, gh, ws_arrive + b,
                       ws_ckey + (int64_t)b * n_chunks * chunk, ws_cidx + (int64_t)b * n_chunks * chunk,
                       ws_cnt + b * n_chunks, ids + b * k, lds);
+}
+
+// The selection as a launch of its own (grid: sequences), after a scoring
+// launch that only wrote the candidate lists and the histogram.
+template <int NT>
+__global__ __launch_bounds__(NT) void k_topk_select(const int32_t* __restrict__ n_entries, int64_t n_max, int k,
+                                                   int chunk, int n_chunks, int cand_cap, int tb_cap,
+                                                   uint32_t* __restrict__ ws_hist, uint32_t* __restrict__ ws_arrive,
+                                                   uint32_t* __restrict__ ws_ckey, int32_t* __restrict__ ws_cidx,
+                                                   const int32_t* __restrict__ ws_cnt, int32_t* __restrict__ ids) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  const int64_t b = blockIdx.x;
+  int64_t nv = n_entries ? (int64_t)n_entries[b] : n_max;
+  nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
+  select_sequence<NT, false>(nv, k, n_chunks, chunk, cand_cap, tb_cap, ws_hist + b * kHistBins, ws_arrive + b,
+                             ws_ckey + (int64_t)b * n_chunks * chunk, ws_cidx + (int64_t)b * n_chunks * chunk,
+                             ws_cnt + b * n_chunks, ids + b * k, lds);
 }
 
 // ------------------------------------------------------------- planning / launch
@@ -1007,16 +1041,19 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, bool fp4, TopkPlan* p) {
   // Workgroups of 1024 threads, about one per compute unit: every CU streams
   // with 16 waves, and the selection that ends each sequence runs with 16.
-  p->threads = kTopkThreads;
+  p->fused = kTopkFused;
+  p->threads = kTopkFused ? kTopkThreads : kTopkScoreThreads;
   int64_t chunk = chunk_hint;
   if (chunk == 0) {
-    // about 256 scoring workgroups over the batch, chunks of 1024 .. 16384
-    // entries; more when a sequence would need more chunks than the
-    // selection tracks
-    const int64_t groups = 256;
+    // fused: about 256 workgroups of 1024 threads over the batch, chunks of
+    // 1024 .. 16384 entries; separate selection: about 768 (bf16 keys) or
+    // 1536 (fp4 keys) workgroups of 256, chunks of 512 .. 4096 or 8192; more
+    // when a sequence would need more chunks than the selection tracks
+    const int64_t groups = p->fused ? 256 : (fp4 ? 1536 : 768);
+    const int64_t cap = p->fused ? 16384 : (fp4 ? 8192 : 4096);
     const int64_t want = (B * n_max + groups - 1) / groups;
-    chunk = 1024;
-    while (chunk < want && chunk < 16384) chunk *= 2;
+    chunk = p->fused ? 1024 : 512;
+    while (chunk < want && chunk < cap) chunk *= 2;
     while ((n_max + chunk - 1) / chunk > kMaxChunks && chunk < 16384) chunk *= 2;
   }
   if (chunk < 256 || chunk > 16384 || chunk % 256 != 0) return false;
@@ -1031,8 +1068,9 @@ bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, bool fp4, TopkPl
   p->cand_cap = k <= 1024 ? 2048 : 4096;
   p->tb_cap = kTbCap;
   const size_t score_words = (size_t)kHistBins + (size_t)chunk;
-  const size_t select_words = select_lds_words(p->cand_cap, p->tb_cap, (int)p->n_chunks, p->threads / kWave);
-  p->lds_bytes = 4 * (score_words > select_words ? score_words : select_words);
+  const size_t select_words = select_lds_words(p->cand_cap, p->tb_cap, (int)p->n_chunks, kTopkThreads / kWave);
+  p->lds_bytes = 4 * (p->fused && select_words > score_words ? select_words : score_words);
+  p->select_lds_bytes = 4 * select_words;
   const size_t nb = (size_t)B;
   const size_t slots = nb * (size_t)p->n_chunks * (size_t)chunk;
   size_t off = 0;
@@ -1046,11 +1084,11 @@ bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, bool fp4, TopkPl
   return true;
 }
 
-template <int DI, bool FP4, int NT>
+template <int DI, bool FP4, int NT, bool FUSED>
 static hipError_t launch_t(const TopkPlan& p, const uint16_t* q_idx, const void* k_idx,
                            const uint8_t* k_scale, const int32_t* n_entries, int64_t B, int64_t n_max,
                            int k, int32_t* ids, uint8_t* ws, hipStream_t stream) {
-  auto kern = k_index_topk<DI, FP4, NT>;
+  auto kern = k_index_topk<DI, FP4, NT, FUSED>;
   if (p.lds_bytes > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
@@ -1062,19 +1100,32 @@ static hipError_t launch_t(const TopkPlan& p, const uint16_t* q_idx, const void*
                      reinterpret_cast<uint32_t*>(ws + p.off_hist), reinterpret_cast<uint32_t*>(ws + p.off_arrive),
                      reinterpret_cast<uint32_t*>(ws + p.off_ckey), reinterpret_cast<int32_t*>(ws + p.off_cidx),
                      reinterpret_cast<int32_t*>(ws + p.off_cnt), ids);
+  hipError_t e = hipGetLastError();
+  if (FUSED || e != hipSuccess) return e;
+  auto sel = k_topk_select<kTopkThreads>;
+  if (p.select_lds_bytes > 65536) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(sel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)p.select_lds_bytes);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(sel, dim3((unsigned)B), dim3(kTopkThreads), p.select_lds_bytes, stream, n_entries, n_max, k,
+                     (int)p.chunk, (int)p.n_chunks, p.cand_cap, p.tb_cap,
+                     reinterpret_cast<uint32_t*>(ws + p.off_hist), reinterpret_cast<uint32_t*>(ws + p.off_arrive),
+                     reinterpret_cast<uint32_t*>(ws + p.off_ckey), reinterpret_cast<int32_t*>(ws + p.off_cidx),
+                     reinterpret_cast<const int32_t*>(ws + p.off_cnt), ids);
   return hipGetLastError();
 }
 
-template <int NT>
+template <int NT, bool FUSED>
 static hipError_t launch_nt(const TopkPlan& p, const uint16_t* q_idx, bool fp4, const void* k_idx,
                             const uint8_t* k_scale, const int32_t* n_entries, int64_t B, int64_t n_max,
                             int Di, int k, int32_t* ids, uint8_t* ws, hipStream_t stream) {
   if (fp4) {
-    return Di == 128 ? launch_t<128, true, NT>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream)
-                     : launch_t<32, true, NT>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream);
+    return Di == 128 ? launch_t<128, true, NT, FUSED>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream)
+                     : launch_t<32, true, NT, FUSED>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream);
   }
-  return Di == 128 ? launch_t<128, false, NT>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream)
-                   : launch_t<32, false, NT>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream);
+  return Di == 128 ? launch_t<128, false, NT, FUSED>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream)
+                   : launch_t<32, false, NT, FUSED>(p, q_idx, k_idx, k_scale, n_entries, B, n_max, k, ids, ws, stream);
 }
 
 hipError_t launch_index_topk(const TopkPlan& p, const uint16_t* q_idx, bool fp4, const void* k_idx,
@@ -1082,7 +1133,8 @@ hipError_t launch_index_topk(const TopkPlan& p, const uint16_t* q_idx, bool fp4,
                              int64_t n_max, int Di, int k, int32_t* ids, void* workspace,
                              hipStream_t stream) {
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  return launch_nt<kTopkThreads>(p, q_idx, fp4, k_idx, k_scale, n_entries, B, n_max, Di, k, ids, ws, stream);
+  if (p.fused) return launch_nt<kTopkThreads, true>(p, q_idx, fp4, k_idx, k_scale, n_entries, B, n_max, Di, k, ids, ws, stream);
+  return launch_nt<kTopkScoreThreads, false>(p, q_idx, fp4, k_idx, k_scale, n_entries, B, n_max, Di, k, ids, ws, stream);
 }
 
 }  // namespace cskv

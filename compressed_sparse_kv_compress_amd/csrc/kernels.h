@@ -28,9 +28,11 @@ hipError_t launch_append(int kind, const uint16_t* s_new, const float* g_new, co
 // entry).
 struct TopkPlan {
   int64_t chunk, n_chunks;     // entries per scoring workgroup, workgroups per sequence
-  int threads;                 // workgroup size
+  bool fused;                  // selection by the scoring launch's last chunk per sequence
+  int threads;                 // scoring workgroup size
   int cand_cap, tb_cap;        // selection: candidates gathered in LDS, threshold-bin keys listed
-  size_t lds_bytes;            // dynamic LDS per workgroup
+  size_t lds_bytes;            // dynamic LDS per scoring workgroup
+  size_t select_lds_bytes;     // dynamic LDS of a selection workgroup (separate launch)
   size_t off_hist, off_arrive, off_cnt, off_ckey, off_cidx;
   size_t zero_bytes;           // leading bytes that must be zero between calls
   size_t bytes;                // workspace bytes
