@@ -50,6 +50,8 @@ _lib_topk = _sig("cskv_index_topk", _i32, _p, _i32, _p, _p, _p, _i64, _i64, _i32
 _lib_attend_ws = _sig("cskv_attend_workspace", _sz, _i64, _i32, _i32, _i64, _i32)
 _lib_attend = _sig("cskv_attend", _i32, _p, _i64, _i32, _i32, _i32, _p, _p, _i64, _p, _i32, _p,
                    _i32, _p, _p, _i32, _i64, _p, _i32, _f32, _p, _f32, _p, _i32, _p, _sz, _p)
+_lib_attend_noalloc = _sig("cskv_attend_noalloc", _i32, _p, _i64, _i32, _i32, _i32, _p, _p, _i64, _p, _i32, _p,
+                           _i32, _p, _p, _i32, _i64, _p, _i32, _f32, _p, _f32, _p, _i32, _p)
 _lib_append = _sig("cskv_append", _i32, _i32, _p, _p, _p, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _i64,
                    _p, _p, _p)
 _lib_enc8 = _sig("cskv_encode_fp8_rows", _i32, _i32, _p, _i64, _i32, _p, _p, _p)
@@ -59,6 +61,7 @@ _lib_dec4 = _sig("cskv_decode_fp4_g16", _i32, _p, _p, _i64, _i32, _p, _p)
 
 EXPORTS = ["cskv_status_string", "cskv_last_error", "cskv_version", "cskv_compress", "cskv_append",
            "cskv_index_topk_workspace", "cskv_index_topk", "cskv_attend_workspace", "cskv_attend",
+           "cskv_attend_noalloc",
            "cskv_encode_fp8_rows", "cskv_decode_fp8_rows", "cskv_encode_fp4_g16", "cskv_decode_fp4_g16"]
 
 
@@ -273,7 +276,7 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
            q_pos: torch.Tensor | None = None, cache_scale: torch.Tensor | None = None,
            window_scale: torch.Tensor | None = None, n_entries: torch.Tensor | None = None,
            n_window: torch.Tensor | None = None, out: torch.Tensor | None = None,
-           splits: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
+           splits: int = 0, workspace: torch.Tensor | None = None, noalloc: bool = False) -> torch.Tensor:
     """O [B, H, D] fp32: softmax attention of Q [B, H, D] (bf16) over the cache
     rows named by ids [B, k] (or all of the first n_entries rows when ids is
     None) followed by the window rows [B, W, D], then inverse RoPE on the last
@@ -320,6 +323,12 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
         out = torch.empty((B, H, D), dtype=torch.float32, device=Q.device)
     elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, D) or not out.is_contiguous():
         raise ValueError("out must be contiguous fp32 [B, H, D]")
+    if noalloc:
+        _check(_lib_attend_noalloc(_ptr(Q), B, H, D, cache_dt, _ptr(cache), _ptr(cache_scale),
+                                   cache.shape[1], _ptr(ids), k, _ptr(n_entries), FP8_E4M3 if win_fp8 else BF16,
+                                   _ptr(window), _ptr(window_scale), W, wstride, _ptr(n_window), rope_dims,
+                                   rope_base, _ptr(q_pos), softmax_scale, _ptr(out), splits, _stream(Q.device)))
+        return out
     max_keys = (k if ids is not None else cache.shape[1]) + W
     nbytes = _lib_attend_ws(B, H, D, max_keys, splits)
     if workspace is not None:
@@ -333,6 +342,17 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
                        softmax_scale, _ptr(out), splits, _ptr(ws), 0 if ws is None else ws.numel(),
                        _stream(Q.device)))
     return out
+
+
+def attend_noalloc(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, window: torch.Tensor | None,
+                   **kw) -> torch.Tensor:
+    """attend() through cskv_attend_noalloc: the split partials live in the
+    library's per-device scratch array instead of a workspace, and the call
+    allocates nothing (pass ``out`` too, for a caller that cannot allocate).
+    Calls that overlap in time on one GPU share that scratch and race."""
+    if "workspace" in kw:
+        raise TypeError("attend_noalloc takes no workspace")
+    return attend(Q, cache, ids, window, noalloc=True, **kw)
 
 
 # ------------------------------------------------------------------ codecs

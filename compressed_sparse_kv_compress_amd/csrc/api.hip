@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/cskv.h"
 #include "kernels.h"
@@ -200,14 +201,16 @@ size_t cskv_attend_workspace(int64_t B, int32_t H, int32_t D, int64_t max_keys, 
   return bytes;
 }
 
-cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t cache_dtype,
-                        const void* cache, const float* cache_scale, int64_t cache_rows,
-                        const int32_t* ids, int32_t k, const int32_t* n_entries,
-                        int32_t window_dtype, const void* window, const float* window_scale,
-                        int32_t W, int64_t window_batch_stride, const int32_t* n_window,
-                        int32_t rope_dims, float rope_base, const int64_t* q_pos,
-                        float softmax_scale, float* O,
-                        int32_t splits, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// Validation and planning shared by cskv_attend and cskv_attend_noalloc.
+static cskv_status attend_prepare(const void* Q, int64_t B, int32_t H, int32_t D, int32_t cache_dtype,
+                                  const void* cache, const float* cache_scale, int64_t cache_rows,
+                                  const int32_t* ids, int32_t k, const int32_t* n_entries, int32_t window_dtype,
+                                  const void* window, const float* window_scale, int32_t W,
+                                  int64_t window_batch_stride, const int32_t* n_window, int32_t rope_dims,
+                                  float rope_base, const int64_t* q_pos, float softmax_scale, float* O,
+                                  int32_t splits, cskv::AttendPlan* plan, cskv::AttendArgs* a) {
   CHECK(B >= 0 && cache_rows >= 0 && W >= 0, CSKV_EINVAL, "attend: negative size");
   CHECK(H >= 1 && H <= 64, CSKV_EUNSUPPORTED, "attend: H=%d (supported: 1..64)", H);
   CHECK(D == 128 || D == 512, CSKV_EUNSUPPORTED, "attend: D=%d (supported: 128, 512)", D);
@@ -238,41 +241,115 @@ cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t 
   CHECK(aligned(Q, 16) && aligned(O, 4) && (!cache || aligned(cache, 16)) &&
             (!window || aligned(window, 16)),
         CSKV_EINVAL, "attend: Q, cache and window must be 16-byte aligned");
-  cskv::AttendPlan plan;
   const int64_t max_keys = n_sel_max + W;
-  CHECK(cskv::plan_attend(B, H, D, max_keys, ids != nullptr, splits, &plan), CSKV_EUNSUPPORTED,
+  CHECK(cskv::plan_attend(B, H, D, max_keys, ids != nullptr, splits, plan), CSKV_EUNSUPPORTED,
         "attend: no plan for %lld key slots (sparse reads support at most 524288)", (long long)max_keys);
+  a->Q = reinterpret_cast<const uint16_t*>(Q);
+  a->B = B;
+  a->H = H;
+  a->D = D;
+  a->cache_fp8 = cache_dtype == CSKV_FP8_E4M3;
+  a->cache_mix = cache_dtype == CSKV_FP8_ROPE64;
+  a->cache_fp4 = cache_dtype == CSKV_FP4_E2M1;
+  a->cache = cache;
+  a->cache_scale = cache_scale;
+  a->cache_rows = cache_rows;
+  a->ids = ids;
+  a->k = ids ? k : 0;
+  a->n_entries = ids ? nullptr : n_entries;
+  a->win_fp8 = window_dtype == CSKV_FP8_E4M3;
+  a->window = window;
+  a->window_scale = window_scale;
+  a->W = W;
+  a->n_window = W > 0 ? n_window : nullptr;
+  a->win_bstride = window_batch_stride;
+  a->rope_dims = rope_dims;
+  a->rope_base = rope_base;
+  a->q_pos = q_pos;
+  a->softmax_scale = softmax_scale;
+  a->O = O;
+  return ok();
+}
+
+// Scratch of cskv_attend_noalloc: the split partials of an attend call, in a
+// file-scope device array instead of a caller workspace. Host code must not
+// use this name as an address (on the host it is a stand-in); the device
+// address of each GPU's copy comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[CSKV_ATTEND_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's scratch array (looked up the
+// first time a call runs on that device).
+cskv_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CSKV_EHIP, "attend_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  CHECK(dev >= 0 && dev < kMaxDevices, CSKV_EUNSUPPORTED, "attend_noalloc: device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(CSKV_EHIP, "attend_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+}  // namespace
+
+extern "C" {
+
+cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t cache_dtype,
+                        const void* cache, const float* cache_scale, int64_t cache_rows,
+                        const int32_t* ids, int32_t k, const int32_t* n_entries,
+                        int32_t window_dtype, const void* window, const float* window_scale,
+                        int32_t W, int64_t window_batch_stride, const int32_t* n_window,
+                        int32_t rope_dims, float rope_base, const int64_t* q_pos,
+                        float softmax_scale, float* O,
+                        int32_t splits, void* workspace, size_t workspace_bytes, void* stream) {
+  cskv::AttendPlan plan;
+  cskv::AttendArgs a;
+  const cskv_status st = attend_prepare(Q, B, H, D, cache_dtype, cache, cache_scale, cache_rows, ids, k, n_entries,
+                                        window_dtype, window, window_scale, W, window_batch_stride, n_window,
+                                        rope_dims, rope_base, q_pos, softmax_scale, O, splits, &plan, &a);
+  if (st != CSKV_OK || B == 0) return st;
   CHECK(workspace_bytes >= plan.bytes, CSKV_EINVAL, "attend: workspace %zu bytes < %zu required",
         workspace_bytes, plan.bytes);
   CHECK(plan.bytes == 0 || (workspace && aligned(workspace, 256)), CSKV_EINVAL,
         "attend: workspace must be non-null and 256-byte aligned");
-  cskv::AttendArgs a;
-  a.Q = reinterpret_cast<const uint16_t*>(Q);
-  a.B = B;
-  a.H = H;
-  a.D = D;
-  a.cache_fp8 = cache_dtype == CSKV_FP8_E4M3;
-  a.cache_mix = cache_dtype == CSKV_FP8_ROPE64;
-  a.cache_fp4 = cache_dtype == CSKV_FP4_E2M1;
-  a.cache = cache;
-  a.cache_scale = cache_scale;
-  a.cache_rows = cache_rows;
-  a.ids = ids;
-  a.k = ids ? k : 0;
-  a.n_entries = ids ? nullptr : n_entries;
-  a.win_fp8 = window_dtype == CSKV_FP8_E4M3;
-  a.window = window;
-  a.window_scale = window_scale;
-  a.W = W;
-  a.n_window = W > 0 ? n_window : nullptr;
-  a.win_bstride = window_batch_stride;
-  a.rope_dims = rope_dims;
-  a.rope_base = rope_base;
-  a.q_pos = q_pos;
-  a.softmax_scale = softmax_scale;
-  a.O = O;
   return hip_status(cskv::launch_attend(plan, a, workspace, reinterpret_cast<hipStream_t>(stream)),
                     "attend launch");
+}
+
+cskv_status cskv_attend_noalloc(const void* Q, int64_t B, int32_t H, int32_t D, int32_t cache_dtype,
+                                const void* cache, const float* cache_scale, int64_t cache_rows,
+                                const int32_t* ids, int32_t k, const int32_t* n_entries,
+                                int32_t window_dtype, const void* window, const float* window_scale,
+                                int32_t W, int64_t window_batch_stride, const int32_t* n_window,
+                                int32_t rope_dims, float rope_base, const int64_t* q_pos,
+                                float softmax_scale, float* O, int32_t splits, void* stream) {
+  cskv::AttendPlan plan;
+  cskv::AttendArgs a;
+  const cskv_status st = attend_prepare(Q, B, H, D, cache_dtype, cache, cache_scale, cache_rows, ids, k, n_entries,
+                                        window_dtype, window, window_scale, W, window_batch_stride, n_window,
+                                        rope_dims, rope_base, q_pos, softmax_scale, O, splits, &plan, &a);
+  if (st != CSKV_OK || B == 0) return st;
+  CHECK(plan.bytes <= (size_t)CSKV_ATTEND_NOALLOC_SCRATCH_BYTES, CSKV_EUNSUPPORTED,
+        "attend_noalloc: the call needs %zu bytes of scratch, more than the %d the library holds per device "
+        "(use cskv_attend with a workspace, or fewer splits or sequences per call)",
+        plan.bytes, CSKV_ATTEND_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (plan.bytes > 0) {
+    const cskv_status s2 = scratch_of_current_device(&ws);
+    if (s2 != CSKV_OK) return s2;
+  }
+  return hip_status(cskv::launch_attend(plan, a, ws, reinterpret_cast<hipStream_t>(stream)),
+                    "attend_noalloc launch");
 }
 
 // ------------------------------------------------------------------ codecs

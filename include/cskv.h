@@ -226,6 +226,32 @@ cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t 
                         int32_t splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * cskv_attend without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).
+ *
+ * Arguments, results and errors are those of cskv_attend; the split partials
+ * that cskv_attend keeps in the caller's workspace live instead in a scratch
+ * array of CSKV_ATTEND_NOALLOC_SCRATCH_BYTES that the library holds in each
+ * GPU's memory for the life of the process (its device address is looked up
+ * on the first call on a device). The call allocates nothing. A call whose
+ * plan needs more scratch than that returns CSKV_EUNSUPPORTED with a message
+ * naming both sizes (the plan needs B * splits * 64 * (2 D + 8) bytes; e.g.
+ * 16.9 MB for 16 sequences of 16 splits at D = 512). Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (two streams,
+ * or two threads with their own streams) race and give wrong results; calls
+ * ordered on one stream do not. The scratch keeps no state between calls.
+ */
+#define CSKV_ATTEND_NOALLOC_SCRATCH_BYTES (32 << 20)
+cskv_status cskv_attend_noalloc(const void* Q, int64_t B, int32_t H, int32_t D, int32_t cache_dtype,
+                                const void* cache, const float* cache_scale, int64_t cache_rows,
+                                const int32_t* ids, int32_t k, const int32_t* n_entries,
+                                int32_t window_dtype, const void* window, const float* window_scale,
+                                int32_t W, int64_t window_batch_stride, const int32_t* n_window,
+                                int32_t rope_dims, float rope_base, const int64_t* q_pos,
+                                float softmax_scale, float* O, int32_t splits, void* stream);
+
+/* ------------------------------------------------------------------------
  * Cache codecs ([P1] quantisation paragraph: fp8 attention cache, "partly
  * token-wise"; fp4 indexer cache. [P3] "Three mechanisms", third: E2M1 values
  * with one E4M3 scale per 16 channels). The same device routines run fused

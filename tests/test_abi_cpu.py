@@ -153,3 +153,25 @@ def test_codec_validation(lib):
     assert lib._lib_enc4(lib.F32, p, 4, 24, p, p, None) == lib.EINVAL
     assert lib._lib_dec4(p, p, 4, 24, p, None) == lib.EINVAL
     assert lib._lib_enc8(lib.F32, None, 0, 128, None, None, None) == lib.OK
+
+
+def test_attend_noalloc_validation(lib):
+    """The no-allocation attend validates like attend and rejects, on the host,
+    a call whose split partials would not fit the library's scratch array."""
+    p = ctypes.c_void_p(256)
+    f = lib._lib_attend_noalloc
+
+    def call(**kw):
+        a = dict(Q=p, B=1, H=64, D=512, cdt=lib.BF16, cache=p, cs=None, rows=10, ids=p, k=4, ne=None,
+                 wdt=lib.BF16, win=p, ws_=None, W=4, wst=4, nw=None, R=64, base=10000.0, pos=p, tau=0.1, O=p,
+                 splits=1, stream=None)
+        a.update(kw)
+        return f(*a.values())
+
+    assert call(H=65) == lib.EUNSUPPORTED
+    assert call(R=63) == lib.EINVAL
+    assert call(cdt=lib.FP8_E4M3) == lib.EINVAL            # fp8 cache without scales
+    # 4096 sequences x 64 splits of partials: far beyond the 32 MiB scratch
+    assert call(B=4096, k=4000, splits=64) == lib.EUNSUPPORTED
+    assert b"scratch" in lib._lib_last_error()
+    assert call(B=0) == lib.OK
