@@ -1,5 +1,6 @@
 // C ABI of libcskv: argument validation, launch planning, error reporting.
 // Everything is checked on the host before any kernel is enqueued.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -265,6 +266,7 @@ static cskv_status attend_prepare(const void* Q, int64_t B, int32_t H, int32_t D
   a->win_bstride = window_batch_stride;
   a->rope_dims = rope_dims;
   a->rope_base = rope_base;
+  for (int i = 0; i < rope_dims / 2; ++i) a->inv_freq[i] = std::pow((double)rope_base, -2.0 * i / rope_dims);
   a->q_pos = q_pos;
   a->softmax_scale = softmax_scale;
   a->O = O;

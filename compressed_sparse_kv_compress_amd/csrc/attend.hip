@@ -361,27 +361,6 @@ __device__ __forceinline__ void issue_tile(const RowSrc& rsrc, int64_t tile0, in
   }
 }
 
-// Widens a staged fp8 tile into a bf16 tile: thread t converts the 64 codes
-// of row t/8, logical chunks 8(t%8) .. 8(t%8)+7 (empty rows hold zero codes).
-template <int D>
-__device__ __forceinline__ void widen_tile(const uint8_t* stage, uint16_t* tile) {
-  using C = AttCfg<D, true, true>;
-  const int t = threadIdx.x;
-  const int r = t >> 3, part = t & 7;
-  const uint8_t* src = stage + r * D + part * 64;
-  uint4 c[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) c[j] = *reinterpret_cast<const uint4*>(src + 16 * j);
-  uint16_t* row = tile + r * C::KROW;
-  const int swz = chunk_swz(r);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ch0 = 8 * part + 2 * j;          // logical chunks ch0, ch0 + 1
-    *reinterpret_cast<uint4*>(row + 8 * (ch0 ^ swz)) = fp8x8_to_bf16x8(make_uint2(c[j].x, c[j].y));
-    *reinterpret_cast<uint4*>(row + 8 * ((ch0 + 1) ^ swz)) = fp8x8_to_bf16x8(make_uint2(c[j].z, c[j].w));
-  }
-}
-
 // A 16-byte LDS store the compiler does not see as one: it would otherwise
 // wait for every LDS DMA in flight first (it cannot tell the DMA targets from
 // this address). Used only for stores into a tile whose DMA has landed; the
@@ -392,6 +371,42 @@ __device__ __forceinline__ void lds_store_b128_unordered(void* p, uint4 v) {
   const u32x4v d = {v.x, v.y, v.z, v.w};
   asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(d) : "memory");
 }
+
+// Widens a staged fp8 tile into a bf16 tile: thread t converts the 64 codes
+// of row t/8, logical chunks 8(t%8) .. 8(t%8)+7 (empty rows hold zero codes).
+template <int D>
+__device__ __forceinline__ void widen_tile(const uint8_t* stage, uint16_t* tile) {
+  using C = AttCfg<D, true, true>;
+  const int t = threadIdx.x;
+  const int r = t >> 3, part = t & 7;
+  const uint8_t* src = stage + r * D + part * 64;
+  // the staged codes are read in one asm block that waits for its own reads:
+  // as ordinary LDS reads the compiler would first wait for every DMA in
+  // flight (it cannot tell this staging slot from the ones still landing),
+  // which empties the ring on every tile
+  uint4 c[4];
+  {
+    const uint32_t a0 = (uint32_t)reinterpret_cast<uintptr_t>(src);
+    asm volatile(
+        "ds_read_b128 %0, %4\n"
+        "ds_read_b128 %1, %4 offset:16\n"
+        "ds_read_b128 %2, %4 offset:32\n"
+        "ds_read_b128 %3, %4 offset:48\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3])
+        : "v"(a0)
+        : "memory");
+  }
+  uint16_t* row = tile + r * C::KROW;
+  const int swz = chunk_swz(r);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ch0 = 8 * part + 2 * j;          // logical chunks ch0, ch0 + 1
+    lds_store_b128_unordered(row + 8 * (ch0 ^ swz), fp8x8_to_bf16x8(make_uint2(c[j].x, c[j].y)));
+    lds_store_b128_unordered(row + 8 * ((ch0 + 1) ^ swz), fp8x8_to_bf16x8(make_uint2(c[j].z, c[j].w)));
+  }
+}
+
 
 // Raw rows (mixed or fp4) are widened in place in two phases: a read phase
 // that takes one thread's share of the tile's raw bytes into registers, then
@@ -774,10 +789,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
     }
     if (pass == 0 && splits == 1 && t < a.rope_dims / 2) {
       // the rotary table of a single split, while the first tiles are in flight
-      const double theta = pow((double)a.rope_base, -2.0 * (double)t / (double)a.rope_dims);
-      const double ang = -(double)a.q_pos[b] * theta;
-      cos_l[t] = (float)cos(ang);
-      sin_l[t] = (float)sin(ang);
+      double sn, cs;
+      sincos(-(double)a.q_pos[b] * a.inv_freq[t], &sn, &cs);
+      cos_l[t] = (float)cs;
+      sin_l[t] = (float)sn;
     }
     for (int i = 0; i < n_tiles; i += kNStage) {
       step(std::integral_constant<int, 0>{}, i);
@@ -852,238 +867,6 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   }
 }
 
-// Head-split attention for sparse bf16 reads (D = 512, H a multiple of 16):
-// workgroup (head group hg, sequence b) takes heads 16hg .. 16hg+15 over all
-// of the sequence's key slots, so there are no partials and no merge. Tiles
-// hold 64 slots in a ring of two LDS buffers, one tile ahead; wave w computes
-// S^T for slots 16w .. 16w+15 of a tile (each key row is read from LDS once)
-// and O^T for channels 128w .. 128w+127, with the transposing reads and the
-// probability layout of the all-heads kernel (the four waves' probabilities
-// meet in a 2 KiB buffer). Softmax, the reference maximum and the second pass
-// are as there. The four head groups of a sequence get workgroup ids that are
-// equal mod 8: workgroups are dealt to the 8 XCDs by id mod 8, so the groups
-// share one XCD's L2 and three of their four reads of a key row hit it.
-constexpr int kHsTK = 64;   // key slots per head-split tile
-
-// An 8-byte LDS store the compiler does not see as one. It would otherwise
-// wait for every LDS DMA in flight first (it cannot tell the DMA's target from
-// this address). Callers store only to LDS that no DMA targets, and the next
-// lds_barrier() waits for the store (lgkmcnt(0)).
-__device__ __forceinline__ void lds_store_b64_unordered(void* p, uint32_t lo, uint32_t hi) {
-  const uint32_t addr = (uint32_t)reinterpret_cast<uintptr_t>(p);   // LDS offset
-  const uint64_t d = ((uint64_t)hi << 32) | lo;
-  asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(d) : "memory");
-}
-
-template <int D>
-__global__ __launch_bounds__(kAttThreads, 1) void k_attend_hs(AttendArgs a, int n_hg) {
-  using C = AttCfg<D, false, false>;
-  static_assert(C::kDma, "bf16 rows by DMA");
-  constexpr int KS = D / 32;          // k-steps of QK^T
-  constexpr int CTW = D / 64;         // 16-channel tiles of O^T per wave
-  constexpr int KROW = C::KROW;
-  __shared__ __attribute__((aligned(16))) uint16_t hs_tile0[kHsTK * KROW], hs_tile1[kHsTK * KROW];
-  __shared__ __attribute__((aligned(16))) float hs_pb0[kHsTK], hs_pb1[kHsTK];
-  __shared__ float hs_vs[4];                      // (bf16 rows carry no value scale)
-  // entry ids, then the probabilities [k-step][head][key slot in the k order
-  // of PV] (one LDS object that no DMA targets, so that the compiler orders
-  // the probability stores against no DMA)
-  __shared__ __attribute__((aligned(16))) int32_t ids_p_l[kMaxSplitIds + 2 * 16 * 32 / 2];
-  int32_t* const ids_l = ids_p_l;
-  uint16_t* const p_l = reinterpret_cast<uint16_t*>(ids_p_l + kMaxSplitIds);
-  __shared__ float mx_l[4][16], ls_l[4][16];
-  __shared__ int redo_l;
-  __shared__ __attribute__((aligned(16))) uint8_t dma_first_l[16 * kWave];
-  __shared__ float cos_l[D / 2], sin_l[D / 2];
-
-  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
-  const int l16 = lane & 15, g = lane >> 4;
-  // workgroup id -> (sequence, head group), ids of one sequence equal mod 8
-  const int id = blockIdx.x;
-  const int rest = id >> 3;
-  const int hg = rest % n_hg;
-  const int64_t b = (int64_t)(rest / n_hg) * 8 + (id & 7);
-  if (b >= a.B) return;
-  const int n_sel = a.k;
-  const int64_t n_keys = (int64_t)n_sel + window_rows(a, b);
-  const int n_tiles = (int)((n_keys + kHsTK - 1) / kHsTK);
-  const float tau_log2e = a.softmax_scale * kLog2e;
-  const int h = 16 * hg + l16;                    // this lane's head
-
-  // Q fragment: B operand of S^T = K Q^T; lane holds Q[h][32ks + 8g .. +7]
-  bf16x8_t qf[KS];
-  {
-    const uint16_t* qrow = a.Q + (b * a.H + h) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g));
-  }
-  for (int j = t; j < n_sel; j += kAttThreads) ids_l[j] = a.ids[b * a.k + j];
-  if (t == 0) redo_l = 0;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // QK^T A operand: key row 16w + l16, logical chunk 4ks + g
-  const int krow = 16 * wave + l16;
-  const int qk_off = krow * KROW + 8 * (g ^ chunk_swz(krow));
-  // PV A operand by transposing reads (as in the all-heads kernel; k-step kk
-  // reads rows 32kk ..): lane l16 of group g supplies 4 channels of row
-  // 4g + l16/4 (then 16 + ...), so that lane l16 receives channel c0 + l16
-  const int tq = l16 & 3, tr_r = l16 >> 2;
-  const int tr_row0 = 4 * g + tr_r, tr_row1 = 16 + 4 * g + tr_r;
-  int tr_base0[2], tr_base1[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    tr_base0[e] = tr_row0 * KROW + 8 * ((2 * e + (tq >> 1)) ^ chunk_swz(tr_row0)) + 4 * (tq & 1) + 16 * CTW * wave;
-    tr_base1[e] = tr_row1 * KROW + 8 * ((2 * e + (tq >> 1)) ^ chunk_swz(tr_row1)) + 4 * (tq & 1) + 16 * CTW * wave;
-  }
-  // probabilities: QK^T lane (head l16, g) holds slots 16w + 4g + i, which
-  // are k-step w/2, k order 8g + 4(w%2) + i; PV lane (head l16, g) reads k
-  // order 8g .. 8g+7 of its k-step
-  const int p_wr = (wave >> 1) * 512 + l16 * 32 + 8 * g + 4 * (wave & 1);
-  const int p_rd = l16 * 32 + 8 * g;
-
-  const RowSrc rsrc = row_src<D, false, false>(a, b);
-  auto tile_of = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
-    return decltype(sc)::value == 0 ? hs_tile0 : hs_tile1;
-  };
-  auto pb_of = [&](auto sc) __attribute__((always_inline)) -> float* {
-    return decltype(sc)::value == 0 ? hs_pb0 : hs_pb1;
-  };
-  // a tile of 64 slots is two fills of 32 rows (rows 32 .. 63 keep the
-  // swizzle of rows 0 .. 31, since it depends on (row / 8) mod 4)
-  auto issue = [&](auto sc, int i) __attribute__((always_inline)) {
-    const int64_t s0 = (int64_t)i * kHsTK;
-    issue_tile<D, false, false>(rsrc, s0, 0, n_sel, n_keys, false, ids_l, tile_of(sc), nullptr, pb_of(sc),
-                                hs_vs, wave, lane);
-    issue_tile<D, false, false>(rsrc, s0 + 32, 0, n_sel, n_keys, false, ids_l, tile_of(sc) + 32 * KROW, nullptr,
-                                pb_of(sc) + 32, hs_vs, wave, lane);
-  };
-
-  float m_ref = 0.0f, m_seen, l_run;
-  f32x4_t acc[CTW];   // O^T[16 (CTW wave + j) + 4g + i][16 hg + l16]
-
-  auto qk_softmax = [&](const uint16_t* kt, const float* pbv) __attribute__((always_inline)) {
-    const float4 bias = *reinterpret_cast<const float4*>(pbv + 16 * wave + 4 * g);
-    constexpr int kQD = 4;
-    bf16x8_t ka[KS];
-#pragma unroll
-    for (int ks = 0; ks < kQD; ++ks) ka[ks] = *reinterpret_cast<const bf16x8_t*>(kt + qk_off + 32 * ks);
-    f32x4_t sv = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + kQD < KS) ka[ks + kQD] = *reinterpret_cast<const bf16x8_t*>(kt + qk_off + 32 * (ks + kQD));
-      sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qf[ks], sv, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const float bb[4] = {bias.x, bias.y, bias.z, bias.w};
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = fmaf(sv[i], tau_log2e, bb[i]);
-      m_seen = fmaxf(m_seen, x);
-      p[i] = __builtin_amdgcn_exp2f(x - m_ref);   // exp2(-inf) = 0 for empty slots
-      l_run += p[i];
-    }
-    lds_store_b64_unordered(p_l + p_wr, pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-  };
-
-  auto pv = [&](const uint16_t* kt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8_t pbv = *reinterpret_cast<const bf16x8_t*>(p_l + kk * 512 + p_rd);
-      const uint16_t* kb = kt + kk * 32 * KROW;
-      v4i16_t kr0[CTW], kr1[CTW];
-#pragma unroll
-      for (int j = 0; j < CTW; ++j) {
-        const int e = j & 1, m = j >> 1;
-        kr0[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kb + tr_base0[e] + 32 * m));
-        kr1[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kb + tr_base1[e] + 32 * m));
-      }
-#pragma unroll
-      for (int j = 0; j < CTW; ++j) {
-        const v4i16_t kv[2] = {kr0[j], kr1[j]};
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), pbv, acc[j], 0, 0, 0);
-      }
-    }
-  };
-
-  // one step: tile i sits in ring slot S = i mod 2; it is the only DMA in flight
-  auto step = [&](auto sc, int i) __attribute__((always_inline)) {
-    constexpr int S = decltype(sc)::value;
-    if (i >= n_tiles) return;
-    wait_vm<0>();
-    lds_barrier();   // tile i visible; the other slot and the probabilities are free
-    if (i + 1 < n_tiles) issue(std::integral_constant<int, (S + 1) % 2>{}, i + 1);
-    qk_softmax(tile_of(sc), pb_of(sc));
-    lds_barrier();   // probabilities of all 64 slots visible
-    pv(tile_of(sc));
-  };
-
-  // (still in flight when the first tile wait retires it with everything older)
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g_zero_row + 16 * lane),
-                                   (__attribute__((address_space(3))) void*)dma_first_l, 16, 0, 0);
-#pragma nounroll
-  for (int pass = 0;; ++pass) {
-#pragma unroll
-    for (int j = 0; j < CTW; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    m_seen = -INFINITY;
-    l_run = 0.0f;
-    if (n_tiles > 0) issue(std::integral_constant<int, 0>{}, 0);
-    if (pass == 0 && t < a.rope_dims / 2) {
-      // the rotary table, while the first tile is in flight
-      const double theta = pow((double)a.rope_base, -2.0 * (double)t / (double)a.rope_dims);
-      const double ang = -(double)a.q_pos[b] * theta;
-      cos_l[t] = (float)cos(ang);
-      sin_l[t] = (float)sin(ang);
-    }
-    for (int i = 0; i < n_tiles; i += 2) {
-      step(std::integral_constant<int, 0>{}, i);
-      step(std::integral_constant<int, 1>{}, i + 1);
-    }
-    // each head's largest logit and sum over the four waves' slots
-    float mh = fmaxf(m_seen, __shfl_xor(m_seen, 16, kWave));
-    mh = fmaxf(mh, __shfl_xor(mh, 32, kWave));
-    float lh = l_run + __shfl_xor(l_run, 16, kWave);
-    lh += __shfl_xor(lh, 32, kWave);
-    if (g == 0) {
-      mx_l[wave][l16] = mh;
-      ls_l[wave][l16] = lh;
-    }
-    lds_barrier();   // every wave is done with the ring
-    mh = fmaxf(fmaxf(mx_l[0][l16], mx_l[1][l16]), fmaxf(mx_l[2][l16], mx_l[3][l16]));
-    l_run = ls_l[0][l16] + ls_l[1][l16] + ls_l[2][l16] + ls_l[3][l16];
-    const bool redo = pass == 0 && mh != -INFINITY && (mh > m_ref + kHeadroom || mh < m_ref - kHeadroom);
-    if (__ballot(redo) && lane == 0) redo_l = 1;
-    lds_barrier();   // votes visible; the per-head values read
-    if (redo_l == 0 || pass > 0) break;
-    m_ref = mh != -INFINITY ? mh : 0.0f;
-  }
-
-  wait_vm<0>();   // (with no tiles, the first DMA is still in flight)
-  // lane (l16, g) holds channels 16 (CTW wave + j) + 4g .. +3 of head h
-  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-  const int R = a.rope_dims;
-  float* orow = a.O + (b * a.H + h) * D;
-#pragma unroll
-  for (int j = 0; j < CTW; ++j) {
-    const int c = 16 * (CTW * wave + j) + 4 * g;
-    const f32x4_t v = acc[j];
-    float4 o = make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-    if (c >= D - R) {
-      const int q = (c - (D - R)) >> 1;
-      const float c0 = cos_l[q], s0 = sin_l[q];
-      o = make_float4(o.x * c0 - o.y * s0, o.x * s0 + o.y * c0, o.z, o.w);
-    }
-    if (c + 2 >= D - R) {
-      const int q = (c + 2 - (D - R)) >> 1;
-      const float c1 = cos_l[q], s1 = sin_l[q];
-      o = make_float4(o.x, o.y, o.z * c1 - o.w * s1, o.z * s1 + o.w * c1);
-    }
-    *reinterpret_cast<float4*>(orow + c) = o;
-  }
-}
-
 // Log-sum-exp merge of a sequence's splits, then inverse RoPE. Workgroup
 // (q, b) combines partial block q (a 16-channel tile of every head: 256
 // blocks of 4 channels): thread t owns block t, i.e. head 16 (t / 64) + t % 16
@@ -1114,10 +897,10 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
     const int c = 16 * q + 2 * t;
     if (c >= D - R) {
       const int jj = (c - (D - R)) >> 1;
-      const double th = pow((double)a.rope_base, -2.0 * (double)jj / (double)R);
-      const double ang = -(double)a.q_pos[b] * th;
-      cs_l[0][t] = (float)cos(ang);
-      cs_l[1][t] = (float)sin(ang);
+      double sn, cs;
+      sincos(-(double)a.q_pos[b] * a.inv_freq[jj], &sn, &cs);
+      cs_l[0][t] = (float)cs;
+      cs_l[1][t] = (float)sn;
     }
   }
   // thread (grp, hh0) folds the (reference maximum, sum) pairs of head hh0
@@ -1221,8 +1004,6 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
 // ------------------------------------------------------------- planning / launch
 
 bool plan_attend(int64_t B, int H, int D, int64_t max_keys, bool sparse, int splits_hint, AttendPlan* p) {
-  (void)H;
-  (void)D;
   const int64_t tiles = max_keys <= 0 ? 1 : (max_keys + kTK - 1) / kTK;
   int64_t splits = splits_hint;
   if (splits <= 0) {
@@ -1243,12 +1024,7 @@ bool plan_attend(int64_t B, int H, int D, int64_t max_keys, bool sparse, int spl
   splits = (tiles + tiles_per - 1) / tiles_per;
   p->splits = (int)splits;
   p->keys_per_split = tiles_per * kTK;
-  // sparse reads with automatic splits may take the head-split kernel instead
-  // when it has a workgroup for every compute unit (with fewer, its one tile
-  // in flight per workgroup leaves it latency-bound and the split kernel is
-  // faster); launch_attend checks the row formats, D, H and k
-  p->head_split = sparse && splits_hint == 0 && B * (H / 16) >= 256;
-  // bf16 partials, then an fp32 (reference maximum, sum) pair per head
+  // workspace: bf16 partials, then an fp32 (reference maximum, sum) pair per head
   p->bytes = splits > 1 ? (size_t)B * splits * kHMax * ((size_t)D * 2 + 8) : 0;
   return true;
 }
@@ -1277,14 +1053,6 @@ static hipError_t launch_attend_t(const AttendPlan& p, const AttendArgs& a, void
 
 hipError_t launch_attend(const AttendPlan& p, const AttendArgs& a, void* workspace,
                          hipStream_t stream) {
-  if (p.head_split && a.ids && a.D == 512 && !a.cache_fp8 && !a.cache_mix && !a.cache_fp4 && !a.win_fp8 &&
-      a.H % 16 == 0 &&
-      a.k <= kMaxSplitIds) {
-    const int n_hg = a.H / 16;
-    const unsigned n_wg = (unsigned)(8 * ((a.B + 7) / 8) * n_hg);
-    hipLaunchKernelGGL(k_attend_hs<512>, dim3(n_wg), dim3(kAttThreads), 0, stream, a, n_hg);
-    return hipGetLastError();
-  }
   if (a.D == 512) {
     if (a.cache_mix) return a.win_fp8 ? launch_attend_t<512, kFmtMix, true>(p, a, workspace, stream)
                                       : launch_attend_t<512, kFmtMix, false>(p, a, workspace, stream);

@@ -47,8 +47,7 @@ hipError_t launch_index_topk(const TopkPlan& plan, const uint16_t* q_idx, bool f
 struct AttendPlan {
   int splits;            // key-row splits per sequence
   int64_t keys_per_split;
-  size_t bytes;          // workspace bytes (partials), 0 when splits == 1
-  bool head_split;       // sparse reads may use the head-split kernel (no partials)
+  size_t bytes;          // workspace bytes: the splits' partials (none with one split)
 };
 // Plans the key-slot splits of an attend call; sparse calls stage their entry
 // ids in LDS, which bounds a split's length. False if no plan exists.
@@ -75,6 +74,9 @@ struct AttendArgs {
   int rope_dims;
   float rope_base;
   const int64_t* q_pos;
+  // rotary frequencies theta_i = rope_base^(-2i / rope_dims), i < rope_dims / 2,
+  // in fp64, computed on the host (they depend on no device data)
+  double inv_freq[256];
   float softmax_scale;
   float* O;
 };

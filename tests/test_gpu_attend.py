@@ -187,13 +187,13 @@ def test_fp8_logits_far_from_zero(cskv):
 
 
 @pytest.mark.parametrize("B,H,k,W,R", [
-    (64, 64, 512, 128, 64),   # the c4a layer shape, at a batch that takes the head-split kernel
+    (64, 64, 512, 128, 64),   # the c4a layer shape of the 61-layer step (one split per CU at auto splits)
     (64, 64, 300, 40, 64),    # a ragged last tile and a short window
     (256, 16, 100, 0, 0),     # one head group, no window, no rotation
 ])
-def test_sparse_head_split_matches_oracle(cskv, B, H, k, W, R):
-    """Sparse bf16 reads with automatic splits at B x H/16 >= 256 run the
-    head-split kernel (no partials); some sequences end in -1 ids."""
+def test_sparse_large_batch_matches_oracle(cskv, B, H, k, W, R):
+    """Sparse bf16 reads at large batches, automatic splits and one split;
+    some sequences end in -1 ids."""
     D, N = 512, 2000
     seed = 700 + B + H
     Q = _bf16(seed, synth.T_Q, (B, H, D))
@@ -212,8 +212,8 @@ def test_sparse_head_split_matches_oracle(cskv, B, H, k, W, R):
         assert err <= 2e-2, (splits, err)
 
 
-def test_sparse_head_split_far_logits(cskv):
-    """The head-split kernel's second pass: heads against, along and across a
+def test_sparse_large_batch_far_logits(cskv):
+    """The second pass at a large batch: heads against, along and across a
     common row direction, so some heads' logits lie far below zero."""
     B, H, D, N, k, W, R = 64, 64, 512, 1200, 256, 40, 64
     seed = 64
