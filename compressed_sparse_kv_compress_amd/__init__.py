@@ -7,6 +7,7 @@ and the current stream.
 """
 from ._lib import (  # noqa: F401
     BF16, C128A, C4A, EHIP, EINVAL, EUNSUPPORTED, F32, FP4_E2M1, FP8_E4M3, FP8_ROPE64, LIB_PATH, MIX_ROPE, OK,
-    CskvError, append, attend, attend_noalloc, compress, decode_fp4_g16, decode_fp8_rows, encode_fp4_g16,
+    CskvError, append, attend, attend_noalloc, attend_window_partial, compress, decode_fp4_g16, decode_fp8_rows,
+    encode_fp4_g16, partial_bytes,
     encode_fp8_rows, index_topk, raw, version,
 )

@@ -52,6 +52,11 @@ _lib_attend = _sig("cskv_attend", _i32, _p, _i64, _i32, _i32, _i32, _p, _p, _i64
                    _i32, _p, _p, _i32, _i64, _p, _i32, _f32, _p, _f32, _p, _i32, _p, _sz, _p)
 _lib_attend_noalloc = _sig("cskv_attend_noalloc", _i32, _p, _i64, _i32, _i32, _i32, _p, _p, _i64, _p, _i32, _p,
                            _i32, _p, _p, _i32, _i64, _p, _i32, _f32, _p, _f32, _p, _i32, _p)
+_lib_attend_part = _sig("cskv_attend_with_partial", _i32, _p, _i64, _i32, _i32, _i32, _p, _p, _i64, _p, _i32, _p,
+                        _i32, _p, _p, _i32, _i64, _p, _i32, _f32, _p, _f32, _p, _p, _i32, _p, _sz, _p)
+_lib_partial_bytes = _sig("cskv_attend_partial_bytes", _sz, _i64, _i32, _i32)
+_lib_window_partial = _sig("cskv_attend_window_partial", _i32, _p, _i64, _i32, _i32, _i32, _p, _p, _i32, _i64, _p,
+                           _f32, _p, _p)
 _lib_append = _sig("cskv_append", _i32, _i32, _p, _p, _p, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _i64,
                    _p, _p, _p)
 _lib_enc8 = _sig("cskv_encode_fp8_rows", _i32, _i32, _p, _i64, _i32, _p, _p, _p)
@@ -61,7 +66,8 @@ _lib_dec4 = _sig("cskv_decode_fp4_g16", _i32, _p, _p, _i64, _i32, _p, _p)
 
 EXPORTS = ["cskv_status_string", "cskv_last_error", "cskv_version", "cskv_compress", "cskv_append",
            "cskv_index_topk_workspace", "cskv_index_topk", "cskv_attend_workspace", "cskv_attend",
-           "cskv_attend_noalloc",
+           "cskv_attend_noalloc", "cskv_attend_partial_bytes", "cskv_attend_window_partial",
+           "cskv_attend_with_partial",
            "cskv_encode_fp8_rows", "cskv_decode_fp8_rows", "cskv_encode_fp4_g16", "cskv_decode_fp4_g16"]
 
 
@@ -271,20 +277,44 @@ def index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, k: int, k_scale: torch.
 
 # ------------------------------------------------------------------ attend
 
+def _window_args(window, window_scale, B, D):
+    """(window or None, W, batch stride in rows, fp8?) of an attend window [B, W, D]."""
+    if window is None or window.shape[1] == 0:
+        return None, 0, 0, False
+    if window.dim() != 3 or window.shape[0] != B or window.shape[2] != D:
+        raise ValueError("window must be [B, W, D]")
+    if window.stride(2) != 1 or window.stride(1) != D or window.stride(0) % D != 0:
+        raise ValueError("window rows must be dense with a whole-row batch stride")
+    W = window.shape[1]
+    wstride = window.stride(0) // D
+    win_fp8 = window.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if win_fp8:
+        if window_scale is None or window_scale.dtype != torch.float32:
+            raise ValueError("an fp8 window needs window_scale fp32 [B, W]")
+        if window_scale.stride(1) != 1 or window_scale.stride(0) != wstride:
+            raise ValueError("window_scale must share the window's batch stride (in rows)")
+    else:
+        _bf16_like(window, "window")
+    return window, W, wstride, win_fp8
+
+
 def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, window: torch.Tensor | None, *,
            softmax_scale: float, rope_dims: int = 0, rope_base: float = 10000.0,
            q_pos: torch.Tensor | None = None, cache_scale: torch.Tensor | None = None,
            window_scale: torch.Tensor | None = None, n_entries: torch.Tensor | None = None,
            n_window: torch.Tensor | None = None, out: torch.Tensor | None = None,
-           splits: int = 0, workspace: torch.Tensor | None = None, noalloc: bool = False) -> torch.Tensor:
+           splits: int = 0, workspace: torch.Tensor | None = None, noalloc: bool = False,
+           partial: torch.Tensor | None = None) -> torch.Tensor:
     """O [B, H, D] fp32: softmax attention of Q [B, H, D] (bf16) over the cache
     rows named by ids [B, k] (or all of the first n_entries rows when ids is
     None) followed by the window rows [B, W, D], then inverse RoPE on the last
     rope_dims channels at positions q_pos [B] int64. The window may be a view
     whose last two dimensions are dense (e.g. the tail of a state span).
     n_window [B] int32 keeps only the first n_window[b] window rows (a ring
-    from append() that has not wrapped yet)."""
-    _need_cuda(Q, cache, ids, window, q_pos, cache_scale, window_scale, n_entries, n_window, out)
+    from append() that has not wrapped yet). With ``partial`` (from
+    attend_window_partial, complete on this stream), O also covers that
+    partial's keys, in the same softmax (cskv_attend_with_partial)."""
+    _need_cuda(Q, cache, ids, window, q_pos, cache_scale, window_scale, n_entries, n_window, out, partial)
     _bf16_like(Q, "Q")
     _dense(Q, "Q"); _dense(cache, "cache")
     B, H, D = Q.shape
@@ -299,30 +329,17 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
     if n_window is not None and (n_window.dtype != torch.int32 or n_window.numel() != B
                                  or not n_window.is_contiguous()):
         raise ValueError("n_window must be contiguous int32 [B]")
-    W, wstride, win_fp8 = 0, 0, False
-    if window is not None and window.shape[1] > 0:
-        if window.dim() != 3 or window.shape[0] != B or window.shape[2] != D:
-            raise ValueError("window must be [B, W, D]")
-        if window.stride(2) != 1 or window.stride(1) != D or window.stride(0) % D != 0:
-            raise ValueError("window rows must be dense with a whole-row batch stride")
-        W = window.shape[1]
-        wstride = window.stride(0) // D
-        win_fp8 = window.dtype in (torch.uint8, torch.float8_e4m3fn)
-        if win_fp8:
-            if window_scale is None or window_scale.dtype != torch.float32:
-                raise ValueError("an fp8 window needs window_scale fp32 [B, W]")
-            if window_scale.stride(1) != 1 or window_scale.stride(0) != wstride:
-                raise ValueError("window_scale must share the window's batch stride (in rows)")
-        else:
-            _bf16_like(window, "window")
-    else:
-        window = None
+    window, W, wstride, win_fp8 = _window_args(window, window_scale, B, D)
     if rope_dims and (q_pos is None or q_pos.dtype != torch.int64 or q_pos.numel() != B):
         raise ValueError("rope_dims > 0 needs q_pos int64 [B]")
     if out is None:
         out = torch.empty((B, H, D), dtype=torch.float32, device=Q.device)
     elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, D) or not out.is_contiguous():
         raise ValueError("out must be contiguous fp32 [B, H, D]")
+    if partial is not None:
+        if noalloc:
+            raise ValueError("attend_noalloc takes no partial")
+        _check_partial(partial, B, H, D)
     if noalloc:
         _check(_lib_attend_noalloc(_ptr(Q), B, H, D, cache_dt, _ptr(cache), _ptr(cache_scale),
                                    cache.shape[1], _ptr(ids), k, _ptr(n_entries), FP8_E4M3 if win_fp8 else BF16,
@@ -335,12 +352,59 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
         ws = _caller_workspace(workspace, nbytes, "workspace")
     else:
         ws = _workspace("attend", nbytes, Q.device)
+    if partial is not None:
+        _check(_lib_attend_part(_ptr(Q), B, H, D, cache_dt, _ptr(cache), _ptr(cache_scale),
+                                cache.shape[1], _ptr(ids), k, _ptr(n_entries), FP8_E4M3 if win_fp8 else BF16,
+                                _ptr(window), _ptr(window_scale), W, wstride, _ptr(n_window), rope_dims, rope_base,
+                                _ptr(q_pos), softmax_scale, _ptr(partial), _ptr(out), splits, _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(Q.device)))
+        return out
     _check(_lib_attend(_ptr(Q), B, H, D, cache_dt, _ptr(cache), _ptr(cache_scale),
                        cache.shape[1], _ptr(ids), k, _ptr(n_entries), FP8_E4M3 if win_fp8 else BF16,
                        _ptr(window), _ptr(window_scale), W, wstride, _ptr(n_window), rope_dims, rope_base,
                        _ptr(q_pos),
                        softmax_scale, _ptr(out), splits, _ptr(ws), 0 if ws is None else ws.numel(),
                        _stream(Q.device)))
+    return out
+
+
+def partial_bytes(B: int, H: int, D: int) -> int:
+    """Bytes of an attend partial of B sequences and H heads (0 if unsupported)."""
+    return _lib_partial_bytes(B, H, D)
+
+
+def _check_partial(partial: torch.Tensor, B: int, H: int, D: int) -> None:
+    need = _lib_partial_bytes(B, H, D)
+    if (partial.dtype != torch.float32 or not partial.is_contiguous()
+            or partial.numel() * 4 < need or partial.data_ptr() % 16):
+        raise ValueError(f"partial must be a contiguous, 16-byte aligned fp32 buffer of {need} bytes")
+
+
+def attend_window_partial(Q: torch.Tensor, window: torch.Tensor | None, *, softmax_scale: float,
+                          window_scale: torch.Tensor | None = None, n_window: torch.Tensor | None = None,
+                          out: torch.Tensor | None = None) -> torch.Tensor:
+    """The attend partial of Q [B, H, D] over the window rows alone
+    (cskv_attend_window_partial): a flat fp32 buffer holding values
+    [B, H, D] (normalised by their own softmax sum, not rotated) and then
+    (reference maximum in log2 units, sum) pairs [B, H]. Pass it to
+    attend(..., partial=) with the selected entries; it needs no indexer
+    result, so it can run on another stream while the indexer runs."""
+    _need_cuda(Q, window, window_scale, n_window, out)
+    _bf16_like(Q, "Q")
+    _dense(Q, "Q")
+    B, H, D = Q.shape
+    window, W, wstride, win_fp8 = _window_args(window, window_scale, B, D)
+    if n_window is not None and (n_window.dtype != torch.int32 or n_window.numel() != B
+                                 or not n_window.is_contiguous()):
+        raise ValueError("n_window must be contiguous int32 [B]")
+    need = _lib_partial_bytes(B, H, D)
+    if out is None:
+        out = torch.empty(max(need // 4, 1), dtype=torch.float32, device=Q.device)
+    else:
+        _check_partial(out, B, H, D)
+    _check(_lib_window_partial(_ptr(Q), B, H, D, FP8_E4M3 if win_fp8 else BF16, _ptr(window),
+                               _ptr(window_scale), W, wstride, _ptr(n_window), softmax_scale, _ptr(out),
+                               _stream(Q.device)))
     return out
 
 

@@ -270,6 +270,8 @@ static cskv_status attend_prepare(const void* Q, int64_t B, int32_t H, int32_t D
   a->q_pos = q_pos;
   a->softmax_scale = softmax_scale;
   a->O = O;
+  a->part_out = nullptr;
+  a->part_in = nullptr;
   return ok();
 }
 
@@ -326,6 +328,54 @@ cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t 
         "attend: workspace must be non-null and 256-byte aligned");
   return hip_status(cskv::launch_attend(plan, a, workspace, reinterpret_cast<hipStream_t>(stream)),
                     "attend launch");
+}
+
+cskv_status cskv_attend_with_partial(const void* Q, int64_t B, int32_t H, int32_t D, int32_t cache_dtype,
+                                     const void* cache, const float* cache_scale, int64_t cache_rows,
+                                     const int32_t* ids, int32_t k, const int32_t* n_entries,
+                                     int32_t window_dtype, const void* window, const float* window_scale,
+                                     int32_t W, int64_t window_batch_stride, const int32_t* n_window,
+                                     int32_t rope_dims, float rope_base, const int64_t* q_pos,
+                                     float softmax_scale, const float* partial, float* O,
+                                     int32_t splits, void* workspace, size_t workspace_bytes, void* stream) {
+  cskv::AttendPlan plan;
+  cskv::AttendArgs a;
+  const cskv_status st = attend_prepare(Q, B, H, D, cache_dtype, cache, cache_scale, cache_rows, ids, k, n_entries,
+                                        window_dtype, window, window_scale, W, window_batch_stride, n_window,
+                                        rope_dims, rope_base, q_pos, softmax_scale, O, splits, &plan, &a);
+  if (st != CSKV_OK || B == 0) return st;
+  CHECK(partial && aligned(partial, 16), CSKV_EINVAL, "attend_with_partial: partial must be non-null and 16-byte aligned");
+  CHECK(workspace_bytes >= plan.bytes, CSKV_EINVAL, "attend_with_partial: workspace %zu bytes < %zu required",
+        workspace_bytes, plan.bytes);
+  CHECK(plan.bytes == 0 || (workspace && aligned(workspace, 256)), CSKV_EINVAL,
+        "attend_with_partial: workspace must be non-null and 256-byte aligned");
+  a.part_in = partial;
+  return hip_status(cskv::launch_attend(plan, a, workspace, reinterpret_cast<hipStream_t>(stream)),
+                    "attend_with_partial launch");
+}
+
+size_t cskv_attend_partial_bytes(int64_t B, int32_t H, int32_t D) {
+  if (B < 0 || H < 1 || H > 64 || (D != 128 && D != 512)) return 0;
+  return (size_t)B * H * ((size_t)D + 2) * sizeof(float);
+}
+
+cskv_status cskv_attend_window_partial(const void* Q, int64_t B, int32_t H, int32_t D, int32_t window_dtype,
+                                       const void* window, const float* window_scale, int32_t W,
+                                       int64_t window_batch_stride, const int32_t* n_window, float softmax_scale,
+                                       float* partial, void* stream) {
+  cskv::AttendPlan plan;
+  cskv::AttendArgs a;
+  // dense reads of no cache rows: the keys are the window rows alone, in one split
+  const cskv_status st = attend_prepare(Q, B, H, D, CSKV_BF16, nullptr, nullptr, 0, nullptr, 0, nullptr,
+                                        window_dtype, window, window_scale, W, window_batch_stride, n_window,
+                                        0, 1.0f, nullptr, softmax_scale, partial, 1, &plan, &a);
+  if (st != CSKV_OK || B == 0) return st;
+  CHECK(aligned(partial, 16), CSKV_EINVAL, "attend_window_partial: partial must be 16-byte aligned");
+  CHECK(plan.splits == 1 && plan.bytes == 0, CSKV_EUNSUPPORTED, "attend_window_partial: no one-split plan");
+  a.O = nullptr;
+  a.part_out = partial;
+  return hip_status(cskv::launch_attend(plan, a, nullptr, reinterpret_cast<hipStream_t>(stream)),
+                    "attend_window_partial launch");
 }
 
 cskv_status cskv_attend_noalloc(const void* Q, int64_t B, int32_t H, int32_t D, int32_t cache_dtype,

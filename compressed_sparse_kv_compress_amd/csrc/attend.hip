@@ -541,8 +541,13 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
 
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int l16 = lane & 15, g = lane >> 4;
-  const int64_t b = blockIdx.y;
-  const int s = blockIdx.x;
+  // workgroup id -> (sequence, split): the splits of a sequence get ids that
+  // are equal mod 8, and workgroups are dealt to the 8 XCDs by id mod 8, so a
+  // sequence's Q is fetched into one L2 once and its other splits hit it
+  const int r = blockIdx.x >> 3;
+  const int64_t b = (int64_t)(r / splits) * 8 + (blockIdx.x & 7);
+  const int s = r % splits;
+  if (b >= a.B) return;
   const bool dense = a.ids == nullptr;
   int64_t n_sel;
   if (dense) {
@@ -768,6 +773,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
                                    (__attribute__((address_space(3))) void*)dma_first_l, 16, 0, 0);
 #pragma nounroll
   for (int pass = 0;; ++pass) {
+    // prologue: the first three tiles, then the accumulators are cleared while they land
+    if (n_tiles > 0) issue(std::integral_constant<int, 0>{}, 0);
+    if (n_tiles > 1) issue(std::integral_constant<int, 1>{}, 1);
+    if (n_tiles > 2) issue(std::integral_constant<int, 2>{}, 2);
 #pragma unroll
     for (int j = 0; j < CTW; ++j) {
 #pragma unroll
@@ -775,10 +784,6 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
     }
     m_seen = -INFINITY;
     l_run = 0.0f;
-    // prologue: the first three tiles
-    if (n_tiles > 0) issue(std::integral_constant<int, 0>{}, 0);
-    if (n_tiles > 1) issue(std::integral_constant<int, 1>{}, 1);
-    if (n_tiles > 2) issue(std::integral_constant<int, 2>{}, 2);
     if constexpr (C::kDmaRaw) {
       // raw rows: the first tile is widened here, later ones under the
       // previous tile's PV products
@@ -820,20 +825,61 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   __syncthreads();
   // for head tile ht, the lane holds channels 16 (CTW wave + j) + 4g .. +3 of
   // head 16 ht + l16
-  if (splits == 1) {
-    const int R = a.rope_dims;
+  if (splits == 1 && a.part_out) {
+    // the call's partial in the public layout: values normalised by their own
+    // sum, no rotation, then (reference maximum, sum) per head
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
       const int hh = 16 * ht + l16;
       if (hh >= a.H) continue;
       const float L = lsum_l[hh];
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      float* prow = a.part_out + (b * a.H + hh) * D;
+#pragma unroll
+      for (int j = 0; j < CTW; ++j) {
+        const f32x4_t v = acc[j][ht];
+        *reinterpret_cast<float4*>(prow + 16 * (CTW * wave + j) + 4 * g) =
+            make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+      }
+    }
+    if (t < a.H) {
+      reinterpret_cast<float2*>(a.part_out + a.B * a.H * D)[b * a.H + t] = make_float2(mref_l[t], lsum_l[t]);
+    }
+  } else if (splits == 1) {
+    const int R = a.rope_dims;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const int hh = 16 * ht + l16;
+      if (hh >= a.H) continue;
+      // with a partial over other keys: log-sum-exp weights of this call's
+      // keys (wi) and of the partial (we, which also undoes its normalisation);
+      // a side with sum 0 saw no key and takes no part
+      float L = lsum_l[hh], wi = 1.0f, we = 0.0f;
+      const float* erow = nullptr;
+      if (a.part_in) {
+        const float2 e = reinterpret_cast<const float2*>(a.part_in + a.B * a.H * D)[b * a.H + hh];
+        if (e.y > 0.0f) {
+          const float mi = mref_l[hh];
+          const float M = L > 0.0f ? fmaxf(mi, e.x) : e.x;
+          wi = L > 0.0f ? exp2f(mi - M) : 0.0f;
+          we = exp2f(e.x - M) * e.y;
+          L = L * wi + we;
+          erow = a.part_in + (b * a.H + hh) * D;
+        }
+      }
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      wi *= inv;
+      we *= inv;
       float* orow = a.O + (b * a.H + hh) * D;
 #pragma unroll
       for (int j = 0; j < CTW; ++j) {
         const int c = 16 * (CTW * wave + j) + 4 * g;
         const f32x4_t v = acc[j][ht];
-        float4 o = make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        float4 o = make_float4(v[0] * wi, v[1] * wi, v[2] * wi, v[3] * wi);
+        if (erow) {
+          const float4 ev = *reinterpret_cast<const float4*>(erow + c);
+          o = make_float4(fmaf(ev.x, we, o.x), fmaf(ev.y, we, o.y), fmaf(ev.z, we, o.z), fmaf(ev.w, we, o.w));
+        }
         if (c >= D - R) {
           const int q = (c - (D - R)) >> 1;
           const float c0 = cos_l[q], s0 = sin_l[q];
@@ -887,8 +933,14 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
   extern __shared__ float w_l[];            // [splits][kHMax] weights
   __shared__ float mq_l[4][kHMax], lq_l[4][kHMax];
   __shared__ float cs_l[2][8];              // rotary cos/sin of this tile's (up to 8) pairs
-  const int64_t b = blockIdx.y;
-  const int q = blockIdx.x;                 // 16-channel tile: wave slice q / CTW, j = q % CTW
+  __shared__ float we_l[kHMax];             // weight of a partial over other keys (a.part_in)
+  // workgroup id -> (sequence, channel tile) with a sequence's tiles on one
+  // XCD (ids equal mod 8), the one whose L2 its splits' partials went through
+  constexpr int NQ = D / 16;
+  const int rq = blockIdx.x >> 3;
+  const int64_t b = (int64_t)(rq / NQ) * 8 + (blockIdx.x & 7);
+  const int q = rq % NQ;                    // 16-channel tile: wave slice q / CTW, j = q % CTW
+  if (b >= a.B) return;
   const int t = threadIdx.x;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml) + b * splits * kHMax;
   const int R = a.rope_dims;
@@ -943,6 +995,8 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
       if (grp + 4 * u < splits) fold(mlr[u]);
     }
     for (int sp = grp + 4 * kMlU; sp < splits; sp += 4) fold(ml[(int64_t)sp * kHMax + hh0]);
+    // a partial over other keys counts as one more split (group 0 folds it)
+    if (a.part_in && grp == 0 && hh0 < a.H) fold(reinterpret_cast<const float2*>(a.part_in + a.B * a.H * D)[b * a.H + hh0]);
     mq_l[grp][hh0] = M;
     lq_l[grp][hh0] = L;
   }
@@ -965,6 +1019,9 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
       if (sp < splits) w_l[sp * kHMax + hh0] = weight(mlr[u]);
     }
     for (int sp = grp + 4 * kMlU; sp < splits; sp += 4) w_l[sp * kHMax + hh0] = weight(ml[(int64_t)sp * kHMax + hh0]);
+    if (a.part_in && grp == 0) {
+      we_l[hh0] = hh0 < a.H ? weight(reinterpret_cast<const float2*>(a.part_in + a.B * a.H * D)[b * a.H + hh0]) : 0.0f;
+    }
   }
   __syncthreads();
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -987,6 +1044,13 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
   }
   if (hh >= a.H) return;
   const int c = 16 * q + 4 * (lane >> 4);
+  if (a.part_in) {
+    const float we = we_l[hh];
+    if (we > 0.0f) {
+      const float4 ev = *reinterpret_cast<const float4*>(a.part_in + (b * a.H + hh) * D + c);
+      o = make_float4(fmaf(ev.x, we, o.x), fmaf(ev.y, we, o.y), fmaf(ev.z, we, o.z), fmaf(ev.w, we, o.w));
+    }
+  }
   // (the weights already divide by L)
   if (c >= D - R) {
     const int pr = (c - 16 * q) >> 1;
@@ -1035,12 +1099,12 @@ static hipError_t launch_attend_t(const AttendPlan& p, const AttendArgs& a, void
   auto kern = k_attend<D, CF, WFP8>;
   uint16_t* ws_acc = reinterpret_cast<uint16_t*>(workspace);
   float* ws_ml = p.splits > 1 ? reinterpret_cast<float*>(ws_acc + (size_t)a.B * p.splits * kHMax * D) : nullptr;
-  dim3 grid((unsigned)p.splits, (unsigned)a.B);
-  hipLaunchKernelGGL(kern, grid, dim3(kAttThreads), 0, stream, a, p.splits,
+  const int64_t b8 = 8 * ((a.B + 7) / 8);   // sequences padded to whole XCD rounds
+  hipLaunchKernelGGL(kern, dim3((unsigned)(b8 * p.splits)), dim3(kAttThreads), 0, stream, a, p.splits,
                      p.keys_per_split, ws_acc, ws_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  const dim3 mgrid((unsigned)(D / 16), (unsigned)a.B);
+  const dim3 mgrid((unsigned)(b8 * (D / 16)));
   const size_t mlds = (size_t)p.splits * kHMax * sizeof(float);
   if (p.splits <= 4)
     hipLaunchKernelGGL((k_attend_merge<D, 4>), mgrid, dim3(256), mlds, stream, a, p.splits, ws_acc, ws_ml);

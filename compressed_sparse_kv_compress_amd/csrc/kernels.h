@@ -79,6 +79,10 @@ struct AttendArgs {
   double inv_freq[256];
   float softmax_scale;
   float* O;
+  // partials in the public layout: values [B][H][D] fp32 (normalised by their
+  // own sum, not rotated), then (reference maximum in log2 units, sum) [B][H]
+  float* part_out;           // one split: write this call's partial there instead of O
+  const float* part_in;      // a partial over other keys, merged into O (or NULL)
 };
 hipError_t launch_attend(const AttendPlan& plan, const AttendArgs& a, void* workspace,
                          hipStream_t stream);

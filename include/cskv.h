@@ -226,6 +226,50 @@ cskv_status cskv_attend(const void* Q, int64_t B, int32_t H, int32_t D, int32_t 
                         int32_t splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Attention in two parts that can overlap ([P3] "Three mechanisms instead of
+ * one trick": the extra bookkeeping must not eat the saving; [P2] Step 6
+ * "The newest tokens stay uncompressed": the window rows do not depend on
+ * the indexer). The window-only part runs while the indexer selects entries
+ * (on another stream); the attend over the selected entries then merges it
+ * with log-sum-exp weights, so that both parts together give cskv_attend's O
+ * over entries and window in one softmax.
+ *
+ * A partial of B sequences and H heads (caller-owned device memory of
+ * cskv_attend_partial_bytes(B, H, D) bytes, 16-byte aligned):
+ *   values [B, H, D] fp32:  sum_j p_j K_j / sum_j p_j over the partial's keys
+ *                           (no rotation), with p_j = exp2(x_j - m)
+ *   stats  [B, H] x (m, l) fp32 pairs, after the values:  x_j = softmax_scale
+ *          * log2(e) * Q[b,h].K_j, m a reference (the largest x_j, or a value
+ *          within 64 of it), l = sum_j exp2(x_j - m); l = 0 when there was
+ *          no key (then the values are 0 and m means nothing)
+ *
+ * cskv_attend_window_partial: the partial over the window rows alone
+ * (arguments as in cskv_attend; W may be 0, n_window may be NULL). It needs
+ * no workspace.
+ *
+ * cskv_attend_with_partial: cskv_attend (same arguments, results and
+ * workspace) whose O also covers the keys of `partial` (typically the call
+ * passes W = 0 and the window partial of the same Q). The partial must be
+ * complete before the call starts on `stream` (record an event after the
+ * partial's call and wait for it on `stream`).
+ * EINVAL for a null or misaligned partial; cskv_attend_partial_bytes returns
+ * 0 for unsupported sizes.
+ */
+size_t cskv_attend_partial_bytes(int64_t B, int32_t H, int32_t D);
+cskv_status cskv_attend_window_partial(const void* Q, int64_t B, int32_t H, int32_t D, int32_t window_dtype,
+                                       const void* window, const float* window_scale, int32_t W,
+                                       int64_t window_batch_stride, const int32_t* n_window, float softmax_scale,
+                                       float* partial, void* stream);
+cskv_status cskv_attend_with_partial(const void* Q, int64_t B, int32_t H, int32_t D, int32_t cache_dtype,
+                                     const void* cache, const float* cache_scale, int64_t cache_rows,
+                                     const int32_t* ids, int32_t k, const int32_t* n_entries,
+                                     int32_t window_dtype, const void* window, const float* window_scale,
+                                     int32_t W, int64_t window_batch_stride, const int32_t* n_window,
+                                     int32_t rope_dims, float rope_base, const int64_t* q_pos,
+                                     float softmax_scale, const float* partial, float* O,
+                                     int32_t splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * cskv_attend without a workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation).

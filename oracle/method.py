@@ -170,6 +170,41 @@ def attend(Q: np.ndarray, cache: np.ndarray, ids: np.ndarray | None, window: np.
     return inverse_rope(attention(Q, K, tau), R, base, q_pos)
 
 
+# ------------------------------------------------------- split attention
+#
+# [P1] "How DeepSeek V4 Uses Less Memory: KV Cache Explained", the passage on
+# the decode-path kernels: the indexer runs on a stream of its own beside the
+# main attention path. Reading: the window rows need no indexer result, so
+# their share of the softmax can be computed while the indexer runs and be
+# combined with the selected entries' share afterwards. A softmax over the
+# union of disjoint key sets follows exactly from each set's normalised output
+# and its log-sum-exp: O = sum_s 2^(lse_s - LSE) O_s, LSE = log2 sum_s 2^lse_s.
+
+def attention_partial(Q: np.ndarray, K: np.ndarray, tau: float):
+    """(O, lse) of Q [H, D] over keys K [N, D]: O = attention(Q, K, tau) and
+    lse[h] = log2 sum_j 2^x_hj with x = tau log2(e) Q[h].K_j (log2 units).
+    No key: O = 0 and lse = -inf."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    if K.shape[0] == 0:
+        return np.zeros_like(Q), np.full(Q.shape[0], -np.inf)
+    x = tau * np.log2(np.e) * (Q @ K.T)
+    m = x.max(axis=1, keepdims=True)
+    lse = m[:, 0] + np.log2(np.exp2(x - m).sum(axis=1))
+    return attention(Q, K, tau), lse
+
+
+def merge_partials(parts):
+    """Combines partials (O_s, lse_s) over disjoint key sets into the output
+    over their union; sets without keys (lse = -inf) take no part."""
+    lses = np.stack([lse for _, lse in parts])            # [S, H]
+    top = lses.max(axis=0)
+    w = np.exp2(lses - np.where(np.isfinite(top), top, 0.0))   # 0 for a set without keys
+    total = w.sum(axis=0)
+    w = w / np.where(total > 0, total, 1.0)
+    return sum(w[s][:, None] * np.asarray(parts[s][0], dtype=np.float64) for s in range(len(parts)))
+
+
 # ------------------------------------------------------------ decode layers
 
 def c4a_decode(Q, q_idx, k_idx, cache, window, k, tau, R, base, q_pos, n_entries=None):

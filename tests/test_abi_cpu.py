@@ -175,3 +175,29 @@ def test_attend_noalloc_validation(lib):
     assert call(B=4096, k=4000, splits=64) == lib.EUNSUPPORTED
     assert b"scratch" in lib._lib_last_error()
     assert call(B=0) == lib.OK
+
+
+def test_attend_partial_sizes_and_validation(lib):
+    """The overlap entry points: partial sizes, and host-side argument checks
+    (null or misaligned partial, unsupported shapes) before any launch."""
+    assert lib._lib_partial_bytes(32, 64, 512) == 32 * 64 * (512 + 2) * 4
+    assert lib._lib_partial_bytes(1, 8, 128) == 8 * 130 * 4
+    assert lib._lib_partial_bytes(1, 65, 512) == 0 and lib._lib_partial_bytes(1, 8, 384) == 0
+    p = ctypes.c_void_p(256)
+    f = lib._lib_attend_part
+
+    def call(**kw):
+        a = dict(Q=p, B=1, H=64, D=512, cdt=lib.BF16, cache=p, cs=None, rows=10, ids=p, k=4, ne=None,
+                 wdt=lib.BF16, win=None, ws_=None, W=0, wst=0, nw=None, R=64, base=10000.0, pos=p, tau=0.1,
+                 part=p, O=p, splits=1, ws=None, wsb=0, stream=None)
+        a.update(kw)
+        return f(*a.values())
+
+    assert call(part=None) == lib.EINVAL
+    assert call(part=ctypes.c_void_p(264)) == lib.EINVAL         # not 16-byte aligned
+    assert call(H=65) == lib.EUNSUPPORTED
+    assert call(B=0, part=None) == lib.OK
+    g = lib._lib_window_partial
+    assert g(p, 1, 64, 384, lib.BF16, p, None, 4, 4, None, 0.1, p, None) == lib.EUNSUPPORTED
+    assert g(p, 1, 64, 512, lib.FP8_E4M3, p, None, 4, 4, None, 0.1, p, None) == lib.EINVAL   # no window scales
+    assert g(p, 1, 64, 512, lib.BF16, p, None, 4, 4, None, 0.1, None, None) == lib.EINVAL    # no partial

@@ -360,6 +360,39 @@ def test_attention_closed_forms():
     assert np.all(M.attention(Q, np.zeros((0, 6)), 0.5) == 0)
 
 
+def test_partials_merge_to_attention_over_the_union():
+    """Log-sum-exp merge of partials over disjoint key sets equals attention
+    over all keys; the log-sum-exp equals scipy's (natural log, rescaled)."""
+    from scipy.special import logsumexp
+    H, D, tau = 6, 16, 0.3
+    Q = RNG.standard_normal((H, D))
+    K = RNG.standard_normal((40, D))
+    O_all = M.attention(Q, K, tau)
+    for cuts in ([13], [1, 39], [7, 20, 33]):
+        parts = [M.attention_partial(Q, Kp, tau) for Kp in np.split(K, cuts)]
+        np.testing.assert_allclose(M.merge_partials(parts), O_all, rtol=1e-12, atol=1e-12)
+    O, lse = M.attention_partial(Q, K, tau)
+    np.testing.assert_allclose(O, O_all, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, logsumexp(tau * (Q @ K.T), axis=1) / math.log(2), rtol=1e-12)
+
+
+def test_partial_special_cases():
+    H, D = 3, 8
+    Q = RNG.standard_normal((H, D))
+    k1 = RNG.standard_normal(D)
+    O, lse = M.attention_partial(Q, k1[None], 0.5)          # one key: the key, lse = its logit
+    np.testing.assert_allclose(O, np.tile(k1, (H, 1)), atol=1e-15)
+    np.testing.assert_allclose(lse, 0.5 * (Q @ k1) / math.log(2), rtol=1e-13)
+    O0, lse0 = M.attention_partial(Q, np.zeros((0, D)), 0.5)   # no key
+    assert np.all(O0 == 0) and np.all(lse0 == -np.inf)
+    K = RNG.standard_normal((5, D))
+    part = M.attention_partial(Q, K, 0.5)
+    np.testing.assert_allclose(M.merge_partials([part, (O0, lse0)]), part[0], atol=1e-15)
+    assert np.all(M.merge_partials([(O0, lse0), (O0, lse0)]) == 0)
+    # two copies of one key set: the same output (weights 1/2 each)
+    np.testing.assert_allclose(M.merge_partials([part, part]), part[0], atol=1e-14)
+
+
 def test_gather_sparse_dense_and_window():
     cache = RNG.standard_normal((50, 16))
     win = RNG.standard_normal((5, 16))
