@@ -283,11 +283,13 @@ class Mixed61(Workload):
         self.N4, self.N128 = c4a_entries(L), c128a_entries(L)
         self.layers = []
         i = 0
-        for layer in range(c.layers):
+        for layer in (c.only_layers or range(c.layers)):
             if layer % 10 == 0:
                 log(f"setup: layer {layer + 1}/{c.layers}")
             kind = c.layer_kind(layer)
-            lay = {"kind": kind}
+            lay = {"kind": kind, "layer": layer}
+            if c.only_layers and c.reuses(layer) is not None:
+                raise ValueError("a subset of layers cannot include one that reuses another layer's ids")
             span_T = 132 if kind == "c4a" else 128
             lay["span"] = sd.new((B, span_T, D), s.KIND_NORMAL_BF16, self.key(i, s.T_S, layer), device=self.dev)
             lay["gate"] = sd.new((B, span_T), s.KIND_NORMAL_F32, self.key(i, s.T_GATE, layer), device=self.dev)

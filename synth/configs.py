@@ -40,6 +40,7 @@ class Workload:
     rope_base: float = 10000.0
     layers: int = 1
     reuse_ids: bool = False     # mixed stack: every second c4a layer reuses the ids of the one before
+    only_layers: tuple = ()     # mixed stack: build just these layers of the stack (checks of late layers)
     description: str = ""
 
     @property

@@ -50,19 +50,22 @@ def test_compress_fp4_rows(cskv, kind, T):
     assert flips <= 0.01 * B * n * D and scale_flips <= 0.01 * B * n * (D // 16)
 
 
-def test_append_fp4_rows_equal_compress(cskv):
-    B, T, W = 2, 90, 128
+@pytest.mark.parametrize("kind,T", [("c4a", 90), ("c128a", 300)])
+def test_append_fp4_rows_equal_compress(cskv, kind, T):
+    """Appending one state at a time writes the same fp4 rows as compressing
+    the whole span (c128a: two complete entries and a partial block)."""
+    B, W = 2, 128
     S, g = _states(75, B, T)
-    n = M.entry_count("c4a", T)
+    n = M.entry_count(kind, T)
     rows = torch.zeros((B, n, RB), dtype=torch.uint8, device="cuda")
     ring = torch.zeros((B, W, D), dtype=torch.bfloat16, device="cuda")
     rg = torch.zeros((B, W), dtype=torch.float32, device="cuda")
     Sd, gd = to_dev_bf16(S), to_dev(g)
     for p in range(T):
-        cskv.append("c4a", Sd[:, p].contiguous(), gd[:, p].contiguous(),
+        cskv.append(kind, Sd[:, p].contiguous(), gd[:, p].contiguous(),
                     torch.full((B,), p, dtype=torch.int64, device="cuda"), ring, rg, rows)
     ref = torch.zeros_like(rows)
-    cskv.compress("c4a", Sd, gd, ref)
+    cskv.compress(kind, Sd, gd, ref)
     assert torch.equal(rows, ref)
 
 

@@ -46,7 +46,8 @@ def _check_layer(wl, layer, b, full_cache_rows=None):
     """Oracle for sequence b of one layer: the cache rows the step reads are the
     drawn prefix plus the entries compressed from the appended span."""
     c = wl.cfg
-    lay = wl.layers[layer]
+    lay = next(x for x in wl.layers if x["layer"] == layer)
+    assert lay["kind"] == c.layer_kind(layer)
     kind = lay["kind"]
     key = lambda tensor: wl.key(0, tensor, layer)
     D, H, W = c.D, c.H, c.W
@@ -69,7 +70,8 @@ def _check_layer(wl, layer, b, full_cache_rows=None):
         q = F.bf16_to_f64(synth.int_bf16(ikey(synth.T_QIDX), b * Di, Di, c.idx_range))
         kk = F.bf16_to_f64(synth.int_bf16(ikey(synth.T_KIDX), b * N * Di, N * Di, c.idx_range).reshape(N, Di))
         ids = M.topk_ids(M.index_scores(q, kk), c.k)
-        assert np.array_equal(wl.layers[src]["ids"][b].cpu().numpy(), ids), (layer, b)
+        src_lay = next(x for x in wl.layers if x["layer"] == src)
+        assert np.array_equal(src_lay["ids"][b].cpu().numpy(), ids), (layer, b)
         # only the selected rows are needed: drawn rows, or rows the span rewrote
         cache = np.zeros((N, D))
         drawn = [r for r in ids if r < first or r >= first + new.shape[0]]
@@ -103,6 +105,18 @@ def test_mixed_step_full_size_first_layers(cskv):
     wl = _run(cfg, cskv)
     for layer in (0, 1):
         for b in (0, cfg.B - 1):
+            _check_layer(wl, layer, b)
+
+
+@pytest.mark.slow
+def test_mixed_step_full_size_late_layers(cskv):
+    """The last two layers of the 61-layer workload (59: c4a, 60: c128a) at full
+    size, each with its own input streams (built alone: the step's layers share
+    no data), on first, middle and last sequences."""
+    cfg = dataclasses.replace(configs.MIXED_61, only_layers=(59, 60))
+    wl = _run(cfg, cskv)
+    for layer in (59, 60):
+        for b in (0, cfg.B // 2, cfg.B - 1):
             _check_layer(wl, layer, b)
 
 

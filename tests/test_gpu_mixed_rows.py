@@ -61,21 +61,24 @@ def test_compress_mixed_rows(cskv, kind, T):
             np.testing.assert_allclose(np.abs(F.e4m3_decode(codes[b])).max(axis=1), 448.0)
 
 
-def test_append_mixed_rows_equal_compress(cskv):
-    B, T, W = 2, 90, 128
+@pytest.mark.parametrize("kind,T", [("c4a", 90), ("c128a", 300)])
+def test_append_mixed_rows_equal_compress(cskv, kind, T):
+    """Appending one state at a time writes the same mixed rows as compressing
+    the whole span (c128a: two complete entries and a partial block)."""
+    B, W = 2, 128
     S, g = _states(55, B, T)
-    n = M.entry_count("c4a", T)
+    n = M.entry_count(kind, T)
     mix = torch.zeros((B, n, D + R), dtype=torch.uint8, device="cuda")
     msc = torch.zeros((B, n), dtype=torch.float32, device="cuda")
     ring = torch.zeros((B, W, D), dtype=torch.bfloat16, device="cuda")
     rg = torch.zeros((B, W), dtype=torch.float32, device="cuda")
     Sd, gd = to_dev_bf16(S), to_dev(g)
     for p in range(T):
-        cskv.append("c4a", Sd[:, p].contiguous(), gd[:, p].contiguous(), torch.full((B,), p, dtype=torch.int64,
+        cskv.append(kind, Sd[:, p].contiguous(), gd[:, p].contiguous(), torch.full((B,), p, dtype=torch.int64,
                     device="cuda"), ring, rg, mix, msc)
     ref = torch.zeros_like(mix)
     rsc = torch.zeros_like(msc)
-    cskv.compress("c4a", Sd, gd, ref, rsc)
+    cskv.compress(kind, Sd, gd, ref, rsc)
     assert torch.equal(mix, ref) and torch.equal(msc, rsc)
 
 

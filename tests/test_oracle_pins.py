@@ -201,9 +201,18 @@ def test_e4m3_saturation_nan_and_roundtrip():
     assert np.array_equal(F.e4m3_encode(F.E4M3_TABLE[finite].astype(np.float32)), finite)
 
 
-def test_e2m1_table_and_torch():
+def test_e2m1_table_matches_format():
+    """The 16 E2M1 values: the literal set, and the bit-level definition (sign,
+    2 exponent bits with bias 1, 1 mantissa bit; exponent 0 is subnormal)."""
     assert F.E2M1_TABLE[:8].tolist() == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
     assert np.array_equal(F.E2M1_TABLE[8:], -F.E2M1_TABLE[:8])
+    for code in range(16):
+        s, e, m = code >> 3, (code >> 1) & 3, code & 1
+        mag = 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1 + 0.5 * m)
+        assert F.E2M1_TABLE[code] == (-mag if s else mag), code
+
+
+def test_e2m1_table_and_torch():
     # torch's packed fp4 dtype shares the nibble layout; its decode goes through a
     # float conversion only in recent builds, so compare when it is available.
     try:
