@@ -1045,16 +1045,21 @@ bool plan_topk(int64_t B, int64_t n_max, int k, int chunk_hint, bool fp4, TopkPl
   p->threads = kTopkFused ? kTopkThreads : kTopkScoreThreads;
   int64_t chunk = chunk_hint;
   if (chunk == 0) {
-    // fused: about 256 workgroups of 1024 threads over the batch, chunks of
-    // 1024 .. 16384 entries; separate selection: about 768 (bf16 keys) or
-    // 1536 (fp4 keys) workgroups of 256, chunks of 512 .. 4096 or 8192; more
-    // when a sequence would need more chunks than the selection tracks
+    // fused: at most about 256 workgroups of 1024 threads over the batch,
+    // chunks of 1024 .. 16384 entries; separate selection: about 768 (bf16
+    // keys) or 1536 (fp4 keys) workgroups of 256, chunks of 512 .. 4096 or
+    // 8192. A sequence gets groups / B chunks, each a multiple of 256 entries,
+    // so that an entry count just past a power of two (a growing context)
+    // neither doubles the chunk (idling CUs) nor adds a chunk per sequence
+    // (a second round of workgroups); more chunks when a sequence would need
+    // more than the selection tracks
     const int64_t groups = p->fused ? 256 : (fp4 ? 1536 : 768);
     const int64_t cap = p->fused ? 16384 : (fp4 ? 8192 : 4096);
-    const int64_t want = (B * n_max + groups - 1) / groups;
-    chunk = p->fused ? 1024 : 512;
-    while (chunk < want && chunk < cap) chunk *= 2;
-    while ((n_max + chunk - 1) / chunk > kMaxChunks && chunk < 16384) chunk *= 2;
+    const int64_t per_seq = groups / B > 1 ? groups / B : 1;
+    chunk = ((n_max + per_seq - 1) / per_seq + 255) / 256 * 256;
+    const int64_t floor_chunk = p->fused ? 1024 : 512;
+    chunk = chunk < floor_chunk ? floor_chunk : (chunk > cap ? cap : chunk);
+    while ((n_max + chunk - 1) / chunk > kMaxChunks && chunk < 16384) chunk = chunk * 2 > 16384 ? 16384 : chunk * 2;
   }
   if (chunk < 256 || chunk > 16384 || chunk % 256 != 0) return false;
   // (a chunk smaller than one round of the 1024-thread score loop leaves
