@@ -674,14 +674,39 @@ def dominant_kernels(kind):
     return ("k_index_topk",) if kind != "c128a" else ("k_attend", "k_attend_merge")
 
 
+def _code_only(text):
+    """C++ source text without comments and blank space (what the compiler
+    sees), so that a comment edit does not retire recorded counters."""
+    import re
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif text[i] == '"':            # string literal, kept whole
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def kernel_source_digest():
+    """Digest of the kernel sources' code (comments and spacing excluded)."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".h")):
             h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -4,7 +4,7 @@
 // compressed entries per query (default k = 512). [P2] Step 5: a learned
 // indexer scores every compressed block; the query reads only the chosen ones.
 //
-// One launch, k_index_topk (grid: chunks x sequences, 256 threads):
+// One launch, k_index_topk (grid: chunks x sequences, 1024 threads):
 //   Scoring. Each workgroup streams one chunk of a sequence's indexer keys
 //     once from HBM with 16-byte non-temporal loads (bf16, or fp4 codes +
 //     E4M3 group scales dequantised in registers), computes each entry's
@@ -22,13 +22,15 @@
 //     chunk of its sequence is done; it reads their results with agent-scope
 //     atomic loads and finishes the selection while the other sequences are
 //     still being scored.
-//   Selection. From the complete histogram it finds the true threshold bin,
-//     gathers into LDS the candidates at or above it (counting the next 8 key
-//     bits of the threshold bin's keys on the way), which fixes the 20-bit
-//     prefix of the k-th largest key; the few keys sharing it are ranked
-//     against each other (a radix select on the last 12 bits when there are
-//     many). It writes the ids in ascending entry order (ties go to the lower
-//     entry) and clears the histogram and the counter for the next call.
+//   Selection. From the complete histogram it finds the true threshold bin
+//     and gathers the candidates at or above it, in entry order, into
+//     registers (a few per thread; LDS or global memory when there are more),
+//     listing the threshold bin's keys in LDS, which fixes the 20-bit prefix
+//     of the k-th largest key; the few keys sharing it are ranked against each
+//     other (a radix select on the last 12 bits when there are many). One
+//     block scan places every id in ascending entry order (ties go to the
+//     lower entry); the histogram and the counter are cleared for the next
+//     call.
 // The selection is exact: every entry of a bin above the threshold bin is in
 // the top k, and the threshold bin is resolved on full keys.
 #include "kernels.h"

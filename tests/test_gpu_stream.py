@@ -182,8 +182,9 @@ def test_stream_decode_step_matches_oracle(cskv, kind):
 
 @pytest.mark.parametrize("B", [4, 64])
 def test_attend_ragged_window_counts(cskv, B):
-    """n_window keeps the leading rows of each window (0, partial, all W), for
-    the split kernel (B = 4) and the head-split kernel (B = 64, sparse bf16)."""
+    """n_window keeps the leading rows of each window (0, partial, all W), at a
+    small batch (B = 4: several splits per sequence) and a large one (B = 64:
+    one split per sequence, no merge)."""
     H, D, R, W, N, k = 64, 512, 64, 128, 300, 64
     rng = np.random.default_rng(8 + B)
     Q = synth.normal_bf16(synth.stream_key(90 + B, synth.T_Q), 0, B * H * D).reshape(B, H, D)
