@@ -135,7 +135,9 @@ def _workspace(purpose: str, nbytes: int, device, layout=None) -> torch.Tensor |
     if buf is None or buf.numel() < nbytes:
         if buf is not None:
             _retired.append(buf)
-        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        # zeroed by a fill kernel (not a memset, which a captured graph
+        # would hold as a node of its own)
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev).zero_()
         _workspaces[key] = buf
     return buf
 

@@ -61,3 +61,41 @@ def test_graph_replays_match_eager(cskv, dense):
         if not dense:
             assert torch.equal(ids, ref_ids), r
         assert torch.equal(out, ref_out), r
+
+
+def test_graph_replays_after_other_shapes_on_the_capture_stream(cskv):
+    """Between replays, eager calls on the capture stream itself: index_topk
+    with another batch size (a workspace layout of its own) and an attend
+    large enough to grow the stream's attend workspace (the captured buffer is
+    retired, not freed). Every replay still gives the eager result."""
+    B, N, D, H, Di, W, k = 4, 6000, 512, 64, 128, 128, 512
+    x = _inputs(73, B, N, D, H, Di, W)
+    big = _inputs(74, 7, 3 * N, D, H, Di, W)
+    ids = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+
+    def step():
+        cskv.index_topk(x["qidx"], x["kidx"], k, ids=ids)
+        cskv.attend(x["Q"], x["cache"], ids, x["win"], softmax_scale=D ** -0.5, rope_dims=64, q_pos=x["pos"],
+                    out=out)
+
+    with torch.cuda.stream(s):
+        step()                                 # eager on the capture stream: sizes its workspaces
+    torch.cuda.synchronize()
+    ref_ids, ref_out = ids.clone(), out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    ids_big = torch.empty((7, k), dtype=torch.int32, device="cuda")
+    for r in range(4):
+        ids.fill_(-7)
+        out.zero_()
+        g.replay()
+        with torch.cuda.stream(s):
+            cskv.index_topk(big["qidx"], big["kidx"], k, ids=ids_big)          # another layout
+            cskv.attend(big["Q"], big["cache"], None, big["win"], softmax_scale=D ** -0.5, rope_dims=64,
+                        q_pos=big["pos"], splits=40 + r)                        # grows the attend workspace
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ref_ids), r
+        assert torch.equal(out, ref_out), r
