@@ -13,7 +13,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcskv.so")
+# CSKV_LIBRARY names another build of the same library (the host-sanitized
+# build that the CPU tests of the argument checks load); default: in-tree
+LIB_PATH = os.environ.get("CSKV_LIBRARY") or os.path.join(_HERE, "libcskv.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
