@@ -533,7 +533,9 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   __shared__ __attribute__((aligned(16))) float vs0[kVsLen], vs1[kVsLen], vs2[kVsLen], vs3[kVsLen];
   __shared__ int32_t ids_l[kMaxSplitIds];
   // probabilities of the tile, row h: key slots in the k order of the PV product
+  // (bf16 rows alternate two buffers: tile i's are written while tile i-1's are read)
   __shared__ __attribute__((aligned(16))) uint16_t p_l[kHMax * kTK];
+  __shared__ __attribute__((aligned(16))) uint16_t p_l1[C::kDma ? kHMax * kTK : 8];
   __shared__ float mref_l[kHMax], lsum_l[kHMax];
   __shared__ int redo_l;
   // target of one DMA issued before any tile: the compiler's bookkeeping of
@@ -585,7 +587,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   }
   if (t == 0) redo_l = 0;
   // rows of heads without a computing wave stay zero
-  for (int j = t; j < kHMax * kTK / 8; j += kAttThreads) reinterpret_cast<uint4*>(p_l)[j] = make_uint4(0, 0, 0, 0);
+  for (int j = t; j < kHMax * kTK / 8; j += kAttThreads) {
+    reinterpret_cast<uint4*>(p_l)[j] = make_uint4(0, 0, 0, 0);
+    if constexpr (C::kDma) reinterpret_cast<uint4*>(p_l1)[j] = make_uint4(0, 0, 0, 0);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -644,7 +649,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
 
   // QK^T and softmax of this wave's 16 heads on a ready bf16 tile with its slot
   // biases and value scales; the probabilities go to p_l
-  auto qk_softmax = [&](const uint16_t* kt, const float* pbv, const float* vsv) __attribute__((always_inline)) {
+  auto qk_softmax = [&](const uint16_t* kt, const float* pbv, const float* vsv, uint16_t* pw) __attribute__((always_inline)) {
     // slot metadata of keys 4g .. 4g+3 and 16+4g .. 16+4g+3 (same for all heads)
     const float4 b_lo = *reinterpret_cast<const float4*>(pbv + 4 * g);
     const float4 b_hi = *reinterpret_cast<const float4*>(pbv + 16 + 4 * g);
@@ -691,12 +696,12 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
       if constexpr (C::kScaled) p[i] *= vv[i];
     }
     // k slot j of group g is key 4g+j (j < 4) or 16+4g+j-4: the lane's 8 values in order
-    uint4 pw;
-    pw.x = pack_bf16x2(p[0], p[1]);
-    pw.y = pack_bf16x2(p[2], p[3]);
-    pw.z = pack_bf16x2(p[4], p[5]);
-    pw.w = pack_bf16x2(p[6], p[7]);
-    *reinterpret_cast<uint4*>(p_l + 16 * wave * kTK + p_off) = pw;
+    uint4 pq;
+    pq.x = pack_bf16x2(p[0], p[1]);
+    pq.y = pack_bf16x2(p[2], p[3]);
+    pq.z = pack_bf16x2(p[4], p[5]);
+    pq.w = pack_bf16x2(p[6], p[7]);
+    *reinterpret_cast<uint4*>(pw + 16 * wave * kTK + p_off) = pq;
   };
 
   // raw rows: this thread's share of the next tile, read before this tile's
@@ -760,12 +765,127 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
       if (nxt) wait_tile<C::kOpsPerTile>(min(kNStage - 2, n_tiles - 2 - i));
       raw_read<D>(tile_of(std::integral_constant<int, SN>{}), raw);
     }
-    if (wave_on) qk_softmax(tile_of(sc), pb_of(sc), vs_of(sc));
+    if (wave_on) qk_softmax(tile_of(sc), pb_of(sc), vs_of(sc), p_l);
     lds_barrier();   // probabilities of all heads visible
     if constexpr (C::kDmaRaw) {
       pv(tile_of(sc), std::true_type{}, tile_of(std::integral_constant<int, SN>{}), nxt);
     } else {
       pv(tile_of(sc), std::false_type{}, nullptr, false);
+    }
+  };
+
+  // bf16 rows, software-pipelined: step i runs QK^T and the softmax of tile i
+  // with the PV products of tile i-1 interleaved (the matrix cores take PV while
+  // LDS serves QK^T's row reads), one barrier a step. Tiles move two ahead: the
+  // slot of tile i-2, whose PV ended in step i-1, takes tile i+2. Step i writes
+  // its probabilities to buffer i % 2 and reads tile i-1's from the other.
+  auto p_buf = [&](auto par) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (decltype(par)::value == 0) return p_l;
+    else return p_l1;
+  };
+  auto qk_pv = [&](const uint16_t* kt, const float* pbv, const uint16_t* kp, const uint16_t* pr,
+                   uint16_t* pw) __attribute__((always_inline)) {
+    const float4 b_lo = *reinterpret_cast<const float4*>(pbv + 4 * g);
+    const float4 b_hi = *reinterpret_cast<const float4*>(pbv + 16 + 4 * g);
+    bf16x8_t pbo[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) pbo[ht] = *reinterpret_cast<const bf16x8_t*>(pr + 16 * ht * kTK + p_off);
+    constexpr int kQD = 4;
+    constexpr int kPD = 2;
+    bf16x8_t ka0[KS], ka1[KS];
+    v4i16_t kr0[CTW], kr1[CTW];
+    auto read_kt = [&](int j) __attribute__((always_inline)) {
+      const int e = j & 1, m = j >> 1;
+      kr0[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kp + tr_base0[e] + 32 * m));
+      kr1[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kp + tr_base1[e] + 32 * m));
+    };
+#pragma unroll
+    for (int ks = 0; ks < kQD; ++ks) {
+      ka0[ks] = *reinterpret_cast<const bf16x8_t*>(kt + qk_off0 + 32 * ks);
+      ka1[ks] = *reinterpret_cast<const bf16x8_t*>(kt + qk_off1 + 32 * ks);
+    }
+#pragma unroll
+    for (int j = 0; j < kPD; ++j) read_kt(j);
+    f32x4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    static_assert(KS == 2 * CTW, "one PV channel tile per two QK^T k-steps");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + kQD < KS) {
+        ka0[ks + kQD] = *reinterpret_cast<const bf16x8_t*>(kt + qk_off0 + 32 * (ks + kQD));
+        ka1[ks + kQD] = *reinterpret_cast<const bf16x8_t*>(kt + qk_off1 + 32 * (ks + kQD));
+      }
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[ks], qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[ks], qf[ks], s1, 0, 0, 0);
+      if (ks & 1) {
+        const int j = ks >> 1;
+        if (j + kPD < CTW) read_kt(j + kPD);
+        const v4i16_t kk[2] = {kr0[j], kr1[j]};
+        const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, kk);
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) acc[j][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, pbo[ht], acc[j][ht], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float bb[8] = {b_lo.x, b_lo.y, b_lo.z, b_lo.w, b_hi.x, b_hi.y, b_hi.z, b_hi.w};
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = fmaf(s0[i], tau_log2e, bb[i]);
+      x[4 + i] = fmaf(s1[i], tau_log2e, bb[4 + i]);
+    }
+    m_seen = fmaxf(m_seen, fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                 fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
+      l_run += p[i];
+    }
+    uint4 pq;
+    pq.x = pack_bf16x2(p[0], p[1]);
+    pq.y = pack_bf16x2(p[2], p[3]);
+    pq.z = pack_bf16x2(p[4], p[5]);
+    pq.w = pack_bf16x2(p[6], p[7]);
+    *reinterpret_cast<uint4*>(pw + 16 * wave * kTK + p_off) = pq;
+  };
+  // the PV products of the last tile alone, from probability buffer pr
+  auto pv_only = [&](const uint16_t* kp, const uint16_t* pr) __attribute__((always_inline)) {
+    bf16x8_t pbo[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) pbo[ht] = *reinterpret_cast<const bf16x8_t*>(pr + 16 * ht * kTK + p_off);
+    v4i16_t kr0[CTW], kr1[CTW];
+#pragma unroll
+    for (int j = 0; j < CTW; ++j) {
+      const int e = j & 1, m = j >> 1;
+      kr0[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kp + tr_base0[e] + 32 * m));
+      kr1[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kp + tr_base1[e] + 32 * m));
+    }
+#pragma unroll
+    for (int j = 0; j < CTW; ++j) {
+      const v4i16_t kk[2] = {kr0[j], kr1[j]};
+      const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, kk);
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) acc[j][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, pbo[ht], acc[j][ht], 0, 0, 0);
+    }
+  };
+  // step i (i % 4 == S): tile i in slot S, tile i-1 in slot S-1
+  auto pstep = [&](auto sc, int i) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
+    constexpr int SP = (S + kNStage - 1) % kNStage;
+    if (i > n_tiles) return;
+    if (i < n_tiles) wait_tile<C::kOpsPerTile>(i + 1 < n_tiles ? 1 : 0);
+    lds_barrier();   // tile i and probabilities i-1 visible; slot S+2 (tile i-2) free
+    if (i + 2 < n_tiles) issue(std::integral_constant<int, (S + 2) % kNStage>{}, i + 2);
+    uint16_t* pw = p_buf(std::integral_constant<int, S & 1>{});
+    const uint16_t* pr = p_buf(std::integral_constant<int, (S & 1) ^ 1>{});
+    if (i < n_tiles && wave_on) {
+      if (i >= 1) {
+        qk_pv(tile_of(sc), pb_of(sc), tile_of(std::integral_constant<int, SP>{}), pr, pw);
+      } else {
+        qk_softmax(tile_of(sc), pb_of(sc), vs_of(sc), pw);
+      }
+    } else if (i >= 1) {
+      pv_only(tile_of(std::integral_constant<int, SP>{}), pr);
     }
   };
 
@@ -776,10 +896,11 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
                                    (__attribute__((address_space(3))) void*)dma_first_l, 16, 0, 0);
 #pragma nounroll
   for (int pass = 0;; ++pass) {
-    // prologue: the first three tiles, then the accumulators are cleared while they land
+    // prologue: the first tiles (two for bf16 rows, three otherwise), then the
+    // accumulators are cleared while they land
     if (n_tiles > 0) issue(std::integral_constant<int, 0>{}, 0);
     if (n_tiles > 1) issue(std::integral_constant<int, 1>{}, 1);
-    if (n_tiles > 2) issue(std::integral_constant<int, 2>{}, 2);
+    if (!C::kDma && n_tiles > 2) issue(std::integral_constant<int, 2>{}, 2);
 #pragma unroll
     for (int j = 0; j < CTW; ++j) {
 #pragma unroll
@@ -802,11 +923,20 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
       cos_l[t] = (float)cs;
       sin_l[t] = (float)sn;
     }
-    for (int i = 0; i < n_tiles; i += kNStage) {
-      step(std::integral_constant<int, 0>{}, i);
-      step(std::integral_constant<int, 1>{}, i + 1);
-      step(std::integral_constant<int, 2>{}, i + 2);
-      step(std::integral_constant<int, 3>{}, i + 3);
+    if constexpr (C::kDma) {
+      for (int i = 0; i <= n_tiles; i += kNStage) {
+        pstep(std::integral_constant<int, 0>{}, i);
+        pstep(std::integral_constant<int, 1>{}, i + 1);
+        pstep(std::integral_constant<int, 2>{}, i + 2);
+        pstep(std::integral_constant<int, 3>{}, i + 3);
+      }
+    } else {
+      for (int i = 0; i < n_tiles; i += kNStage) {
+        step(std::integral_constant<int, 0>{}, i);
+        step(std::integral_constant<int, 1>{}, i + 1);
+        step(std::integral_constant<int, 2>{}, i + 2);
+        step(std::integral_constant<int, 3>{}, i + 3);
+      }
     }
     // the head's largest logit over the split (every tile has landed: no DMA in flight)
     float mh = fmaxf(m_seen, __shfl_xor(m_seen, 16, kWave));
