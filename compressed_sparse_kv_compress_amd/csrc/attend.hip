@@ -74,6 +74,7 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 static __device__ __attribute__((aligned(16))) uint8_t g_zero_row[1024];
 static __device__ float g_empty_scale = 0.0f;
 static __device__ float g_one_scale = 1.0f;
+static __device__ int32_t g_no_count = 0;   // read in place of an absent count
 
 // Swizzle of a tile row's 16-byte chunks.
 __device__ __forceinline__ int chunk_swz(int row) { return (row >> 2) & 3; }
@@ -515,8 +516,9 @@ __device__ __forceinline__ void widen_raw_tile(uint16_t* tile) {
 }
 
 template <int D, int CF, bool WFP8>
-__global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int splits, int64_t keys_per_split,
-                                                          uint16_t* __restrict__ ws_acc, float* __restrict__ ws_ml) {
+__global__ __launch_bounds__(kAttThreads, 1) void k_attend(int splits, int64_t keys_per_split,
+                                                          uint16_t* __restrict__ ws_acc, float* __restrict__ ws_ml,
+                                                          AttendArgs a) {
   using C = AttCfg<D, CF, WFP8>;
   constexpr int KS = D / 32;          // k-steps of QK^T
   constexpr int CTW = D / 64;         // 16-channel tiles of O^T per wave (a quarter of D)
@@ -544,6 +546,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   __shared__ __attribute__((aligned(16))) uint8_t dma_first_l[16 * kWave];
   __shared__ float cos_l[D / 2], sin_l[D / 2];
 
+  // The argument block is fresh memory at every launch: its scalar fields fill
+  // its first four cache lines, fetched here together (one round trip rather
+  // than one per line at first use).
+  asm volatile("" ::"s"(splits), "s"(a.Q), "s"(a.k), "s"(a.rope_dims), "s"(a.part_in));
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   const int l16 = lane & 15, g = lane >> 4;
   // workgroup id -> (sequence, split): the splits of a sequence get ids that
@@ -554,32 +560,40 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(AttendArgs a, int spl
   const int s = r % splits;
   if (b >= a.B) return;
   const bool dense = a.ids == nullptr;
+  // the sequence's entry and window counts, loaded alongside Q (from a dummy
+  // when absent, so that no load waits behind a branch)
+  const int32_t* ne_p = dense && a.n_entries ? a.n_entries + b : &g_no_count;
+  const int32_t* nw_p = a.n_window ? a.n_window + b : &g_no_count;
+  const int32_t ne_v = *ne_p, nw_v = *nw_p;
+  const int h = 16 * wave + l16;            // this lane's head
+  const bool wave_on = 16 * wave < a.H;     // wave-uniform
+  // Q fragment: B operand of S^T = K Q^T; lane holds Q[h][32ks + 8g .. +7]
+  bf16x8_t qf[KS];
+  {
+    // (every lane loads, from row 0 when it has no head, so that the loads
+    // are one straight run ahead of the counts' first use)
+    const bool qok = wave_on && h < a.H;
+    const uint16_t* qrow = a.Q + (b * a.H + (qok ? h : 0)) * D;
+    uint4 qv[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qv[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8_t, qok ? qv[ks] : make_uint4(0, 0, 0, 0));
+  }
   int64_t n_sel;
   if (dense) {
-    n_sel = a.n_entries ? (int64_t)a.n_entries[b] : a.cache_rows;
+    n_sel = a.n_entries ? (int64_t)ne_v : a.cache_rows;
     n_sel = n_sel < 0 ? 0 : (n_sel > a.cache_rows ? a.cache_rows : n_sel);
   } else {
     n_sel = a.k;
   }
-  const int64_t n_keys = n_sel + window_rows(a, b);
+  const int64_t n_win = !a.n_window ? (int64_t)a.W : (nw_v < 0 ? 0 : (nw_v > a.W ? (int64_t)a.W : (int64_t)nw_v));
+  const int64_t n_keys = n_sel + n_win;
   const int64_t lo = (int64_t)s * keys_per_split;
   const int64_t hi = lo + keys_per_split < n_keys ? lo + keys_per_split : n_keys;
   const int n_tiles = hi > lo ? (int)((hi - lo + kTK - 1) / kTK) : 0;
   const float tau_log2e = a.softmax_scale * kLog2e;
-  const int h = 16 * wave + l16;            // this lane's head
-  const bool wave_on = 16 * wave < a.H;     // wave-uniform
-
-  // Q fragment: B operand of S^T = K Q^T; lane holds Q[h][32ks + 8g .. +7]
-  bf16x8_t qf[KS];
-  {
-    const bool qok = wave_on && h < a.H;
-    const uint16_t* qrow = a.Q + (b * a.H + (qok ? h : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = qok ? *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
-      qf[ks] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
   // the split's entry ids (sparse)
   if (!dense) {
     const int64_t n_ids = min(hi, n_sel) - lo;
@@ -1059,9 +1073,8 @@ constexpr int kMergeMaxSplits = 256;
 // U: partial blocks a thread loads at once (4, 8 or 16: the smallest that
 // holds every split when there are at most 16, so that no load repeats another)
 template <int D, int U>
-__global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
-                                                      const uint16_t* __restrict__ ws_acc,
-                                                      const float* __restrict__ ws_ml) {
+__global__ __launch_bounds__(256) void k_attend_merge(int splits, const uint16_t* __restrict__ ws_acc,
+                                                      const float* __restrict__ ws_ml, AttendArgs a) {
   constexpr int CTW = D / 64;
   extern __shared__ float w_l[];            // [splits][kHMax] weights
   __shared__ float mq_l[4][kHMax], lq_l[4][kHMax];
@@ -1070,6 +1083,8 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
   // workgroup id -> (sequence, channel tile) with a sequence's tiles on one
   // XCD (ids equal mod 8), the one whose L2 its splits' partials went through
   constexpr int NQ = D / 16;
+  // the argument block's scalar lines, fetched together
+  asm volatile("" ::"s"(splits), "s"(a.Q), "s"(a.k), "s"(a.rope_dims), "s"(a.part_in));
   const int rq = blockIdx.x >> 3;
   const int64_t b = (int64_t)(rq / NQ) * 8 + (blockIdx.x & 7);
   const int q = rq % NQ;                    // 16-channel tile: wave slice q / CTW, j = q % CTW
@@ -1077,16 +1092,16 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
   const int t = threadIdx.x;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml) + b * splits * kHMax;
   const int R = a.rope_dims;
-  // rotary pairs of channels 16q .. 16q+15 that lie in the last R channels
-  if (t < 8) {
-    const int c = 16 * q + 2 * t;
-    if (c >= D - R) {
-      const int jj = (c - (D - R)) >> 1;
-      double sn, cs;
-      sincos(-(double)a.q_pos[b] * a.inv_freq[jj], &sn, &cs);
-      cs_l[0][t] = (float)cs;
-      cs_l[1][t] = (float)sn;
-    }
+  // rotary pairs of channels 16q .. 16q+15 that lie in the last R channels:
+  // thread t < 8 takes pair t; its frequency and position load with the rest,
+  // the angle's sine and cosine are taken once the weights are stored
+  const int c_rot = 16 * q + 2 * t;
+  const bool rot = t < 8 && c_rot >= D - R;
+  double f_rot = 0.0;
+  int64_t p_rot = 0;
+  if (rot) {
+    f_rot = a.inv_freq[(c_rot - (D - R)) >> 1];
+    p_rot = a.q_pos[b];
   }
   // thread (grp, hh0) folds the (reference maximum, sum) pairs of head hh0
   // over splits grp, grp + 4, ..; the first kMlU of them (every split when
@@ -1155,6 +1170,14 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttendArgs a, int splits,
     if (a.part_in && grp == 0) {
       we_l[hh0] = hh0 < a.H ? weight(reinterpret_cast<const float2*>(a.part_in + a.B * a.H * D)[b * a.H + hh0]) : 0.0f;
     }
+  }
+  if (rot) {
+    // (opaque until here, so that no use of the two loads moves up to them)
+    asm volatile("" : "+v"(p_rot), "+v"(f_rot));
+    double sn, cs;
+    sincos(-(double)p_rot * f_rot, &sn, &cs);
+    cs_l[0][t] = (float)cs;
+    cs_l[1][t] = (float)sn;
   }
   __syncthreads();
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -1233,18 +1256,18 @@ static hipError_t launch_attend_t(const AttendPlan& p, const AttendArgs& a, void
   uint16_t* ws_acc = reinterpret_cast<uint16_t*>(workspace);
   float* ws_ml = p.splits > 1 ? reinterpret_cast<float*>(ws_acc + (size_t)a.B * p.splits * kHMax * D) : nullptr;
   const int64_t b8 = 8 * ((a.B + 7) / 8);   // sequences padded to whole XCD rounds
-  hipLaunchKernelGGL(kern, dim3((unsigned)(b8 * p.splits)), dim3(kAttThreads), 0, stream, a, p.splits,
-                     p.keys_per_split, ws_acc, ws_ml);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(b8 * p.splits)), dim3(kAttThreads), 0, stream, p.splits,
+                     p.keys_per_split, ws_acc, ws_ml, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const dim3 mgrid((unsigned)(b8 * (D / 16)));
   const size_t mlds = (size_t)p.splits * kHMax * sizeof(float);
   if (p.splits <= 4)
-    hipLaunchKernelGGL((k_attend_merge<D, 4>), mgrid, dim3(256), mlds, stream, a, p.splits, ws_acc, ws_ml);
+    hipLaunchKernelGGL((k_attend_merge<D, 4>), mgrid, dim3(256), mlds, stream, p.splits, ws_acc, ws_ml, a);
   else if (p.splits <= 8)
-    hipLaunchKernelGGL((k_attend_merge<D, 8>), mgrid, dim3(256), mlds, stream, a, p.splits, ws_acc, ws_ml);
+    hipLaunchKernelGGL((k_attend_merge<D, 8>), mgrid, dim3(256), mlds, stream, p.splits, ws_acc, ws_ml, a);
   else
-    hipLaunchKernelGGL((k_attend_merge<D, 16>), mgrid, dim3(256), mlds, stream, a, p.splits, ws_acc, ws_ml);
+    hipLaunchKernelGGL((k_attend_merge<D, 16>), mgrid, dim3(256), mlds, stream, p.splits, ws_acc, ws_ml, a);
   return hipGetLastError();
 }
 

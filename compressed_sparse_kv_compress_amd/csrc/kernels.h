@@ -74,15 +74,16 @@ struct AttendArgs {
   int rope_dims;
   float rope_base;
   const int64_t* q_pos;
-  // rotary frequencies theta_i = rope_base^(-2i / rope_dims), i < rope_dims / 2,
-  // in fp64, computed on the host (they depend on no device data)
-  double inv_freq[256];
   float softmax_scale;
   float* O;
   // partials in the public layout: values [B][H][D] fp32 (normalised by their
   // own sum, not rotated), then (reference maximum in log2 units, sum) [B][H]
   float* part_out;           // one split: write this call's partial there instead of O
   const float* part_in;      // a partial over other keys, merged into O (or NULL)
+  // rotary frequencies theta_i = rope_base^(-2i / rope_dims), i < rope_dims / 2,
+  // in fp64, computed on the host (they depend on no device data). Last, so
+  // that the scalar fields above share the argument block's first cache lines.
+  double inv_freq[256];
 };
 hipError_t launch_attend(const AttendPlan& plan, const AttendArgs& a, void* workspace,
                          hipStream_t stream);
