@@ -4,7 +4,9 @@
 // compressed entries per query (default k = 512). [P2] Step 5: a learned
 // indexer scores every compressed block; the query reads only the chosen ones.
 //
-// One launch, k_index_topk (grid: chunks x sequences, 1024 threads):
+// One launch, k_index_topk (grid: chunks x sequences, 1024 threads; one
+// dimension with a sequence's chunks on one XCD when the batch is a multiple
+// of 8):
 //   Scoring. Each workgroup streams one chunk of a sequence's indexer keys
 //     once from HBM with 16-byte non-temporal loads (bf16, or fp4 codes +
 //     E4M3 group scales dequantised in registers), computes each entry's
@@ -898,15 +900,28 @@ __global__ __launch_bounds__(NT) void k_index_topk(
     const uint8_t* __restrict__ k_scale, const int32_t* __restrict__ n_entries, int64_t n_max,
     int chunk, int n_chunks, int k, int cand_cap, int tb_cap, uint32_t* __restrict__ ws_hist,
     uint32_t* __restrict__ ws_arrive, uint32_t* __restrict__ ws_ckey, int32_t* __restrict__ ws_cidx,
-    int32_t* __restrict__ ws_cnt, int32_t* __restrict__ ids) {
+    int32_t* __restrict__ ws_cnt, int32_t* __restrict__ ids, int xcd) {
   constexpr int NW = NT / kWave;
   constexpr int BPT = kHistBins / NT;
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ int wcnt_l[NW];
   __shared__ int last_l;
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
-  const int64_t b = blockIdx.y;
-  const int c = blockIdx.x;
+  // workgroup -> (sequence, chunk). With `xcd` (a 1-D grid, the batch a
+  // multiple of 8) a sequence's chunks get ids equal mod 8, and workgroups are
+  // dealt to the 8 XCDs by id mod 8, so they run on one XCD: the sequence's
+  // query and histogram lines stay in one L2, and its selection starts on the
+  // XCD that scored its chunks.
+  int64_t b;
+  int c;
+  if (xcd) {
+    const int r = blockIdx.x >> 3;
+    b = (int64_t)(r / n_chunks) * 8 + (blockIdx.x & 7);
+    c = r % n_chunks;
+  } else {
+    b = blockIdx.y;
+    c = blockIdx.x;
+  }
   int64_t nv = n_entries ? (int64_t)n_entries[b] : n_max;
   nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
   const int64_t start = (int64_t)c * chunk;
@@ -936,14 +951,14 @@ __global__ __launch_bounds__(NT) void k_index_topk(
 
     // Add the chunk histogram into the sequence's. A bin's returned count plus
     // the chunk's own is at most its final count; untouched bins count 0.
-    uint32_t now[BPT];
+    // (all of a thread's returning atomics are in flight at once)
+    uint32_t hv[BPT], now[BPT];
 #pragma unroll
-    for (int u = 0; u < BPT; ++u) {
-      const uint32_t h = hist[t + u * NT];
-      now[u] = h ? atomicAdd(&gh[t + u * NT], h) + h : 0u;
-    }
+    for (int u = 0; u < BPT; ++u) hv[u] = hist[t + u * NT];
 #pragma unroll
-    for (int u = 0; u < BPT; ++u) hist[t + u * NT] = now[u];
+    for (int u = 0; u < BPT; ++u) now[u] = hv[u] ? atomicAdd(&gh[t + u * NT], hv[u]) : 0u;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) hist[t + u * NT] = hv[u] ? now[u] + hv[u] : 0u;
     __syncthreads();
     int tb_above, tb_count;
     const int tb = wave_threshold_bin(hist, k, tb_above, tb_count);   // at or below the final threshold bin
@@ -1101,12 +1116,14 @@ static hipError_t launch_t(const TopkPlan& p, const uint16_t* q_idx, const void*
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
     if (e != hipSuccess) return e;
   }
-  dim3 grid((unsigned)p.n_chunks, (unsigned)B);
+  // a sequence's chunks on one XCD when the batch fills whole XCD rounds
+  const bool xcd = FUSED && B % 8 == 0 && B * p.n_chunks <= 0x7FFFFFFF;
+  const dim3 grid = xcd ? dim3((unsigned)(B * p.n_chunks)) : dim3((unsigned)p.n_chunks, (unsigned)B);
   hipLaunchKernelGGL(kern, grid, dim3(NT), p.lds_bytes, stream, q_idx, k_idx, k_scale, n_entries,
                      n_max, (int)p.chunk, (int)p.n_chunks, k, p.cand_cap, p.tb_cap,
                      reinterpret_cast<uint32_t*>(ws + p.off_hist), reinterpret_cast<uint32_t*>(ws + p.off_arrive),
                      reinterpret_cast<uint32_t*>(ws + p.off_ckey), reinterpret_cast<int32_t*>(ws + p.off_cidx),
-                     reinterpret_cast<int32_t*>(ws + p.off_cnt), ids);
+                     reinterpret_cast<int32_t*>(ws + p.off_cnt), ids, xcd ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (FUSED || e != hipSuccess) return e;
   auto sel = k_topk_select<kTopkThreads>;
