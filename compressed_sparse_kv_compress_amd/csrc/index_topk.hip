@@ -905,7 +905,7 @@ __global__ __launch_bounds__(NT) void k_index_topk(
   constexpr int BPT = kHistBins / NT;
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ int wcnt_l[NW];
-  __shared__ int last_l;
+  __shared__ int last_l, tb_l;
   const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
   // workgroup -> (sequence, chunk). With `xcd` (a 1-D grid, the batch a
   // multiple of 8) a sequence's chunks get ids equal mod 8, and workgroups are
@@ -960,8 +960,15 @@ __global__ __launch_bounds__(NT) void k_index_topk(
 #pragma unroll
     for (int u = 0; u < BPT; ++u) hist[t + u * NT] = hv[u] ? now[u] + hv[u] : 0u;
     __syncthreads();
-    int tb_above, tb_count;
-    const int tb = wave_threshold_bin(hist, k, tb_above, tb_count);   // at or below the final threshold bin
+    // the bin at or below the final threshold bin: found by wave 0 alone (16
+    // waves reading the whole histogram would queue 256 KiB of LDS reads)
+    if (wave == 0) {
+      int tb_above, tb_count;
+      const int tb0 = wave_threshold_bin(hist, k, tb_above, tb_count);
+      if (lane == 0) tb_l = tb0;
+    }
+    __syncthreads();
+    const int tb = tb_l;
 
     // The chunk's entries at or above that bin go to its list in entry order:
     // wave w counts those of its share of the chunk, then writes them after
