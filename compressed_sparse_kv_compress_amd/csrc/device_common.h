@@ -211,11 +211,22 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 
 // Inclusive prefix sum over the wave (lane 0 first).
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(v, o, kWave);
-    if (lane_id() >= o) v += t;
-  }
+  // DPP: sums within each row of 16 lanes by shifts of 1, 2, 4 and 8 (lanes
+  // shifted in from outside the row add 0), then lane 15's row total into
+  // rows 1 and 3 and lane 31's running total into rows 2 and 3. Each step is
+  // one VALU add (a shuffle would be an LDS round trip).
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
   return v;
+}
+// The value of lane `src` (the same in every lane of the wave): a scalar read
+// instead of a shuffle through LDS.
+__device__ __forceinline__ int lane_value(int v, int src) {
+  return __builtin_amdgcn_readlane(v, __builtin_amdgcn_readfirstlane(src));
 }
 
 // Orderable key of a score: larger score -> larger key; -0 equals +0; NaN -> 0

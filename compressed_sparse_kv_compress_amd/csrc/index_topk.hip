@@ -97,8 +97,8 @@ __device__ int block_exclusive_scan(int v, int* scratch, int& total) {
   // the waves' totals, scanned across the first NT / 64 lanes
   const int x = lane < NT / kWave ? scratch[lane] : 0;
   const int wincl = wave_inclusive_scan(x);
-  total = __shfl(wincl, NT / kWave - 1);
-  const int before = wave > 0 ? __shfl(wincl, wave - 1) : 0;
+  total = lane_value(wincl, NT / kWave - 1);
+  const int before = wave > 0 ? lane_value(wincl, wave - 1) : 0;
   __syncthreads();
   return before + incl - v;
 }
@@ -358,14 +358,14 @@ __device__ int wave_threshold_bin(const uint32_t* hist, int k, int& above, int& 
   count = 0;
   if (m == 0) return 0;
   const int L = __ffsll((unsigned long long)m) - 1;
-  const int seg_above = __shfl(incl - s, L);
+  const int seg_above = lane_value(incl - s, L);
   const int top = kHistBins - 1 - 64 * L;
   const int cnt = (int)hist[top - lane];
   const int incl2 = wave_inclusive_scan(cnt) + seg_above;
   const uint64_t m2 = __ballot(incl2 - cnt < k && k <= incl2);
   const int F = __ffsll((unsigned long long)m2) - 1;
-  above = __shfl(incl2 - cnt, F);
-  count = __shfl(cnt, F);
+  above = lane_value(incl2 - cnt, F);
+  count = lane_value(cnt, F);
   return top - F;
 }
 
@@ -448,8 +448,8 @@ __device__ __forceinline__ int waves_before(const int* cnt, int wave, int& all) 
   const int lane = lane_id();
   const int x = lane < NW ? cnt[lane] : 0;
   const int incl = wave_inclusive_scan(x);
-  all = __shfl(incl, NW - 1);
-  return wave > 0 ? __shfl(incl, wave - 1) : 0;
+  all = lane_value(incl, NW - 1);
+  return wave > 0 ? lane_value(incl, wave - 1) : 0;
 }
 
 // The common case of the selection, with the candidates kept in registers.
@@ -520,7 +520,7 @@ __device__ __forceinline__ bool select_registers(bool take_all, int k, int total
   const int wincl = wave_inclusive_scan(ntb);
   int slot = 0;
   if (lane == kWave - 1 && wincl > 0) slot = atomicAdd(&L.misc[5], wincl);
-  slot = __shfl(slot, kWave - 1) + wincl - ntb;
+  slot = lane_value(slot, kWave - 1) + wincl - ntb;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     if ((tbm >> u) & 1u) {
@@ -559,9 +559,9 @@ __device__ __forceinline__ bool select_registers(bool take_all, int k, int total
       run2 += hc[j];
     }
     const int owner = __ffsll((unsigned long long)__ballot(m > 0 && rem > 0)) - 1;
-    sb = __shfl(sb, owner);
-    rem = __shfl(rem, owner);   // keys to take among those sharing the prefix
-    m = __shfl(m, owner);       // keys sharing the prefix
+    sb = lane_value(sb, owner);
+    rem = lane_value(rem, owner);   // keys to take among those sharing the prefix
+    m = lane_value(m, owner);       // keys sharing the prefix
     if (m > kTieCap) return false;
     pstar = ((uint32_t)tbin << kSubBits) | (uint32_t)sb;
     // the keys sharing the prefix, with their entries
@@ -573,7 +573,7 @@ __device__ __forceinline__ bool select_registers(bool take_all, int k, int total
       if (mt) {
         int s2 = 0;
         if (lane == 0) s2 = atomicAdd(&L.misc[3], __popcll(mt));
-        s2 = __shfl(s2, 0) + __popcll(mt & lanemask_lt());
+        s2 = lane_value(s2, 0) + __popcll(mt & lanemask_lt());
         if (tie && s2 < kTieCap) {
           L.tkey[s2] = key;
           L.tpos[s2] = L.bpos[i];
@@ -814,9 +814,9 @@ __device__ __forceinline__ void select_sequence(int64_t nv, int k, int n_lists, 
         run2 += hc[j];
       }
       const int owner = __ffsll((unsigned long long)__ballot(m > 0 && rem > 0)) - 1;
-      sb = __shfl(sb, owner);
-      rem = __shfl(rem, owner);                    // keys to take among those sharing the prefix
-      m = __shfl(m, owner);                        // keys sharing the prefix
+      sb = lane_value(sb, owner);
+      rem = lane_value(rem, owner);                    // keys to take among those sharing the prefix
+      m = lane_value(m, owner);                        // keys sharing the prefix
       const uint32_t pstar = ((uint32_t)tbin << kSubBits) | (uint32_t)sb;   // 20-bit prefix
       const int nb = L.misc[5];
       if (m <= kTieCap && nb <= tbcap) {
@@ -832,7 +832,7 @@ __device__ __forceinline__ void select_sequence(int64_t nv, int k, int n_lists, 
           if (mt) {
             int slot2 = 0;
             if (lane == 0) slot2 = atomicAdd(&L.misc[3], __popcll(mt));
-            slot2 = __shfl(slot2, 0) + __popcll(mt & lanemask_lt());
+            slot2 = lane_value(slot2, 0) + __popcll(mt & lanemask_lt());
             if (tie && slot2 < kTieCap) {   // (there are exactly m of them)
               L.tkey[slot2] = key;
               L.tpos[slot2] = L.bpos[i];
