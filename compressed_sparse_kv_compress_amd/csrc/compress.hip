@@ -56,7 +56,7 @@ __device__ __forceinline__ void store_entry(const float* acc, int lane, void* ca
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) amax = fmaxf(amax, fabsf(acc[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));          // the group's other 8 channels
+    amax = fmaxf(amax, dpp_f32<kDppQuadSwap1>(amax));       // the group's other 8 channels
     uint32_t sc = f32_to_e4m3(amax / 6.0f);
     if (e4m3_to_f32(sc) == 0.0f && amax > 0.0f) sc = 0x01u;
     const float sv = e4m3_to_f32(sc);

@@ -194,14 +194,33 @@ __device__ __forceinline__ float sum_row16(float v) {
   return v;
 }
 
+// Row broadcasts (GFX9): lane 15 of each row into rows 1 and 3, lane 31 into
+// rows 2 and 3. Lanes of the rows left out get `old`.
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_rows_f32(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+
+// Maximum and sum over the wave, in every lane: DPP within each row of 16
+// lanes, the rows folded into lane 63 by row broadcasts, then read back as a
+// scalar (no LDS shuffles).
 __device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));
+  v = fmaxf(v, dpp_f32<kDppRowRor4>(v));
+  v = fmaxf(v, dpp_f32<kDppRowRor8>(v));
+  v = fmaxf(v, dpp_rows_f32<kDppRowBcast15, 0xA>(v, v));
+  v = fmaxf(v, dpp_rows_f32<kDppRowBcast31, 0xC>(v, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v = sum_row16(v);
+  v += dpp_rows_f32<kDppRowBcast15, 0xA>(0.0f, v);
+  v += dpp_rows_f32<kDppRowBcast31, 0xC>(0.0f, v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
