@@ -953,8 +953,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(int splits, int64_t k
       }
     }
     // the head's largest logit over the split (every tile has landed: no DMA in flight)
-    float mh = fmaxf(m_seen, __shfl_xor(m_seen, 16, kWave));
-    mh = fmaxf(mh, __shfl_xor(mh, 32, kWave));
+    const float mh = max_xor32(max_xor16(m_seen));
     const bool redo = pass == 0 && wave_on && mh != -INFINITY &&
                       (mh > m_ref + kHeadroom || mh < m_ref - kHeadroom);
     if (__ballot(redo) && lane == 0) redo_l = 1;
@@ -962,8 +961,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(int splits, int64_t k
     if (redo_l == 0 || pass > 0) break;
     m_ref = mh != -INFINITY ? mh : 0.0f;
   }
-  l_run += __shfl_xor(l_run, 16, kWave);
-  l_run += __shfl_xor(l_run, 32, kWave);
+  l_run = add_xor32(add_xor16(l_run));
   // every wave holds channels of all heads: share each head's reference and sum
   if (g == 0) {
     mref_l[h] = m_ref;
