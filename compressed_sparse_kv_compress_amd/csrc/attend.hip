@@ -932,10 +932,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(int splits, int64_t k
     }
     if (pass == 0 && splits == 1 && t < a.rope_dims / 2) {
       // the rotary table of a single split, while the first tiles are in flight
-      double sn, cs;
-      sincos(-(double)a.q_pos[b] * a.inv_freq[t], &sn, &cs);
-      cos_l[t] = (float)cs;
-      sin_l[t] = (float)sn;
+      sincos_rad(-(double)a.q_pos[b] * a.inv_freq[t], &sin_l[t], &cos_l[t]);
     }
     if constexpr (C::kDma) {
       for (int i = 0; i <= n_tiles; i += kNStage) {
@@ -1172,10 +1169,7 @@ __global__ __launch_bounds__(256) void k_attend_merge(int splits, const uint16_t
   if (rot) {
     // (opaque until here, so that no use of the two loads moves up to them)
     asm volatile("" : "+v"(p_rot), "+v"(f_rot));
-    double sn, cs;
-    sincos(-(double)p_rot * f_rot, &sn, &cs);
-    cs_l[0][t] = (float)cs;
-    cs_l[1][t] = (float)sn;
+    sincos_rad(-(double)p_rot * f_rot, &cs_l[1][t], &cs_l[0][t]);
   }
   __syncthreads();
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);

@@ -203,6 +203,15 @@ __device__ __forceinline__ float dpp_rows_f32(float old, float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROWS, 0xF, false));
 }
 
+// cos and sin of an angle in radians (fp64, any size; rotary angles reach
+// ~1e6): reduced to [-pi, pi] in fp64, then evaluated in fp32. The reduction
+// error is ~1e-10 rad at 1e6, so the results are within ~1.5 ulp of the fp64
+// functions rounded to fp32, which cost a slow large-argument reduction.
+__device__ __forceinline__ void sincos_rad(double a, float* s, float* c) {
+  const double r = a - 6.283185307179586 * rint(a * 0.15915494309189535);
+  sincosf((float)r, s, c);
+}
+
 // v combined with lane l ^ 16 and with lane l ^ 32 (gfx950 lane swaps: for a
 // register swapped with itself, the two results hold v and v[l ^ 16] (or
 // v[l ^ 32]) in some order, so their sum or maximum is the pair's).
