@@ -69,6 +69,22 @@ def test_topk_ragged_entry_counts(cskv):
     assert np.array_equal(ids, _oracle_ids(q, kk, k, nv))
 
 
+@pytest.mark.parametrize("B,N,chunk", [(8, 3000, 256), (16, 5000, 0), (8, 20000, 1024), (9, 3000, 256)])
+def test_topk_batches_of_whole_xcd_rounds(cskv, B, N, chunk):
+    """A batch that is a multiple of 8 runs a one-dimensional grid whose ids put
+    each sequence's chunks on one XCD (B = 9 keeps the two-dimensional grid):
+    ids byte-exact against the oracle, with ragged counts (an empty sequence, a
+    short one, a chunk boundary), twice on one workspace."""
+    Di, k = 128, 512
+    q, kk = _bf16_case(7000 + B * 10 + N // 1000, B, N, Di, 8)
+    nv = np.array([N - 97 * b for b in range(B)], dtype=np.int32)
+    nv[1], nv[2], nv[3] = 0, 300, min(N, 2 * max(chunk, 256))
+    ref = _oracle_ids(q, kk, k, nv)
+    for _ in range(2):
+        ids = cskv.index_topk(to_dev_bf16(q), to_dev_bf16(kk), k, n_entries=to_dev(nv), chunk=chunk).cpu().numpy()
+        assert np.array_equal(ids, ref)
+
+
 def test_topk_short_sequences_leave_workspace_clear(cskv):
     """Calls on one workspace where some sequences hold no more than k entries,
     followed by calls where they hold more: every call must match the oracle
