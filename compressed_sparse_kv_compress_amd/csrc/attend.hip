@@ -882,23 +882,26 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(int splits, int64_t k
       for (int ht = 0; ht < 4; ++ht) acc[j][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, pbo[ht], acc[j][ht], 0, 0, 0);
     }
   };
-  // step i (i % 4 == S): tile i in slot S, tile i-1 in slot S-1
-  auto pstep = [&](auto sc, int i) __attribute__((always_inline)) {
+  // step i (i % 4 == S): tile i in slot S, tile i-1 in slot S-1. The first
+  // step (FIRST, i = 0: QK^T and softmax alone) runs ahead of the loop, so
+  // that the loop's four steps have one shape: with the first tile's path
+  // inside step 0 the compiler gave that step a second accumulator bank and
+  // copied 120 accumulators back after it, every fourth tile.
+  auto pstep = [&](auto sc, auto first, int i) __attribute__((always_inline)) {
     constexpr int S = decltype(sc)::value;
     constexpr int SP = (S + kNStage - 1) % kNStage;
+    constexpr bool FIRST = decltype(first)::value;
     if (i > n_tiles) return;
     if (i < n_tiles) wait_tile<C::kOpsPerTile>(i + 1 < n_tiles ? 1 : 0);
     lds_barrier();   // tile i and probabilities i-1 visible; slot S+2 (tile i-2) free
     if (i + 2 < n_tiles) issue(std::integral_constant<int, (S + 2) % kNStage>{}, i + 2);
     uint16_t* pw = p_buf(std::integral_constant<int, S & 1>{});
     const uint16_t* pr = p_buf(std::integral_constant<int, (S & 1) ^ 1>{});
-    if (i < n_tiles && wave_on) {
-      if (i >= 1) {
-        qk_pv(tile_of(sc), pb_of(sc), tile_of(std::integral_constant<int, SP>{}), pr, pw);
-      } else {
-        qk_softmax(tile_of(sc), pb_of(sc), vs_of(sc), pw);
-      }
-    } else if (i >= 1) {
+    if constexpr (FIRST) {
+      if (i < n_tiles && wave_on) qk_softmax(tile_of(sc), pb_of(sc), vs_of(sc), pw);
+    } else if (i < n_tiles && wave_on) {
+      qk_pv(tile_of(sc), pb_of(sc), tile_of(std::integral_constant<int, SP>{}), pr, pw);
+    } else {
       pv_only(tile_of(std::integral_constant<int, SP>{}), pr);
     }
   };
@@ -935,11 +938,12 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_attend(int splits, int64_t k
       sincos_rad(-(double)a.q_pos[b] * a.inv_freq[t], &sin_l[t], &cos_l[t]);
     }
     if constexpr (C::kDma) {
-      for (int i = 0; i <= n_tiles; i += kNStage) {
-        pstep(std::integral_constant<int, 0>{}, i);
-        pstep(std::integral_constant<int, 1>{}, i + 1);
-        pstep(std::integral_constant<int, 2>{}, i + 2);
-        pstep(std::integral_constant<int, 3>{}, i + 3);
+      pstep(std::integral_constant<int, 0>{}, std::true_type{}, 0);
+      for (int i = 1; i <= n_tiles; i += kNStage) {
+        pstep(std::integral_constant<int, 1>{}, std::false_type{}, i);
+        pstep(std::integral_constant<int, 2>{}, std::false_type{}, i + 1);
+        pstep(std::integral_constant<int, 3>{}, std::false_type{}, i + 2);
+        pstep(std::integral_constant<int, 0>{}, std::false_type{}, i + 3);
       }
     } else {
       for (int i = 0; i < n_tiles; i += kNStage) {
