@@ -88,12 +88,15 @@ def version() -> int:
     return int(_lib_version())
 
 
+# Pointers and streams go to ctypes as plain integers (the c_void_p argtypes
+# convert them): a per-argument c_void_p object costs more than the call's
+# own conversion, and a decode step makes these calls once per layer.
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _stream(device=None):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _need_cuda(*ts):
@@ -116,7 +119,7 @@ _workspaces: dict = {}
 _retired: list = []
 
 
-def _workspace(purpose: str, nbytes: int, device, layout=None) -> torch.Tensor | None:
+def _workspace(purpose: str, nbytes: int, device, layout=None, stream=None) -> torch.Tensor | None:
     """A scratch buffer for one (purpose, device, current stream, layout).
 
     Calls on one stream are ordered, so they can share a buffer; calls on two
@@ -127,11 +130,13 @@ def _workspace(purpose: str, nbytes: int, device, layout=None) -> torch.Tensor |
     another layout's state. A stateless buffer (layout None) grows on demand.
     No buffer is ever freed while the process runs (a grown one is retired,
     not dropped), so a HIP graph captured with a buffer's address can be
-    replayed after later eager calls of any shape."""
+    replayed after later eager calls of any shape. ``stream`` is the
+    device's current stream handle when the caller has it already."""
     if nbytes == 0:
         return None
-    dev = torch.device(device)
-    stream = torch.cuda.current_stream(dev).cuda_stream
+    dev = device if isinstance(device, torch.device) else torch.device(device)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
     key = (purpose, dev.index, stream, layout)
     buf = _workspaces.get(key)
     if buf is None or buf.numel() < nbytes:
@@ -142,6 +147,19 @@ def _workspace(purpose: str, nbytes: int, device, layout=None) -> torch.Tensor |
         buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev).zero_()
         _workspaces[key] = buf
     return buf
+
+
+_ws_sizes: dict = {}
+
+
+def _ws_bytes(fn, *args) -> int:
+    """A workspace-size query of the library, remembered per argument set
+    (the sizes depend on the arguments alone)."""
+    key = (id(fn), args)   # (ctypes functions are not hashable; these live as long as the module)
+    n = _ws_sizes.get(key)
+    if n is None:
+        n = _ws_sizes[key] = int(fn(*args))
+    return n
 
 
 def _caller_workspace(ws: torch.Tensor, nbytes: int, name: str) -> torch.Tensor:
@@ -269,13 +287,14 @@ def index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, k: int, k_scale: torch.
         ids = torch.empty((B, k), dtype=torch.int32, device=q_idx.device)
     elif ids.dtype != torch.int32 or tuple(ids.shape) != (B, k) or not ids.is_contiguous():
         raise ValueError("ids must be contiguous int32 [B, k]")
-    nbytes = _lib_topk_ws(B, N, Di, k, key_dtype, chunk)   # 0 also when the call will reject
+    nbytes = _ws_bytes(_lib_topk_ws, B, N, Di, k, key_dtype, chunk)   # 0 also when the call will reject
+    stream = _stream(q_idx.device)
     if workspace is not None:
         ws = _caller_workspace(workspace, nbytes, "workspace")
     else:
-        ws = _workspace("index_topk", nbytes, q_idx.device, layout=(B, N, Di, k, key_dtype, chunk))
+        ws = _workspace("index_topk", nbytes, q_idx.device, layout=(B, N, Di, k, key_dtype, chunk), stream=stream)
     _check(_lib_topk(_ptr(q_idx), key_dtype, _ptr(k_idx), _ptr(k_scale), _ptr(n_entries), B, N, Di, k,
-                     _ptr(ids), chunk, _ptr(ws), 0 if ws is None else ws.numel(), _stream(q_idx.device)))
+                     _ptr(ids), chunk, _ptr(ws), 0 if ws is None else ws.numel(), stream))
     return ids
 
 
@@ -283,14 +302,20 @@ def index_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, k: int, k_scale: torch.
 
 def _window_args(window, window_scale, B, D):
     """(window or None, W, batch stride in rows, fp8?) of an attend window [B, W, D]."""
-    if window is None or window.shape[1] == 0:
+    if window is None:
         return None, 0, 0, False
-    if window.dim() != 3 or window.shape[0] != B or window.shape[2] != D:
+    shape = window.shape
+    if len(shape) != 3 or shape[0] != B or shape[2] != D:
+        if len(shape) >= 2 and shape[1] == 0:
+            return None, 0, 0, False
         raise ValueError("window must be [B, W, D]")
-    if window.stride(2) != 1 or window.stride(1) != D or window.stride(0) % D != 0:
+    W = shape[1]
+    if W == 0:
+        return None, 0, 0, False
+    st = window.stride()
+    if st[2] != 1 or st[1] != D or st[0] % D != 0:
         raise ValueError("window rows must be dense with a whole-row batch stride")
-    W = window.shape[1]
-    wstride = window.stride(0) // D
+    wstride = st[0] // D
     win_fp8 = window.dtype in (torch.uint8, torch.float8_e4m3fn)
     if win_fp8:
         if window_scale is None or window_scale.dtype != torch.float32:
@@ -351,24 +376,25 @@ def attend(Q: torch.Tensor, cache: torch.Tensor, ids: torch.Tensor | None, windo
                                    rope_base, _ptr(q_pos), softmax_scale, _ptr(out), splits, _stream(Q.device)))
         return out
     max_keys = (k if ids is not None else cache.shape[1]) + W
-    nbytes = _lib_attend_ws(B, H, D, max_keys, splits)
+    nbytes = _ws_bytes(_lib_attend_ws, B, H, D, max_keys, splits)
+    stream = _stream(Q.device)
     if workspace is not None:
         ws = _caller_workspace(workspace, nbytes, "workspace")
     else:
-        ws = _workspace("attend", nbytes, Q.device)
+        ws = _workspace("attend", nbytes, Q.device, stream=stream)
     if partial is not None:
         _check(_lib_attend_part(_ptr(Q), B, H, D, cache_dt, _ptr(cache), _ptr(cache_scale),
                                 cache.shape[1], _ptr(ids), k, _ptr(n_entries), FP8_E4M3 if win_fp8 else BF16,
                                 _ptr(window), _ptr(window_scale), W, wstride, _ptr(n_window), rope_dims, rope_base,
                                 _ptr(q_pos), softmax_scale, _ptr(partial), _ptr(out), splits, _ptr(ws),
-                                0 if ws is None else ws.numel(), _stream(Q.device)))
+                                0 if ws is None else ws.numel(), stream))
         return out
     _check(_lib_attend(_ptr(Q), B, H, D, cache_dt, _ptr(cache), _ptr(cache_scale),
                        cache.shape[1], _ptr(ids), k, _ptr(n_entries), FP8_E4M3 if win_fp8 else BF16,
                        _ptr(window), _ptr(window_scale), W, wstride, _ptr(n_window), rope_dims, rope_base,
                        _ptr(q_pos),
                        softmax_scale, _ptr(out), splits, _ptr(ws), 0 if ws is None else ws.numel(),
-                       _stream(Q.device)))
+                       stream))
     return out
 
 
