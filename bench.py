@@ -39,7 +39,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: at least 5; for workloads whose steps carry no state, "
+                         "as many more as run 25 ms, so that the GPU clock has settled before the timed steps)")
     ap.add_argument("--workload", default=None,
                     choices=["c4a_128k_bf16", "c128a_1m_bf16", "c4a_1m_fp8_fp4", "mixed61_256k_bf16", "tiny_c4a_2k",
                              "stream_c4a_128k_bf16", "c128a_1m_mixed", "c128a_1m_fp4", "mixed61_256k_reuse"])
@@ -804,8 +806,18 @@ def measure(cfg, args, with_cpu):
     from synth import device as sd
 
     cls = {"c4a": C4aLayer, "c128a": C128aLayer, "mixed": Mixed61, "stream": StreamC4a}[cfg.kind]
-    wl = cls(cfg, args, torch, cskv, sd, synth)
     stateful = cfg.kind in ("mixed", "stream")   # steps that carry state: no input-set rotation, no graphs
+    # Warmup steps: --warmup exactly when given. By default at least 5, and
+    # for stateless steps more until 25 ms of them have run: after only a few
+    # short steps the GPU clock is still ramping (c128a 1M on one box: 44.7-45.2
+    # us per timed step after 5 warmup steps, 39.5-40.5 us after 200). Steps
+    # that carry state keep 5 (more would change the context they time; the
+    # 61-layer steps are long, the streaming ones are not).
+    auto_warm = args.warmup is None
+    args = argparse.Namespace(**vars(args))
+    if auto_warm:
+        args.warmup = 5
+    wl = cls(cfg, args, torch, cskv, sd, synth)
     n_sets = args.sets or (1 if stateful else 4)
     log(f"{cfg.name}: setup ({n_sets} input set{'s' if n_sets > 1 else ''})")
     t_setup = time.perf_counter()
@@ -821,14 +833,26 @@ def measure(cfg, args, with_cpu):
 
     mixed = cfg.kind == "mixed"
     n4 = wl.n_dominant() if mixed else 1
-    for i in range(args.warmup):
+    def warm_step(i):
         if stateful:
             wl.step(i)
         else:
             st = wl.sets[i % n_sets]
             wl.dominant(st)
             wl.rest(st)
+
+    for i in range(args.warmup):
+        warm_step(i)
     torch.cuda.synchronize()
+    if auto_warm and not stateful:
+        t_warm = time.perf_counter()
+        n_warm = args.warmup
+        while time.perf_counter() - t_warm < 0.025 and n_warm < 20000:
+            for _ in range(5):
+                warm_step(n_warm)
+                n_warm += 1
+            torch.cuda.synchronize()
+        args.warmup = n_warm
     # Optionally the calls of each input set are captured once into HIP graphs
     # (the dominant call in a graph of its own, so that its duration is timed on
     # the launch stream) and replayed.
@@ -913,6 +937,7 @@ def measure(cfg, args, with_cpu):
         "value": round(tokens, 1),
         "unit": "tokens/s",
         "ms_per_step": round(ms_step, 5),
+        "warmup": args.warmup,
         "dtype": ("bf16" if cfg.cache_dtype == "bf16" and cfg.key_dtype == "bf16" else
                   "fp8 + bf16 rotary (bf16 MFMA, fp32 accumulate)" if cfg.cache_dtype == "mixed" else
                   "fp4 E2M1 + E4M3/16 (bf16 MFMA, fp32 accumulate)" if cfg.cache_dtype == "fp4" else
@@ -1000,7 +1025,7 @@ def main():
     probe_gbs = hbm_probe()
     out = {
         "metric": head["metric"], "value": head["value"], "unit": head["unit"], "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "steps": args.steps, "warmup": head["warmup"], "ms_per_step": head["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"],
         "data": "synthetic (SplitMix64 streams; caches built by the library's compress kernel)"
                 if cfg.kind not in ("mixed", "stream") else
