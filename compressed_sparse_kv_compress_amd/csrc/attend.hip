@@ -1270,6 +1270,15 @@ static hipError_t launch_attend_t(const AttendPlan& p, const AttendArgs& a, void
 hipError_t launch_attend(const AttendPlan& p, const AttendArgs& a, void* workspace,
                          hipStream_t stream) {
   if (a.D == 512) {
+    // The variant follows the rows the call reads: without cache rows (a
+    // window-only partial) the cache's format is moot, and without window rows
+    // (entries only) the window's, so such calls take the DMA variant of the
+    // one format they read rather than a mixed one that fills tiles through
+    // registers.
+    const bool no_cache = a.ids ? a.k == 0 : a.cache_rows == 0;
+    if (no_cache) return a.win_fp8 && a.W > 0 ? launch_attend_t<512, kFmtFp8, true>(p, a, workspace, stream)
+                                              : launch_attend_t<512, kFmtBf16, false>(p, a, workspace, stream);
+    if (a.W == 0 && a.cache_fp8) return launch_attend_t<512, kFmtFp8, true>(p, a, workspace, stream);
     if (a.cache_mix) return a.win_fp8 ? launch_attend_t<512, kFmtMix, true>(p, a, workspace, stream)
                                       : launch_attend_t<512, kFmtMix, false>(p, a, workspace, stream);
     if (a.cache_fp4) return a.win_fp8 ? launch_attend_t<512, kFmtFp4, true>(p, a, workspace, stream)
