@@ -328,7 +328,10 @@ __device__ void score_chunk_fp4(const uint16_t* q, const uint8_t* codes_g, const
       g1s = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<1>(v[u].w), qp[13], g1s, false);
       g1s = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<2>(v[u].w), qp[14], g1s, false);
       g1s = __builtin_amdgcn_fdot2_f32_bf16(fp4x2_to_bf16x2<3>(v[u].w), qp[15], g1s, false);
-      float p = fmaf(g1s, e4m3_to_f32(s[u] >> 8), g0s * e4m3_to_f32(s[u] & 0xFFu));
+      // the two E4M3 group scales, exactly, through the hardware converter
+      // (byte 0 -> low half, byte 1 -> high half of a bf16 pair)
+      const uint32_t sb = fp8x2_to_bf16x2<false>(s[u] & 0xFFFFu);
+      float p = fmaf(g1s, __uint_as_float(sb & 0xFFFF0000u), g0s * __uint_as_float(sb << 16));
       if constexpr (LPE == 4) p = sum_quad(p);
       const int e = (g0 + NW * u) * EPL + sub;
       if (part == 0 && e < n) put_key(keys, hist, e, p);

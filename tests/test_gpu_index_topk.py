@@ -61,6 +61,34 @@ def test_topk_fp4_matches_oracle(cskv):
             assert np.array_equal(ids[b], M.topk_ids(s, k)), (chunk, b)
 
 
+@pytest.mark.parametrize("case", ["subnormal", "mantissas", "zero_nan"])
+def test_topk_fp4_scale_codes(cskv, case):
+    """Group-scale codes beyond powers of two, which the kernel decodes with the
+    hardware E4M3 converter: subnormals (m * 2^-9), every mantissa of one
+    exponent, both signs, zero and NaN (a NaN scale makes the entry's score NaN,
+    which ranks below every number). Within a case the scales share one
+    exponent range, so the fp32 sums are exact and the ids compare byte for
+    byte."""
+    B, N, Di, k = 2, 6000, 128, 512
+    rng = np.random.default_rng({"subnormal": 11, "mantissas": 12, "zero_nan": 13}[case])
+    q = synth.int_bf16(synth.stream_key(91, synth.T_QIDX), 0, B * Di, 8).reshape(B, Di)
+    codes = rng.integers(0, 256, size=(B, N, Di // 2), dtype=np.uint8)
+    shape = (B, N, Di // 16)
+    sign = (rng.integers(0, 2, size=shape) << 7).astype(np.uint8)
+    if case == "subnormal":
+        sc = rng.integers(0, 8, size=shape).astype(np.uint8) | sign          # exponent field 0
+    elif case == "mantissas":
+        sc = np.uint8(7 << 3) | rng.integers(0, 8, size=shape).astype(np.uint8) | sign   # 1.0 .. 1.875
+    else:
+        pick = np.array([0x38, 0x40, 0xB8, 0x00, 0x80, 0x7F, 0xFF], dtype=np.uint8)   # 1, 2, -1, +-0, NaN
+        sc = pick[rng.choice(len(pick), size=shape, p=[0.4, 0.3, 0.2, 0.04, 0.04, 0.01, 0.01])]
+    for chunk in (0, 1024):
+        ids = cskv.index_topk(to_dev_bf16(q), to_dev(codes), k, k_scale=to_dev(sc), chunk=chunk).cpu().numpy()
+        for b in range(B):
+            s = M.index_scores(F.bf16_to_f64(q[b]), F.decode_fp4_g16(codes[b], sc[b]))
+            assert np.array_equal(ids[b], M.topk_ids(s, k)), (case, chunk, b)
+
+
 def test_topk_ragged_entry_counts(cskv):
     B, N, Di, k = 6, 9000, 128, 512
     q, kk = _bf16_case(5, B, N, Di, 8)
