@@ -134,20 +134,30 @@ __device__ __forceinline__ void fold_c4a(const RowSlice<D>* lo, const RowSlice<D
   float m = g[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) m = fmaxf(m, g[j]);
-  float e[8], z = 0.0f;
+  // every lane holds the same 8 logits: lane j (mod 8) takes the exponential
+  // and the weight of state j once, and the fold reads them with readlane
+  // (the same operations on the same values, and the sum in the same order,
+  // as 8 exponentials and 8 divisions in every lane)
+  const int lane = lane_id();
+  float gl = g[0];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) { e[j] = expf(g[j] - m); z += e[j]; }
+  for (int j = 1; j < 8; ++j) gl = (lane & 7) == j ? g[j] : gl;
+  const float el = expf(gl - m);
+  float z = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) z += lane_value(el, j);
+  const float wl = el / z;
 #pragma unroll
   for (int i = 0; i < RowSlice<D>::CPL; ++i) acc[i] = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float w = e[j] / z;
+    const float w = lane_value(wl, j);
 #pragma unroll
     for (int i = 0; i < RowSlice<D>::CPL; ++i) acc[i] = fmaf(w, lo[j].v[i], acc[i]);
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float w = e[4 + j] / z;
+    const float w = lane_value(wl, 4 + j);
 #pragma unroll
     for (int i = 0; i < RowSlice<D>::CPL; ++i) acc[i] = fmaf(w, hi[j].v[i], acc[i]);
   }
@@ -208,42 +218,39 @@ __device__ __forceinline__ void fold_c128a(RowAt row_at, GateAt gate_at, float (
   constexpr int NW = kCompressThreads / kWave;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
-  // 4 batches of 8 states, the next batch's rows and logits loaded while the
-  // current one is folded; the first batch is loaded with the logits
+  // 4 batches of 8 states, the next batch's rows loaded while the current
+  // one is folded
   RowSlice<D> r[8], nx[8];
-  float gr[8], gn[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    load_row<D>(row_at(32 * wave + u), lane, r[u]);
-    gr[u] = gate_at(32 * wave + u);
-  }
-  // softmax over the 128 logits; every wave computes the same max and sum
+  for (int u = 0; u < 8; ++u) load_row<D>(row_at(32 * wave + u), lane, r[u]);
+  // softmax over the 128 logits; every wave computes the same max and sum.
+  // Lane l holds states l and l + 64 and takes their weights once; the fold
+  // reads state s's weight from lane s mod 64 with readlane (the same
+  // operations on the same values as one exponential and one division per
+  // state in every lane)
   const float g0 = gate_at(lane), g1 = gate_at(lane + 64);
   const float m = wave_max(fmaxf(g0, g1));
-  const float z = wave_sum(expf(g0 - m) + expf(g1 - m));
+  const float e0 = expf(g0 - m), e1 = expf(g1 - m);
+  const float z = wave_sum(e0 + e1);
+  const float w0 = e0 / z, w1 = e1 / z;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = 0.0f;
 #pragma unroll
   for (int j0 = 0; j0 < 32; j0 += 8) {
     if (j0 + 8 < 32) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        load_row<D>(row_at(32 * wave + j0 + 8 + u), lane, nx[u]);
-        gn[u] = gate_at(32 * wave + j0 + 8 + u);
-      }
+      for (int u = 0; u < 8; ++u) load_row<D>(row_at(32 * wave + j0 + 8 + u), lane, nx[u]);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float w = expf(gr[u] - m) / z;
+      const int st = 32 * wave + j0 + u;   // (wave-uniform)
+      const float w = lane_value(st < 64 ? w0 : w1, st & 63);
 #pragma unroll
       for (int i = 0; i < CPL; ++i) acc[i] = fmaf(w, r[u].v[i], acc[i]);
     }
     if (j0 + 8 < 32) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        r[u] = nx[u];
-        gr[u] = gn[u];
-      }
+      for (int u = 0; u < 8; ++u) r[u] = nx[u];
     }
   }
 #pragma unroll

@@ -276,6 +276,10 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 __device__ __forceinline__ int lane_value(int v, int src) {
   return __builtin_amdgcn_readlane(v, __builtin_amdgcn_readfirstlane(src));
 }
+// (the float's bits, not a conversion of its value)
+__device__ __forceinline__ float lane_value(float v, int src) {
+  return __int_as_float(lane_value(__float_as_int(v), src));
+}
 
 // Orderable key of a score: larger score -> larger key; -0 equals +0; NaN -> 0
 // (below every number, -inf included).
