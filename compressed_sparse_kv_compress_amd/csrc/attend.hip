@@ -11,7 +11,9 @@
 // and run on 16x16x32 bf16 MFMA. A workgroup (4 waves, one per compute unit)
 // owns one sequence and a contiguous split of its key slots; wave w owns heads
 // 16w .. 16w+15. Key rows move in tiles of 32 slots through a ring of four LDS
-// buffers, three tiles ahead of their use:
+// buffers, two (bf16 rows: the step that runs QK^T on a tile also runs PV on
+// the one before, so that slot is still in use) or three tiles ahead of
+// their use:
 //   - bf16 rows of 1 KiB go by direct HBM->LDS DMA (non-temporal, one wave
 //     instruction per row, no registers); fp8 rows go by DMA into a staging
 //     ring and one cooperative pass widens the codes to bf16 exactly, and the
