@@ -262,3 +262,50 @@ def test_far_negative_logits_with_empty_splits(cskv, sparse):
                         n_entries=None if nv is None else to_dev(nv), splits=splits)
         err = row_rel_err(O.cpu().numpy(), ref)
         assert err <= 2e-2, (splits, err)
+
+
+@pytest.mark.parametrize("B,H,k,W,R,fmt", [
+    (32, 64, 512, 128, 64, "bf16"),   # the c4a 128K layer
+    (8, 64, 512, 128, 64, "fp8"),     # the c4a 1M layer
+    (4, 64, 300, 40, 64, "bf16"),     # a ragged last tile
+    (16, 40, 100, 7, 0, "bf16"),      # heads not a multiple of 16, no rotation
+    (8, 64, 1100, 128, 64, "bf16"),   # more entries than the c4a layers select
+    (12, 64, 512, 0, 64, "fp8"),      # no window; a batch that is not a multiple of 8
+])
+def test_sparse_ragged_windows_match_oracle(cskv, B, H, k, W, R, fmt):
+    """Sparse reads at automatic splits and at one split against the oracle,
+    with ragged window counts (n_window) and some sequences ending in -1 ids."""
+    D, N = 512, 2500
+    seed = 900 + B + k
+    Q = _bf16(seed, synth.T_Q, (B, H, D))
+    rng = np.random.default_rng(seed)
+    ids = np.stack([sorted_ids(rng, N, k, n_valid=k - (7 if b % 5 == 2 else 0)) for b in range(B)])
+    nw = np.array([W - (13 * b) % (W + 1) for b in range(B)], dtype=np.int32)
+    pos = np.array([1000 + 4093 * b for b in range(B)], dtype=np.int64)
+    tau = 1 / np.sqrt(D)
+    extra = {}
+    if fmt == "bf16":
+        cache = _bf16(seed, synth.T_CACHE, (B, N, D))
+        win = _bf16(seed, synth.T_WIN, (B, W, D))
+        c64, w64 = F.bf16_to_f64(cache), F.bf16_to_f64(win)
+        cache_d, win_d = to_dev_bf16(cache), to_dev_bf16(win) if W else None
+        tol = 2e-2
+    else:
+        cache = synth.fp8_codes(synth.stream_key(seed, synth.T_CACHE), 0, B * N * D).reshape(B, N, D)
+        cs = synth.pos_scale(synth.stream_key(seed, synth.T_CACHE_SCALE), 0, B * N).reshape(B, N)
+        win = synth.fp8_codes(synth.stream_key(seed, synth.T_WIN), 0, B * W * D).reshape(B, W, D)
+        wsc = synth.pos_scale(synth.stream_key(seed, synth.T_WIN_SCALE), 0, B * W).reshape(B, W)
+        c64, w64 = F.decode_fp8_rows(cache, cs), F.decode_fp8_rows(win, wsc)
+        cache_d, win_d = to_dev(cache), to_dev(win) if W else None
+        extra = {"cache_scale": to_dev(cs)}
+        if W:
+            extra["window_scale"] = to_dev(wsc)
+        tol = 6e-2
+    Q64 = F.bf16_to_f64(Q)
+    ref = np.stack([M.attend(Q64[b], c64[b], ids[b], w64[b, :nw[b]] if nw[b] > 0 else None, tau, R, 10000.0,
+                             pos[b]) for b in range(B)])
+    for splits in (0, 1):
+        O = cskv.attend(to_dev_bf16(Q), cache_d, to_dev(ids), win_d, softmax_scale=tau, rope_dims=R,
+                        q_pos=to_dev(pos), n_window=to_dev(nw) if W else None, splits=splits, **extra)
+        err = row_rel_err(O.cpu().numpy(), ref)
+        assert err <= tol, (splits, err)
