@@ -309,3 +309,42 @@ def test_sparse_ragged_windows_match_oracle(cskv, B, H, k, W, R, fmt):
                         q_pos=to_dev(pos), n_window=to_dev(nw) if W else None, splits=splits, **extra)
         err = row_rel_err(O.cpu().numpy(), ref)
         assert err <= tol, (splits, err)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_attend_skips_invalid_ids(cskv, fmt):
+    """Ids past the cache (and -1 padding) stay out of the softmax for bf16 and
+    fp8 rows too, whether they fall in a tile whose 8 rows per wave all come
+    from the cache (scalar row addresses) or not, at several split counts."""
+    B, H, D, N, k, W, R = 2, 64, 512, 400, 256, 24, 64
+    seed = 31
+    rng = np.random.default_rng(seed)
+    ids = np.full((B, k), -1, dtype=np.int32)
+    ids[0, :100] = np.sort(rng.choice(N, size=100, replace=False))
+    ids[1, :] = np.sort(rng.choice(N, size=k, replace=False))
+    ids[1, 3] = N                          # first id past the cache
+    ids[1, 64:72] = N + np.arange(8)       # a whole wave's 8 rows of one tile
+    ids[1, 130] = (1 << 31) - 1
+    Q = _bf16(seed, synth.T_Q, (B, H, D))
+    if fmt == "bf16":
+        cache = _bf16(seed, synth.T_CACHE, (B, N, D))
+        win = _bf16(seed, synth.T_WIN, (B, W, D))
+        c64, w64 = F.bf16_to_f64(cache), F.bf16_to_f64(win)
+        args, extra, tol = (to_dev_bf16(cache), to_dev_bf16(win)), {}, 2e-2
+    else:
+        cache = synth.fp8_codes(synth.stream_key(seed, synth.T_CACHE), 0, B * N * D).reshape(B, N, D)
+        cs = synth.pos_scale(synth.stream_key(seed, synth.T_CACHE_SCALE), 0, B * N).reshape(B, N)
+        win = synth.fp8_codes(synth.stream_key(seed, synth.T_WIN), 0, B * W * D).reshape(B, W, D)
+        wsc = synth.pos_scale(synth.stream_key(seed, synth.T_WIN_SCALE), 0, B * W).reshape(B, W)
+        c64, w64 = F.decode_fp8_rows(cache, cs), F.decode_fp8_rows(win, wsc)
+        args, extra, tol = (to_dev(cache), to_dev(win)), {"cache_scale": to_dev(cs), "window_scale": to_dev(wsc)}, 6e-2
+    pos = np.array([321, 1 << 18], dtype=np.int64)
+    tau = 1 / np.sqrt(D)
+    Q64 = F.bf16_to_f64(Q)
+    ref = np.stack([M.attend(Q64[b], c64[b], ids[b][(ids[b] >= 0) & (ids[b] < N)], w64[b], tau, R, 10000.0, pos[b])
+                    for b in range(B)])
+    for splits in (0, 1, 3):
+        O = cskv.attend(to_dev_bf16(Q), args[0], to_dev(ids), args[1], softmax_scale=tau, rope_dims=R,
+                        q_pos=to_dev(pos), splits=splits, **extra)
+        err = row_rel_err(O.cpu().numpy(), ref)
+        assert err <= tol, (splits, err)
